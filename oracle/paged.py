@@ -1,0 +1,166 @@
+"""numpy fp64 oracle for paged decode attention (vectorised twin of pkv_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU baseline, never by the product path.  It shares no code with
+the HIP library, nor with the C oracle beside it: format decoders, layout
+offsets and arithmetic are written out again here.
+
+Definition followed (first page, TensorRT-LLM concept page: "key mechanisms"
+for pages and the page table, "compile-time graph optimization" for the
+page-table lookup on cache reads and writes, "runtime execution model" for
+decode reading and updating the pages): with g = h // (Hq // Hkv) and
+L = seq_lens[b], token t of sequence b lives in slot t % P of page
+block_tables[b, t // P]; the output is softmax(scale * q K^T) V over those
+L tokens, computed in fp64 after exact widening of the stored elements, with
+fp8 elements multiplied by their (page, kv head) scale.  L = 0 gives zeros.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+# ---------------------------------------------------------------- decoding ----
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp64: the pattern is the upper half of a binary32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _e4m3_table() -> np.ndarray:
+    """All 256 OCP e4m3fn codes: bias 7, subnormal m * 2**-9, S.1111.111 = NaN."""
+    t = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        s, e, m = code >> 7, (code >> 3) & 0xF, code & 0x7
+        if e == 0xF and m == 0x7:
+            v = math.nan
+        elif e == 0:
+            v = m * 2.0 ** -9
+        else:
+            v = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        t[code] = -v if s else v
+    return t
+
+
+E4M3_TABLE = _e4m3_table()
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_to_f64(x)
+    if dtype == "fp8":
+        return e4m3_to_f64(x)
+    raise ValueError(dtype)
+
+
+# ------------------------------------------------------------------ layout ----
+
+def _offsets(P: int, D: int, kv_dtype: str):
+    """Element offsets inside one (page, head) chunk, as [P, D] arrays (K, V)."""
+    E = 16 // ELEM_BYTES[kv_dtype]
+    TB = 4 * E
+    j = np.arange(P).reshape(P, 1)
+    d = np.arange(D).reshape(1, D)
+    k = (d // E * P + j) * E + d % E
+    blk, r = j // TB, j % TB
+    v = blk * (TB * D) + ((r % 16) // 4 * D + d) * E + (4 * (r // 16) + r % 4)
+    return k, v
+
+
+def gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b):
+    """Stored K, V elements of sequence b in logical order: [Hkv, L, D] each."""
+    NP, Hkv, PD = k_pool.shape
+    D = PD // P
+    L = max(int(seq_lens[b]), 0)
+    koff, voff = _offsets(P, D, kv_dtype)
+    t = np.arange(L)
+    pages = np.asarray(block_tables[b])[t // P].astype(np.int64)
+    if L and (pages.min() < 0 or pages.max() >= NP):
+        raise IndexError("page id out of range")
+    slot = t % P
+    k = k_pool[pages[None, :, None], np.arange(Hkv)[:, None, None], koff[slot][None, :, :]]
+    v = v_pool[pages[None, :, None], np.arange(Hkv)[:, None, None], voff[slot][None, :, :]]
+    return k, v, pages
+
+
+def decode_row_group(q_rows, k, v, scale):
+    """fp64 attention of G query rows [G, D] over keys/values [L, D]."""
+    s = float(scale) * (q_rows @ k.T)                     # [G, L]
+    m = s.max(axis=1, keepdims=True)
+    w = np.exp(s - m)
+    return (w @ v) / w.sum(axis=1, keepdims=True)
+
+
+def decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens, Hq, P, scale,
+           k_scales=None, v_scales=None, batches=None):
+    """fp64 [B, Hq, D] outputs (rows of sequences not in ``batches`` stay zero)."""
+    B = len(seq_lens)
+    NP, Hkv, PD = k_pool.shape
+    D = PD // P
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    qf = widen(q, q_dtype).reshape(B, Hq, D)
+    for b in (range(B) if batches is None else batches):
+        if int(seq_lens[b]) <= 0:
+            continue
+        k, v, pages = gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b)
+        kf, vf = widen(k, kv_dtype), widen(v, kv_dtype)
+        if kv_dtype == "fp8":
+            kf = kf * np.asarray(k_scales, np.float64)[pages].T[:, :, None]
+            vf = vf * np.asarray(v_scales, np.float64)[pages].T[:, :, None]
+        for g in range(Hkv):
+            out[b, g * G:(g + 1) * G] = decode_row_group(qf[b, g * G:(g + 1) * G], kf[g], vf[g], scale)
+    return out
+
+
+def append(k_new, v_new, kv_dtype, block_tables, seq_lens, k_pool, v_pool, P):
+    """In place: token L-1 of each sequence (L = seq_lens[b] >= 1) into its page slot."""
+    NP, Hkv, PD = k_pool.shape
+    D = PD // P
+    koff, voff = _offsets(P, D, kv_dtype)
+    for b in range(len(seq_lens)):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        t = L - 1
+        pg = int(block_tables[b][t // P])
+        if not 0 <= pg < NP:
+            raise IndexError("page id out of range")
+        k_pool[pg][:, koff[t % P]] = k_new[b]          # k_pool[pg] is a view
+        v_pool[pg][:, voff[t % P]] = v_new[b]
+
+
+# ------------------------------------------------- split-KV partitions -------
+
+def partition_partials(q_rows, k, v, scale, part):
+    """Per partition of ``part`` tokens: normalised output and log-sum-exp.
+
+    Returns (o [S, G, D], lse [S, G]); lse_s = m_s + ln sum exp(s_t - m_s).
+    """
+    L = k.shape[0]
+    outs, lses = [], []
+    for t0 in range(0, L, part):
+        s = float(scale) * (q_rows @ k[t0:t0 + part].T)
+        m = s.max(axis=1, keepdims=True)
+        w = np.exp(s - m)
+        l = w.sum(axis=1, keepdims=True)
+        outs.append((w @ v[t0:t0 + part]) / l)
+        lses.append((m + np.log(l))[:, 0])
+    return np.stack(outs), np.stack(lses)
+
+
+def merge_partials(o, lse):
+    """Combine partition results: weights exp(lse_s - max lse), normalised."""
+    M = lse.max(axis=0, keepdims=True)
+    w = np.exp(lse - M)                                   # [S, G]
+    return (w[:, :, None] * o).sum(axis=0) / w.sum(axis=0)[:, None]
