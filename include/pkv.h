@@ -1,0 +1,179 @@
+/*
+ * pkv.h - paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Every pointer argument is DEVICE memory owned by the
+ * caller unless stated otherwise; the library allocates and frees nothing.
+ * Calls are asynchronous and ordered on the given HIP stream (`stream` is a
+ * hipStream_t passed as void*, NULL = the null stream); they never synchronise
+ * and never read device memory from the host.  Pointers must stay valid until
+ * the stream work has completed.  Calls on different streams may run
+ * concurrently provided they do not write the same memory.
+ *
+ * Source of the operations.  The first page (TensorRT-LLM concept page,
+ * "key mechanisms" section) stores each sequence's K/V cache in fixed-size
+ * pages of, e.g., 64 or 128 tokens drawn from a shared pool, maps logical
+ * token positions to physical pages through a page table, and allocates new
+ * pages as a sequence grows.  Its "compile-time graph optimization" section
+ * puts a page-table lookup in front of every cache read and write, and its
+ * "runtime execution model" section has each decode iteration's attention
+ * read and update those pages, with the host passing the page tables in for
+ * every iteration.  The attention computed is single-query softmax attention
+ * softmax(scale * q K^T) V per query head over the tokens of its sequence.
+ *
+ * ---------------------------------------------------------------------------
+ * Shapes and notation
+ *   B   batch (sequences)          Hq  query heads     Hkv  kv heads
+ *   G = Hq / Hkv (query heads per kv head; query head h reads kv head h / G)
+ *   D   head dimension (64 or 128)  P   page size in tokens
+ *   NP  pages in the pool           MP  block-table width (pages per sequence)
+ *   L_b = seq_lens[b]
+ *
+ * Tensors (row-major, element types given by the dtype arguments)
+ *   q            [B][Hq][D]
+ *   out          [B][Hq][D]
+ *   k_new, v_new [B][Hkv][D]
+ *   block_tables int32 [B][MP]; entry j of row b is the physical page holding
+ *                tokens [j*P, (j+1)*P) of sequence b.  Entries at or past
+ *                ceil(L_b / P) are never read (may be -1).
+ *   seq_lens     int32 [B]; number of tokens of sequence b in the cache,
+ *                INCLUDING the token appended this step.  0 is allowed.
+ *   k_scales, v_scales  fp32 [NP][Hkv], fp8 cache only: stored value times
+ *                scale is the real value, one scale per (page, kv head).
+ *   k_pool, v_pool      NP * Hkv chunks, one per (page, kv head), each holding
+ *                P * D elements; chunk (pg, g) starts at element
+ *                (pg * Hkv + g) * P * D.
+ *
+ * Layout inside one chunk.  Let E = 16 / (element bytes) (fp32 4, bf16 8,
+ * fp8 16) and TB = 4 * E.  For token slot j in [0, P) and dimension d:
+ *   K (j, d) at element ((d / E) * P + j) * E + d % E
+ *   V (j, d) at element blk * TB * D + (c * D + d) * E + e, where
+ *            blk = j / TB, r = j % TB, c = (r % 16) / 4, e = 4 * (r / 16) + r % 4
+ * i.e. each 16-byte group holds E consecutive dimensions of one token for K,
+ * and E tokens of one dimension for V, arranged so that a 64-lane wavefront
+ * reading one 16-byte group per lane receives matrix-core operand fragments
+ * directly.  P must be a multiple of TB (fp32: 16, bf16: 32, fp8: 64).
+ * ---------------------------------------------------------------------------
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+/* Return codes.  0 is success; every failure is negative and leaves all device
+ * memory untouched (arguments are checked before anything is launched). */
+enum {
+  PKV_OK = 0,
+  PKV_E_NULL = -1,      /* a required pointer is NULL                       */
+  PKV_E_SHAPE = -2,     /* unsupported or inconsistent sizes                 */
+  PKV_E_DTYPE = -3,     /* unsupported dtype combination                     */
+  PKV_E_WORKSPACE = -4, /* workspace NULL or smaller than required           */
+  PKV_E_HIP = -5        /* a HIP runtime call or kernel launch failed        */
+};
+
+/* kv_append - write this step's new K/V token of every sequence into its page.
+ *
+ * The "paged store" of the first page ("key mechanisms"), preceded by the
+ * page-table lookup of its "compile-time graph optimization" section: for each
+ * b with L_b >= 1, token position t = L_b - 1 goes to slot t % P of page
+ * block_tables[b][t / P]; k_new[b][g][:] and v_new[b][g][:] are copied there
+ * bit for bit for every kv head g.  Sequences with L_b <= 0 are skipped.
+ *
+ * kv_dtype: element type of k_new/v_new and of the pools (any pkv_dtype; fp8
+ *   bytes are copied as given).
+ * Writes only the addressed slots of k_pool/v_pool.  Two sequences must not
+ * address the same slot in one call (the writes would race).  A page id
+ * outside [0, num_pages), or t / P >= max_pages_per_seq, skips that sequence.
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (sizes <= 0, D not 64/128, P not a multiple
+ * of TB or > 1024), PKV_E_DTYPE, PKV_E_HIP. */
+int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype,
+                  const int32_t* block_tables, int max_pages_per_seq,
+                  const int32_t* seq_lens, int batch,
+                  void* k_pool, void* v_pool, int num_pages,
+                  int num_kv_heads, int head_dim, int page_size, void* stream);
+
+/* Bytes of scratch that pkv_paged_attn_decode / pkv_paged_attn_decode_fp8 need
+ * for these sizes on the current HIP device (0 if the sizes are invalid).
+ * The workspace holds split-KV partial results (per-head running max, sum and
+ * unnormalised output of each partial range); it needs no initialisation and
+ * its contents after a call are unspecified. */
+size_t pkv_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim);
+
+/* paged_attn_decode - one decode step of attention over the paged cache.
+ *
+ * For b in [0,B), h in [0,Hq), g = h / G, tokens t < L_b read through the
+ * page table (see the header comment):
+ *   out[b][h][:] = sum_t softmax_t(scale * q[b][h] . k_t) v_t     (0 if L_b = 0)
+ * Each kv page chunk is read once per kv head and shared by its G query heads.
+ * Long sequences are split into ranges processed in parallel and combined by
+ * their log-sum-exp; partition_tokens chooses the range granularity: 0 lets
+ * the library choose, otherwise a positive multiple of TB (e.g. 512 tokens).
+ * Accumulation is fp32; out is rounded to nearest-even when bf16.
+ *
+ * Supported dtypes (q / kv / out): F32/F32/F32, BF16/BF16/BF16, BF16/BF16/F32.
+ * Sizes: D in {64, 128}; 1 <= G <= 16 with Hq % Hkv == 0; P a multiple of TB
+ * and <= 1024; batch >= 0 (batch 0 is a no-op).
+ * Page ids used must lie in [0, num_pages) and L_b <= MP * P; a row whose
+ * sequence breaks this gets NaN outputs (nothing outside the pools is read).
+ * workspace: device memory of at least pkv_decode_workspace_bytes(...) bytes.
+ * Writes out and workspace only. */
+int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype,
+                          const void* k_pool, const void* v_pool, pkv_dtype kv_dtype,
+                          const int32_t* block_tables, int max_pages_per_seq,
+                          const int32_t* seq_lens, int batch, int num_pages,
+                          int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                          float scale, int partition_tokens,
+                          void* out, pkv_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attn_decode_fp8 - as pkv_paged_attn_decode for an fp8 e4m3 cache.
+ *
+ * The pools hold OCP fp8 e4m3 ("fn") bytes; real value = decoded byte times
+ * k_scales / v_scales [page][kv head].  Following the first page ("key
+ * mechanisms": FP8 data is widened to 16 bits before the matrix product and
+ * accumulated wide), bytes are widened exactly in registers; the K scale is
+ * folded into the logits and the V scale into the probabilities; accumulation
+ * is fp32.  q is BF16; out is BF16 or F32.  Same sizes and errors as above,
+ * plus PKV_E_NULL when a scale pointer is NULL. */
+int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype,
+                              const void* k_pool, const void* v_pool,
+                              const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables, int max_pages_per_seq,
+                              const int32_t* seq_lens, int batch, int num_pages,
+                              int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                              float scale, int partition_tokens,
+                              void* out, pkv_dtype out_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* debug_gather - copy each sequence's cached tokens out of the pages into
+ * contiguous rows, through the same page-table lookup and chunk addressing
+ * the decode kernels use (for bit-exact tests of that address path).
+ * k_out, v_out: [B][Hkv][max_pages_per_seq * P][D] elements of kv_dtype; row
+ * t < L_b of (b, g) receives token t; rows at or past L_b are not written.
+ * Sequences with a bad page id or L_b > MP * P are skipped entirely. */
+int pkv_debug_gather(const void* k_pool, const void* v_pool, pkv_dtype kv_dtype,
+                     const int32_t* block_tables, int max_pages_per_seq,
+                     const int32_t* seq_lens, int batch, int num_pages,
+                     int num_kv_heads, int head_dim, int page_size,
+                     void* k_out, void* v_out, void* stream);
+
+/* Static text for a return code. */
+const char* pkv_strerror(int code);
+
+/* Detail of the last failure on the calling thread ("" if none).  The string
+ * is thread-local and valid until the thread's next pkv call. */
+const char* pkv_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,97 @@
+"""Paged KV-cache decode attention for MI355X (gfx950): Python binding of libpkv.so.
+
+Argument marshalling only.  Every step runs in the HIP kernels of
+``csrc/``; tensors are torch tensors used as device memory, and work is
+queued on torch's current HIP stream.  The functions mirror the C ABI in
+``include/pkv.h`` (same names without the ``pkv_`` prefix).
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._native import NativeLibraryMissing, lib  # noqa: F401
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        L = lib()
+        msg = L.pkv_last_error().decode() or L.pkv_strerror(code).decode()
+        super().__init__(f"{fn} failed ({code}): {msg}")
+        self.code = code
+
+
+def _code(dtype) -> int:
+    return _DTYPE_CODE[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise PkvError(fn, rc)
+
+
+def kv_append(k_new, v_new, kv_dtype, block_tables, seq_lens, k_pool, v_pool,
+              num_kv_heads, head_dim, page_size, stream=None):
+    """Write each sequence's new token (position seq_lens[b]-1) into its page."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("kv_append", lib().pkv_kv_append(
+        _ptr(k_new), _ptr(v_new), _code(kv_dtype), _ptr(block_tables), MP, _ptr(seq_lens), B,
+        _ptr(k_pool), _ptr(v_pool), NP, num_kv_heads, head_dim, page_size, _stream(stream)))
+
+
+def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim) -> int:
+    return int(lib().pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim))
+
+
+def paged_attn_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens,
+                      num_q_heads, num_kv_heads, head_dim, page_size, scale, out, out_dtype,
+                      workspace, partition_tokens=0, stream=None):
+    """softmax(scale * q K^T) V over each sequence's pages (f32 or bf16 cache)."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("paged_attn_decode", lib().pkv_paged_attn_decode(
+        _ptr(q), _code(q_dtype), _ptr(k_pool), _ptr(v_pool), _code(kv_dtype), _ptr(block_tables),
+        MP, _ptr(seq_lens), B, NP, num_q_heads, num_kv_heads, head_dim, page_size, float(scale),
+        int(partition_tokens), _ptr(out), _code(out_dtype), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def paged_attn_decode_fp8(q, q_dtype, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                          num_q_heads, num_kv_heads, head_dim, page_size, scale, out, out_dtype,
+                          workspace, partition_tokens=0, stream=None):
+    """As paged_attn_decode for an fp8 e4m3 cache with per-(page, kv head) scales."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("paged_attn_decode_fp8", lib().pkv_paged_attn_decode_fp8(
+        _ptr(q), _code(q_dtype), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), MP, _ptr(seq_lens), B, NP, num_q_heads, num_kv_heads, head_dim,
+        page_size, float(scale), int(partition_tokens), _ptr(out), _code(out_dtype), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def debug_gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, num_kv_heads, head_dim,
+                 page_size, k_out, v_out, stream=None):
+    """Copy cached tokens to contiguous [B, Hkv, MP*P, D] rows (tests of the address path)."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("debug_gather", lib().pkv_debug_gather(
+        _ptr(k_pool), _ptr(v_pool), _code(kv_dtype), _ptr(block_tables), MP, _ptr(seq_lens), B, NP,
+        num_kv_heads, head_dim, page_size, _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def version() -> int:
+    return int(lib().pkv_version())

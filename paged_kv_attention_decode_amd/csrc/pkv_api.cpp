@@ -1,0 +1,208 @@
+// C-ABI entry points of libpkv.so (declared in include/pkv.h): argument
+// validation, workspace sizing and dispatch to the HIP kernels.  Every check
+// runs before any HIP call, so invalid arguments never touch the device.
+#include "pkv.h"
+
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3; }
+
+// Shared size checks for every entry point that reads the pools.
+int check_pool_shape(int kv_dtype, int max_pages, int batch, int num_pages, int num_kv_heads,
+                     int head_dim, int page_size) {
+  if (!valid_dtype(kv_dtype)) return fail(PKV_E_DTYPE, "unknown kv dtype %d", kv_dtype);
+  if (batch < 0) return fail(PKV_E_SHAPE, "batch %d < 0", batch);
+  if (max_pages <= 0 || num_pages <= 0 || num_kv_heads <= 0)
+    return fail(PKV_E_SHAPE, "max_pages_per_seq %d, num_pages %d, num_kv_heads %d must be > 0",
+                max_pages, num_pages, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_E_SHAPE, "head_dim %d not supported (64 or 128)", head_dim);
+  const int tb = pkv::v_block_tokens(kv_dtype);
+  if (page_size <= 0 || page_size > 1024 || page_size % tb)
+    return fail(PKV_E_SHAPE, "page_size %d must be a positive multiple of %d and <= 1024", page_size, tb);
+  return PKV_OK;
+}
+
+int check_decode(const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                 const int32_t* block_tables, int max_pages, const int32_t* seq_lens, int batch,
+                 int num_pages, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                 int partition_tokens, const void* out, int out_dtype, const void* workspace,
+                 size_t workspace_bytes) {
+  if (batch > 0 && (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out || !workspace))
+    return fail(PKV_E_NULL, "a required pointer is NULL");
+  int rc = check_pool_shape(kv_dtype, max_pages, batch, num_pages, num_kv_heads, head_dim, page_size);
+  if (rc) return rc;
+  const int want_q = kv_dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
+  if (q_dtype != want_q)
+    return fail(PKV_E_DTYPE, "q dtype %d unsupported with kv dtype %d (need %d)", q_dtype, kv_dtype, want_q);
+  if (out_dtype != PKV_F32 && !(out_dtype == PKV_BF16 && kv_dtype != PKV_F32))
+    return fail(PKV_E_DTYPE, "out dtype %d unsupported with kv dtype %d", out_dtype, kv_dtype);
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(PKV_E_SHAPE, "num_q_heads %d not a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (G > 16) return fail(PKV_E_SHAPE, "group size %d > 16", G);
+  const int tb = pkv::v_block_tokens(kv_dtype);
+  if (partition_tokens < 0 || partition_tokens % tb)
+    return fail(PKV_E_SHAPE, "partition_tokens %d must be 0 or a positive multiple of %d", partition_tokens, tb);
+  if (batch > 0) {
+    const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim);
+    if (need == 0) return fail(PKV_E_HIP, "could not query the current HIP device");
+    if (workspace_bytes < need)
+      return fail(PKV_E_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  }
+  return PKV_OK;
+}
+
+int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+               const float* k_scales, const float* v_scales, const int32_t* block_tables,
+               int max_pages, const int32_t* seq_lens, int batch, int num_pages, int num_q_heads,
+               int num_kv_heads, int head_dim, int page_size, float scale, int partition_tokens,
+               void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_pages, seq_lens, batch,
+                        num_pages, num_q_heads, num_kv_heads, head_dim, page_size, partition_tokens,
+                        out, out_dtype, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (batch == 0) return PKV_OK;
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.partials = static_cast<float*>(workspace);
+  a.kvt = kv_dtype;
+  a.out_bf16 = out_dtype == PKV_BF16;
+  a.batch = batch;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.page_size = page_size;
+  // Default range granularity: one decode step (the V block), the finest split.
+  a.partition_tokens = partition_tokens ? partition_tokens : pkv::v_block_tokens(kv_dtype);
+  a.scale = scale;
+  hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char* pkv_strerror(int code) {
+  switch (code) {
+    case PKV_OK: return "success";
+    case PKV_E_NULL: return "null pointer argument";
+    case PKV_E_SHAPE: return "unsupported or inconsistent sizes";
+    case PKV_E_DTYPE: return "unsupported dtype combination";
+    case PKV_E_WORKSPACE: return "workspace missing or too small";
+    case PKV_E_HIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+size_t pkv_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim) {
+  if (batch < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0)
+    return 0;
+  const int cus = pkv::device_cu_count();
+  if (cus <= 0) return 0;
+  const size_t G = (size_t)(num_q_heads / num_kv_heads);
+  // two partial slots (first and last range) per resident wave
+  return 2 * (size_t)cus * pkv::kMaxWavesPerCU * G * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype, const int32_t* block_tables,
+                  int max_pages_per_seq, const int32_t* seq_lens, int batch, void* k_pool, void* v_pool,
+                  int num_pages, int num_kv_heads, int head_dim, int page_size, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && (!k_new || !v_new || !block_tables || !seq_lens || !k_pool || !v_pool))
+    return fail(PKV_E_NULL, "a required pointer is NULL");
+  int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
+  if (rc) return rc;
+  if (batch == 0) return PKV_OK;
+  pkv::AppendArgs a{k_new, v_new, block_tables, seq_lens, k_pool, v_pool, (int)kv_dtype, batch,
+                    max_pages_per_seq, num_pages, num_kv_heads, head_dim, page_size};
+  hipError_t e = pkv::launch_append(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return PKV_OK;
+}
+
+int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
+                          pkv_dtype kv_dtype, const int32_t* block_tables, int max_pages_per_seq,
+                          const int32_t* seq_lens, int batch, int num_pages, int num_q_heads,
+                          int num_kv_heads, int head_dim, int page_size, float scale,
+                          int partition_tokens, void* out, pkv_dtype out_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (kv_dtype == PKV_FP8_E4M3)
+    return fail(PKV_E_DTYPE, "fp8 cache: use pkv_paged_attn_decode_fp8 (it carries the scales)");
+  return run_decode(q, q_dtype, k_pool, v_pool, kv_dtype, nullptr, nullptr, block_tables, max_pages_per_seq,
+                    seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
+                    partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
+                              const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                              int max_pages_per_seq, const int32_t* seq_lens, int batch, int num_pages,
+                              int num_q_heads, int num_kv_heads, int head_dim, int page_size, float scale,
+                              int partition_tokens, void* out, pkv_dtype out_dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 scales are NULL");
+  return run_decode(q, q_dtype, k_pool, v_pool, PKV_FP8_E4M3, k_scales, v_scales, block_tables,
+                    max_pages_per_seq, seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim,
+                    page_size, scale, partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pkv_debug_gather(const void* k_pool, const void* v_pool, pkv_dtype kv_dtype, const int32_t* block_tables,
+                     int max_pages_per_seq, const int32_t* seq_lens, int batch, int num_pages,
+                     int num_kv_heads, int head_dim, int page_size, void* k_out, void* v_out, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && (!k_pool || !v_pool || !block_tables || !seq_lens || !k_out || !v_out))
+    return fail(PKV_E_NULL, "a required pointer is NULL");
+  int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
+  if (rc) return rc;
+  if (batch == 0) return PKV_OK;
+  pkv::GatherArgs a{k_pool, v_pool, block_tables, seq_lens, k_out, v_out, (int)kv_dtype, batch,
+                    max_pages_per_seq, num_pages, num_kv_heads, head_dim, page_size};
+  hipError_t e = pkv::launch_gather(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal host interface between the C-ABI entry points (pkv_api.cpp) and the
+// HIP kernels (pkv_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+// Tokens per 16-byte V group block (and per decode step): 4 * (16 / element bytes).
+inline int v_block_tokens(int kvt) { return kvt == KV_F32 ? 16 : kvt == KV_BF16 ? 32 : 64; }
+inline int elem_bytes(int kvt) { return kvt == KV_F32 ? 4 : kvt == KV_BF16 ? 2 : 1; }
+
+// Upper bound on decode wavefronts per compute unit; sizes the partial-result
+// workspace together with the device's compute-unit count.
+constexpr int kMaxWavesPerCU = 16;
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* k_pool;
+  void* v_pool;
+  int kvt, batch, max_pages, num_pages, num_kv_heads, head_dim, page_size;
+};
+
+struct GatherArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* k_out;
+  void* v_out;
+  int kvt, batch, max_pages, num_pages, num_kv_heads, head_dim, page_size;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scales;   // fp8 only
+  const float* v_scales;   // fp8 only
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* out;
+  float* partials;         // workspace
+  int kvt;                 // KvType; q is f32 for KV_F32, bf16 otherwise
+  bool out_bf16;
+  int batch, max_pages, num_pages, num_q_heads, num_kv_heads, head_dim, page_size;
+  int partition_tokens;    // > 0, multiple of v_block_tokens(kvt)
+  float scale;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+// Launches the split decode kernel and the log-sum-exp merge kernel.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Compute units of the current device (cached per device); <= 0 on failure.
+int device_cu_count();
+
+}  // namespace pkv

@@ -1,0 +1,707 @@
+// HIP kernels for paged KV-cache decode attention on CDNA4 (gfx950).
+//
+// Operations (first page, TensorRT-LLM concept page): the cache is kept in
+// fixed-size pages reached through a per-sequence page table ("key mechanisms");
+// a page-table lookup precedes every cache read and write ("compile-time graph
+// optimization"); each decode iteration's attention reads the pages and the
+// new token is stored into them ("runtime execution model").  The attention is
+// softmax(scale * q K^T) V per query head; long caches are split into ranges
+// combined by log-sum-exp, the rule FlashAttention-style kernels (named on the
+// first page's "compile-time graph optimization" section and the fourth page)
+// use to merge partial softmax results.
+//
+// Design for gfx950
+// -----------------
+// * One wavefront owns a contiguous, equal share of all (sequence, kv head,
+//   range) work units, so every wave streams the same number of bytes and the
+//   grid drains together; the share is derived on the device from seq_lens.
+// * A kv page chunk is read once per kv head: the G query heads of the group are
+//   the N columns of 16x16 MFMA tiles (padded to 16).
+// * The page layout puts each 16-byte group where a lane needs it as an MFMA
+//   operand: K groups hold E consecutive dims of one token (QK^T A operand,
+//   tokens = M), V groups hold E tokens of one dim (PV A operand, dims = M), so
+//   K and V go from HBM straight into operand registers with 256-byte
+//   contiguous runs per 16 lanes and no LDS round trip.
+// * The QK^T output layout (lane = head column, 4 token rows per lane) is
+//   exactly the PV B-operand layout, so probabilities never cross lanes.
+// * Online softmax in the log2 domain; the running max needs two cross-lane
+//   steps per tile; the running sum stays lane-local until the end.
+// * Probabilities enter the bf16 MFMA as a hi + lo bf16 pair (~16 bits).
+// * fp8 e4m3 is widened exactly to bf16 in registers; the K scale multiplies
+//   the logits, the V scale the probabilities.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int KVT> struct Kv;
+template <> struct Kv<KV_F32> { static constexpr int EB = 4; typedef uint32_t elem_t; };
+template <> struct Kv<KV_BF16> { static constexpr int EB = 2; typedef uint16_t elem_t; };
+template <> struct Kv<KV_FP8> { static constexpr int EB = 1; typedef uint8_t elem_t; };
+
+// ---------------------------------------------------------------------------
+// Chunk addressing shared by every kernel.  A (page, kv head) chunk holds P
+// tokens x D elements; E = 16 / element bytes; V blocks hold TB = 4E tokens.
+// ---------------------------------------------------------------------------
+template <int E>
+__device__ __forceinline__ int k_elem(int j, int d, int P) {
+  return ((d / E) * P + j) * E + (d % E);
+}
+template <int E>
+__device__ __forceinline__ int v_elem(int j, int d, int D) {
+  constexpr int TB = 4 * E;
+  const int blk = j / TB, r = j % TB;
+  const int c = (r & 15) >> 2, e = 4 * (r >> 4) + (r & 3);
+  return blk * TB * D + (c * D + d) * E + e;
+}
+__device__ __forceinline__ size_t chunk_elem(int page, int g, int Hkv, int P, int D) {
+  return ((size_t)page * (size_t)Hkv + (size_t)g) * (size_t)P * (size_t)D;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level helpers (64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int x = __shfl_up(v, o);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+__device__ __forceinline__ float fbits(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t ubits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = ubits(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+// Upper halves of two fp32 words packed as (lo, hi) bf16 pair = truncation.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(ubits(hi), ubits(lo), 0x07060302u);
+}
+// p = hi + lo with hi, lo bf16 (truncated): ~16 significant bits of p.
+__device__ __forceinline__ u32x2_t split_pair(float a, float b) {
+  const float ra = a - fbits(ubits(a) & 0xffff0000u);
+  const float rb = b - fbits(ubits(b) & 0xffff0000u);
+  return u32x2_t{pack_hi16(a, b), pack_hi16(ra, rb)};
+}
+// Probabilities of two 16-token tiles (8 per lane) as hi and lo bf16x8 operands.
+__device__ __forceinline__ void split_probs(const float (&x)[4], const float (&y)[4], float mul,
+                                           u32x4_t& hi, u32x4_t& lo) {
+  const u32x2_t a = split_pair(x[0] * mul, x[1] * mul), b = split_pair(x[2] * mul, x[3] * mul);
+  const u32x2_t c = split_pair(y[0] * mul, y[1] * mul), d = split_pair(y[2] * mul, y[3] * mul);
+  hi = u32x4_t{a.x, b.x, c.x, d.x};
+  lo = u32x4_t{a.y, b.y, c.y, d.y};
+}
+// Four fp8 e4m3 bytes -> four bf16 (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  u32x2_t r;
+  r.x = pack_hi16(a.x, a.y);
+  r.y = pack_hi16(b.x, b.y);
+  return r;
+}
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const u32x2_t a = fp8x4_to_bf16x4(w0), b = fp8x4_to_bf16x4(w1);
+  return u32x4_t{a.x, a.y, b.x, b.y};
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t ld16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Work split.  Units are (b, g, range) in b-major, then g, then range order;
+// range r of (b, g) covers tokens [r*PT, min(L_b, (r+1)*PT)).  With T units and
+// at most Wmax waves, k = ceil(T / Wmax) and W = ceil(T / k) waves get work;
+// wave w owns units [floor(w*T/W), floor((w+1)*T/W)).
+// ---------------------------------------------------------------------------
+struct Split {
+  int64_t T;
+  int64_t W;
+};
+__device__ __forceinline__ Split make_split(int64_t T, int Wmax) {
+  Split s;
+  s.T = T;
+  const int64_t k = (T + Wmax - 1) / Wmax;
+  s.W = T > 0 ? (T + k - 1) / k : 0;
+  return s;
+}
+__device__ __forceinline__ int64_t range_begin(const Split& s, int64_t w) { return w * s.T / s.W; }
+// The wave whose range contains unit idx.
+__device__ __forceinline__ int64_t wave_of(const Split& s, int64_t idx) {
+  return ((idx + 1) * s.W - 1) / s.T;
+}
+__device__ __forceinline__ int ranges_of(int L, int PT) { return L > 0 ? (L + PT - 1) / PT : 0; }
+
+// ---------------------------------------------------------------------------
+// Decode: split kernel
+// ---------------------------------------------------------------------------
+template <int KVT, int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const void* __restrict__ q_, const uint8_t* __restrict__ kpool,
+    const uint8_t* __restrict__ vpool, const float* __restrict__ kscales,
+    const float* __restrict__ vscales, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, void* __restrict__ out_, float* __restrict__ partials,
+    int B, int MP, int NP, int Hq, int Hkv, int G, int P, int PT, int Wmax, float scale_log2) {
+  constexpr int EB = Kv<KVT>::EB;
+  constexpr int E = 16 / EB;        // elements per 16-byte group
+  constexpr int TS = 4 * E;         // tokens per step (= V block)
+  constexpr int NSUB = TS / 16;     // 16-token QK^T tiles per step
+  constexpr int NKK = D / (4 * E);  // K groups per lane per 16-token tile
+  constexpr int NDT = D / 16;       // 16-dim PV tiles
+  constexpr int NQ = KVT == KV_FP8 ? 2 * NKK : NKK;
+
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, c4 = lane >> 4;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+
+  // ---- this wave's unit range -------------------------------------------------
+  int np_sum = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int bb = b0 + lane;
+    np_sum += wave_sum(ranges_of(bb < B ? seq_lens[bb] : 0, PT));
+  }
+  const Split sp = make_split((int64_t)np_sum * Hkv, Wmax);
+  if (w >= sp.W) return;
+  const int64_t u0 = range_begin(sp, w), u1 = range_begin(sp, w + 1);
+
+  // sequence holding unit u0, and the number of units before it
+  int b = 0;
+  int64_t base = 0;
+  {
+    int64_t run = 0;
+    for (int b0 = 0;; b0 += 64) {
+      const int bb = b0 + lane;
+      const int np = ranges_of(bb < B ? seq_lens[bb] : 0, PT);
+      const int incl = wave_incl_scan(np, lane);
+      const uint64_t hit = __ballot(run + (int64_t)incl * Hkv > u0);
+      if (hit) {
+        const int f = __builtin_ctzll(hit);
+        b = b0 + f;
+        base = run + (int64_t)__shfl(incl - np, f) * Hkv;
+        break;
+      }
+      run += (int64_t)__shfl(incl, 63) * Hkv;
+    }
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  int Lb = seq_lens[b];
+  int npb = ranges_of(Lb, PT);
+
+  const float NEG_INF = -__builtin_inff();
+  const bool hv = r16 < G;
+
+  for (int64_t u = u0; u < u1;) {
+    const int64_t off = u - base;
+    const int g = (int)(off / npb);
+    const int rg = (int)(off - (int64_t)g * npb);
+    const int64_t S = base + (int64_t)g * npb, Eu = S + npb;
+    const int64_t ue = Eu < u1 ? Eu : u1;
+    const int tok0 = rg * PT;
+    const int tok1 = min(Lb, (int)(ue - S) * PT);
+    const bool complete = (u == S) && (ue == Eu);
+    const bool first = (u == u0);
+    const int h = g * G + r16;
+
+    // ---- query operand: B matrix of QK^T (K dim = head dims, N = heads) --------
+    u32x4_t qop[NQ];
+    if (KVT == KV_F32) {
+      const float* q = static_cast<const float*>(q_) + ((size_t)b * Hq + h) * D;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        qop[kk] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + (c4 + 4 * kk) * 4)) : u32x4_t{0, 0, 0, 0};
+    } else {
+      const uint16_t* q = static_cast<const uint16_t*>(q_) + ((size_t)b * Hq + h) * D;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        // bf16 cache: group kk covers dims 8*(c4+4kk) .. +8.
+        // fp8 cache: group kk covers dims 16*(c4+4kk) .. +16, split in two halves.
+        const int d0 = KVT == KV_BF16 ? 8 * (c4 + 4 * i) : 16 * (c4 + 4 * (i >> 1)) + 8 * (i & 1);
+        qop[i] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + d0)) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+
+    f32x4_t O[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = NEG_INF, l = 0.f;
+    bool bad = false;
+
+    int pgi = tok0 / P;
+    int j0 = tok0 - pgi * P;
+    const int32_t* btrow = bt + (size_t)b * MP;
+    for (int t = tok0; t < tok1; t += TS) {
+      const int page = pgi < MP ? btrow[pgi] : -1;
+      if ((unsigned)page >= (unsigned)NP) {
+        bad = true;
+      } else {
+        const size_t ch = chunk_elem(page, g, Hkv, P, D) * EB;
+        const uint8_t* kc = kpool + ch;
+        const uint8_t* vc = vpool + ch;
+        u32x4_t kr[NSUB][NKK], vr[NDT];
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+            kr[sub][kk] = ld16(kc + (size_t)k_elem<E>(j0 + 16 * sub + r16, (c4 + 4 * kk) * E, P) * EB);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          vr[dt] = ld16(vc + (size_t)v_elem<E>(j0 + 4 * c4, dt * 16 + r16, D) * EB);
+
+        float kmul = scale_log2, vmul = 1.f;
+        if (KVT == KV_FP8) {
+          kmul *= kscales[(size_t)page * Hkv + g];
+          vmul = vscales[(size_t)page * Hkv + g];
+        }
+
+        // ---- S = K q^T: rows = 16 tokens, columns = heads ----------------------
+        float s[NSUB][4];
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            if (KVT == KV_F32) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc = mfma_f32(fbits(kr[sub][kk][e]), fbits(qop[kk][e]), acc);
+            } else if (KVT == KV_BF16) {
+              acc = mfma_bf16(kr[sub][kk], qop[kk], acc);
+            } else {
+              acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][0], kr[sub][kk][1]), qop[2 * kk], acc);
+              acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][2], kr[sub][kk][3]), qop[2 * kk + 1], acc);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[sub][i] = acc[i] * kmul;
+        }
+
+        // ---- ragged last step: mask logits, zero V of absent tokens ------------
+        if (t + TS > tok1) {
+#pragma unroll
+          for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t + 16 * sub + 4 * c4 + i >= tok1) s[sub][i] = NEG_INF;
+          u32x4_t keep;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t msk = 0;
+#pragma unroll
+            for (int byte = 0; byte < 4; ++byte) {
+              const int e = (4 * k + byte) / EB;
+              const int tok = t + 16 * (e >> 2) + 4 * c4 + (e & 3);
+              if (tok < tok1) msk |= 0xffu << (8 * byte);
+            }
+            keep[k] = msk;
+          }
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) vr[dt] &= keep;
+        }
+
+        // ---- online softmax (log2 domain) ---------------------------------------
+        float tmax = NEG_INF;
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[sub][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mnew = fmaxf(m, tmax);
+        const float alpha = mnew == NEG_INF ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+        float p[NSUB][4];
+        float lsum = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[sub][i] = __builtin_amdgcn_exp2f(s[sub][i] - mnew);
+            lsum += p[sub][i];
+          }
+        l = l * alpha + lsum;
+        if (__ballot(mnew > m)) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+        }
+        m = mnew;
+
+        // ---- O^T += V^T P^T: rows = 16 dims, columns = heads ---------------------
+        if (KVT == KV_F32) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[dt] = mfma_f32(fbits(vr[dt][i]), p[0][i], O[dt]);
+        } else if (KVT == KV_BF16) {
+          u32x4_t ph, pl;
+          split_probs(p[0], p[1], 1.f, ph, pl);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            O[dt] = mfma_bf16(vr[dt], ph, O[dt]);
+            O[dt] = mfma_bf16(vr[dt], pl, O[dt]);
+          }
+        } else {
+          u32x4_t ph[2], pl[2];
+          split_probs(p[0], p[1], vmul, ph[0], pl[0]);
+          split_probs(p[2], p[3], vmul, ph[1], pl[1]);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const u32x4_t a0 = fp8x8_to_bf16x8(vr[dt][0], vr[dt][1]);
+            const u32x4_t a1 = fp8x8_to_bf16x8(vr[dt][2], vr[dt][3]);
+            O[dt] = mfma_bf16(a0, ph[0], O[dt]);
+            O[dt] = mfma_bf16(a0, pl[0], O[dt]);
+            O[dt] = mfma_bf16(a1, ph[1], O[dt]);
+            O[dt] = mfma_bf16(a1, pl[1], O[dt]);
+          }
+        }
+      }
+      j0 += TS;
+      if (j0 == P) {
+        j0 = 0;
+        ++pgi;
+      }
+    }
+
+    // ---- finish the segment ------------------------------------------------------
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    const float qnan = __builtin_nanf("");
+    if (complete) {
+      if (hv) {
+        const float inv = bad ? qnan : 1.f / lt;
+        const size_t o = ((size_t)b * Hq + h) * D + 4 * c4;
+        if (OUT_BF16) {
+          uint16_t* out = static_cast<uint16_t*>(out_);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            u32x2_t v;
+            v.x = bf16_rne(O[dt][0] * inv) | (bf16_rne(O[dt][1] * inv) << 16);
+            v.y = bf16_rne(O[dt][2] * inv) | (bf16_rne(O[dt][3] * inv) << 16);
+            *reinterpret_cast<u32x2_t*>(out + o + dt * 16) = v;
+          }
+        } else {
+          float* out = static_cast<float*>(out_);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            *reinterpret_cast<f32x4_t*>(out + o + dt * 16) = O[dt] * inv;
+        }
+      }
+    } else {
+      float* ps = partials + (size_t)(2 * w + (first ? 0 : 1)) * G * (D + 2);
+      if (hv) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<f32x4_t*>(ps + r16 * D + dt * 16 + 4 * c4) = O[dt];
+        if (c4 == 0) {
+          ps[G * D + r16] = bad ? qnan : m;
+          ps[G * D + G + r16] = lt;
+        }
+      }
+    }
+
+    // ---- next segment ------------------------------------------------------------
+    u = ue;
+    if (u < u1 && u == base + (int64_t)npb * Hkv) {
+      base = u;
+      do {
+        ++b;
+        Lb = seq_lens[b];
+        npb = ranges_of(Lb, PT);
+      } while (npb == 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: log-sum-exp merge of split ranges, and zero rows for empty sequences.
+// One workgroup per (b, g).
+// ---------------------------------------------------------------------------
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_merge_kernel(
+    const int32_t* __restrict__ seq_lens, const float* __restrict__ partials,
+    void* __restrict__ out_, int B, int Hq, int Hkv, int G, int D, int PT, int Wmax) {
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  __shared__ int red_tot[4], red_pre[4];
+  int tot = 0, pre = 0;
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    const int np = ranges_of(seq_lens[i], PT);
+    tot += np;
+    if (i < b) pre += np;
+  }
+  tot = wave_sum(tot);
+  pre = wave_sum(pre);
+  if ((threadIdx.x & 63) == 0) {
+    red_tot[threadIdx.x >> 6] = tot;
+    red_pre[threadIdx.x >> 6] = pre;
+  }
+  __syncthreads();
+  tot = red_tot[0] + red_tot[1] + red_tot[2] + red_tot[3];
+  pre = red_pre[0] + red_pre[1] + red_pre[2] + red_pre[3];
+
+  const int npb = ranges_of(seq_lens[b], PT);
+  if (npb == 0) {
+    for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+      const size_t o = ((size_t)b * Hq + g * G) * D + x;
+      if (OUT_BF16)
+        static_cast<uint16_t*>(out_)[o] = 0;
+      else
+        static_cast<float*>(out_)[o] = 0.f;
+    }
+    return;
+  }
+  const Split sp = make_split((int64_t)tot * Hkv, Wmax);
+  const int64_t S = (int64_t)pre * Hkv + (int64_t)g * npb, Eu = S + npb;
+  const int64_t wf = wave_of(sp, S);
+  if (wf == wave_of(sp, Eu - 1)) return;  // one wave covered it and wrote the output
+  const int stride = G * (D + 2);
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+    const int hh = x / D;
+    float M = -__builtin_inff();
+    for (int64_t w = wf;;) {
+      const int64_t slot = 2 * w + (range_begin(sp, w) >= S ? 0 : 1);
+      M = fmaxf(M, partials[slot * stride + G * D + hh]);
+      const int64_t nx = range_begin(sp, w + 1);
+      if (nx >= Eu) break;
+      w = wave_of(sp, nx);
+    }
+    float num = 0.f, den = 0.f;
+    bool nan = false;
+    for (int64_t w = wf;;) {
+      const int64_t slot = 2 * w + (range_begin(sp, w) >= S ? 0 : 1);
+      const float* ps = partials + slot * stride;
+      const float ms = ps[G * D + hh];
+      nan |= ms != ms;
+      const float f = __builtin_amdgcn_exp2f(ms - M);
+      num += f * ps[x];
+      den += f * ps[G * D + G + hh];
+      const int64_t nx = range_begin(sp, w + 1);
+      if (nx >= Eu) break;
+      w = wave_of(sp, nx);
+    }
+    const float r = nan ? __builtin_nanf("") : num / den;
+    const size_t o = ((size_t)b * Hq + g * G) * D + x;
+    if (OUT_BF16)
+      static_cast<uint16_t*>(out_)[o] = (uint16_t)bf16_rne(r);
+    else
+      static_cast<float*>(out_)[o] = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append: one workgroup per sequence; element-wise copy through the page table.
+// ---------------------------------------------------------------------------
+template <int KVT>
+__global__ __launch_bounds__(256) void append_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
+    void* __restrict__ kpool, void* __restrict__ vpool, int MP, int NP, int Hkv, int D, int P) {
+  typedef typename Kv<KVT>::elem_t T;
+  constexpr int E = 16 / Kv<KVT>::EB;
+  const int b = blockIdx.x;
+  const int L = seq_lens[b];
+  if (L <= 0) return;
+  const int t = L - 1, pgi = t / P, j = t - pgi * P;
+  if (pgi >= MP) return;
+  const int page = bt[(size_t)b * MP + pgi];
+  if ((unsigned)page >= (unsigned)NP) return;
+  const T* kn = static_cast<const T*>(k_new) + (size_t)b * Hkv * D;
+  const T* vn = static_cast<const T*>(v_new) + (size_t)b * Hkv * D;
+  for (int x = threadIdx.x; x < Hkv * D; x += blockDim.x) {
+    const int g = x / D, d = x - g * D;
+    const size_t ch = chunk_elem(page, g, Hkv, P, D);
+    static_cast<T*>(kpool)[ch + k_elem<E>(j, d, P)] = kn[x];
+    static_cast<T*>(vpool)[ch + v_elem<E>(j, d, D)] = vn[x];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Debug gather: contiguous copy of each sequence's tokens, same addressing.
+// ---------------------------------------------------------------------------
+template <int KVT>
+__global__ __launch_bounds__(256) void gather_kernel(
+    const void* __restrict__ kpool, const void* __restrict__ vpool,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
+    void* __restrict__ k_out, void* __restrict__ v_out, int MP, int NP, int Hkv, int D, int P) {
+  typedef typename Kv<KVT>::elem_t T;
+  constexpr int E = 16 / Kv<KVT>::EB;
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int L = seq_lens[b];
+  if (L <= 0 || L > MP * P) return;
+  const int npg = (L + P - 1) / P;
+  int ok = 1;
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+    const int pg = bt[(size_t)b * MP + i];
+    if ((unsigned)pg >= (unsigned)NP) ok = 0;
+  }
+  if (!__syncthreads_and(ok)) return;
+  const size_t rows = (size_t)MP * P;
+  T* ko = static_cast<T*>(k_out) + ((size_t)b * Hkv + g) * rows * D;
+  T* vo = static_cast<T*>(v_out) + ((size_t)b * Hkv + g) * rows * D;
+  for (size_t x = threadIdx.x; x < (size_t)L * D; x += blockDim.x) {
+    const int t = (int)(x / D), d = (int)(x - (size_t)t * D);
+    const int pgi = t / P, j = t - pgi * P;
+    const size_t ch = chunk_elem(bt[(size_t)b * MP + pgi], g, Hkv, P, D);
+    ko[x] = static_cast<const T*>(kpool)[ch + k_elem<E>(j, d, P)];
+    vo[x] = static_cast<const T*>(vpool)[ch + v_elem<E>(j, d, D)];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+struct DevInfo {
+  int cus = 0;
+};
+std::mutex g_mu;
+DevInfo g_dev[64];
+
+typedef void (*decode_fn_t)(const void*, const uint8_t*, const uint8_t*, const float*, const float*,
+                            const int32_t*, const int32_t*, void*, float*, int, int, int, int, int, int,
+                            int, int, int, float);
+
+template <int KVT, int D, bool OB>
+decode_fn_t decode_fn() {
+  return decode_split_kernel<KVT, D, OB>;
+}
+
+decode_fn_t pick_decode(int kvt, int D, bool ob) {
+#define PKV_PICK(K)                                                              \
+  if (kvt == K) {                                                                \
+    if (D == 64) return ob ? decode_fn<K, 64, true>() : decode_fn<K, 64, false>();  \
+    return ob ? decode_fn<K, 128, true>() : decode_fn<K, 128, false>();          \
+  }
+  PKV_PICK(KV_F32)
+  PKV_PICK(KV_BF16)
+  PKV_PICK(KV_FP8)
+#undef PKV_PICK
+  return nullptr;
+}
+
+// Resident decode waves per compute unit for one kernel instantiation (cached).
+int waves_per_cu(decode_fn_t fn, int dev) {
+  static std::mutex mu;
+  static struct {
+    decode_fn_t fn;
+    int dev;
+    int waves;
+  } cache[64];
+  static int n = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  for (int i = 0; i < n; ++i)
+    if (cache[i].fn == fn && cache[i].dev == dev) return cache[i].waves;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(fn), 256, 0) !=
+          hipSuccess ||
+      blocks <= 0)
+    blocks = 1;
+  int waves = blocks * 4;
+  if (waves > kMaxWavesPerCU) waves = kMaxWavesPerCU;
+  if (n < 64) cache[n++] = {fn, dev, waves};
+  return waves;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_dev[dev].cus <= 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    g_dev[dev].cus = cus;
+  }
+  return g_dev[dev].cus;
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.batch <= 0) return hipSuccess;
+  dim3 grid(a.batch), block(256);
+#define PKV_APPEND(K)                                                                              \
+  hipLaunchKernelGGL(append_kernel<K>, grid, block, 0, s, a.k_new, a.v_new, a.block_tables,        \
+                     a.seq_lens, a.k_pool, a.v_pool, a.max_pages, a.num_pages, a.num_kv_heads,     \
+                     a.head_dim, a.page_size)
+  if (a.kvt == KV_F32) PKV_APPEND(KV_F32);
+  else if (a.kvt == KV_BF16) PKV_APPEND(KV_BF16);
+  else PKV_APPEND(KV_FP8);
+#undef PKV_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+  if (a.batch <= 0) return hipSuccess;
+  dim3 grid(a.batch * a.num_kv_heads), block(256);
+#define PKV_GATHER(K)                                                                              \
+  hipLaunchKernelGGL(gather_kernel<K>, grid, block, 0, s, a.k_pool, a.v_pool, a.block_tables,      \
+                     a.seq_lens, a.k_out, a.v_out, a.max_pages, a.num_pages, a.num_kv_heads,       \
+                     a.head_dim, a.page_size)
+  if (a.kvt == KV_F32) PKV_GATHER(KV_F32);
+  else if (a.kvt == KV_BF16) PKV_GATHER(KV_BF16);
+  else PKV_GATHER(KV_FP8);
+#undef PKV_GATHER
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.batch <= 0) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int cus = device_cu_count();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  decode_fn_t fn = pick_decode(a.kvt, a.head_dim, a.out_bf16);
+  if (!fn) return hipErrorInvalidValue;
+  const int Wmax = cus * waves_per_cu(fn, dev);
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  dim3 grid((Wmax + 3) / 4), block(256);
+  hipLaunchKernelGGL(fn, grid, block, 0, s, a.q, static_cast<const uint8_t*>(a.k_pool),
+                     static_cast<const uint8_t*>(a.v_pool), a.k_scales, a.v_scales, a.block_tables,
+                     a.seq_lens, a.out, a.partials, a.batch, a.max_pages, a.num_pages, a.num_q_heads,
+                     a.num_kv_heads, G, a.page_size, a.partition_tokens, Wmax, scale_log2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 mgrid(a.batch * a.num_kv_heads);
+  if (a.out_bf16)
+    hipLaunchKernelGGL(decode_merge_kernel<true>, mgrid, block, 0, s, a.seq_lens, a.partials, a.out,
+                       a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim, a.partition_tokens, Wmax);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<false>, mgrid, block, 0, s, a.seq_lens, a.partials, a.out,
+                       a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim, a.partition_tokens, Wmax);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,90 @@
+"""Shared helpers for the GPU parity tests: upload a workload, run the HIP path
+through the C ABI, run the oracle on the same bytes, compare."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+import paged_kv_attention_decode_amd as pkv
+from oracle import c_oracle
+
+# Spec tolerances: bf16/fp32 cache: max-abs <= 1e-2 and mean-abs <= 1e-3;
+# fp8 e4m3 cache: max-abs <= 3e-2 (mean-abs reported).
+TOL = {"f32": (1e-2, 1e-3), "bf16": (1e-2, 1e-3), "fp8": (3e-2, None)}
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def dev_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def host_bytes(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+class DeviceWorkload:
+    """A workload's tensors resident in HBM."""
+
+    def __init__(self, wl, device="cuda"):
+        self.wl = wl
+        self.q = dev_tensor(wl.q, device)
+        self.k_pool = dev_tensor(wl.k_pool, device)
+        self.v_pool = dev_tensor(wl.v_pool, device)
+        self.bt = dev_tensor(wl.block_tables, device)
+        self.sl = dev_tensor(wl.seq_lens, device)
+        self.ks = None if wl.k_scales is None else dev_tensor(wl.k_scales, device)
+        self.vs = None if wl.v_scales is None else dev_tensor(wl.v_scales, device)
+        odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+        self.out = torch.empty((wl.B, wl.Hq, wl.D), dtype=odt, device=device)
+        nbytes = pkv.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+    def decode(self, seq_lens=None, partition_tokens=None, out=None):
+        wl = self.wl
+        sl = self.sl if seq_lens is None else seq_lens
+        pt = wl.partition_tokens if partition_tokens is None else partition_tokens
+        out = self.out if out is None else out
+        if wl.kv_dtype == "fp8":
+            pkv.paged_attn_decode_fp8(self.q, wl.q_dtype, self.k_pool, self.v_pool, self.ks, self.vs,
+                                      self.bt, sl, wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out,
+                                      wl.out_dtype, self.ws, pt)
+        else:
+            pkv.paged_attn_decode(self.q, wl.q_dtype, self.k_pool, self.v_pool, wl.kv_dtype, self.bt,
+                                  sl, wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype,
+                                  self.ws, pt)
+        return out
+
+    def append(self, k_new, v_new, seq_lens):
+        wl = self.wl
+        pkv.kv_append(k_new, v_new, wl.kv_dtype, self.bt, seq_lens, self.k_pool, self.v_pool,
+                      wl.Hkv, wl.D, wl.P)
+
+
+def oracle_decode(wl, k_pool=None, v_pool=None, seq_lens=None, pairs=None):
+    return c_oracle.decode(wl.q, wl.q_dtype, wl.k_pool if k_pool is None else k_pool,
+                           wl.v_pool if v_pool is None else v_pool, wl.kv_dtype, wl.block_tables,
+                           wl.seq_lens if seq_lens is None else seq_lens, wl.Hq, wl.P, wl.scale,
+                           wl.k_scales, wl.v_scales, pairs=pairs, nthreads=ORACLE_THREADS)
+
+
+def gpu_out(out: torch.Tensor) -> np.ndarray:
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = ""):
+    """Element-wise comparison at the benchmark spec's tolerance; returns (max, mean)."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(ref).all(), f"{what}: oracle produced non-finite values"
+    assert np.isfinite(got).all(), f"{what}: GPU produced non-finite values"
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    tmax, tmean = TOL[kv_dtype]
+    assert mx <= tmax, f"{what}: max-abs {mx:.3e} > {tmax}"
+    if tmean is not None:
+        assert mean <= tmean, f"{what}: mean-abs {mean:.3e} > {tmean}"
+    return mx, mean

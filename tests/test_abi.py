@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol that
+include/pkv.h declares, and rejects bad arguments before touching a device."""
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_decode_amd as pkv
+from paged_kv_attention_decode_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    syms = declared_symbols()
+    for name in ("pkv_kv_append", "pkv_paged_attn_decode", "pkv_paged_attn_decode_fp8",
+                 "pkv_decode_workspace_bytes", "pkv_debug_gather"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    L = pkv.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert set(declared_symbols()) == set(_native.SIGNATURES)
+
+
+def test_version_and_strerror():
+    assert pkv.version() == 100
+    L = pkv.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.pkv_strerror(code)
+    assert L.pkv_strerror(-99) == b"unknown error code"
+
+
+def _append(**over):
+    a = dict(k=1, v=1, dt=1, bt=1, mp=4, sl=1, b=2, kp=1, vp=1, np_=8, hkv=2, d=128, p=64)
+    a.update(over)
+    L = pkv.lib()
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return L.pkv_kv_append(vp(a["k"]), vp(a["v"]), a["dt"], vp(a["bt"]), a["mp"], vp(a["sl"]), a["b"],
+                           vp(a["kp"]), vp(a["vp"]), a["np_"], a["hkv"], a["d"], a["p"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=0), -1), (dict(bt=0), -1), (dict(d=96), -2), (dict(p=48), -2), (dict(p=2048), -2),
+    (dict(dt=7), -3), (dict(hkv=0), -2), (dict(mp=0), -2), (dict(b=-1), -2),
+    (dict(dt=2, p=32), -2), (dict(dt=0, p=16, k=0), -1),
+])
+def test_append_rejects_bad_arguments(over, code):
+    # Pointers are fake non-NULL host values: validation must fail before any use.
+    assert _append(**over) == code
+    assert pkv.lib().pkv_last_error()
+
+
+def test_batch_zero_is_a_noop_without_device():
+    assert _append(b=0, k=0, v=0) == 0
+
+
+def _decode(fn="pkv_paged_attn_decode", **over):
+    a = dict(q=1, qdt=1, kp=1, vp=1, kvdt=1, bt=1, mp=4, sl=1, b=2, np_=8, hq=8, hkv=2, d=128, p=64,
+             scale=0.1, pt=0, out=1, odt=1, ws=1, wsb=1 << 30)
+    a.update(over)
+    L = pkv.lib()
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    if fn == "pkv_paged_attn_decode":
+        return L.pkv_paged_attn_decode(vp(a["q"]), a["qdt"], vp(a["kp"]), vp(a["vp"]), a["kvdt"], vp(a["bt"]),
+                                       a["mp"], vp(a["sl"]), a["b"], a["np_"], a["hq"], a["hkv"], a["d"], a["p"],
+                                       a["scale"], a["pt"], vp(a["out"]), a["odt"], vp(a["ws"]), a["wsb"], None)
+    return L.pkv_paged_attn_decode_fp8(vp(a["q"]), a["qdt"], vp(a["kp"]), vp(a["vp"]), vp(a.get("ks", 1)),
+                                       vp(a.get("vs", 1)), vp(a["bt"]), a["mp"], vp(a["sl"]), a["b"], a["np_"],
+                                       a["hq"], a["hkv"], a["d"], a["p"], a["scale"], a["pt"], vp(a["out"]),
+                                       a["odt"], vp(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), -1), (dict(out=0), -1), (dict(ws=0), -1), (dict(kvdt=2), -3),
+    (dict(qdt=0), -3), (dict(kvdt=0, qdt=0, p=16, odt=1), -3), (dict(hq=9), -2), (dict(hq=64, hkv=2), -2),
+    (dict(d=80), -2), (dict(p=40), -2), (dict(pt=48), -2), (dict(pt=-32), -2), (dict(np_=0), -2),
+])
+def test_decode_rejects_bad_arguments(over, code):
+    assert _decode(**over) == code
+
+
+@pytest.mark.parametrize("over,code", [(dict(ks=0), -1), (dict(vs=0), -1), (dict(qdt=0), -3),
+                                       (dict(p=32), -2), (dict(pt=96), -2)])
+def test_decode_fp8_rejects_bad_arguments(over, code):
+    assert _decode("pkv_paged_attn_decode_fp8", **over) == code
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_native, "_lib", None)
+    monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(_native.NativeLibraryMissing):
+        _native.lib()

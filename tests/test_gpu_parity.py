@@ -1,0 +1,281 @@
+"""GPU parity: the HIP path through the C ABI against the CPU fp64 oracle.
+
+Appends and gathers must match byte for byte; attention outputs must satisfy
+max-abs <= 1e-2 and mean-abs <= 1e-3 (fp32 / bf16 cache) or max-abs <= 3e-2
+(fp8 e4m3 cache), element by element, on the same seeded bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_decode_amd as pkv
+from oracle import c_oracle, paged
+from workloads import codec, configs, layout
+
+from _helpers import DeviceWorkload, check_close, dev_tensor, gpu_out, host_bytes, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_vs_oracle(wl, what, partition_tokens=None):
+    dw = DeviceWorkload(wl)
+    out = dw.decode(partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    ref = oracle_decode(wl)
+    return check_close(gpu_out(out), ref, wl.kv_dtype, what)
+
+
+# ------------------------------------------------------------------ formats ----
+
+def test_fp8_codes_exhaustive_through_decode():
+    """Single-token sequences return their value row: all 256 e4m3 codes, scale 1."""
+    D, P = 128, 64
+    codes = np.arange(256, dtype=np.uint8).reshape(2, 1, 1, D)      # [B, L=1, Hkv=1, D]
+    kp = layout.empty_pool(4, 1, P, D, "fp8")
+    vp = layout.empty_pool(4, 1, P, D, "fp8")
+    bt = np.array([[2], [0]], np.int32)
+    for b in range(2):
+        layout.pack_sequence(kp, bt[b], np.zeros((1, 1, D), np.uint8), P, layout.k_chunk_index(P, D, "fp8"), "fp8")
+        layout.pack_sequence(vp, bt[b], codes[b, :1], P, layout.v_chunk_index(P, D, "fp8"), "fp8")
+    ones = np.ones((4, 1), np.float32)
+    q = codec.f32_to_bf16_bits(np.ones((2, 1, D), np.float32))
+    out = torch.empty((2, 1, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pkv.decode_workspace_bytes(2, 1, 1, D), dtype=torch.uint8, device="cuda")
+    pkv.paged_attn_decode_fp8(dev_tensor(q), "bf16", dev_tensor(kp), dev_tensor(vp), dev_tensor(ones),
+                              dev_tensor(ones), dev_tensor(bt), dev_tensor(np.array([1, 1], np.int32)),
+                              1, 1, D, P, 0.1, out, "f32", ws)
+    got = out.cpu().numpy().astype(np.float64).reshape(256)
+    ref = paged.E4M3_TABLE
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+# ------------------------------------------------------------- append/gather ----
+
+APPEND_CASES = [("f32", 16, 64), ("bf16", 32, 128), ("bf16", 64, 128), ("bf16", 128, 64),
+                ("fp8", 64, 128), ("fp8", 128, 64)]
+
+
+@pytest.mark.parametrize("kv_dtype,P,D", APPEND_CASES)
+def test_append_bit_exact(kv_dtype, P, D):
+    lens0 = [0, 1, P - 2, P - 1, P, 2 * P - 1, 3 * P + 5]
+    wl = configs.custom(seed=31, lens=[x + 2 for x in lens0], Hq=8, Hkv=4, D=D, P=P, kv_dtype=kv_dtype)
+    # start from the pool holding lens0 tokens: re-pack with the shorter lengths
+    ref_k = layout.empty_pool(wl.num_pages, wl.Hkv, P, D, kv_dtype)
+    ref_v = layout.empty_pool(wl.num_pages, wl.Hkv, P, D, kv_dtype)
+    ki, vi = layout.k_chunk_index(P, D, kv_dtype), layout.v_chunk_index(P, D, kv_dtype)
+    for b, n in enumerate(lens0):
+        k, v, _, _ = configs.seq_tokens(wl.seed, b, n, wl.Hkv, D, kv_dtype, P)
+        pages = wl.block_tables[b, :int(configs.pages_needed(np.array([n]), P)[0])]
+        layout.pack_sequence(ref_k, pages, k, P, ki, kv_dtype)
+        layout.pack_sequence(ref_v, pages, v, P, vi, kv_dtype)
+    dk, dv = dev_tensor(ref_k), dev_tensor(ref_v)
+    bt = dev_tensor(wl.block_tables)
+    rng = np.random.default_rng(5)
+    for step in range(2):
+        lens = np.array([x + step + 1 for x in lens0], np.int32)
+        lens[0] = 0 if step == 0 else lens[0]        # a sequence that does not append this step
+        kn = rng.integers(0, 255, (wl.B, wl.Hkv, D * layout.ELEM_BYTES[kv_dtype]), dtype=np.uint8)
+        vn = rng.integers(0, 255, (wl.B, wl.Hkv, D * layout.ELEM_BYTES[kv_dtype]), dtype=np.uint8)
+        kn = kn.view(layout.NP_DTYPE[kv_dtype])
+        vn = vn.view(layout.NP_DTYPE[kv_dtype])
+        pkv.kv_append(dev_tensor(kn), dev_tensor(vn), kv_dtype, bt, dev_tensor(lens), dk, dv, wl.Hkv, D, P)
+        c_oracle.append(kn, vn, kv_dtype, wl.block_tables, lens, ref_k, ref_v, P)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bytes(dk), ref_k.view(np.uint8).reshape(-1))
+        assert np.array_equal(host_bytes(dv), ref_v.view(np.uint8).reshape(-1))
+
+
+@pytest.mark.parametrize("kv_dtype,P,D", APPEND_CASES)
+def test_gather_bit_exact(kv_dtype, P, D):
+    wl = configs.custom(seed=32, lens=[1, P, P + 1, 3 * P - 1, 0], Hq=4, Hkv=2, D=D, P=P, kv_dtype=kv_dtype)
+    dw = DeviceWorkload(wl)
+    fill = layout.POISON[kv_dtype]
+    ko = torch.empty((wl.B, wl.Hkv, wl.max_pages * P, D), dtype=dw.k_pool.dtype, device="cuda")
+    vo = torch.empty_like(ko)
+    ko.view(torch.uint8).fill_(0xAB)
+    vo.view(torch.uint8).fill_(0xAB)
+    pkv.debug_gather(dw.k_pool, dw.v_pool, kv_dtype, dw.bt, dw.sl, wl.Hkv, D, P, ko, vo)
+    torch.cuda.synchronize()
+    rk, rv = c_oracle.gather(wl.k_pool, wl.v_pool, kv_dtype, wl.block_tables, wl.seq_lens, P, fill)
+    gk = ko.cpu().view(torch.uint8).numpy().reshape(wl.B, wl.Hkv, wl.max_pages * P, -1)
+    gv = vo.cpu().view(torch.uint8).numpy().reshape(wl.B, wl.Hkv, wl.max_pages * P, -1)
+    rk8 = rk.view(np.uint8).reshape(gk.shape)
+    rv8 = rv.view(np.uint8).reshape(gv.shape)
+    for b in range(wl.B):
+        L = int(wl.seq_lens[b])
+        assert np.array_equal(gk[b, :, :L], rk8[b, :, :L])
+        assert np.array_equal(gv[b, :, :L], rv8[b, :, :L])
+        assert (gk[b, :, L:] == 0xAB).all() and (gv[b, :, L:] == 0xAB).all()
+
+
+# ------------------------------------------------------------ decode: edges ----
+
+EDGE = [
+    dict(seed=41, lens=[1, 15, 16, 17, 100], Hq=4, Hkv=4, D=64, P=16, kv_dtype="f32"),
+    dict(seed=42, lens=[3, 33, 250], Hq=8, Hkv=4, D=128, P=32, kv_dtype="f32"),
+    dict(seed=43, lens=[1, 31, 32, 33, 63, 64, 65, 511, 512, 513], Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16"),
+    dict(seed=44, lens=[2, 40, 300], Hq=4, Hkv=4, D=64, P=32, kv_dtype="bf16"),
+    dict(seed=45, lens=[7, 129, 1000], Hq=32, Hkv=2, D=128, P=128, kv_dtype="bf16"),
+    dict(seed=46, lens=[255, 256, 257, 2000], Hq=16, Hkv=8, D=128, P=256, kv_dtype="bf16"),
+    dict(seed=47, lens=[5, 77, 900], Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16", out_dtype="f32"),
+    dict(seed=48, lens=[511, 512, 513, 1025, 3000], Hq=64, Hkv=8, D=128, P=128, kv_dtype="bf16",
+         partition_tokens=512, q_mult=3.0),
+    dict(seed=49, lens=[0, 5, 0, 700, 0], Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16"),
+    dict(seed=50, lens=[1, 63, 64, 65, 1000], Hq=32, Hkv=8, D=128, P=64, kv_dtype="fp8"),
+    dict(seed=51, lens=[64, 200, 1300], Hq=16, Hkv=4, D=64, P=128, kv_dtype="fp8", out_dtype="f32"),
+    dict(seed=52, lens=[20000], Hq=8, Hkv=1, D=128, P=64, kv_dtype="bf16", q_mult=3.0),
+    dict(seed=53, lens=[1, 2, 3, 4, 5] * 400, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16"),
+    dict(seed=54, lens=[100, 4097], Hq=12, Hkv=4, D=128, P=64, kv_dtype="fp8", partition_tokens=128),
+]
+
+
+@pytest.mark.parametrize("spec", EDGE, ids=lambda s: f"{s['kv_dtype']}-D{s['D']}-P{s['P']}-G{s['Hq'] // s['Hkv']}-s{s['seed']}")
+def test_decode_edge_cases(spec):
+    wl = configs.custom(**spec)
+    _decode_vs_oracle(wl, f"seed {spec['seed']}")
+
+
+def test_decode_all_empty_sequences():
+    wl = configs.custom(seed=55, lens=[0, 0, 0], Hq=8, Hkv=2, D=128, P=64, kv_dtype="bf16")
+    dw = DeviceWorkload(wl)
+    dw.out.fill_(7.0)
+    out = dw.decode()
+    torch.cuda.synchronize()
+    assert (gpu_out(out) == 0).all()
+
+
+def test_decode_batch_zero_is_noop():
+    wl = configs.custom(seed=56, lens=[3], Hq=8, Hkv=2, D=128, P=64, kv_dtype="bf16")
+    dw = DeviceWorkload(wl)
+    dw.out.fill_(7.0)
+    pkv.lib().pkv_paged_attn_decode  # symbol present
+    rc = pkv.lib().pkv_paged_attn_decode(None, 1, None, None, 1, None, 1, None, 0, 1, 8, 2, 128, 64,
+                                         0.1, 0, None, 1, None, 0, None)
+    assert rc == 0
+
+
+# ------------------------------------------------------- decode: invariants ----
+
+def test_decode_deterministic_and_page_permutation_invariant():
+    wl = configs.custom(seed=61, lens=[300, 1, 2000, 64], Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16")
+    dw = DeviceWorkload(wl)
+    a = gpu_out(dw.decode()).copy()
+    b = gpu_out(dw.decode()).copy()
+    assert np.array_equal(a, b)
+    perm = np.random.default_rng(3).permutation(wl.num_pages)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(wl.num_pages)
+    wl.k_pool, wl.v_pool = wl.k_pool[inv].copy(), wl.v_pool[inv].copy()
+    wl.block_tables = np.where(wl.block_tables >= 0, perm[np.maximum(wl.block_tables, 0)], -1).astype(np.int32)
+    c = gpu_out(DeviceWorkload(wl).decode())
+    assert np.array_equal(a, c)
+
+
+def test_decode_poison_invariant():
+    wl = configs.custom(seed=62, lens=[33, 65, 100], Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16")
+    a = gpu_out(DeviceWorkload(wl).decode()).copy()
+    # unused pages and the unused tail slots all hold NaN poison already; make it +-inf / junk
+    valid = np.zeros(wl.k_pool.shape, bool)
+    ki = layout.k_chunk_index(wl.P, wl.D, "bf16")
+    vi = layout.v_chunk_index(wl.P, wl.D, "bf16")
+    valid_v = np.zeros(wl.v_pool.shape, bool)
+    for b in range(wl.B):
+        for t in range(int(wl.seq_lens[b])):
+            pg = wl.block_tables[b, t // wl.P]
+            valid[pg, :, ki[t % wl.P]] = True
+            valid_v[pg, :, vi[t % wl.P]] = True
+    wl.k_pool = np.where(valid, wl.k_pool, np.uint16(0x7F80))     # +inf
+    wl.v_pool = np.where(valid_v, wl.v_pool, np.uint16(0xFF80))   # -inf
+    b2 = gpu_out(DeviceWorkload(wl).decode())
+    assert np.array_equal(a, b2)
+
+
+def test_partition_choice_within_tolerance():
+    wl = configs.custom(seed=63, lens=[5000, 1234], Hq=64, Hkv=8, D=128, P=128, kv_dtype="bf16", q_mult=3.0)
+    ref = oracle_decode(wl)
+    dw = DeviceWorkload(wl)
+    for pt in (0, 128, 512, 4096):
+        out = gpu_out(dw.decode(partition_tokens=pt))
+        check_close(out, ref, "bf16", f"partition {pt}")
+
+
+def test_bad_page_id_gives_nan_row():
+    wl = configs.custom(seed=64, lens=[100, 100], Hq=8, Hkv=2, D=128, P=64, kv_dtype="bf16")
+    wl.block_tables[1, 1] = wl.num_pages + 5          # out of range: row must be NaN, nothing faults
+    dw = DeviceWorkload(wl)
+    out = gpu_out(dw.decode())
+    assert np.isnan(out[1]).all()
+    ref = oracle_decode(wl, seq_lens=np.array([100, 0], np.int32))
+    check_close(out[0:1], ref[0:1], "bf16", "good row beside a bad one")
+
+
+def test_error_codes_on_device():
+    wl = configs.custom(seed=65, lens=[10], Hq=8, Hkv=2, D=128, P=64, kv_dtype="bf16")
+    dw = DeviceWorkload(wl)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attn_decode(dw.q, "bf16", dw.k_pool, dw.v_pool, "bf16", dw.bt, dw.sl, 8, 2, 128, 64,
+                              0.1, dw.out, "bf16", small)
+    assert e.value.code == -4
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attn_decode(dw.q, "bf16", dw.k_pool, dw.v_pool, "fp8", dw.bt, dw.sl, 8, 2, 128, 64,
+                              0.1, dw.out, "bf16", dw.ws)
+    assert e.value.code == -3
+
+
+# --------------------------------------------------------- the five configs ----
+
+def test_config_tiny_fp32():
+    mx, mean = _decode_vs_oracle(configs.tiny_fp32(), "tiny_fp32")
+    assert mx < 1e-5                       # fp32 data, fp32 MFMA: far inside the bound
+
+
+def test_config_llama3_8b_bf16():
+    _decode_vs_oracle(configs.llama3_8b_bf16(), "llama3_8b_bf16")
+
+
+def test_config_fp8_kv():
+    _decode_vs_oracle(configs.fp8_kv(), "fp8_kv")
+
+
+def test_config_inflight_16_steps():
+    """Each step: append one token per sequence on the GPU (bit-exact against the
+    oracle append), then decode (full comparison at the first and last step,
+    sampled rows in between)."""
+    wl = configs.inflight_bf16()
+    dw = DeviceWorkload(wl)
+    ref_k, ref_v = wl.k_pool.copy(), wl.v_pool.copy()
+    rng = np.random.default_rng(0)
+    for s, st in enumerate(wl.steps):
+        sl = dev_tensor(st.seq_lens)
+        dw.append(dev_tensor(st.k_new), dev_tensor(st.v_new), sl)
+        c_oracle.append(st.k_new, st.v_new, "bf16", wl.block_tables, st.seq_lens, ref_k, ref_v, wl.P)
+        out = gpu_out(dw.decode(seq_lens=sl))
+        if s in (0, len(wl.steps) - 1):
+            assert np.array_equal(host_bytes(dw.k_pool), ref_k.view(np.uint8).reshape(-1))
+            assert np.array_equal(host_bytes(dw.v_pool), ref_v.view(np.uint8).reshape(-1))
+            ref = oracle_decode(wl, ref_k, ref_v, st.seq_lens)
+            check_close(out, ref, "bf16", f"step {s}")
+        else:
+            pairs = np.stack([rng.integers(0, wl.B, 48), rng.integers(0, wl.Hq, 48)], 1)
+            ref = oracle_decode(wl, ref_k, ref_v, st.seq_lens, pairs=pairs)
+            check_close(out[pairs[:, 0], pairs[:, 1]], ref[pairs[:, 0], pairs[:, 1]], "bf16", f"step {s}")
+
+
+def test_config_long_splitkv_reduced():
+    """Same shape family as the long-context workload at B=2, L=16384: full comparison."""
+    _decode_vs_oracle(configs.long_splitkv_bf16(B=2, L=16384), "long_splitkv B=2 L=16384")
+
+
+def test_config_long_splitkv_full_sampled():
+    """B=8 x 131072 tokens, 512-token partitions: sampled rows against the oracle."""
+    wl = configs.long_splitkv_bf16()
+    dw = DeviceWorkload(wl)
+    out = gpu_out(dw.decode())
+    rng = np.random.default_rng(1)
+    pairs = np.stack([rng.integers(0, wl.B, 24), rng.integers(0, wl.Hq, 24)], 1)
+    ref = oracle_decode(wl, pairs=pairs)
+    check_close(out[pairs[:, 0], pairs[:, 1]], ref[pairs[:, 0], pairs[:, 1]], "bf16", "long full")
+    assert np.isfinite(out).all()

@@ -24,6 +24,8 @@ stored as fp32, bf16 (nearest-even) or fp8 e4m3 with one fp32 scale per
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -83,6 +85,10 @@ class Workload:
 # ----------------------------------------------------------------------------
 # Draw helpers
 # ----------------------------------------------------------------------------
+
+
+def _workers() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def _child(seed: int, *key: int) -> np.random.Generator:
@@ -223,7 +229,7 @@ def _assemble(name, seed, B, Hq, Hkv, D, P, num_pages, kv_dtype, q_dtype, out_dt
     if kv_dtype == "fp8":
         ks = np.full((num_pages, Hkv), np.nan, dtype=np.float32)
         vs = np.full((num_pages, Hkv), np.nan, dtype=np.float32)
-    for b in range(B):
+    def fill(b):
         n = int(pool_lens[b])
         pages = bt[b, :int(pages_needed(np.array([n]), P)[0])]
         k, v, kls, vls = seq_tokens(seed, b, n, Hkv, D, kv_dtype, P)
@@ -232,6 +238,11 @@ def _assemble(name, seed, B, Hq, Hkv, D, P, num_pages, kv_dtype, q_dtype, out_dt
         if kv_dtype == "fp8" and len(pages):
             ks[pages] = kls
             vs[pages] = vls
+
+    # Sequences own disjoint pages, so they can be drawn and placed concurrently;
+    # each draws from its own child stream, so the result does not depend on order.
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(fill, range(B)))
     return Workload(name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, D=D, P=P,
                     num_pages=num_pages, max_pages=max_pages, kv_dtype=kv_dtype,
                     q_dtype=q_dtype, out_dtype=out_dtype, scale=np.float32(scale),
