@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode iteration of one layer over a paged KV cache on one MI355X.
+
+A step is the whole hot path for one layer: kv_append of each sequence's new
+token into its page, then paged decode attention over every cached token
+(split ranges merged by log-sum-exp).  Inputs are seeded synthetic data
+already resident in HBM.  Consecutive steps rotate over ``--layers`` copies of
+the cache (one per layer, as in a model), so no step finds its K/V in the
+256 MB last-level cache left warm by the step before.
+
+Prints one JSON line:
+  value   = algorithmic HBM bytes of a step / wall time per step (GB/s),
+  roofline.achieved = algorithmic bytes of one decode call / its mean duration
+            measured with HIP events on the launch stream,
+  cpu_baseline = the fp64 CPU oracle on this host (append + decode, full batch).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+METRIC = "paged decode attention: KV HBM GB/s (fraction of peak) + seqs/s per layer"
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", "pkv_kernels.hip")
+WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "tiny_fp32"]
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_bf16", choices=WORKLOADS)
+    ap.add_argument("--layers", type=int, default=0, help="cache copies to rotate over (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def alg_bytes(wl, seq_lens):
+    """Bytes the method must move: (decode bytes, append bytes) for one step."""
+    import numpy as np
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    qb = 4 if wl.q_dtype == "f32" else 2
+    ob = 4 if wl.out_dtype == "f32" else 2
+    L = seq_lens.astype(np.int64)
+    pages = (L + wl.P - 1) // wl.P
+    kv = int(L.sum()) * wl.Hkv * wl.D * eb * 2
+    dec = kv + wl.B * wl.Hq * wl.D * (qb + ob) + int(pages.sum()) * 4 + wl.B * 4
+    if wl.kv_dtype == "fp8":
+        dec += int(pages.sum()) * wl.Hkv * 4 * 2
+    app = 2 * (wl.B * wl.Hkv * wl.D * eb * 2) + wl.B * 8
+    return dec, app, kv
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(3):
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "ms": ms,
+                      "copy_gbs_read_plus_write": 2 * n / ms / 1e6}))
+
+
+class DeviceEvents:
+    """HIP timing events recorded on the launch stream with a device-scope release.
+
+    hipEventReleaseToDevice keeps the record from adding the system-scope cache
+    write-back that a default event performs, which would otherwise open a gap of
+    several microseconds between the kernels being timed.
+    """
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self, n):
+        import ctypes
+        import torch
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")      # the runtime torch already loaded
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.RELEASE_TO_DEVICE))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(e)
+
+    def record(self, i):
+        rc = self.hip.hipEventRecord(self.ev[i], self.stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, i):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[2 * i], self.ev[2 * i + 1])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def cpu_baseline(wl, steps, seconds):
+    """The fp64 C oracle on this host: repeated full steps (append + decode)."""
+    import numpy as np
+    from oracle import c_oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    reps, kv_total, seqs, t0 = 0, 0, 0, time.perf_counter()
+    while True:
+        st = steps[reps % len(steps)]
+        c_oracle.append(st["k_new"], st["v_new"], wl.kv_dtype, wl.block_tables, st["seq_lens"], kp, vp, wl.P)
+        c_oracle.decode(wl.q, wl.q_dtype, kp, vp, wl.kv_dtype, wl.block_tables, st["seq_lens"], wl.Hq,
+                        wl.P, wl.scale, wl.k_scales, wl.v_scales, nthreads=threads)
+        d, a, _ = alg_bytes(wl, st["seq_lens"])
+        kv_total += d + a
+        seqs += wl.B
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": kv_total / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seqs_per_s_per_layer": seqs / el,
+            "sample": f"full batch of {wl.B} sequences, {reps} step(s) of append + fp64 decode "
+                      f"(C oracle, {threads} threads), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.exit("bench.py measures one GPU: the decode path runs on a single MI355X and has no "
+                 "multi-GPU mode (use --gpus 1)")
+    import numpy as np
+    import torch
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import paged_kv_attention_decode_amd as pkv
+    from workloads import configs
+
+    gen = configs.CONFIGS[args.workload]
+    wl = gen()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def T(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    # Per-step inputs: the in-flight workload carries its own growing steps;
+    # the others re-append the token at position L-1 every step (same cost).
+    rng = np.random.default_rng(1234)
+    if wl.steps:
+        steps = [{"seq_lens": s.seq_lens, "k_new": s.k_new, "v_new": s.v_new} for s in wl.steps]
+    else:
+        eb_dt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[wl.kv_dtype]
+        if wl.kv_dtype == "f32":
+            kn = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
+            vn = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
+        else:
+            from workloads import codec
+            kf = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
+            vf = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
+            if wl.kv_dtype == "bf16":
+                kn, vn = codec.f32_to_bf16_bits(kf), codec.f32_to_bf16_bits(vf)
+            else:                       # bytes at a typical quantised magnitude
+                kn, vn = codec.e4m3_encode(kf * 100), codec.e4m3_encode(vf * 100)
+        steps = [{"seq_lens": wl.seq_lens.copy(), "k_new": kn.astype(eb_dt), "v_new": vn.astype(eb_dt)}]
+
+    pool_bytes = wl.k_pool.nbytes + wl.v_pool.nbytes
+    layers = args.layers or max(1, min(8, math.ceil(2.0e9 / pool_bytes)))
+    q = T(wl.q)
+    bt = T(wl.block_tables)
+    kps = [T(wl.k_pool) for _ in range(layers)]
+    vps = [T(wl.v_pool) for _ in range(layers)]
+    ks = None if wl.k_scales is None else T(wl.k_scales)
+    vs = None if wl.v_scales is None else T(wl.v_scales)
+    dsteps = [{"sl": T(s["seq_lens"]), "kn": T(s["k_new"]), "vn": T(s["v_new"])} for s in steps]
+    odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    out = torch.empty((wl.B, wl.Hq, wl.D), dtype=odt, device=dev)
+    ws = torch.zeros(pkv.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None, k=0):
+        s = dsteps[i % len(dsteps)]
+        kp, vp = kps[i % layers], vps[i % layers]
+        pkv.kv_append(s["kn"], s["vn"], wl.kv_dtype, bt, s["sl"], kp, vp, wl.Hkv, wl.D, wl.P)
+        if ev is not None:
+            ev.record(2 * k)
+        if wl.kv_dtype == "fp8":
+            pkv.paged_attn_decode_fp8(q, wl.q_dtype, kp, vp, ks, vs, bt, s["sl"], wl.Hq, wl.Hkv, wl.D, wl.P,
+                                      wl.scale, out, wl.out_dtype, ws, wl.partition_tokens)
+        else:
+            pkv.paged_attn_decode(q, wl.q_dtype, kp, vp, wl.kv_dtype, bt, s["sl"], wl.Hq, wl.Hkv, wl.D,
+                                  wl.P, wl.scale, out, wl.out_dtype, ws, wl.partition_tokens)
+        if ev is not None:
+            ev.record(2 * k + 1)
+
+    for i in range(args.warmup):
+        step(i)
+    evs = DeviceEvents(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs, i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [evs.elapsed_ms(i) for i in range(args.steps)]
+    evs.close()
+    dec_mean = float(np.mean(dec_ms))
+
+    step_bytes, dec_bytes, kv_bytes = 0, 0, 0
+    for i in range(args.steps):
+        d, a, kvb = alg_bytes(wl, steps[(args.warmup + i) % len(steps)]["seq_lens"])
+        step_bytes += d + a
+        dec_bytes += d
+        kv_bytes += kvb
+    step_bytes /= args.steps
+    dec_bytes /= args.steps
+    kv_bytes /= args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_mean * 1e-3) / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"decode_{args.workload}_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256_16") == kernel_hash():
+            traffic = tr.get("hbm_bytes_per_decode_call")
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8e4m3 (kv) / bf16 (q, out)", "f32": "f32"}[wl.kv_dtype],
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled pages)",
+        "config": {"workload": args.workload, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.D, "page_size": wl.P,
+                   "mean_seq_len": float(np.mean(steps[0]["seq_lens"])),
+                   "partition_tokens": wl.partition_tokens, "layers_rotated": layers,
+                   "step": "kv_append + paged_attn_decode (split + LSE merge)"},
+        "seqs_per_s_per_layer": round(wl.B / (ms_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": int(kv_bytes),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "paged_attn_decode call (split kernel + merge kernel)",
+                     "decode_ms_mean": round(dec_mean, 5), "decode_ms_min": round(min(dec_ms), 5),
+                     "alg_bytes_per_call": int(dec_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

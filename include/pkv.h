@@ -101,8 +101,11 @@ int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype,
 /* Bytes of scratch that pkv_paged_attn_decode / pkv_paged_attn_decode_fp8 need
  * for these sizes on the current HIP device (0 if the sizes are invalid).
  * The workspace holds split-KV partial results (per-head running max, sum and
- * unnormalised output of each partial range); it needs no initialisation and
- * its contents after a call are unspecified. */
+ * unnormalised output of each partial range) followed by one 16-byte merge
+ * descriptor per (sequence, kv head).  It needs no initialisation and its
+ * contents after a call are unspecified.  Calls that share a workspace must not
+ * overlap in time (issue them on one stream); a workspace sized for batch B
+ * serves any call with batch <= B and the same head counts and head_dim. */
 size_t pkv_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim);
 
 /* paged_attn_decode - one decode step of attention over the paged cache.
@@ -122,6 +125,9 @@ size_t pkv_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, 
  * Page ids used must lie in [0, num_pages) and L_b <= MP * P; a row whose
  * sequence breaks this gets NaN outputs (nothing outside the pools is read).
  * workspace: device memory of at least pkv_decode_workspace_bytes(...) bytes.
+ * The call launches two kernels on the stream: the split kernel (which also
+ * finishes every (sequence, kv head) that one wavefront covered entirely) and
+ * a merge kernel for the pairs split over several wavefronts.
  * Writes out and workspace only. */
 int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype,
                           const void* k_pool, const void* v_pool, pkv_dtype kv_dtype,

@@ -99,6 +99,9 @@ int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
   a.seq_lens = seq_lens;
   a.out = out;
   a.partials = static_cast<float*>(workspace);
+  a.descs = reinterpret_cast<int4*>(static_cast<char*>(workspace) +
+                                      pkv::partials_bytes(pkv::device_cu_count(), num_q_heads / num_kv_heads,
+                                                          head_dim));
   a.kvt = kv_dtype;
   a.out_bf16 = out_dtype == PKV_BF16;
   a.batch = batch;
@@ -141,9 +144,9 @@ size_t pkv_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, 
     return 0;
   const int cus = pkv::device_cu_count();
   if (cus <= 0) return 0;
-  const size_t G = (size_t)(num_q_heads / num_kv_heads);
-  // two partial slots (first and last range) per resident wave
-  return 2 * (size_t)cus * pkv::kMaxWavesPerCU * G * ((size_t)head_dim + 2) * sizeof(float);
+  // two partial slots (first and last range) per resident wave, then the descriptors
+  return pkv::partials_bytes(cus, num_q_heads / num_kv_heads, head_dim) +
+         (size_t)batch * (size_t)num_kv_heads * 16;
 }
 
 int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype, const int32_t* block_tables,

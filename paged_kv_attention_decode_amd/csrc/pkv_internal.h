@@ -18,6 +18,12 @@ inline int elem_bytes(int kvt) { return kvt == KV_F32 ? 4 : kvt == KV_BF16 ? 2 :
 // workspace together with the device's compute-unit count.
 constexpr int kMaxWavesPerCU = 16;
 
+// Workspace layout: partial slots (2 per wave) then B * Hkv 16-byte descriptors.
+inline size_t partials_bytes(int cus, int G, int D) {
+  size_t b = 2 * (size_t)cus * kMaxWavesPerCU * (size_t)G * ((size_t)D + 2) * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
 struct AppendArgs {
   const void* k_new;
   const void* v_new;
@@ -47,7 +53,8 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
-  float* partials;         // workspace
+  float* partials;         // workspace: partial-result slots
+  int4* descs;             // workspace: per-(b, g) merge descriptors
   int kvt;                 // KvType; q is f32 for KV_F32, bf16 otherwise
   bool out_bf16;
   int batch, max_pages, num_pages, num_q_heads, num_kv_heads, head_dim, page_size;
@@ -57,7 +64,7 @@ struct DecodeArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
-// Launches the split decode kernel and the log-sum-exp merge kernel.
+// Launches the decode kernel and the log-sum-exp merge kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Compute units of the current device (cached per device); <= 0 on failure.
 int device_cu_count();

@@ -164,8 +164,85 @@ __device__ __forceinline__ int64_t wave_of(const Split& s, int64_t idx) {
 }
 __device__ __forceinline__ int ranges_of(int L, int PT) { return L > 0 ? (L + PT - 1) / PT : 0; }
 
+// Store 4 consecutive outputs.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_out4(void* out_, size_t idx, f32x4_t v) {
+  if (OUT_BF16) {
+    u32x2_t p;
+    p.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+    p.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out_) + idx) = p;
+  } else {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(out_) + idx) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Decode: split kernel
+// Log-sum-exp merge of the n partial ranges of one (b, g), run by one wave.
+// Partial slot layout (floats): O[G][D] unnormalised, then m[G] (log2-domain
+// running max), then l[G] (sum of 2^(s - m)).  Contributor i is wave wf + i;
+// its slot is slot0 for i = 0 and 2 * (wf + i) otherwise.
+//   out = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
+// Lanes own 4 consecutive (h, d) outputs; contributors are read 8 at a time so
+// their loads are in flight together.
+// ---------------------------------------------------------------------------
+template <bool OUT_BF16>
+__device__ void merge_ranges(const float* __restrict__ partials, int64_t slot0, int64_t wf, int n,
+                             void* __restrict__ out_, size_t row0, int G, int D, int lane) {
+  const int stride = G * (D + 2);
+  const int total = G * D;
+  const float NEG_INF = -__builtin_inff();
+  for (int c0 = 0; c0 < total; c0 += 256) {
+    const int x = c0 + 4 * lane;
+    if (x >= total) break;
+    const int h = x / D;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f, M = NEG_INF;
+    bool nan = false;
+    for (int s0 = 0; s0 < n; s0 += 8) {
+      f32x4_t o[8];
+      float ms[8], ls[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (s0 + k < n) {
+          const int64_t slot = (s0 + k == 0) ? slot0 : 2 * (wf + s0 + k);
+          const float* ps = partials + slot * stride;
+          o[k] = *reinterpret_cast<const f32x4_t*>(ps + x);
+          ms[k] = ps[total + h];
+          ls[k] = ps[total + G + h];
+        } else {
+          o[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          ms[k] = NEG_INF;
+          ls[k] = 0.f;
+        }
+      }
+      float mg = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        nan |= ms[k] != ms[k];
+        mg = fmaxf(mg, ms[k]);
+      }
+      const float a = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(M - mg);
+      acc *= a;
+      den *= a;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = ms[k] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ms[k] - mg);
+        acc += f * o[k];
+        den += f * ls[k];
+      }
+      M = mg;
+    }
+    const float inv = nan ? __builtin_nanf("") : 1.f / den;
+    store_out4<OUT_BF16>(out_, row0 + x, acc * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode, part 1: each wave streams its unit range.  A (b, g) covered by one
+// wave is finished here; otherwise each covering wave leaves a partial and the
+// wave holding the first unit of (b, g) leaves a descriptor (first contributing
+// wave, number of contributors, slot of the first) for the merge kernel.
 // ---------------------------------------------------------------------------
 template <int KVT, int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_split_kernel(
@@ -173,7 +250,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint8_t* __restrict__ vpool, const float* __restrict__ kscales,
     const float* __restrict__ vscales, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, void* __restrict__ out_, float* __restrict__ partials,
-    int B, int MP, int NP, int Hq, int Hkv, int G, int P, int PT, int Wmax, float scale_log2) {
+    int4* __restrict__ descs, int B, int MP, int NP, int Hq, int Hkv, int G, int P, int PT,
+    int Wmax, float scale_log2) {
   constexpr int EB = Kv<KVT>::EB;
   constexpr int E = 16 / EB;        // elements per 16-byte group
   constexpr int TS = 4 * E;         // tokens per step (= V block)
@@ -187,10 +265,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
 
   // ---- this wave's unit range -------------------------------------------------
-  int np_sum = 0;
+  int np_sum = 0, n_empty = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int bb = b0 + lane;
-    np_sum += wave_sum(ranges_of(bb < B ? seq_lens[bb] : 0, PT));
+    const int np = ranges_of(bb < B ? seq_lens[bb] : 0, PT);
+    np_sum += wave_sum(np);
+    n_empty += wave_sum(bb < B && np == 0 ? 1 : 0);
+  }
+  // sequences with no tokens get zero rows (sequence b is cleared by wave b mod Wmax)
+  if (n_empty) {
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int bb = b0 + lane;
+      uint64_t mine = __ballot(bb < B && ranges_of(seq_lens[bb < B ? bb : 0], PT) == 0 && bb % Wmax == w);
+      while (mine) {
+        const int be = b0 + __builtin_ctzll(mine);
+        mine &= mine - 1;
+        for (int x = 4 * lane; x < Hq * D; x += 256)
+          store_out4<OUT_BF16>(out_, (size_t)be * Hq * D + x, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+    }
   }
   const Split sp = make_split((int64_t)np_sum * Hkv, Wmax);
   if (w >= sp.W) return;
@@ -399,21 +492,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       if (hv) {
         const float inv = bad ? qnan : 1.f / lt;
         const size_t o = ((size_t)b * Hq + h) * D + 4 * c4;
-        if (OUT_BF16) {
-          uint16_t* out = static_cast<uint16_t*>(out_);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            u32x2_t v;
-            v.x = bf16_rne(O[dt][0] * inv) | (bf16_rne(O[dt][1] * inv) << 16);
-            v.y = bf16_rne(O[dt][2] * inv) | (bf16_rne(O[dt][3] * inv) << 16);
-            *reinterpret_cast<u32x2_t*>(out + o + dt * 16) = v;
-          }
-        } else {
-          float* out = static_cast<float*>(out_);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-            *reinterpret_cast<f32x4_t*>(out + o + dt * 16) = O[dt] * inv;
-        }
+        for (int dt = 0; dt < NDT; ++dt) store_out4<OUT_BF16>(out_, o + dt * 16, O[dt] * inv);
       }
     } else {
       float* ps = partials + (size_t)(2 * w + (first ? 0 : 1)) * G * (D + 2);
@@ -426,6 +506,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
           ps[G * D + G + r16] = lt;
         }
       }
+    }
+    if (u == S && lane == 0) {
+      // descriptor of (b, g): first contributing wave, contributors, its slot
+      const int64_t wl = wave_of(sp, Eu - 1);
+      descs[(size_t)b * Hkv + g] = make_int4((int)w, (int)(wl - w + 1), (int)(2 * w + (first ? 0 : 1)), 0);
     }
 
     // ---- next segment ------------------------------------------------------------
@@ -442,79 +527,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode: log-sum-exp merge of split ranges, and zero rows for empty sequences.
-// One workgroup per (b, g).
+// Decode, part 2: one wave per (b, g) combines the partial ranges of pairs that
+// were split over several waves (log-sum-exp merge, see merge_ranges).
 // ---------------------------------------------------------------------------
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
-    const int32_t* __restrict__ seq_lens, const float* __restrict__ partials,
-    void* __restrict__ out_, int B, int Hq, int Hkv, int G, int D, int PT, int Wmax) {
-  const int bg = blockIdx.x;
+    const int32_t* __restrict__ seq_lens, const int4* __restrict__ descs,
+    const float* __restrict__ partials, void* __restrict__ out_, int B, int Hq, int Hkv, int G, int D) {
+  const int bg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bg >= B * Hkv) return;
   const int b = bg / Hkv, g = bg - b * Hkv;
-  __shared__ int red_tot[4], red_pre[4];
-  int tot = 0, pre = 0;
-  for (int i = threadIdx.x; i < B; i += blockDim.x) {
-    const int np = ranges_of(seq_lens[i], PT);
-    tot += np;
-    if (i < b) pre += np;
-  }
-  tot = wave_sum(tot);
-  pre = wave_sum(pre);
-  if ((threadIdx.x & 63) == 0) {
-    red_tot[threadIdx.x >> 6] = tot;
-    red_pre[threadIdx.x >> 6] = pre;
-  }
-  __syncthreads();
-  tot = red_tot[0] + red_tot[1] + red_tot[2] + red_tot[3];
-  pre = red_pre[0] + red_pre[1] + red_pre[2] + red_pre[3];
-
-  const int npb = ranges_of(seq_lens[b], PT);
-  if (npb == 0) {
-    for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
-      const size_t o = ((size_t)b * Hq + g * G) * D + x;
-      if (OUT_BF16)
-        static_cast<uint16_t*>(out_)[o] = 0;
-      else
-        static_cast<float*>(out_)[o] = 0.f;
-    }
-    return;
-  }
-  const Split sp = make_split((int64_t)tot * Hkv, Wmax);
-  const int64_t S = (int64_t)pre * Hkv + (int64_t)g * npb, Eu = S + npb;
-  const int64_t wf = wave_of(sp, S);
-  if (wf == wave_of(sp, Eu - 1)) return;  // one wave covered it and wrote the output
-  const int stride = G * (D + 2);
-  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
-    const int hh = x / D;
-    float M = -__builtin_inff();
-    for (int64_t w = wf;;) {
-      const int64_t slot = 2 * w + (range_begin(sp, w) >= S ? 0 : 1);
-      M = fmaxf(M, partials[slot * stride + G * D + hh]);
-      const int64_t nx = range_begin(sp, w + 1);
-      if (nx >= Eu) break;
-      w = wave_of(sp, nx);
-    }
-    float num = 0.f, den = 0.f;
-    bool nan = false;
-    for (int64_t w = wf;;) {
-      const int64_t slot = 2 * w + (range_begin(sp, w) >= S ? 0 : 1);
-      const float* ps = partials + slot * stride;
-      const float ms = ps[G * D + hh];
-      nan |= ms != ms;
-      const float f = __builtin_amdgcn_exp2f(ms - M);
-      num += f * ps[x];
-      den += f * ps[G * D + G + hh];
-      const int64_t nx = range_begin(sp, w + 1);
-      if (nx >= Eu) break;
-      w = wave_of(sp, nx);
-    }
-    const float r = nan ? __builtin_nanf("") : num / den;
-    const size_t o = ((size_t)b * Hq + g * G) * D + x;
-    if (OUT_BF16)
-      static_cast<uint16_t*>(out_)[o] = (uint16_t)bf16_rne(r);
-    else
-      static_cast<float*>(out_)[o] = r;
-  }
+  const int L = seq_lens[b];
+  const int4 d = descs[bg];
+  if (L <= 0 || d.y <= 1) return;        // empty (zeroed) or finished by one wave
+  merge_ranges<OUT_BF16>(partials, d.z, d.x, d.y, out_, ((size_t)b * Hq + (size_t)g * G) * D, G, D,
+                         threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------------------
@@ -589,8 +616,8 @@ std::mutex g_mu;
 DevInfo g_dev[64];
 
 typedef void (*decode_fn_t)(const void*, const uint8_t*, const uint8_t*, const float*, const float*,
-                            const int32_t*, const int32_t*, void*, float*, int, int, int, int, int, int,
-                            int, int, int, float);
+                            const int32_t*, const int32_t*, void*, float*, int4*, int, int, int, int, int,
+                            int, int, int, int, float);
 
 template <int KVT, int D, bool OB>
 decode_fn_t decode_fn() {
@@ -690,17 +717,18 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((Wmax + 3) / 4), block(256);
   hipLaunchKernelGGL(fn, grid, block, 0, s, a.q, static_cast<const uint8_t*>(a.k_pool),
                      static_cast<const uint8_t*>(a.v_pool), a.k_scales, a.v_scales, a.block_tables,
-                     a.seq_lens, a.out, a.partials, a.batch, a.max_pages, a.num_pages, a.num_q_heads,
-                     a.num_kv_heads, G, a.page_size, a.partition_tokens, Wmax, scale_log2);
+                     a.seq_lens, a.out, a.partials, a.descs, a.batch, a.max_pages, a.num_pages,
+                     a.num_q_heads, a.num_kv_heads, G, a.page_size, a.partition_tokens, Wmax, scale_log2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 mgrid(a.batch * a.num_kv_heads);
+  const int pairs = a.batch * a.num_kv_heads;
+  dim3 mgrid((pairs + 3) / 4);
   if (a.out_bf16)
-    hipLaunchKernelGGL(decode_merge_kernel<true>, mgrid, block, 0, s, a.seq_lens, a.partials, a.out,
-                       a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim, a.partition_tokens, Wmax);
+    hipLaunchKernelGGL(decode_merge_kernel<true>, mgrid, block, 0, s, a.seq_lens, a.descs, a.partials, a.out,
+                       a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<false>, mgrid, block, 0, s, a.seq_lens, a.partials, a.out,
-                       a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim, a.partition_tokens, Wmax);
+    hipLaunchKernelGGL(decode_merge_kernel<false>, mgrid, block, 0, s, a.seq_lens, a.descs, a.partials, a.out,
+                       a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def dev_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 def host_bytes(t: torch.Tensor) -> np.ndarray:
-    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy().reshape(-1)
 
 
 class DeviceWorkload:
@@ -42,7 +42,7 @@ class DeviceWorkload:
         odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
         self.out = torch.empty((wl.B, wl.Hq, wl.D), dtype=odt, device=device)
         nbytes = pkv.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D)
-        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
 
     def decode(self, seq_lens=None, partition_tokens=None, out=None):
         wl = self.wl
@@ -76,15 +76,30 @@ def gpu_out(out: torch.Tensor) -> np.ndarray:
     return out.float().cpu().numpy().astype(np.float64)
 
 
-def check_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = ""):
-    """Element-wise comparison at the benchmark spec's tolerance; returns (max, mean)."""
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |x| (the most that rounding a value to bf16 can move it)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return np.exp2(e - 8)
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = "",
+                out_rounding: bool = False):
+    """Element-wise comparison at the benchmark spec's tolerance; returns (max, mean).
+
+    With ``out_rounding`` (bf16 outputs of large magnitude in edge-case tests),
+    each element may additionally differ by the half-ulp that storing the exact
+    result as bf16 costs, and the mean bound grows by the mean of that allowance.
+    """
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(ref).all(), f"{what}: oracle produced non-finite values"
     assert np.isfinite(got).all(), f"{what}: GPU produced non-finite values"
     err = np.abs(got - ref)
     mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
     tmax, tmean = TOL[kv_dtype]
-    assert mx <= tmax, f"{what}: max-abs {mx:.3e} > {tmax}"
+    allow = bf16_half_ulp(ref) if out_rounding else np.zeros_like(ref)
+    worst = float((err - allow).max()) if err.size else 0.0
+    assert worst <= tmax, f"{what}: max-abs {mx:.3e} exceeds {tmax} (+ output rounding {out_rounding})"
     if tmean is not None:
-        assert mean <= tmean, f"{what}: mean-abs {mean:.3e} > {tmean}"
+        lim = tmean + (float(allow.mean()) if err.size else 0.0)
+        assert mean <= lim, f"{what}: mean-abs {mean:.3e} > {lim:.3e}"
     return mx, mean

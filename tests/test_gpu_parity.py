@@ -17,12 +17,13 @@ from _helpers import DeviceWorkload, check_close, dev_tensor, gpu_out, host_byte
 pytestmark = pytest.mark.gpu
 
 
-def _decode_vs_oracle(wl, what, partition_tokens=None):
+def _decode_vs_oracle(wl, what, partition_tokens=None, out_rounding=False):
     dw = DeviceWorkload(wl)
     out = dw.decode(partition_tokens=partition_tokens)
     torch.cuda.synchronize()
     ref = oracle_decode(wl)
-    return check_close(gpu_out(out), ref, wl.kv_dtype, what)
+    return check_close(gpu_out(out), ref, wl.kv_dtype, what,
+                       out_rounding=out_rounding and wl.out_dtype == "bf16")
 
 
 # ------------------------------------------------------------------ formats ----
@@ -40,7 +41,7 @@ def test_fp8_codes_exhaustive_through_decode():
     ones = np.ones((4, 1), np.float32)
     q = codec.f32_to_bf16_bits(np.ones((2, 1, D), np.float32))
     out = torch.empty((2, 1, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(pkv.decode_workspace_bytes(2, 1, 1, D), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(pkv.decode_workspace_bytes(2, 1, 1, D), dtype=torch.uint8, device="cuda")
     pkv.paged_attn_decode_fp8(dev_tensor(q), "bf16", dev_tensor(kp), dev_tensor(vp), dev_tensor(ones),
                               dev_tensor(ones), dev_tensor(bt), dev_tensor(np.array([1, 1], np.int32)),
                               1, 1, D, P, 0.1, out, "f32", ws)
@@ -128,13 +129,16 @@ EDGE = [
     dict(seed=52, lens=[20000], Hq=8, Hkv=1, D=128, P=64, kv_dtype="bf16", q_mult=3.0),
     dict(seed=53, lens=[1, 2, 3, 4, 5] * 400, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16"),
     dict(seed=54, lens=[100, 4097], Hq=12, Hkv=4, D=128, P=64, kv_dtype="fp8", partition_tokens=128),
+    dict(seed=57, lens=[1, 2, 3, 4, 5] * 400, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16", out_dtype="f32"),
 ]
 
 
 @pytest.mark.parametrize("spec", EDGE, ids=lambda s: f"{s['kv_dtype']}-D{s['D']}-P{s['P']}-G{s['Hq'] // s['Hkv']}-s{s['seed']}")
 def test_decode_edge_cases(spec):
     wl = configs.custom(**spec)
-    _decode_vs_oracle(wl, f"seed {spec['seed']}")
+    # very short sequences give |out| up to ~4, where bf16 output rounding alone
+    # reaches 1e-2: allow the output format's half-ulp on top of the bound here
+    _decode_vs_oracle(wl, f"seed {spec['seed']}", out_rounding=True)
 
 
 def test_decode_all_empty_sequences():
@@ -201,6 +205,18 @@ def test_partition_choice_within_tolerance():
         check_close(out, ref, "bf16", f"partition {pt}")
 
 
+def test_workspace_reuse_across_calls():
+    """One workspace (filled with junk first) serves successive calls of different
+    lengths; stale descriptors from earlier calls must not leak into later ones."""
+    big = configs.custom(seed=66, lens=[4096] * 4, Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16")
+    dw = DeviceWorkload(big)
+    dw.ws.fill_(0x5A)
+    for lens in ([3000, 17, 900, 4096], [100, 0, 2500, 1], [4096, 4096, 4096, 4096], [0, 5, 0, 64]):
+        sl = np.array(lens, np.int32)
+        out = gpu_out(dw.decode(seq_lens=dev_tensor(sl)))
+        check_close(out, oracle_decode(big, seq_lens=sl), "bf16", f"lens {lens}")
+
+
 def test_bad_page_id_gives_nan_row():
     wl = configs.custom(seed=64, lens=[100, 100], Hq=8, Hkv=2, D=128, P=64, kv_dtype="bf16")
     wl.block_tables[1, 1] = wl.num_pages + 5          # out of range: row must be NaN, nothing faults
@@ -214,7 +230,7 @@ def test_bad_page_id_gives_nan_row():
 def test_error_codes_on_device():
     wl = configs.custom(seed=65, lens=[10], Hq=8, Hkv=2, D=128, P=64, kv_dtype="bf16")
     dw = DeviceWorkload(wl)
-    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    small = torch.zeros(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(pkv.PkvError) as e:
         pkv.paged_attn_decode(dw.q, "bf16", dw.k_pool, dw.v_pool, "bf16", dw.bt, dw.sl, 8, 2, 128, 64,
                               0.1, dw.out, "bf16", small)
