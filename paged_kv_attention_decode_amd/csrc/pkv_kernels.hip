@@ -86,6 +86,13 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   }
   return v;
 }
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ float fbits(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t ubits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
@@ -138,6 +145,11 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
 
 __device__ __forceinline__ u32x4_t ld16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+// Streaming load for K/V: each byte is read exactly once per call, so mark it
+// nontemporal and keep it from displacing other lines in L2 and the MALL.
+__device__ __forceinline__ u32x4_t ld16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
 // ---------------------------------------------------------------------------
@@ -262,21 +274,42 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, c4 = lane >> 4;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform (the compiler cannot tell that threadIdx.x >> 6 is)
+  const int w = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
 
   // ---- this wave's unit range -------------------------------------------------
+  // seq_lens of the first NC*64 sequences are read once, in one round trip, and
+  // kept in registers (prefix counts of ranges); longer batches re-read the rest.
+  constexpr int NC = 4;
+  int Lc[NC], inclc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int bb = c * 64 + lane;
+    Lc[c] = bb < B ? seq_lens[bb] : 0;
+  }
   int np_sum = 0, n_empty = 0;
-  for (int b0 = 0; b0 < B; b0 += 64) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int bb = c * 64 + lane;
+    const int np = ranges_of(Lc[c], PT);
+    const int incl = wave_incl_scan(np, lane);
+    inclc[c] = np_sum + incl;
+    np_sum = uniform(np_sum + __builtin_amdgcn_readlane(incl, 63));
+    n_empty += __builtin_popcountll(__ballot(bb < B && np == 0));
+  }
+  for (int b0 = NC * 64; b0 < B; b0 += 64) {
     const int bb = b0 + lane;
     const int np = ranges_of(bb < B ? seq_lens[bb] : 0, PT);
-    np_sum += wave_sum(np);
-    n_empty += wave_sum(bb < B && np == 0 ? 1 : 0);
+    np_sum = uniform(np_sum + wave_sum(np));
+    n_empty += __builtin_popcountll(__ballot(bb < B && np == 0));
   }
+  n_empty = uniform(n_empty);
   // sequences with no tokens get zero rows (sequence b is cleared by wave b mod Wmax)
   if (n_empty) {
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int bb = b0 + lane;
-      uint64_t mine = __ballot(bb < B && ranges_of(seq_lens[bb < B ? bb : 0], PT) == 0 && bb % Wmax == w);
+      const int L = bb < B ? seq_lens[bb] : 0;
+      uint64_t mine = __ballot(bb < B && ranges_of(L, PT) == 0 && bb % Wmax == w);
       while (mine) {
         const int be = b0 + __builtin_ctzll(mine);
         mine &= mine - 1;
@@ -290,26 +323,42 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int64_t u0 = range_begin(sp, w), u1 = range_begin(sp, w + 1);
 
   // sequence holding unit u0, and the number of units before it
-  int b = 0;
+  int b = -1, Lb = 0;
   int64_t base = 0;
-  {
-    int64_t run = 0;
-    for (int b0 = 0;; b0 += 64) {
-      const int bb = b0 + lane;
-      const int np = ranges_of(bb < B ? seq_lens[bb] : 0, PT);
-      const int incl = wave_incl_scan(np, lane);
-      const uint64_t hit = __ballot(run + (int64_t)incl * Hkv > u0);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (b < 0) {
+      const int np = ranges_of(Lc[c], PT);
+      const uint64_t hit = __ballot((int64_t)inclc[c] * Hkv > u0);
       if (hit) {
-        const int f = __builtin_ctzll(hit);
-        b = b0 + f;
-        base = run + (int64_t)__shfl(incl - np, f) * Hkv;
-        break;
+        const int f = uniform(__builtin_ctzll(hit));
+        b = c * 64 + f;
+        base = (int64_t)__builtin_amdgcn_readlane(inclc[c] - np, f) * Hkv;
+        Lb = __builtin_amdgcn_readlane(Lc[c], f);
       }
-      run += (int64_t)__shfl(incl, 63) * Hkv;
     }
   }
-  b = __builtin_amdgcn_readfirstlane(b);
-  int Lb = seq_lens[b];
+  if (b < 0) {
+    int run = uniform(__builtin_amdgcn_readlane(inclc[NC - 1], 63));
+    for (int b0 = NC * 64;; b0 += 64) {
+      const int bb = b0 + lane;
+      const int L = bb < B ? seq_lens[bb] : 0;
+      const int np = ranges_of(L, PT);
+      const int incl = run + wave_incl_scan(np, lane);
+      const uint64_t hit = __ballot((int64_t)incl * Hkv > u0);
+      if (hit) {
+        const int f = uniform(__builtin_ctzll(hit));
+        b = b0 + f;
+        base = (int64_t)__builtin_amdgcn_readlane(incl - np, f) * Hkv;
+        Lb = __builtin_amdgcn_readlane(L, f);
+        break;
+      }
+      run = uniform(__builtin_amdgcn_readlane(incl, 63));
+    }
+  }
+  b = uniform(b);
+  base = uniform64(base);
+  Lb = uniform(Lb);
   int npb = ranges_of(Lb, PT);
 
   const float NEG_INF = -__builtin_inff();
@@ -317,19 +366,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
   for (int64_t u = u0; u < u1;) {
     const int64_t off = u - base;
-    const int g = (int)(off / npb);
+    const int g = uniform((int)(off / npb));
     const int rg = (int)(off - (int64_t)g * npb);
     const int64_t S = base + (int64_t)g * npb, Eu = S + npb;
     const int64_t ue = Eu < u1 ? Eu : u1;
-    const int tok0 = rg * PT;
-    const int tok1 = min(Lb, (int)(ue - S) * PT);
+    const int tok0 = uniform(rg * PT);
+    const int tok1 = uniform(min(Lb, (int)(ue - S) * PT));
     const bool complete = (u == S) && (ue == Eu);
     const bool first = (u == u0);
     const int h = g * G + r16;
 
     // ---- query operand: B matrix of QK^T (K dim = head dims, N = heads) --------
     u32x4_t qop[NQ];
-    if (KVT == KV_F32) {
+    if constexpr (KVT == KV_F32) {
       const float* q = static_cast<const float*>(q_) + ((size_t)b * Hq + h) * D;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
@@ -349,139 +398,174 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = NEG_INF, l = 0.f;
-    bool bad = false;
 
-    int pgi = tok0 / P;
-    int j0 = tok0 - pgi * P;
-    const int32_t* btrow = bt + (size_t)b * MP;
+    // Loop state is wave-uniform; readfirstlane lets the compiler keep it in
+    // scalar registers, so page ids come from scalar loads (lgkmcnt) that do
+    // not serialise behind the vector K/V loads in flight.
+    int pgi = uniform(tok0 / P);
+    int j0 = uniform(tok0 - pgi * P);
+    // The page table is read through the constant address space: with a uniform
+    // index this is a scalar load.
+    const const_i32_ptr btrow = (const_i32_ptr)(bt + (size_t)b * MP);
+    auto page_of = [&](int idx) -> int {
+      idx = uniform(idx);
+      const int v = btrow[idx < MP ? idx : MP - 1];
+      return idx < MP ? v : -1;
+    };
+    // An invalid page id marks the segment bad (NaN result); page 0 is read instead.
+    u32x4_t kr[NSUB][NKK], vr[NDT];
+    auto load_k = [&](int pg, int j) {
+      const uint8_t* kc = kpool + chunk_elem(pg, g, Hkv, P, D) * EB;
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          kr[sub][kk] = ld16_stream(kc + (size_t)k_elem<E>(j + 16 * sub + r16, (c4 + 4 * kk) * E, P) * EB);
+    };
+    auto load_v = [&](int pg, int j) {
+      const uint8_t* vc = vpool + chunk_elem(pg, g, Hkv, P, D) * EB;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        vr[dt] = ld16_stream(vc + (size_t)v_elem<E>(j + 4 * c4, dt * 16 + r16, D) * EB);
+    };
+    int page = page_of(pgi);
+    bool bad = (unsigned)page >= (unsigned)NP;
+    int pg_ld = bad ? 0 : page;
+    float ksc = 1.f, vsc = 1.f;
+    if constexpr (KVT == KV_FP8) {
+      ksc = kscales[(size_t)pg_ld * Hkv + g];
+      vsc = vscales[(size_t)pg_ld * Hkv + g];
+    }
+    load_k(pg_ld, j0);
+    load_v(pg_ld, j0);
+
+    // Rolling pipeline: the next tile's K loads are issued as soon as this tile's
+    // QK^T has consumed kr, its V loads as soon as PV has consumed vr.  The last
+    // step re-reads its own tile (an L2 hit) so the loop body stays branch-free.
     for (int t = tok0; t < tok1; t += TS) {
-      const int page = pgi < MP ? btrow[pgi] : -1;
-      if ((unsigned)page >= (unsigned)NP) {
-        bad = true;
-      } else {
-        const size_t ch = chunk_elem(page, g, Hkv, P, D) * EB;
-        const uint8_t* kc = kpool + ch;
-        const uint8_t* vc = vpool + ch;
-        u32x4_t kr[NSUB][NKK], vr[NDT];
+      const bool has_next = t + TS < tok1;
+      int pgi_n = pgi, j_n = j0, page_n = page;
+      if (has_next) {
+        j_n = j0 + TS;
+        if (j_n == P) {
+          j_n = 0;
+          ++pgi_n;
+        }
+        page_n = page_of(pgi_n);
+      }
+      const bool bad_n = (unsigned)page_n >= (unsigned)NP;
+      const int pg_ld_n = bad_n ? 0 : page_n;
+      const float kmul = scale_log2 * ksc, vmul = vsc;
+
+      // ---- S = K q^T: rows = 16 tokens, columns = heads --------------------------
+      float s[NSUB][4];
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          if constexpr (KVT == KV_F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = mfma_f32(fbits(kr[sub][kk][e]), fbits(qop[kk][e]), acc);
+          } else if constexpr (KVT == KV_BF16) {
+            acc = mfma_bf16(kr[sub][kk], qop[kk], acc);
+          } else {
+            acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][0], kr[sub][kk][1]), qop[2 * kk], acc);
+            acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][2], kr[sub][kk][3]), qop[2 * kk + 1], acc);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[sub][i] = acc[i] * kmul;
+      }
+      load_k(pg_ld_n, j_n);
+      if constexpr (KVT == KV_FP8) {
+        ksc = kscales[(size_t)pg_ld_n * Hkv + g];
+        vsc = vscales[(size_t)pg_ld_n * Hkv + g];
+      }
+
+      // ---- ragged last step: mask logits, zero V of absent tokens ----------------
+      if (t + TS > tok1) {
 #pragma unroll
         for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-          for (int kk = 0; kk < NKK; ++kk)
-            kr[sub][kk] = ld16(kc + (size_t)k_elem<E>(j0 + 16 * sub + r16, (c4 + 4 * kk) * E, P) * EB);
+          for (int i = 0; i < 4; ++i)
+            if (t + 16 * sub + 4 * c4 + i >= tok1) s[sub][i] = NEG_INF;
+        u32x4_t keep;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t msk = 0;
+#pragma unroll
+          for (int byte = 0; byte < 4; ++byte) {
+            const int e = (4 * k + byte) / EB;
+            const int tok = t + 16 * (e >> 2) + 4 * c4 + (e & 3);
+            if (tok < tok1) msk |= 0xffu << (8 * byte);
+          }
+          keep[k] = msk;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vr[dt] &= keep;
+      }
+
+      // ---- online softmax (log2 domain) -------------------------------------------
+      float tmax = NEG_INF;
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[sub][i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(m, tmax);
+      const float alpha = mnew == NEG_INF ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+      float p[NSUB][4];
+      float lsum = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[sub][i] = __builtin_amdgcn_exp2f(s[sub][i] - mnew);
+          lsum += p[sub][i];
+        }
+      l = l * alpha + lsum;
+      if (__ballot(mnew > m)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+      }
+      m = mnew;
+
+      // ---- O^T += V^T P^T: rows = 16 dims, columns = heads -------------------------
+      if constexpr (KVT == KV_F32) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-          vr[dt] = ld16(vc + (size_t)v_elem<E>(j0 + 4 * c4, dt * 16 + r16, D) * EB);
-
-        float kmul = scale_log2, vmul = 1.f;
-        if (KVT == KV_FP8) {
-          kmul *= kscales[(size_t)page * Hkv + g];
-          vmul = vscales[(size_t)page * Hkv + g];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[dt] = mfma_f32(fbits(vr[dt][i]), p[0][i], O[dt]);
+      } else if constexpr (KVT == KV_BF16) {
+        u32x4_t ph, pl;
+        split_probs(p[0], p[1], 1.f, ph, pl);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          O[dt] = mfma_bf16(vr[dt], ph, O[dt]);
+          O[dt] = mfma_bf16(vr[dt], pl, O[dt]);
         }
-
-        // ---- S = K q^T: rows = 16 tokens, columns = heads ----------------------
-        float s[NSUB][4];
+      } else {
+        u32x4_t ph[2], pl[2];
+        split_probs(p[0], p[1], vmul, ph[0], pl[0]);
+        split_probs(p[2], p[3], vmul, ph[1], pl[1]);
 #pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) {
-            if (KVT == KV_F32) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc = mfma_f32(fbits(kr[sub][kk][e]), fbits(qop[kk][e]), acc);
-            } else if (KVT == KV_BF16) {
-              acc = mfma_bf16(kr[sub][kk], qop[kk], acc);
-            } else {
-              acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][0], kr[sub][kk][1]), qop[2 * kk], acc);
-              acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][2], kr[sub][kk][3]), qop[2 * kk + 1], acc);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[sub][i] = acc[i] * kmul;
-        }
-
-        // ---- ragged last step: mask logits, zero V of absent tokens ------------
-        if (t + TS > tok1) {
-#pragma unroll
-          for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (t + 16 * sub + 4 * c4 + i >= tok1) s[sub][i] = NEG_INF;
-          u32x4_t keep;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            uint32_t msk = 0;
-#pragma unroll
-            for (int byte = 0; byte < 4; ++byte) {
-              const int e = (4 * k + byte) / EB;
-              const int tok = t + 16 * (e >> 2) + 4 * c4 + (e & 3);
-              if (tok < tok1) msk |= 0xffu << (8 * byte);
-            }
-            keep[k] = msk;
-          }
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) vr[dt] &= keep;
-        }
-
-        // ---- online softmax (log2 domain) ---------------------------------------
-        float tmax = NEG_INF;
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[sub][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m, tmax);
-        const float alpha = mnew == NEG_INF ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-        float p[NSUB][4];
-        float lsum = 0.f;
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[sub][i] = __builtin_amdgcn_exp2f(s[sub][i] - mnew);
-            lsum += p[sub][i];
-          }
-        l = l * alpha + lsum;
-        if (__ballot(mnew > m)) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
-        }
-        m = mnew;
-
-        // ---- O^T += V^T P^T: rows = 16 dims, columns = heads ---------------------
-        if (KVT == KV_F32) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) O[dt] = mfma_f32(fbits(vr[dt][i]), p[0][i], O[dt]);
-        } else if (KVT == KV_BF16) {
-          u32x4_t ph, pl;
-          split_probs(p[0], p[1], 1.f, ph, pl);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            O[dt] = mfma_bf16(vr[dt], ph, O[dt]);
-            O[dt] = mfma_bf16(vr[dt], pl, O[dt]);
-          }
-        } else {
-          u32x4_t ph[2], pl[2];
-          split_probs(p[0], p[1], vmul, ph[0], pl[0]);
-          split_probs(p[2], p[3], vmul, ph[1], pl[1]);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const u32x4_t a0 = fp8x8_to_bf16x8(vr[dt][0], vr[dt][1]);
-            const u32x4_t a1 = fp8x8_to_bf16x8(vr[dt][2], vr[dt][3]);
-            O[dt] = mfma_bf16(a0, ph[0], O[dt]);
-            O[dt] = mfma_bf16(a0, pl[0], O[dt]);
-            O[dt] = mfma_bf16(a1, ph[1], O[dt]);
-            O[dt] = mfma_bf16(a1, pl[1], O[dt]);
-          }
+        for (int dt = 0; dt < NDT; ++dt) {
+          const u32x4_t a0 = fp8x8_to_bf16x8(vr[dt][0], vr[dt][1]);
+          const u32x4_t a1 = fp8x8_to_bf16x8(vr[dt][2], vr[dt][3]);
+          O[dt] = mfma_bf16(a0, ph[0], O[dt]);
+          O[dt] = mfma_bf16(a0, pl[0], O[dt]);
+          O[dt] = mfma_bf16(a1, ph[1], O[dt]);
+          O[dt] = mfma_bf16(a1, pl[1], O[dt]);
         }
       }
-      j0 += TS;
-      if (j0 == P) {
-        j0 = 0;
-        ++pgi;
-      }
+      load_v(pg_ld_n, j_n);
+
+      if (has_next) bad |= bad_n;
+      page = page_n;
+      pgi = pgi_n;
+      j0 = j_n;
     }
 
     // ---- finish the segment ------------------------------------------------------
@@ -519,7 +603,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       base = u;
       do {
         ++b;
-        Lb = seq_lens[b];
+        Lb = uniform(seq_lens[b]);
         npb = ranges_of(Lb, PT);
       } while (npb == 0);
     }
