@@ -10,8 +10,8 @@ the cache (one per layer, as in a model), so no step finds its K/V in the
 
 Prints one JSON line:
   value   = algorithmic HBM bytes of a step / wall time per step (GB/s),
-  roofline.achieved = algorithmic bytes of one decode call / its mean duration
-            measured with HIP events on the launch stream,
+  roofline.achieved = algorithmic bytes of one decode_step call / its mean
+            duration measured with HIP events on the launch stream,
   cpu_baseline = the fp64 CPU oracle on this host (append + decode, full batch).
 """
 from __future__ import annotations
@@ -212,17 +212,14 @@ def main():
     torch.cuda.synchronize()
 
     def step(i, ev=None, k=0):
+        """One decode iteration of one layer: append + attention in one decode_step call."""
         s = dsteps[i % len(dsteps)]
         kp, vp = kps[i % layers], vps[i % layers]
-        pkv.kv_append(s["kn"], s["vn"], wl.kv_dtype, bt, s["sl"], kp, vp, wl.Hkv, wl.D, wl.P)
         if ev is not None:
             ev.record(2 * k)
-        if wl.kv_dtype == "fp8":
-            pkv.paged_attn_decode_fp8(q, wl.q_dtype, kp, vp, ks, vs, bt, s["sl"], wl.Hq, wl.Hkv, wl.D, wl.P,
-                                      wl.scale, out, wl.out_dtype, ws, wl.partition_tokens)
-        else:
-            pkv.paged_attn_decode(q, wl.q_dtype, kp, vp, wl.kv_dtype, bt, s["sl"], wl.Hq, wl.Hkv, wl.D,
-                                  wl.P, wl.scale, out, wl.out_dtype, ws, wl.partition_tokens)
+        pkv.decode_step(q, wl.q_dtype, s["kn"], s["vn"], kp, vp, wl.kv_dtype, bt, s["sl"], wl.Hq, wl.Hkv,
+                        wl.D, wl.P, wl.scale, out, wl.out_dtype, ws, k_scales=ks, v_scales=vs,
+                        partition_tokens=wl.partition_tokens)
         if ev is not None:
             ev.record(2 * k + 1)
 
@@ -240,17 +237,15 @@ def main():
     evs.close()
     dec_mean = float(np.mean(dec_ms))
 
-    step_bytes, dec_bytes, kv_bytes = 0, 0, 0
+    step_bytes, kv_bytes = 0, 0
     for i in range(args.steps):
         d, a, kvb = alg_bytes(wl, steps[(args.warmup + i) % len(steps)]["seq_lens"])
         step_bytes += d + a
-        dec_bytes += d
         kv_bytes += kvb
     step_bytes /= args.steps
-    dec_bytes /= args.steps
     kv_bytes /= args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = dec_bytes / (dec_mean * 1e-3) / 1e9
+    achieved = step_bytes / (dec_mean * 1e-3) / 1e9
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"decode_{args.workload}_traffic.json")
@@ -270,15 +265,15 @@ def main():
                    "head_dim": wl.D, "page_size": wl.P,
                    "mean_seq_len": float(np.mean(steps[0]["seq_lens"])),
                    "partition_tokens": wl.partition_tokens, "layers_rotated": layers,
-                   "step": "kv_append + paged_attn_decode (split + LSE merge)"},
+                   "step": "decode_step: kv_append fused into paged decode (split kernel + LSE merge kernel)"},
         "seqs_per_s_per_layer": round(wl.B / (ms_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(kv_bytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "paged_attn_decode call (split kernel + merge kernel)",
-                     "decode_ms_mean": round(dec_mean, 5), "decode_ms_min": round(min(dec_ms), 5),
-                     "alg_bytes_per_call": int(dec_bytes)},
+                     "kernel": "decode_step call (decode_split_kernel + decode_merge_kernel)",
+                     "call_ms_mean": round(dec_mean, 5), "call_ms_min": round(min(dec_ms), 5),
+                     "alg_bytes_per_call": int(step_bytes)},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds)

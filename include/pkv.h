@@ -157,6 +157,31 @@ int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype,
                               void* out, pkv_dtype out_dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* decode_step - one whole decode iteration of the cache for one layer: the
+ * append of pkv_kv_append followed by the attention of pkv_paged_attn_decode
+ * (or of pkv_paged_attn_decode_fp8 when kv_dtype is FP8_E4M3), in one launch.
+ *
+ * The first page's "runtime execution model" has each iteration's attention
+ * both update and read the cache pages.  Here the wavefront that owns the tile
+ * holding token L_b - 1 of (b, g) takes k_new[b][g] / v_new[b][g] straight
+ * into its registers and stores them into the page slot, so the append costs
+ * no launch of its own.  Results equal pkv_kv_append then decode with the same
+ * seq_lens (the pool bytes exactly; out up to the rounding order).
+ * k_scales / v_scales: required for FP8_E4M3 (k_new / v_new are then bytes
+ * already quantised with that page's scale), ignored otherwise.
+ * Same sizes, dtypes, workspace and errors as the decode entry points, plus
+ * PKV_E_NULL for a NULL k_new / v_new.  A sequence whose slot L_b - 1 lies on
+ * a bad page id stores nothing and gets NaN rows. */
+int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_new,
+                    void* k_pool, void* v_pool, pkv_dtype kv_dtype,
+                    const float* k_scales, const float* v_scales,
+                    const int32_t* block_tables, int max_pages_per_seq,
+                    const int32_t* seq_lens, int batch, int num_pages,
+                    int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                    float scale, int partition_tokens,
+                    void* out, pkv_dtype out_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* debug_gather - copy each sequence's cached tokens out of the pages into
  * contiguous rows, through the same page-table lookup and chunk addressing
  * the decode kernels use (for bit-exact tests of that address path).

@@ -83,6 +83,20 @@ def paged_attn_decode_fp8(q, q_dtype, k_pool, v_pool, k_scales, v_scales, block_
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def decode_step(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, block_tables, seq_lens,
+                num_q_heads, num_kv_heads, head_dim, page_size, scale, out, out_dtype, workspace,
+                k_scales=None, v_scales=None, partition_tokens=0, stream=None):
+    """kv_append + decode in one launch (k_new/v_new become token seq_lens[b]-1)."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("decode_step", lib().pkv_decode_step(
+        _ptr(q), _code(q_dtype), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _code(kv_dtype),
+        _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), MP, _ptr(seq_lens), B, NP, num_q_heads,
+        num_kv_heads, head_dim, page_size, float(scale), int(partition_tokens), _ptr(out),
+        _code(out_dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
 def debug_gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, num_kv_heads, head_dim,
                  page_size, k_out, v_out, stream=None):
     """Copy cached tokens to contiguous [B, Hkv, MP*P, D] rows (tests of the address path)."""

@@ -15,6 +15,8 @@ SIGNATURES = {
                                    _f, _i, _vp, _i, _vp, _sz, _vp]),
     "pkv_paged_attn_decode_fp8": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i,
                                        _i, _i, _f, _i, _vp, _i, _vp, _sz, _vp]),
+    "pkv_decode_step": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i,
+                             _i, _f, _i, _vp, _i, _vp, _sz, _vp]),
     "pkv_debug_gather": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "pkv_strerror": (ctypes.c_char_p, [_i]),
     "pkv_last_error": (ctypes.c_char_p, []),

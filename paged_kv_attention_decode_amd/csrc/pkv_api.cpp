@@ -83,7 +83,8 @@ int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
                const float* k_scales, const float* v_scales, const int32_t* block_tables,
                int max_pages, const int32_t* seq_lens, int batch, int num_pages, int num_q_heads,
                int num_kv_heads, int head_dim, int page_size, float scale, int partition_tokens,
-               void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+               void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream,
+               const void* k_new = nullptr, const void* v_new = nullptr) {
   int rc = check_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_pages, seq_lens, batch,
                         num_pages, num_q_heads, num_kv_heads, head_dim, page_size, partition_tokens,
                         out, out_dtype, workspace, workspace_bytes);
@@ -91,6 +92,8 @@ int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
   if (batch == 0) return PKV_OK;
   pkv::DecodeArgs a;
   a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.k_scales = k_scales;
@@ -190,6 +193,24 @@ int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype, const void* k_po
   return run_decode(q, q_dtype, k_pool, v_pool, PKV_FP8_E4M3, k_scales, v_scales, block_tables,
                     max_pages_per_seq, seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim,
                     page_size, scale, partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_new, void* k_pool,
+                    void* v_pool, pkv_dtype kv_dtype, const float* k_scales, const float* v_scales,
+                    const int32_t* block_tables, int max_pages_per_seq, const int32_t* seq_lens, int batch,
+                    int num_pages, int num_q_heads, int num_kv_heads, int head_dim, int page_size, float scale,
+                    int partition_tokens, void* out, pkv_dtype out_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && (!k_new || !v_new)) return fail(PKV_E_NULL, "k_new / v_new are NULL");
+  if (kv_dtype == PKV_FP8_E4M3) {
+    if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 scales are NULL");
+  } else {
+    k_scales = v_scales = nullptr;
+  }
+  return run_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scales, v_scales, block_tables, max_pages_per_seq,
+                    seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
+                    partition_tokens, out, out_dtype, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 int pkv_debug_gather(const void* k_pool, const void* v_pool, pkv_dtype kv_dtype, const int32_t* block_tables,

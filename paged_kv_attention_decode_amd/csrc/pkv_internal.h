@@ -48,6 +48,8 @@ struct DecodeArgs {
   const void* q;
   const void* k_pool;
   const void* v_pool;
+  const void* k_new;       // step entry only (else null): token appended at L_b - 1
+  const void* v_new;
   const float* k_scales;   // fp8 only
   const float* v_scales;   // fp8 only
   const int32_t* block_tables;

@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "pkv_internal.h"
 
@@ -257,13 +258,13 @@ __device__ void merge_ranges(const float* __restrict__ partials, int64_t slot0, 
 // wave, number of contributors, slot of the first) for the merge kernel.
 // ---------------------------------------------------------------------------
 template <int KVT, int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void decode_split_kernel(
-    const void* __restrict__ q_, const uint8_t* __restrict__ kpool,
-    const uint8_t* __restrict__ vpool, const float* __restrict__ kscales,
-    const float* __restrict__ vscales, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ seq_lens, void* __restrict__ out_, float* __restrict__ partials,
-    int4* __restrict__ descs, int B, int MP, int NP, int Hq, int Hkv, int G, int P, int PT,
-    int Wmax, float scale_log2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
+    const void* __restrict__ q_, const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
+    const void* __restrict__ k_new, const void* __restrict__ v_new,
+    const float* __restrict__ kscales, const float* __restrict__ vscales,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens, void* __restrict__ out_,
+    float* __restrict__ partials, int4* __restrict__ descs, int B, int MP, int NP, int Hq, int Hkv,
+    int G, int P, int PT, int Wmax, float scale_log2) {
   constexpr int EB = Kv<KVT>::EB;
   constexpr int E = 16 / EB;        // elements per 16-byte group
   constexpr int TS = 4 * E;         // tokens per step (= V block)
@@ -275,7 +276,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, c4 = lane >> 4;
   // wave-uniform (the compiler cannot tell that threadIdx.x >> 6 is)
-  const int w = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int wv = uniform(threadIdx.x >> 6);
+  const int w = uniform(blockIdx.x * 4 + wv);
+  // per-wave LDS slots: the step entry's new K and V rows, the query operand
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[4][2 * D * Kv<KVT>::EB];
+  __shared__ u32x4_t s_q[4][NQ][64];
 
   // ---- this wave's unit range -------------------------------------------------
   // seq_lens of the first NC*64 sequences are read once, in one round trip, and
@@ -377,21 +382,38 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int h = g * G + r16;
 
     // ---- query operand: B matrix of QK^T (K dim = head dims, N = heads) --------
-    u32x4_t qop[NQ];
-    if constexpr (KVT == KV_F32) {
-      const float* q = static_cast<const float*>(q_) + ((size_t)b * Hq + h) * D;
+    // Parked in this wave's LDS slot and re-read next to each MFMA, so it holds
+    // no registers across the streaming loop.
+    {
+      __builtin_amdgcn_wave_barrier();      // previous segment's reads are done
+      if constexpr (KVT == KV_F32) {
+        const float* q = static_cast<const float*>(q_) + ((size_t)b * Hq + h) * D;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        qop[kk] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + (c4 + 4 * kk) * 4)) : u32x4_t{0, 0, 0, 0};
-    } else {
-      const uint16_t* q = static_cast<const uint16_t*>(q_) + ((size_t)b * Hq + h) * D;
+        for (int kk = 0; kk < NKK; ++kk)
+          s_q[wv][kk][lane] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + (c4 + 4 * kk) * 4)) : u32x4_t{0, 0, 0, 0};
+      } else {
+        const uint16_t* q = static_cast<const uint16_t*>(q_) + ((size_t)b * Hq + h) * D;
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        // bf16 cache: group kk covers dims 8*(c4+4kk) .. +8.
-        // fp8 cache: group kk covers dims 16*(c4+4kk) .. +16, split in two halves.
-        const int d0 = KVT == KV_BF16 ? 8 * (c4 + 4 * i) : 16 * (c4 + 4 * (i >> 1)) + 8 * (i & 1);
-        qop[i] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + d0)) : u32x4_t{0, 0, 0, 0};
+        for (int i = 0; i < NQ; ++i) {
+          // bf16 cache: group kk covers dims 8*(c4+4kk) .. +8.
+          // fp8 cache: group kk covers dims 16*(c4+4kk) .. +16, split in two halves.
+          const int d0 = KVT == KV_BF16 ? 8 * (c4 + 4 * i) : 16 * (c4 + 4 * (i >> 1)) + 8 * (i & 1);
+          s_q[wv][i][lane] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + d0)) : u32x4_t{0, 0, 0, 0};
+        }
       }
+    }
+    auto qop = [&](int i) -> u32x4_t { return s_q[wv][i][lane]; };
+
+    // step entry: the segment that ends the sequence reads the new token row;
+    // it is parked in this wave's LDS slot once the first tile's loads are out.
+    const bool has_new = k_new != nullptr && tok1 == Lb;
+    constexpr int NEWCH = D * EB / 16;              // 16-byte chunks per K (or V) row
+    u32x4_t new_chunk = {0, 0, 0, 0};
+    if (has_new && lane < 2 * NEWCH) {
+      const size_t nrow = (((size_t)b * Hkv + g) * D) * EB;
+      const uint8_t* src = lane < NEWCH ? static_cast<const uint8_t*>(k_new) + nrow
+                                        : static_cast<const uint8_t*>(v_new) + nrow - NEWCH * 16;
+      new_chunk = ld16(src + lane * 16);
     }
 
     f32x4_t O[NDT];
@@ -420,13 +442,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
-          kr[sub][kk] = ld16_stream(kc + (size_t)k_elem<E>(j + 16 * sub + r16, (c4 + 4 * kk) * E, P) * EB);
+          kr[sub][kk] = ld16_stream(kc + (uint32_t)(k_elem<E>(j + 16 * sub + r16, (c4 + 4 * kk) * E, P) * EB));
     };
     auto load_v = [&](int pg, int j) {
       const uint8_t* vc = vpool + chunk_elem(pg, g, Hkv, P, D) * EB;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        vr[dt] = ld16_stream(vc + (size_t)v_elem<E>(j + 4 * c4, dt * 16 + r16, D) * EB);
+        vr[dt] = ld16_stream(vc + (uint32_t)(v_elem<E>(j + 4 * c4, dt * 16 + r16, D) * EB));
     };
     int page = page_of(pgi);
     bool bad = (unsigned)page >= (unsigned)NP;
@@ -438,14 +460,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
     load_k(pg_ld, j0);
     load_v(pg_ld, j0);
+    if (has_new && lane < 2 * NEWCH) *reinterpret_cast<u32x4_t*>(s_new[wv] + lane * 16) = new_chunk;
 
-    // Rolling pipeline: the next tile's K loads are issued as soon as this tile's
-    // QK^T has consumed kr, its V loads as soon as PV has consumed vr.  The last
-    // step re-reads its own tile (an L2 hit) so the loop body stays branch-free.
-    for (int t = tok0; t < tok1; t += TS) {
-      const bool has_next = t + TS < tok1;
+    // One tile of TS tokens.  Streaming tiles (LAST = false) always have a next
+    // tile: its K loads go out as soon as QK^T has consumed kr and its V loads
+    // as soon as PV has consumed vr (rolling pipeline, no stores, no masking).
+    // The last tile of a segment (LAST = true) issues no loads; it masks tokens
+    // at or past tok1 and, for the step entry, takes in the appended token.
+    auto tile = [&](const int t, auto last_tag) {
+      constexpr bool LAST = decltype(last_tag)::value;
       int pgi_n = pgi, j_n = j0, page_n = page;
-      if (has_next) {
+      if constexpr (!LAST) {
         j_n = j0 + TS;
         if (j_n == P) {
           j_n = 0;
@@ -457,6 +482,44 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       const int pg_ld_n = bad_n ? 0 : page_n;
       const float kmul = scale_log2 * ksc, vmul = vsc;
 
+      if constexpr (LAST) {
+        // ---- fused append (step entry): the tile holding token Lb-1 takes this
+        // step's k_new / v_new row (prefetched at segment start) into its
+        // registers in place of the slot's old contents.  The row is stored into
+        // the page by the merge kernel, so this kernel issues no pool stores.
+        if (has_new) {
+          const int rel = Lb - 1 - t;
+          const int sub_t = rel >> 4, r_t = rel & 15;
+          const int c_t = r_t >> 2, e_t = 4 * sub_t + (r_t & 3);
+          typedef typename Kv<KVT>::elem_t T;
+          // bitwise merge (no data-dependent array index, which would force the
+          // tile registers into scratch)
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            const u32x4_t nv = *reinterpret_cast<const u32x4_t*>(s_new[wv] + (c4 + 4 * kk) * 16);
+#pragma unroll
+            for (int sub = 0; sub < NSUB; ++sub) {
+              const uint32_t m = (r16 == r_t && sub == sub_t) ? 0xffffffffu : 0u;
+              kr[sub][kk] = (kr[sub][kk] & ~m) | (nv & m);
+            }
+          }
+          if (c4 == c_t) {
+            const int kw = (e_t * EB) >> 2, sh = ((e_t * EB) & 3) * 8;
+            const uint32_t msk = (uint32_t)((1ull << (8 * EB)) - 1ull) << sh;
+            const T* vrow = reinterpret_cast<const T*>(s_new[wv] + NEWCH * 16);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const uint32_t bits = (uint32_t)vrow[dt * 16 + r16] << sh;
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                const uint32_t mx = x == kw ? msk : 0u;
+                vr[dt][x] = (vr[dt][x] & ~mx) | (bits & mx);
+              }
+            }
+          }
+        }
+      }
+
       // ---- S = K q^T: rows = 16 tokens, columns = heads --------------------------
       float s[NSUB][4];
 #pragma unroll
@@ -465,45 +528,52 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           if constexpr (KVT == KV_F32) {
+            {
+              const u32x4_t qv = qop(kk);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc = mfma_f32(fbits(kr[sub][kk][e]), fbits(qop[kk][e]), acc);
+              for (int e = 0; e < 4; ++e) acc = mfma_f32(fbits(kr[sub][kk][e]), fbits(qv[e]), acc);
+            }
           } else if constexpr (KVT == KV_BF16) {
-            acc = mfma_bf16(kr[sub][kk], qop[kk], acc);
+            acc = mfma_bf16(kr[sub][kk], qop(kk), acc);
           } else {
-            acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][0], kr[sub][kk][1]), qop[2 * kk], acc);
-            acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][2], kr[sub][kk][3]), qop[2 * kk + 1], acc);
+            acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][0], kr[sub][kk][1]), qop(2 * kk), acc);
+            acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][2], kr[sub][kk][3]), qop(2 * kk + 1), acc);
           }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[sub][i] = acc[i] * kmul;
       }
-      load_k(pg_ld_n, j_n);
-      if constexpr (KVT == KV_FP8) {
-        ksc = kscales[(size_t)pg_ld_n * Hkv + g];
-        vsc = vscales[(size_t)pg_ld_n * Hkv + g];
+      if constexpr (!LAST) {
+        load_k(pg_ld_n, j_n);
+        if constexpr (KVT == KV_FP8) {
+          ksc = kscales[(size_t)pg_ld_n * Hkv + g];
+          vsc = vscales[(size_t)pg_ld_n * Hkv + g];
+        }
       }
 
-      // ---- ragged last step: mask logits, zero V of absent tokens ----------------
-      if (t + TS > tok1) {
+      // ---- last step: mask logits, zero V of absent tokens -----------------------
+      if constexpr (LAST) {
+        if (t + TS > tok1) {
 #pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub)
+          for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t + 16 * sub + 4 * c4 + i >= tok1) s[sub][i] = NEG_INF;
-        u32x4_t keep;
+            for (int i = 0; i < 4; ++i)
+              if (t + 16 * sub + 4 * c4 + i >= tok1) s[sub][i] = NEG_INF;
+          u32x4_t keep;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t msk = 0;
+          for (int k = 0; k < 4; ++k) {
+            uint32_t msk = 0;
 #pragma unroll
-          for (int byte = 0; byte < 4; ++byte) {
-            const int e = (4 * k + byte) / EB;
-            const int tok = t + 16 * (e >> 2) + 4 * c4 + (e & 3);
-            if (tok < tok1) msk |= 0xffu << (8 * byte);
+            for (int byte = 0; byte < 4; ++byte) {
+              const int e = (4 * k + byte) / EB;
+              const int tok = t + 16 * (e >> 2) + 4 * c4 + (e & 3);
+              if (tok < tok1) msk |= 0xffu << (8 * byte);
+            }
+            keep[k] = msk;
           }
-          keep[k] = msk;
-        }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) vr[dt] &= keep;
+          for (int dt = 0; dt < NDT; ++dt) vr[dt] &= keep;
+        }
       }
 
       // ---- online softmax (log2 domain) -------------------------------------------
@@ -560,13 +630,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
           O[dt] = mfma_bf16(a1, pl[1], O[dt]);
         }
       }
-      load_v(pg_ld_n, j_n);
+      if constexpr (!LAST) {
+        load_v(pg_ld_n, j_n);
+        bad |= bad_n;
+        page = page_n;
+        pgi = pgi_n;
+        j0 = j_n;
+      }
+    };
 
-      if (has_next) bad |= bad_n;
-      page = page_n;
-      pgi = pgi_n;
-      j0 = j_n;
-    }
+    int t = tok0;
+    for (; t + TS < tok1; t += TS) tile(t, std::false_type{});
+    tile(t, std::true_type{});
 
     // ---- finish the segment ------------------------------------------------------
     float lt = l + __shfl_xor(l, 16);
@@ -614,18 +689,38 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 // Decode, part 2: one wave per (b, g) combines the partial ranges of pairs that
 // were split over several waves (log-sum-exp merge, see merge_ranges).
 // ---------------------------------------------------------------------------
-template <bool OUT_BF16>
+template <int KVT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int32_t* __restrict__ seq_lens, const int4* __restrict__ descs,
-    const float* __restrict__ partials, void* __restrict__ out_, int B, int Hq, int Hkv, int G, int D) {
+    const float* __restrict__ partials, void* __restrict__ out_, int B, int Hq, int Hkv, int G, int D,
+    const void* __restrict__ k_new, const void* __restrict__ v_new, const int32_t* __restrict__ bt,
+    void* __restrict__ kpool, void* __restrict__ vpool, int MP, int NP, int P) {
   const int bg = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (bg >= B * Hkv) return;
+  const int lane = threadIdx.x & 63;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int L = seq_lens[b];
+  if (L <= 0) return;                    // empty: rows zeroed by the split kernel, nothing appended
+  if (k_new != nullptr) {
+    // step entry: store this step's token into slot L-1 (the split kernel
+    // already attended to it from registers)
+    typedef typename Kv<KVT>::elem_t T;
+    constexpr int E = 16 / Kv<KVT>::EB;
+    const int t = L - 1, pgi = t / P, j = t - pgi * P;
+    const int page = pgi < MP ? bt[(size_t)b * MP + pgi] : -1;
+    if ((unsigned)page < (unsigned)NP) {
+      const size_t ch = chunk_elem(page, g, Hkv, P, D);
+      const T* kn = static_cast<const T*>(k_new) + ((size_t)b * Hkv + g) * D;
+      const T* vn = static_cast<const T*>(v_new) + ((size_t)b * Hkv + g) * D;
+      for (int d = lane; d < D; d += 64) {
+        static_cast<T*>(kpool)[ch + k_elem<E>(j, d, P)] = kn[d];
+        static_cast<T*>(vpool)[ch + v_elem<E>(j, d, D)] = vn[d];
+      }
+    }
+  }
   const int4 d = descs[bg];
-  if (L <= 0 || d.y <= 1) return;        // empty (zeroed) or finished by one wave
-  merge_ranges<OUT_BF16>(partials, d.z, d.x, d.y, out_, ((size_t)b * Hq + (size_t)g * G) * D, G, D,
-                         threadIdx.x & 63);
+  if (d.y <= 1) return;                  // finished by one wave
+  merge_ranges<OUT_BF16>(partials, d.z, d.x, d.y, out_, ((size_t)b * Hq + (size_t)g * G) * D, G, D, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -699,9 +794,9 @@ struct DevInfo {
 std::mutex g_mu;
 DevInfo g_dev[64];
 
-typedef void (*decode_fn_t)(const void*, const uint8_t*, const uint8_t*, const float*, const float*,
-                            const int32_t*, const int32_t*, void*, float*, int4*, int, int, int, int, int,
-                            int, int, int, int, float);
+typedef void (*decode_fn_t)(const void*, const uint8_t*, const uint8_t*, const void*, const void*, const float*,
+                            const float*, const int32_t*, const int32_t*, void*, float*, int4*, int, int, int,
+                            int, int, int, int, int, int, float);
 
 template <int KVT, int D, bool OB>
 decode_fn_t decode_fn() {
@@ -800,19 +895,28 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const float scale_log2 = a.scale * 1.4426950408889634f;
   dim3 grid((Wmax + 3) / 4), block(256);
   hipLaunchKernelGGL(fn, grid, block, 0, s, a.q, static_cast<const uint8_t*>(a.k_pool),
-                     static_cast<const uint8_t*>(a.v_pool), a.k_scales, a.v_scales, a.block_tables,
+                     static_cast<const uint8_t*>(a.v_pool), a.k_new, a.v_new, a.k_scales,
+                     a.v_scales, a.block_tables,
                      a.seq_lens, a.out, a.partials, a.descs, a.batch, a.max_pages, a.num_pages,
                      a.num_q_heads, a.num_kv_heads, G, a.page_size, a.partition_tokens, Wmax, scale_log2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int pairs = a.batch * a.num_kv_heads;
   dim3 mgrid((pairs + 3) / 4);
-  if (a.out_bf16)
-    hipLaunchKernelGGL(decode_merge_kernel<true>, mgrid, block, 0, s, a.seq_lens, a.descs, a.partials, a.out,
-                       a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<false>, mgrid, block, 0, s, a.seq_lens, a.descs, a.partials, a.out,
-                       a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim);
+  void* kp = const_cast<void*>(a.k_pool);
+  void* vp = const_cast<void*>(a.v_pool);
+#define PKV_MERGE(K, OB)                                                                           \
+  hipLaunchKernelGGL((decode_merge_kernel<K, OB>), mgrid, block, 0, s, a.seq_lens, a.descs, a.partials, \
+                     a.out, a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim, a.k_new, a.v_new,    \
+                     a.block_tables, kp, vp, a.max_pages, a.num_pages, a.page_size)
+  if (a.kvt == KV_F32) {
+    if (a.out_bf16) PKV_MERGE(KV_F32, true); else PKV_MERGE(KV_F32, false);
+  } else if (a.kvt == KV_BF16) {
+    if (a.out_bf16) PKV_MERGE(KV_BF16, true); else PKV_MERGE(KV_BF16, false);
+  } else {
+    if (a.out_bf16) PKV_MERGE(KV_FP8, true); else PKV_MERGE(KV_FP8, false);
+  }
+#undef PKV_MERGE
   return hipGetLastError();
 }
 

@@ -59,6 +59,16 @@ class DeviceWorkload:
                                   self.ws, pt)
         return out
 
+    def step(self, k_new, v_new, seq_lens, partition_tokens=None, out=None):
+        """Fused append + decode (decode_step entry point)."""
+        wl = self.wl
+        pt = wl.partition_tokens if partition_tokens is None else partition_tokens
+        out = self.out if out is None else out
+        pkv.decode_step(self.q, wl.q_dtype, k_new, v_new, self.k_pool, self.v_pool, wl.kv_dtype, self.bt,
+                        seq_lens, wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, self.ws,
+                        k_scales=self.ks, v_scales=self.vs, partition_tokens=pt)
+        return out
+
     def append(self, k_new, v_new, seq_lens):
         wl = self.wl
         pkv.kv_append(k_new, v_new, wl.kv_dtype, self.bt, seq_lens, self.k_pool, self.v_pool,

@@ -100,3 +100,21 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_native, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(_native.NativeLibraryMissing):
         _native.lib()
+
+
+def _step(**over):
+    a = dict(q=1, qdt=1, kn=1, vn=1, kp=1, vp=1, kvdt=1, ks=0, vs=0, bt=1, mp=4, sl=1, b=2, np_=8, hq=8,
+             hkv=2, d=128, p=64, scale=0.1, pt=0, out=1, odt=1, ws=1, wsb=1 << 30)
+    a.update(over)
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return pkv.lib().pkv_decode_step(vp(a["q"]), a["qdt"], vp(a["kn"]), vp(a["vn"]), vp(a["kp"]), vp(a["vp"]),
+                                     a["kvdt"], vp(a["ks"]), vp(a["vs"]), vp(a["bt"]), a["mp"], vp(a["sl"]),
+                                     a["b"], a["np_"], a["hq"], a["hkv"], a["d"], a["p"], a["scale"], a["pt"],
+                                     vp(a["out"]), a["odt"], vp(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [(dict(kn=0), -1), (dict(vn=0), -1), (dict(kvdt=2, p=64), -1),
+                                       (dict(kvdt=2, p=32, ks=1, vs=1), -2), (dict(d=32), -2),
+                                       (dict(qdt=0), -3), (dict(hq=7), -2)])
+def test_step_rejects_bad_arguments(over, code):
+    assert _step(**over) == code

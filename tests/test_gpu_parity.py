@@ -241,6 +241,65 @@ def test_error_codes_on_device():
     assert e.value.code == -3
 
 
+# ------------------------------------------------- fused step (append+decode) ----
+
+STEP_CASES = [
+    dict(seed=71, lens=[1, 2, 31, 32, 33, 64, 65, 300], Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16"),
+    dict(seed=72, lens=[1, 15, 16, 17, 50], Hq=8, Hkv=4, D=64, P=16, kv_dtype="f32"),
+    dict(seed=73, lens=[1, 63, 64, 65, 129, 700], Hq=32, Hkv=8, D=128, P=64, kv_dtype="fp8"),
+    dict(seed=74, lens=[0, 128, 129, 5000], Hq=64, Hkv=8, D=128, P=128, kv_dtype="bf16", partition_tokens=512),
+    dict(seed=75, lens=[1, 2, 3, 4, 5] * 100, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16", out_dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("spec", STEP_CASES, ids=lambda s: f"{s['kv_dtype']}-P{s['P']}-s{s['seed']}")
+def test_step_equals_append_then_decode(spec):
+    """decode_step leaves the pools byte-identical to kv_append, and its output
+    matches the oracle run on the appended pool."""
+    wl = configs.custom(**spec)
+    lens_now = wl.seq_lens.copy()
+    lens_prev = np.maximum(lens_now - 1, 0)
+    # the cache holds lens_prev tokens; token lens_now-1 arrives this step
+    ki, vi = layout.k_chunk_index(wl.P, wl.D, wl.kv_dtype), layout.v_chunk_index(wl.P, wl.D, wl.kv_dtype)
+    kp = layout.empty_pool(wl.num_pages, wl.Hkv, wl.P, wl.D, wl.kv_dtype)
+    vp = layout.empty_pool(wl.num_pages, wl.Hkv, wl.P, wl.D, wl.kv_dtype)
+    knew = np.zeros((wl.B, wl.Hkv, wl.D), layout.NP_DTYPE[wl.kv_dtype])
+    vnew = np.zeros_like(knew)
+    for b in range(wl.B):
+        n = int(lens_now[b])
+        k, v, _, _ = configs.seq_tokens(wl.seed, b, n, wl.Hkv, wl.D, wl.kv_dtype, wl.P)
+        pages = wl.block_tables[b, :int(configs.pages_needed(np.array([n]), wl.P)[0])]
+        layout.pack_sequence(kp, pages, k[:int(lens_prev[b])], wl.P, ki, wl.kv_dtype)
+        layout.pack_sequence(vp, pages, v[:int(lens_prev[b])], wl.P, vi, wl.kv_dtype)
+        if n:
+            knew[b], vnew[b] = k[n - 1], v[n - 1]
+    wl.k_pool, wl.v_pool = kp, vp
+    dw = DeviceWorkload(wl)
+    out = gpu_out(dw.step(dev_tensor(knew), dev_tensor(vnew), dw.sl))
+    ref_k, ref_v = kp.copy(), vp.copy()
+    c_oracle.append(knew, vnew, wl.kv_dtype, wl.block_tables, lens_now, ref_k, ref_v, wl.P)
+    assert np.array_equal(host_bytes(dw.k_pool), ref_k.view(np.uint8).reshape(-1))
+    assert np.array_equal(host_bytes(dw.v_pool), ref_v.view(np.uint8).reshape(-1))
+    ref = oracle_decode(wl, ref_k, ref_v, lens_now)
+    check_close(out, ref, wl.kv_dtype, f"step seed {spec['seed']}", out_rounding=wl.out_dtype == "bf16")
+
+
+def test_step_bad_page_stores_nothing():
+    wl = configs.custom(seed=76, lens=[70, 70], Hq=8, Hkv=2, D=128, P=64, kv_dtype="bf16")
+    wl.block_tables[1, 1] = wl.num_pages + 3          # slot 69 of sequence 1 lies on a bad page
+    dw = DeviceWorkload(wl)
+    before = host_bytes(dw.k_pool).copy()
+    kn = dev_tensor(np.full((2, 2, 128), 0x3F80, np.uint16))
+    out = gpu_out(dw.step(kn, kn, dw.sl))
+    after = host_bytes(dw.k_pool)
+    assert np.isnan(out[1]).all() and np.isfinite(out[0]).all()
+    # only sequence 0's slot 69 changed
+    changed = np.nonzero(before != after)[0]
+    pg = wl.block_tables[0, 1]
+    lo, hi = pg * wl.Hkv * wl.P * wl.D * 2, (pg + 1) * wl.Hkv * wl.P * wl.D * 2
+    assert changed.size > 0 and (changed >= lo).all() and (changed < hi).all()
+
+
 # --------------------------------------------------------- the five configs ----
 
 def test_config_tiny_fp32():
@@ -278,6 +337,27 @@ def test_config_inflight_16_steps():
             pairs = np.stack([rng.integers(0, wl.B, 48), rng.integers(0, wl.Hq, 48)], 1)
             ref = oracle_decode(wl, ref_k, ref_v, st.seq_lens, pairs=pairs)
             check_close(out[pairs[:, 0], pairs[:, 1]], ref[pairs[:, 0], pairs[:, 1]], "bf16", f"step {s}")
+
+
+def test_config_inflight_16_steps_fused():
+    """The same 16 iterations through the fused decode_step entry point."""
+    wl = configs.inflight_bf16()
+    dw = DeviceWorkload(wl)
+    ref_k, ref_v = wl.k_pool.copy(), wl.v_pool.copy()
+    rng = np.random.default_rng(1)
+    for s, st in enumerate(wl.steps):
+        sl = dev_tensor(st.seq_lens)
+        out = gpu_out(dw.step(dev_tensor(st.k_new), dev_tensor(st.v_new), sl))
+        c_oracle.append(st.k_new, st.v_new, "bf16", wl.block_tables, st.seq_lens, ref_k, ref_v, wl.P)
+        if s in (0, 7, len(wl.steps) - 1):
+            assert np.array_equal(host_bytes(dw.k_pool), ref_k.view(np.uint8).reshape(-1))
+            assert np.array_equal(host_bytes(dw.v_pool), ref_v.view(np.uint8).reshape(-1))
+        if s == len(wl.steps) - 1:
+            check_close(out, oracle_decode(wl, ref_k, ref_v, st.seq_lens), "bf16", f"fused step {s}")
+        else:
+            pairs = np.stack([rng.integers(0, wl.B, 32), rng.integers(0, wl.Hq, 32)], 1)
+            ref = oracle_decode(wl, ref_k, ref_v, st.seq_lens, pairs=pairs)
+            check_close(out[pairs[:, 0], pairs[:, 1]], ref[pairs[:, 0], pairs[:, 1]], "bf16", f"fused step {s}")
 
 
 def test_config_long_splitkv_reduced():
