@@ -3,6 +3,10 @@
  *
  * C ABI of libpkv.so.  Every pointer argument is DEVICE memory owned by the
  * caller unless stated otherwise; the library allocates and frees nothing.
+ * Every tensor pointer (q, out, k_new, v_new, k_pool, v_pool, workspace,
+ * k_out, v_out) must be 16-byte aligned, as the kernels move 16-byte groups;
+ * a misaligned one is rejected with PKV_E_ALIGN.  int32 / fp32 arrays
+ * (block_tables, seq_lens, scales) need only their natural alignment.
  * Calls are asynchronous and ordered on the given HIP stream (`stream` is a
  * hipStream_t passed as void*, NULL = the null stream); they never synchronise
  * and never read device memory from the host.  Pointers must stay valid until
@@ -74,7 +78,8 @@ enum {
   PKV_E_SHAPE = -2,     /* unsupported or inconsistent sizes                 */
   PKV_E_DTYPE = -3,     /* unsupported dtype combination                     */
   PKV_E_WORKSPACE = -4, /* workspace NULL or smaller than required           */
-  PKV_E_HIP = -5        /* a HIP runtime call or kernel launch failed        */
+  PKV_E_HIP = -5,       /* a HIP runtime call or kernel launch failed        */
+  PKV_E_ALIGN = -6      /* a tensor pointer is not 16-byte aligned           */
 };
 
 /* kv_append - write this step's new K/V token of every sequence into its page.
@@ -91,7 +96,7 @@ enum {
  * address the same slot in one call (the writes would race).  A page id
  * outside [0, num_pages), or t / P >= max_pages_per_seq, skips that sequence.
  * Errors: PKV_E_NULL, PKV_E_SHAPE (sizes <= 0, D not 64/128, P not a multiple
- * of TB or > 1024), PKV_E_DTYPE, PKV_E_HIP. */
+ * of TB or > 1024), PKV_E_DTYPE, PKV_E_ALIGN, PKV_E_HIP. */
 int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype,
                   const int32_t* block_tables, int max_pages_per_seq,
                   const int32_t* seq_lens, int batch,
@@ -159,13 +164,15 @@ int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype,
 
 /* decode_step - one whole decode iteration of the cache for one layer: the
  * append of pkv_kv_append followed by the attention of pkv_paged_attn_decode
- * (or of pkv_paged_attn_decode_fp8 when kv_dtype is FP8_E4M3), in one launch.
+ * (or of pkv_paged_attn_decode_fp8 when kv_dtype is FP8_E4M3), with no launch
+ * of its own for the append.
  *
  * The first page's "runtime execution model" has each iteration's attention
- * both update and read the cache pages.  Here the wavefront that owns the tile
- * holding token L_b - 1 of (b, g) takes k_new[b][g] / v_new[b][g] straight
- * into its registers and stores them into the page slot, so the append costs
- * no launch of its own.  Results equal pkv_kv_append then decode with the same
+ * both update and read the cache pages.  Here the wavefront of the split
+ * kernel that owns the tile holding token L_b - 1 of (b, g) takes
+ * k_new[b][g] / v_new[b][g] straight into its registers in place of the
+ * slot's old contents, and the merge kernel, which runs after it on the
+ * stream, stores them into the page slot.  Results equal pkv_kv_append then decode with the same
  * seq_lens (the pool bytes exactly; out up to the rounding order).
  * k_scales / v_scales: required for FP8_E4M3 (k_new / v_new are then bytes
  * already quantised with that page's scale), ignored otherwise.

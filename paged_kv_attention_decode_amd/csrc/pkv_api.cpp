@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
 #include <string>
 
 #include "pkv_internal.h"
@@ -28,6 +29,15 @@ int fail(int code, const char* fmt, ...) {
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(PKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Tensor pointers must be 16-byte aligned (NULLs are reported elsewhere).
+int check_align(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p && misaligned(p)) return fail(PKV_E_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+  return PKV_OK;
 }
 
 bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3; }
@@ -57,6 +67,7 @@ int check_decode(const void* q, int q_dtype, const void* k_pool, const void* v_p
     return fail(PKV_E_NULL, "a required pointer is NULL");
   int rc = check_pool_shape(kv_dtype, max_pages, batch, num_pages, num_kv_heads, head_dim, page_size);
   if (rc) return rc;
+  if (batch > 0 && (rc = check_align({q, k_pool, v_pool, out, workspace}))) return rc;
   const int want_q = kv_dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
   if (q_dtype != want_q)
     return fail(PKV_E_DTYPE, "q dtype %d unsupported with kv dtype %d (need %d)", q_dtype, kv_dtype, want_q);
@@ -136,6 +147,7 @@ const char* pkv_strerror(int code) {
     case PKV_E_DTYPE: return "unsupported dtype combination";
     case PKV_E_WORKSPACE: return "workspace missing or too small";
     case PKV_E_HIP: return "HIP runtime error";
+    case PKV_E_ALIGN: return "tensor pointer not 16-byte aligned";
     default: return "unknown error code";
   }
 }
@@ -161,6 +173,7 @@ int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype, cons
   int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
   if (rc) return rc;
   if (batch == 0) return PKV_OK;
+  if ((rc = check_align({k_new, v_new, k_pool, v_pool}))) return rc;
   pkv::AppendArgs a{k_new, v_new, block_tables, seq_lens, k_pool, v_pool, (int)kv_dtype, batch,
                     max_pages_per_seq, num_pages, num_kv_heads, head_dim, page_size};
   hipError_t e = pkv::launch_append(a, static_cast<hipStream_t>(stream));
@@ -203,6 +216,10 @@ int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const v
                     size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (batch > 0 && (!k_new || !v_new)) return fail(PKV_E_NULL, "k_new / v_new are NULL");
+  if (batch > 0) {
+    const int rc = check_align({k_new, v_new});
+    if (rc) return rc;
+  }
   if (kv_dtype == PKV_FP8_E4M3) {
     if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 scales are NULL");
   } else {
@@ -222,6 +239,7 @@ int pkv_debug_gather(const void* k_pool, const void* v_pool, pkv_dtype kv_dtype,
   int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
   if (rc) return rc;
   if (batch == 0) return PKV_OK;
+  if ((rc = check_align({k_pool, v_pool, k_out, v_out}))) return rc;
   pkv::GatherArgs a{k_pool, v_pool, block_tables, seq_lens, k_out, v_out, (int)kv_dtype, batch,
                     max_pages_per_seq, num_pages, num_kv_heads, head_dim, page_size};
   hipError_t e = pkv::launch_gather(a, static_cast<hipStream_t>(stream));

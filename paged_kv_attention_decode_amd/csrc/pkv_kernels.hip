@@ -295,12 +295,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   int np_sum = 0, n_empty = 0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int bb = c * 64 + lane;
-    const int np = ranges_of(Lc[c], PT);
-    const int incl = wave_incl_scan(np, lane);
-    inclc[c] = np_sum + incl;
-    np_sum = uniform(np_sum + __builtin_amdgcn_readlane(incl, 63));
-    n_empty += __builtin_popcountll(__ballot(bb < B && np == 0));
+    inclc[c] = np_sum;
+    if (c * 64 < B) {                     // uniform: skip chunks past the batch
+      const int bb = c * 64 + lane;
+      const int np = ranges_of(Lc[c], PT);
+      const int incl = wave_incl_scan(np, lane);
+      inclc[c] = np_sum + incl;
+      np_sum = uniform(np_sum + __builtin_amdgcn_readlane(incl, 63));
+      n_empty += __builtin_popcountll(__ballot(bb < B && np == 0));
+    }
   }
   for (int b0 = NC * 64; b0 < B; b0 += 64) {
     const int bb = b0 + lane;
@@ -320,6 +323,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         mine &= mine - 1;
         for (int x = 4 * lane; x < Hq * D; x += 256)
           store_out4<OUT_BF16>(out_, (size_t)be * Hq * D + x, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        // descriptor "nothing to merge or append" for each kv head of the sequence
+        for (int gg = lane; gg < Hkv; gg += 64) descs[(size_t)be * Hkv + gg] = make_int4(0, 0, 0, 0);
       }
     }
   }
@@ -384,22 +389,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // ---- query operand: B matrix of QK^T (K dim = head dims, N = heads) --------
     // Parked in this wave's LDS slot and re-read next to each MFMA, so it holds
     // no registers across the streaming loop.
-    {
-      __builtin_amdgcn_wave_barrier();      // previous segment's reads are done
-      if constexpr (KVT == KV_F32) {
-        const float* q = static_cast<const float*>(q_) + ((size_t)b * Hq + h) * D;
+    // The loads are issued here; the LDS store waits until the segment's first
+    // tile loads are also in flight (below), so the two round trips overlap.
+    u32x4_t qv_ld[NQ];
+    if constexpr (KVT == KV_F32) {
+      const float* q = static_cast<const float*>(q_) + ((size_t)b * Hq + h) * D;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          s_q[wv][kk][lane] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + (c4 + 4 * kk) * 4)) : u32x4_t{0, 0, 0, 0};
-      } else {
-        const uint16_t* q = static_cast<const uint16_t*>(q_) + ((size_t)b * Hq + h) * D;
+      for (int kk = 0; kk < NKK; ++kk)
+        qv_ld[kk] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + (c4 + 4 * kk) * 4)) : u32x4_t{0, 0, 0, 0};
+    } else {
+      const uint16_t* q = static_cast<const uint16_t*>(q_) + ((size_t)b * Hq + h) * D;
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-          // bf16 cache: group kk covers dims 8*(c4+4kk) .. +8.
-          // fp8 cache: group kk covers dims 16*(c4+4kk) .. +16, split in two halves.
-          const int d0 = KVT == KV_BF16 ? 8 * (c4 + 4 * i) : 16 * (c4 + 4 * (i >> 1)) + 8 * (i & 1);
-          s_q[wv][i][lane] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + d0)) : u32x4_t{0, 0, 0, 0};
-        }
+      for (int i = 0; i < NQ; ++i) {
+        // bf16 cache: group kk covers dims 8*(c4+4kk) .. +8.
+        // fp8 cache: group kk covers dims 16*(c4+4kk) .. +16, split in two halves.
+        const int d0 = KVT == KV_BF16 ? 8 * (c4 + 4 * i) : 16 * (c4 + 4 * (i >> 1)) + 8 * (i & 1);
+        qv_ld[i] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + d0)) : u32x4_t{0, 0, 0, 0};
       }
     }
     auto qop = [&](int i) -> u32x4_t { return s_q[wv][i][lane]; };
@@ -460,6 +465,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     load_k(pg_ld, j0);
     load_v(pg_ld, j0);
+    __builtin_amdgcn_wave_barrier();      // the previous segment's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) s_q[wv][i][lane] = qv_ld[i];
     if (has_new && lane < 2 * NEWCH) *reinterpret_cast<u32x4_t*>(s_new[wv] + lane * 16) = new_chunk;
 
     // One tile of TS tokens.  Streaming tiles (LAST = false) always have a next
@@ -669,7 +677,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     if (u == S && lane == 0) {
       // descriptor of (b, g): first contributing wave, contributors, its slot
       const int64_t wl = wave_of(sp, Eu - 1);
-      descs[(size_t)b * Hkv + g] = make_int4((int)w, (int)(wl - w + 1), (int)(2 * w + (first ? 0 : 1)), 0);
+      descs[(size_t)b * Hkv + g] = make_int4((int)w, (int)(wl - w + 1), (int)(2 * w + (first ? 0 : 1)), Lb);
     }
 
     // ---- next segment ------------------------------------------------------------
@@ -699,26 +707,41 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (bg >= B * Hkv) return;
   const int lane = threadIdx.x & 63;
   const int b = bg / Hkv, g = bg - b * Hkv;
-  const int L = seq_lens[b];
+  // descriptor of (b, g), written by the split kernel in this call: first
+  // contributing wave, contributors, slot of the first, sequence length
+  // (all zero for an empty sequence).  Everything below depends only on it.
+  const int4 d = descs[bg];
+  const int L = d.w;
   if (L <= 0) return;                    // empty: rows zeroed by the split kernel, nothing appended
   if (k_new != nullptr) {
     // step entry: store this step's token into slot L-1 (the split kernel
-    // already attended to it from registers)
+    // already attended to it from registers).  K: the token's E-element groups
+    // are 16-byte units of the layout, one store each; V: one element per dim.
     typedef typename Kv<KVT>::elem_t T;
-    constexpr int E = 16 / Kv<KVT>::EB;
+    constexpr int EB = Kv<KVT>::EB, E = 16 / EB;
     const int t = L - 1, pgi = t / P, j = t - pgi * P;
     const int page = pgi < MP ? bt[(size_t)b * MP + pgi] : -1;
+    const size_t nrow = ((size_t)b * Hkv + g) * D;
+    const int ngrp = D / E;
+    u32x4_t kgrp = {0, 0, 0, 0};
+    if (lane < ngrp) kgrp = ld16(static_cast<const uint8_t*>(k_new) + (nrow + (size_t)lane * E) * EB);
+    T vv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int dd = lane + 64 * i;
+      vv[i] = dd < D ? static_cast<const T*>(v_new)[nrow + dd] : T(0);
+    }
     if ((unsigned)page < (unsigned)NP) {
       const size_t ch = chunk_elem(page, g, Hkv, P, D);
-      const T* kn = static_cast<const T*>(k_new) + ((size_t)b * Hkv + g) * D;
-      const T* vn = static_cast<const T*>(v_new) + ((size_t)b * Hkv + g) * D;
-      for (int d = lane; d < D; d += 64) {
-        static_cast<T*>(kpool)[ch + k_elem<E>(j, d, P)] = kn[d];
-        static_cast<T*>(vpool)[ch + v_elem<E>(j, d, D)] = vn[d];
+      if (lane < ngrp)
+        *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(kpool) + (ch + k_elem<E>(j, lane * E, P)) * EB) = kgrp;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int dd = lane + 64 * i;
+        if (dd < D) static_cast<T*>(vpool)[ch + v_elem<E>(j, dd, D)] = vv[i];
       }
     }
   }
-  const int4 d = descs[bg];
   if (d.y <= 1) return;                  // finished by one wave
   merge_ranges<OUT_BF16>(partials, d.z, d.x, d.y, out_, ((size_t)b * Hq + (size_t)g * G) * D, G, D, lane);
 }

@@ -10,6 +10,9 @@ from paged_kv_attention_decode_amd import _native
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pkv.h")
+# Fake non-NULL "device pointers": 16-byte aligned host values that validation
+# must reject arguments around without ever dereferencing.
+F = 0x1000
 
 
 def declared_symbols():
@@ -35,13 +38,13 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_strerror():
     assert pkv.version() == 100
     L = pkv.lib()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.pkv_strerror(code)
     assert L.pkv_strerror(-99) == b"unknown error code"
 
 
 def _append(**over):
-    a = dict(k=1, v=1, dt=1, bt=1, mp=4, sl=1, b=2, kp=1, vp=1, np_=8, hkv=2, d=128, p=64)
+    a = dict(k=F, v=F, dt=1, bt=F, mp=4, sl=F, b=2, kp=F, vp=F, np_=8, hkv=2, d=128, p=64)
     a.update(over)
     L = pkv.lib()
     vp = lambda x: None if x in (0, None) else x  # noqa: E731
@@ -53,6 +56,7 @@ def _append(**over):
     (dict(k=0), -1), (dict(bt=0), -1), (dict(d=96), -2), (dict(p=48), -2), (dict(p=2048), -2),
     (dict(dt=7), -3), (dict(hkv=0), -2), (dict(mp=0), -2), (dict(b=-1), -2),
     (dict(dt=2, p=32), -2), (dict(dt=0, p=16, k=0), -1),
+    (dict(k=F + 8), -6), (dict(vp=F + 2), -6),
 ])
 def test_append_rejects_bad_arguments(over, code):
     # Pointers are fake non-NULL host values: validation must fail before any use.
@@ -65,8 +69,8 @@ def test_batch_zero_is_a_noop_without_device():
 
 
 def _decode(fn="pkv_paged_attn_decode", **over):
-    a = dict(q=1, qdt=1, kp=1, vp=1, kvdt=1, bt=1, mp=4, sl=1, b=2, np_=8, hq=8, hkv=2, d=128, p=64,
-             scale=0.1, pt=0, out=1, odt=1, ws=1, wsb=1 << 30)
+    a = dict(q=F, qdt=1, kp=F, vp=F, kvdt=1, bt=F, mp=4, sl=F, b=2, np_=8, hq=8, hkv=2, d=128, p=64,
+             scale=0.1, pt=0, out=F, odt=1, ws=F, wsb=1 << 30)
     a.update(over)
     L = pkv.lib()
     vp = lambda x: None if x in (0, None) else x  # noqa: E731
@@ -84,6 +88,7 @@ def _decode(fn="pkv_paged_attn_decode", **over):
     (dict(q=0), -1), (dict(out=0), -1), (dict(ws=0), -1), (dict(kvdt=2), -3),
     (dict(qdt=0), -3), (dict(kvdt=0, qdt=0, p=16, odt=1), -3), (dict(hq=9), -2), (dict(hq=64, hkv=2), -2),
     (dict(d=80), -2), (dict(p=40), -2), (dict(pt=48), -2), (dict(pt=-32), -2), (dict(np_=0), -2),
+    (dict(q=F + 4), -6), (dict(kp=F + 8), -6), (dict(out=F + 2), -6), (dict(ws=F + 1), -6),
 ])
 def test_decode_rejects_bad_arguments(over, code):
     assert _decode(**over) == code
@@ -103,8 +108,8 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 
 def _step(**over):
-    a = dict(q=1, qdt=1, kn=1, vn=1, kp=1, vp=1, kvdt=1, ks=0, vs=0, bt=1, mp=4, sl=1, b=2, np_=8, hq=8,
-             hkv=2, d=128, p=64, scale=0.1, pt=0, out=1, odt=1, ws=1, wsb=1 << 30)
+    a = dict(q=F, qdt=1, kn=F, vn=F, kp=F, vp=F, kvdt=1, ks=0, vs=0, bt=F, mp=4, sl=F, b=2, np_=8, hq=8,
+             hkv=2, d=128, p=64, scale=0.1, pt=0, out=F, odt=1, ws=F, wsb=1 << 30)
     a.update(over)
     vp = lambda x: None if x in (0, None) else x  # noqa: E731
     return pkv.lib().pkv_decode_step(vp(a["q"]), a["qdt"], vp(a["kn"]), vp(a["vn"]), vp(a["kp"]), vp(a["vp"]),
@@ -115,6 +120,7 @@ def _step(**over):
 
 @pytest.mark.parametrize("over,code", [(dict(kn=0), -1), (dict(vn=0), -1), (dict(kvdt=2, p=64), -1),
                                        (dict(kvdt=2, p=32, ks=1, vs=1), -2), (dict(d=32), -2),
-                                       (dict(qdt=0), -3), (dict(hq=7), -2)])
+                                       (dict(qdt=0), -3), (dict(hq=7), -2), (dict(kn=F + 8), -6),
+                                       (dict(vn=F + 4), -6)])
 def test_step_rejects_bad_arguments(over, code):
     assert _step(**over) == code
