@@ -191,7 +191,8 @@ __device__ __forceinline__ void store_out4(void* out_, size_t idx, f32x4_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the n partial ranges of one (b, g), run by one wave.
+// Log-sum-exp merge of the n partial ranges of one (b, g) for 256 of its G*D
+// outputs, starting at x0, run by one wave.
 // Partial slot layout (floats): O[G][D] unnormalised, then m[G] (log2-domain
 // running max), then l[G] (sum of 2^(s - m)).  Contributor i is wave wf + i;
 // its slot is slot0 for i = 0 and 2 * (wf + i) otherwise.
@@ -200,55 +201,58 @@ __device__ __forceinline__ void store_out4(void* out_, size_t idx, f32x4_t v) {
 // their loads are in flight together.
 // ---------------------------------------------------------------------------
 template <bool OUT_BF16>
-__device__ void merge_ranges(const float* __restrict__ partials, int64_t slot0, int64_t wf, int n,
-                             void* __restrict__ out_, size_t row0, int G, int D, int lane) {
+__device__ void merge_chunk(const float* __restrict__ partials, int64_t slot0, int64_t wf, int n,
+                            void* __restrict__ out_, size_t row0, int G, int D, int x0, int lane) {
   const int stride = G * (D + 2);
   const int total = G * D;
   const float NEG_INF = -__builtin_inff();
-  for (int c0 = 0; c0 < total; c0 += 256) {
-    const int x = c0 + 4 * lane;
-    if (x >= total) break;
-    const int h = x / D;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f, M = NEG_INF;
-    bool nan = false;
-    for (int s0 = 0; s0 < n; s0 += 8) {
-      f32x4_t o[8];
-      float ms[8], ls[8];
+  const int x = x0 + 4 * lane;
+  if (x >= total) return;
+  const int h = x / D;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f, M = NEG_INF;
+  bool nan = false;
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    f32x4_t o[8];
+    float ms[8], ls[8];
+    // Past the last contributor the last one is re-read (no branch around
+    // the loads, so all of them are in flight at once) and then masked out.
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (s0 + k < n) {
-          const int64_t slot = (s0 + k == 0) ? slot0 : 2 * (wf + s0 + k);
-          const float* ps = partials + slot * stride;
-          o[k] = *reinterpret_cast<const f32x4_t*>(ps + x);
-          ms[k] = ps[total + h];
-          ls[k] = ps[total + G + h];
-        } else {
-          o[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          ms[k] = NEG_INF;
-          ls[k] = 0.f;
-        }
-      }
-      float mg = M;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        nan |= ms[k] != ms[k];
-        mg = fmaxf(mg, ms[k]);
-      }
-      const float a = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(M - mg);
-      acc *= a;
-      den *= a;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float f = ms[k] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ms[k] - mg);
-        acc += f * o[k];
-        den += f * ls[k];
-      }
-      M = mg;
+    for (int k = 0; k < 8; ++k) {
+      const int i = min(s0 + k, n - 1);
+      const int64_t slot = i == 0 ? slot0 : 2 * (wf + i);
+      const float* ps = partials + slot * stride;
+      o[k] = *reinterpret_cast<const f32x4_t*>(ps + x);
+      ms[k] = ps[total + h];
+      ls[k] = ps[total + G + h];
     }
-    const float inv = nan ? __builtin_nanf("") : 1.f / den;
-    store_out4<OUT_BF16>(out_, row0 + x, acc * inv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k >= n) {
+        o[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ms[k] = NEG_INF;
+        ls[k] = 0.f;
+      }
+    }
+    float mg = M;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      nan |= ms[k] != ms[k];
+      mg = fmaxf(mg, ms[k]);
+    }
+    const float a = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(M - mg);
+    acc *= a;
+    den *= a;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float f = ms[k] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ms[k] - mg);
+      acc += f * o[k];
+      den += f * ls[k];
+    }
+    M = mg;
   }
+  const float inv = nan ? __builtin_nanf("") : 1.f / den;
+  store_out4<OUT_BF16>(out_, row0 + x, acc * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -456,6 +460,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         vr[dt] = ld16_stream(vc + (uint32_t)(v_elem<E>(j + 4 * c4, dt * 16 + r16, D) * EB));
     };
     int page = page_of(pgi);
+    // step entry: the wave that writes (b, g)'s descriptor also looks up the
+    // page of slot Lb - 1, where the merge kernel stores the new token (-1:
+    // beyond the table).  Scalar load; it is consumed only at the segment end.
+    const int pg_new = (k_new != nullptr && u == S) ? page_of((Lb - 1) / P) : -1;
     bool bad = (unsigned)page >= (unsigned)NP;
     int pg_ld = bad ? 0 : page;
     float ksc = 1.f, vsc = 1.f;
@@ -675,9 +683,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       }
     }
     if (u == S && lane == 0) {
-      // descriptor of (b, g): first contributing wave, contributors, its slot
+      // descriptor of (b, g): first contributing wave w; 2 * contributors + 1
+      // if its partial is in its second slot (slot 2w + 1, else 2w); the page
+      // of slot Lb - 1 for the step entry; Lb
       const int64_t wl = wave_of(sp, Eu - 1);
-      descs[(size_t)b * Hkv + g] = make_int4((int)w, (int)(wl - w + 1), (int)(2 * w + (first ? 0 : 1)), Lb);
+      descs[(size_t)b * Hkv + g] = make_int4((int)w, (int)(2 * (wl - w + 1) + (first ? 0 : 1)), pg_new, Lb);
     }
 
     // ---- next segment ------------------------------------------------------------
@@ -694,56 +704,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 }
 
 // ---------------------------------------------------------------------------
-// Decode, part 2: one wave per (b, g) combines the partial ranges of pairs that
-// were split over several waves (log-sum-exp merge, see merge_ranges).
+// Decode, part 2: one wave per (b, g) and 256-output chunk of its G*D outputs
+// combines the partial ranges of pairs that were split over several waves
+// (log-sum-exp merge, see merge_chunk); for the step entry the chunk-0 wave
+// also stores this step's token into its page slot.  A chunk per wave keeps
+// the dependent memory round trips to two: the descriptor, then the partials
+// (and the page id) together.
 // ---------------------------------------------------------------------------
 template <int KVT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
-    const int32_t* __restrict__ seq_lens, const int4* __restrict__ descs,
-    const float* __restrict__ partials, void* __restrict__ out_, int B, int Hq, int Hkv, int G, int D,
-    const void* __restrict__ k_new, const void* __restrict__ v_new, const int32_t* __restrict__ bt,
-    void* __restrict__ kpool, void* __restrict__ vpool, int MP, int NP, int P) {
-  const int bg = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int4* __restrict__ descs, const float* __restrict__ partials, void* __restrict__ out_, int B,
+    int Hq, int Hkv, int G, int D, int nchunk, const void* __restrict__ k_new, const void* __restrict__ v_new,
+    void* __restrict__ kpool, void* __restrict__ vpool, int NP, int P) {
+  typedef typename Kv<KVT>::elem_t T;
+  constexpr int EB = Kv<KVT>::EB, E = 16 / EB;
+  // wave-uniform (the compiler cannot tell that threadIdx.x >> 6 is)
+  const int wi = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int bg = wi / nchunk, chunk = wi - bg * nchunk;
   if (bg >= B * Hkv) return;
   const int lane = threadIdx.x & 63;
   const int b = bg / Hkv, g = bg - b * Hkv;
+  const bool app = k_new != nullptr && chunk == 0;
+  // This step's token row (independent of the descriptor, so issued first).
+  // K: its E-element groups are 16-byte units of the layout, one per lane;
+  // V: one element per dimension.  Indexes are clamped rather than branched
+  // on, so the loads stay in flight across the descriptor load.
+  const size_t nrow = ((size_t)b * Hkv + g) * D;
+  const int ngrp = D / E;
+  u32x4_t kgrp = {0, 0, 0, 0};
+  uint32_t vv[2] = {0, 0};                // one element each, kept unpacked
+  if (app) {
+    kgrp = ld16(static_cast<const uint8_t*>(k_new) + (nrow + (size_t)min(lane, ngrp - 1) * E) * EB);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) vv[i] = static_cast<const T*>(v_new)[nrow + min(lane + 64 * i, D - 1)];
+  }
   // descriptor of (b, g), written by the split kernel in this call: first
   // contributing wave, contributors, slot of the first, sequence length
   // (all zero for an empty sequence).  Everything below depends only on it.
   const int4 d = descs[bg];
   const int L = d.w;
   if (L <= 0) return;                    // empty: rows zeroed by the split kernel, nothing appended
-  if (k_new != nullptr) {
-    // step entry: store this step's token into slot L-1 (the split kernel
-    // already attended to it from registers).  K: the token's E-element groups
-    // are 16-byte units of the layout, one store each; V: one element per dim.
-    typedef typename Kv<KVT>::elem_t T;
-    constexpr int EB = Kv<KVT>::EB, E = 16 / EB;
-    const int t = L - 1, pgi = t / P, j = t - pgi * P;
-    const int page = pgi < MP ? bt[(size_t)b * MP + pgi] : -1;
-    const size_t nrow = ((size_t)b * Hkv + g) * D;
-    const int ngrp = D / E;
-    u32x4_t kgrp = {0, 0, 0, 0};
-    if (lane < ngrp) kgrp = ld16(static_cast<const uint8_t*>(k_new) + (nrow + (size_t)lane * E) * EB);
-    T vv[2];
+  const int n = d.y >> 1;
+  if (n > 1)                             // else finished by one wave
+    merge_chunk<OUT_BF16>(partials, 2 * (int64_t)d.x + (d.y & 1), d.x, n, out_,
+                          ((size_t)b * Hq + (size_t)g * G) * D, G, D, 256 * chunk, lane);
+  // step entry: store the token into slot L-1 of page d.z (the split kernel
+  // already attended to it from registers)
+  if (app && (unsigned)d.z < (unsigned)NP) {
+    const int j = (L - 1) % P;
+    const size_t ch = chunk_elem(d.z, g, Hkv, P, D);
+    if (lane < ngrp)
+      *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(kpool) + (ch + k_elem<E>(j, lane * E, P)) * EB) = kgrp;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int dd = lane + 64 * i;
-      vv[i] = dd < D ? static_cast<const T*>(v_new)[nrow + dd] : T(0);
-    }
-    if ((unsigned)page < (unsigned)NP) {
-      const size_t ch = chunk_elem(page, g, Hkv, P, D);
-      if (lane < ngrp)
-        *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(kpool) + (ch + k_elem<E>(j, lane * E, P)) * EB) = kgrp;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int dd = lane + 64 * i;
-        if (dd < D) static_cast<T*>(vpool)[ch + v_elem<E>(j, dd, D)] = vv[i];
-      }
+      if (dd < D) static_cast<T*>(vpool)[ch + v_elem<E>(j, dd, D)] = (T)vv[i];
     }
   }
-  if (d.y <= 1) return;                  // finished by one wave
-  merge_ranges<OUT_BF16>(partials, d.z, d.x, d.y, out_, ((size_t)b * Hq + (size_t)g * G) * D, G, D, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -925,13 +942,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int pairs = a.batch * a.num_kv_heads;
-  dim3 mgrid((pairs + 3) / 4);
+  const int nchunk = (G * a.head_dim + 255) / 256;
+  dim3 mgrid((unsigned)(((int64_t)pairs * nchunk + 3) / 4));
   void* kp = const_cast<void*>(a.k_pool);
   void* vp = const_cast<void*>(a.v_pool);
 #define PKV_MERGE(K, OB)                                                                           \
-  hipLaunchKernelGGL((decode_merge_kernel<K, OB>), mgrid, block, 0, s, a.seq_lens, a.descs, a.partials, \
-                     a.out, a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim, a.k_new, a.v_new,    \
-                     a.block_tables, kp, vp, a.max_pages, a.num_pages, a.page_size)
+  hipLaunchKernelGGL((decode_merge_kernel<K, OB>), mgrid, block, 0, s, a.descs, a.partials, a.out,     \
+                     a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim, nchunk, a.k_new, a.v_new,  \
+                     kp, vp, a.num_pages, a.page_size)
   if (a.kvt == KV_F32) {
     if (a.out_bf16) PKV_MERGE(KV_F32, true); else PKV_MERGE(KV_F32, false);
   } else if (a.kvt == KV_BF16) {
