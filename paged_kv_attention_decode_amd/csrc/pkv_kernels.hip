@@ -34,6 +34,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -930,7 +931,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (cus <= 0) return hipErrorInvalidDevice;
   decode_fn_t fn = pick_decode(a.kvt, a.head_dim, a.out_bf16);
   if (!fn) return hipErrorInvalidValue;
-  const int Wmax = cus * waves_per_cu(fn, dev);
+  // Resident waves: enough for about 64 KB of K/V tiles in flight per CU (a
+  // tile is 128 * D bytes in every dtype), i.e. one wave per SIMD at D = 128.
+  // More waves than that do not raise the streaming rate: two waves on one
+  // SIMD issue in age order, so the second one starts late and finishes last,
+  // stretching the tail of the launch.
+  const int Wmax = cus * std::min(waves_per_cu(fn, dev), 512 / a.head_dim);
   const int G = a.num_q_heads / a.num_kv_heads;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   dim3 grid((Wmax + 3) / 4), block(256);
