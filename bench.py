@@ -152,6 +152,57 @@ def cpu_baseline(wl, steps, seconds):
                       f"(C oracle, {threads} threads), {el:.1f} s"}
 
 
+def diagnostics(pkv, wl, q, bt, kps, vps, ks, vs, dsteps, out, ws, step, i0, n=30):
+    """Per-launch spread and the parts of a step, measured after the timed region.
+
+    Each launch here is bracketed by its own event pair (whose packets add a few
+    microseconds, which is why the timed region does not use them): decode_step
+    median / p10 / p90, the standalone kv_append and paged decode calls, and the
+    step on one cache copy reused (warm MALL) for contrast."""
+    import numpy as np
+    import torch
+    layers = len(kps)
+    s0 = dsteps[0]
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        ev = DeviceEvents(n)
+        torch.cuda.synchronize()
+        for i in range(n):
+            ev.record(2 * i)
+            fn(i)
+            ev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        us = np.array([ev.elapsed_ms(i) * 1e3 for i in range(n)])
+        ev.close()
+        return us
+
+    def app(i):
+        pkv.kv_append(s0["kn"], s0["vn"], wl.kv_dtype, bt, s0["sl"], kps[i % layers], vps[i % layers],
+                      wl.Hkv, wl.D, wl.P)
+
+    def dec(i):
+        if wl.kv_dtype == "fp8":
+            pkv.paged_attn_decode_fp8(q, wl.q_dtype, kps[i % layers], vps[i % layers], ks, vs, bt, s0["sl"],
+                                      wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws,
+                                      wl.partition_tokens)
+        else:
+            pkv.paged_attn_decode(q, wl.q_dtype, kps[i % layers], vps[i % layers], wl.kv_dtype, bt, s0["sl"],
+                                  wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws,
+                                  wl.partition_tokens)
+
+    st = timed(lambda i: step(i0 + i))
+    ap = timed(app)
+    de = timed(dec)
+    hot = timed(lambda i: step(i0 + i * layers))      # always the same cache copy
+    q3 = lambda a: [round(float(np.percentile(a, p)), 2) for p in (50, 10, 90)]  # noqa: E731
+    return {"note": "per-launch HIP events around each call (adds event packets); us as [median, p10, p90]",
+            "decode_step_us": q3(st), "kv_append_us": q3(ap), "paged_decode_us": q3(de),
+            "decode_step_same_cache_copy_us": q3(hot),
+            "seqs_per_s_append_plus_decode": round(wl.B / ((np.median(ap) + np.median(de)) * 1e-6), 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -239,6 +290,8 @@ def main():
     dec_mean = evs.elapsed_ms(0) / args.steps
     evs.close()
 
+    diag = diagnostics(pkv, wl, q, bt, kps, vps, ks, vs, dsteps, out, ws, step, args.warmup + args.steps)
+
     step_bytes, kv_bytes = 0, 0
     for i in range(args.steps):
         d, a, kvb = alg_bytes(wl, steps[(args.warmup + i) % len(steps)]["seq_lens"])
@@ -276,6 +329,7 @@ def main():
                      "kernel": "decode_step launch (decode_split_kernel + decode_merge_kernel)",
                      "call_ms_mean": round(dec_mean, 5), "alg_bytes_per_call": int(step_bytes)},
     }
+    rec["diagnostics"] = diag
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
