@@ -164,3 +164,88 @@ def merge_partials(o, lse):
     M = lse.max(axis=0, keepdims=True)
     w = np.exp(lse - M)                                   # [S, G]
     return (w[:, :, None] * o).sum(axis=0) / w.sum(axis=0)[:, None]
+
+
+# ------------------------------------- fp8 append with dynamic page scales ----
+#
+# Source: the concept page's "compile-time graph optimization" section inserts
+# a dynamic scaling-factor computation where data enters an FP8 product; the
+# yololab page ("FP8 與極致量化") gives FP8 as the way to halve the bandwidth a
+# model needs.  Applied here where new K/V data enter the fp8 cache.  Reading
+# (the pages fix no granularity or update rule): one fp32 scale per (page, kv
+# head), real value = decoded byte * scale, scale = amax / 448 of the tokens
+# written so far; the scale only grows, and when it grows the page's earlier
+# tokens are re-encoded under the new one.  Every step below is one fp32
+# operation rounded to nearest even, so the result is a unique byte image.
+
+E4M3_FINITE_MAX = 448.0
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP e4m3fn code: the nearest finite e4m3 value, a tie going to
+    the even code (even significand), magnitudes above 448 saturating to 448,
+    NaN -> 0x7F; the sign of x (also of -0) is kept.  Written as a search over
+    the 127 non-negative finite codes, which increase with their value."""
+    x = np.asarray(x, dtype=np.float32)
+    pos = E4M3_TABLE[:127]
+    a = np.abs(np.where(np.isnan(x), np.float32(0), x)).astype(np.float64)
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - pos[lo], pos[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(a >= E4M3_FINITE_MAX, 126, code).astype(np.uint8)
+    code = code | (np.signbit(x).astype(np.uint8) << np.uint8(7))
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def append_fp8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
+                       k_scales, v_scales, P):
+    """In place: token L-1 of each sequence into its fp8 page, with the page scale
+    kept at amax / 448 of the page's tokens (K and V each on their own).
+
+    For each b with L = seq_lens[b] >= 1, t = L - 1, page pg = block_tables[b, t//P]
+    (a table index or page id out of range skips the sequence), slot j = t % P,
+    and each kv head g, separately for K and V with x = the new row widened to
+    fp32 and a = max |x|:
+      j == 0 (first token of the page): s = a / 448, or 1 when a == 0;
+      j > 0, s0 = the page's current scale: if a / s0 <= 448 then s = s0;
+        otherwise s = a / 448 and every earlier slot j' < j is re-encoded:
+        byte' = enc((dec(byte) * s0) / s);
+      the new token: byte = enc(x / s); the page scale becomes s.
+    Arithmetic is fp32 (each division and product rounded to nearest even);
+    enc is e4m3_encode, dec the exact e4m3 value.
+    """
+    NP, Hkv, PD = k_pool.shape
+    D = PD // P
+    MP = np.asarray(block_tables).shape[1]
+    koff, voff = _offsets(P, D, "fp8")
+    f32 = np.float32
+    c448 = f32(E4M3_FINITE_MAX)
+    for b in range(len(seq_lens)):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        t = L - 1
+        if t // P >= MP:
+            continue
+        pg = int(block_tables[b][t // P])
+        if not 0 <= pg < NP:
+            continue
+        j = t % P
+        for new, pool, scales, off in ((k_new, k_pool, k_scales, koff), (v_new, v_pool, v_scales, voff)):
+            for g in range(Hkv):
+                x = widen(np.asarray(new)[b, g], new_dtype).astype(np.float32)   # exact
+                a = f32(np.abs(x).max())
+                if j == 0:
+                    s = f32(a / c448) if a > 0 else f32(1)
+                else:
+                    s0 = f32(scales[pg, g])
+                    if f32(a / s0) <= c448:
+                        s = s0
+                    else:
+                        s = f32(a / c448)
+                        idx = off[:j]                                          # [j, D]
+                        real = e4m3_to_f64(pool[pg, g, idx]).astype(np.float32) * s0
+                        pool[pg, g, idx] = e4m3_encode(real.astype(np.float32) / s)
+                pool[pg, g, off[j]] = e4m3_encode(x / s)
+                scales[pg, g] = s
