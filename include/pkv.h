@@ -103,6 +103,40 @@ int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype,
                   void* k_pool, void* v_pool, int num_pages,
                   int num_kv_heads, int head_dim, int page_size, void* stream);
 
+/* kv_append_fp8 - append into an fp8 e4m3 cache, quantising on write with
+ * dynamic per-(page, kv head) scales.
+ *
+ * The concept page's "compile-time graph optimization" section computes a
+ * dynamic scaling factor where data enters FP8 arithmetic; the yololab page's
+ * FP8 section gives FP8 as the way to halve memory bandwidth.  Here new K/V rows
+ * enter the fp8 cache: for each b with L_b >= 1, token t = L_b - 1 goes to slot
+ * j = t % P of page pg = block_tables[b][t / P], and for each kv head g, for K
+ * and V separately, with x = the new row widened to fp32 and a = max |x|:
+ *   j == 0 (first token of the page): s = a / 448 (1 if a == 0);
+ *   j > 0, s0 = scales[pg][g]: s = s0 if a / s0 <= 448; otherwise s = a / 448
+ *     and every earlier slot of the page is re-encoded as enc((dec(byte) * s0) / s);
+ *   the new row is stored as enc(x / s); scales[pg][g] = s.
+ * Each division and product is one fp32 operation rounded to nearest even;
+ * enc is e4m3 round-to-nearest-even saturating at +-448; dec is exact.  So
+ * the bytes and scales written are fully determined by the inputs.
+ *
+ * new_dtype: BF16 or F32 (k_new, v_new [B][Hkv][D]; finite values).
+ * k_pool/v_pool: fp8 pools; k_scales/v_scales fp32 [NP][Hkv], read and written
+ *   (a page's scale must be the one this function last wrote for it, or any
+ *   positive scale that encodes the page's bytes, when j > 0).
+ * Writes only the addressed page of each sequence (all its earlier slots when
+ * its scale grows) and its two scales.  Two sequences must not append into the
+ * same page in one call.  Sequences with L_b <= 0, t / P >= max_pages_per_seq or
+ * a page id outside [0, num_pages) are skipped.
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (as pkv_kv_append with P a multiple of 64),
+ * PKV_E_DTYPE (new_dtype), PKV_E_ALIGN, PKV_E_HIP. */
+int pkv_kv_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype,
+                      const int32_t* block_tables, int max_pages_per_seq,
+                      const int32_t* seq_lens, int batch,
+                      void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                      int num_pages, int num_kv_heads, int head_dim, int page_size,
+                      void* stream);
+
 /* Bytes of scratch that pkv_paged_attn_decode / pkv_paged_attn_decode_fp8 need
  * for these sizes on the current HIP device (0 if the sizes are invalid).
  * The workspace holds split-KV partial results (per-head running max, sum and

@@ -53,6 +53,19 @@ def kv_append(k_new, v_new, kv_dtype, block_tables, seq_lens, k_pool, v_pool,
         _ptr(k_pool), _ptr(v_pool), NP, num_kv_heads, head_dim, page_size, _stream(stream)))
 
 
+def kv_append_fp8(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool, k_scales, v_scales,
+                  num_kv_heads, head_dim, page_size, stream=None):
+    """Quantise each sequence's new bf16/f32 K/V row into its fp8 page, keeping the
+    per-(page, kv head) scales at amax / 448 (earlier tokens re-encoded when a
+    scale grows)."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("kv_append_fp8", lib().pkv_kv_append_fp8(
+        _ptr(k_new), _ptr(v_new), _code(new_dtype), _ptr(block_tables), MP, _ptr(seq_lens), B,
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), NP, num_kv_heads, head_dim, page_size,
+        _stream(stream)))
+
+
 def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim) -> int:
     return int(lib().pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim))
 

@@ -181,6 +181,29 @@ int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype, cons
   return PKV_OK;
 }
 
+int pkv_kv_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype, const int32_t* block_tables,
+                      int max_pages_per_seq, const int32_t* seq_lens, int batch, void* k_pool, void* v_pool,
+                      float* k_scales, float* v_scales, int num_pages, int num_kv_heads, int head_dim,
+                      int page_size, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && (!k_new || !v_new || !block_tables || !seq_lens || !k_pool || !v_pool || !k_scales ||
+                    !v_scales))
+    return fail(PKV_E_NULL, "a required pointer is NULL");
+  int rc = check_pool_shape(PKV_FP8_E4M3, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim,
+                            page_size);
+  if (rc) return rc;
+  if (new_dtype != PKV_BF16 && new_dtype != PKV_F32)
+    return fail(PKV_E_DTYPE, "new-row dtype %d unsupported (bf16 or f32)", new_dtype);
+  if (batch == 0) return PKV_OK;
+  if ((rc = check_align({k_new, v_new, k_pool, v_pool}))) return rc;
+  pkv::AppendFp8Args a{k_new,    v_new,    new_dtype == PKV_BF16, block_tables, seq_lens,
+                       k_pool,   v_pool,   k_scales,              v_scales,     batch,
+                       max_pages_per_seq, num_pages, num_kv_heads, head_dim, page_size};
+  hipError_t e = pkv::launch_append_fp8(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 append launch");
+  return PKV_OK;
+}
+
 int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
                           pkv_dtype kv_dtype, const int32_t* block_tables, int max_pages_per_seq,
                           const int32_t* seq_lens, int batch, int num_pages, int num_q_heads,

@@ -24,6 +24,19 @@ inline size_t partials_bytes(int cus, int G, int D) {
   return (b + 255) & ~(size_t)255;
 }
 
+struct AppendFp8Args {
+  const void* k_new;
+  const void* v_new;
+  bool new_bf16;            // rows are bf16 (else fp32)
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* k_pool;
+  void* v_pool;
+  float* k_scales;
+  float* v_scales;
+  int batch, max_pages, num_pages, num_kv_heads, head_dim, page_size;
+};
+
 struct AppendArgs {
   const void* k_new;
   const void* v_new;
@@ -65,6 +78,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_fp8(const AppendFp8Args& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 // Launches the decode kernel and the log-sum-exp merge kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

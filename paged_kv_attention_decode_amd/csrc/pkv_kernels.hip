@@ -792,6 +792,161 @@ __global__ __launch_bounds__(256) void append_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// fp8 append with dynamic page scales (quantise on write).
+//
+// One wave per (sequence, kv head); K, then V, each with its own scale:
+// a = max |x| of the new row (widened to fp32);
+//   slot j == 0 (first token of the page): s = a / 448 (1 if a == 0);
+//   else, s0 = the page's scale: s = s0 if a / s0 <= 448, otherwise
+//   s = a / 448 and every earlier slot is re-encoded, enc((dec(byte) * s0) / s);
+// the new row is stored as enc(x / s) and the page scale becomes s.
+// Every division and product is one correctly rounded fp32 operation.
+// ---------------------------------------------------------------------------
+
+// fp32 -> e4m3fn: nearest value, ties to the even significand, saturating at
+// +-448 (NaN -> 0x7F).  With e = max(exponent(|x|), -6), the e4m3 step at |x|
+// is 2^(e-3) (the subnormal step 2^-9 below 2^-6), k = rint(|x| / 2^(e-3)) is
+// exact in fp32, and the code is 8 * (e + 6) + k: a carry of k to 16 lands on
+// the next binade's first code, and below 2^-6 the code is k itself.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t sign = (ubits(x) >> 24) & 0x80u;
+  if (x != x) return 0x7Fu;
+  const float a = fminf(fabsf(x), 448.f);
+  const int e = max((int)((ubits(a) >> 23) & 0xFFu) - 127, -6);
+  const int k = (int)rintf(ldexpf(a, 3 - e));
+  return sign | (uint32_t)(8 * (e + 6) + k);
+}
+
+// Four e4m3 bytes of a word re-encoded under a new scale: enc((dec(byte) * s0) / s).
+__device__ __forceinline__ uint32_t requant4(uint32_t w, float s0, float s) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  const float v[4] = {a.x, a.y, b.x, b.y};
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float real = v[i] * s0;        // rounded product, then a rounded quotient
+    r |= e4m3_encode(real / s) << (8 * i);
+  }
+  return r;
+}
+
+template <bool IN_BF16, int D>
+__global__ __launch_bounds__(256) void append_fp8_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
+    uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool,
+    float* __restrict__ kscales, float* __restrict__ vscales, int B, int MP, int NP, int Hkv, int P) {
+  constexpr int NPL = D / 64;           // new-row elements per lane (consecutive dims)
+  constexpr int TB = 64;                // V block of the fp8 layout, tokens
+  __shared__ uint8_t s_nb[4][D];        // the new row's encoded bytes (V pass of a re-encode)
+  const int wv = uniform(threadIdx.x >> 6);
+  const int bg = uniform(blockIdx.x * 4 + wv);
+  if (bg >= B * Hkv) return;
+  const int lane = threadIdx.x & 63;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int L = uniform(((const_i32_ptr)seq_lens)[b]);
+  if (L <= 0) return;
+  const int t = L - 1, pgi = t / P, j = t - pgi * P;
+  if (pgi >= MP) return;
+  const int pg = uniform(((const_i32_ptr)bt)[(size_t)b * MP + pgi]);
+  if ((unsigned)pg >= (unsigned)NP) return;
+  const size_t ch = chunk_elem(pg, g, Hkv, P, D);        // byte offset (1-byte elements)
+  const size_t row = ((size_t)b * Hkv + g) * D + (size_t)lane * NPL;
+  const int d0 = lane * NPL;
+
+#pragma unroll 1
+  for (int which = 0; which < 2; ++which) {
+    const void* src = which ? v_new : k_new;
+    uint8_t* pool = (which ? vpool : kpool) + ch;
+    float* scale_p = (which ? vscales : kscales) + (size_t)pg * Hkv + g;
+    float x[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      x[i] = IN_BF16 ? fbits((uint32_t)static_cast<const uint16_t*>(src)[row + i] << 16)
+                     : static_cast<const float*>(src)[row + i];
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) a = fmaxf(a, fabsf(x[i]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+    a = fbits(uniform((int)ubits(a)));
+    float s;
+    bool requant = false;
+    float s0 = 1.f;
+    if (j == 0) {
+      s = a > 0.f ? a / 448.f : 1.f;
+    } else {
+      s0 = fbits(uniform((int)ubits(*scale_p)));
+      if (a / s0 <= 448.f) {
+        s = s0;
+      } else {
+        s = a / 448.f;
+        requant = true;
+      }
+    }
+    uint32_t nb[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) nb[i] = e4m3_encode(x[i] / s);
+
+    if (which == 0) {
+      // K: earlier slots are whole 16-byte groups (16 dims of one token)
+      if (requant) {
+        const int ngrp = (D / 16) * j;
+        for (int gi = lane; gi < ngrp; gi += 64) {
+          const int c = gi / j, jj = gi - c * j;
+          u32x4_t* gp = reinterpret_cast<u32x4_t*>(pool + ((size_t)c * P + jj) * 16);
+          u32x4_t w = *gp;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w[q] = requant4(w[q], s0, s);
+          *gp = w;
+        }
+      }
+      // the new token's dims d0.. are consecutive bytes of one group
+      uint8_t* kp = pool + k_elem<16>(j, d0, P);
+      if (NPL == 2)
+        *reinterpret_cast<uint16_t*>(kp) = (uint16_t)(nb[0] | (nb[NPL - 1] << 8));
+      else
+        *kp = (uint8_t)nb[0];
+    } else if (!requant) {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) pool[v_elem<16>(j, d0 + i, D)] = (uint8_t)nb[i];
+    } else {
+      // V: a 16-byte group holds 16 tokens of one dim from one 64-token block;
+      // rewrite blocks 0 .. j/64 group by group: tokens < j re-encoded, token j
+      // takes the new byte, later slots keep their bytes.
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) s_nb[wv][d0 + i] = (uint8_t)nb[i];
+      __builtin_amdgcn_wave_barrier();   // one wave's LDS operations complete in order
+      const int ngrp = (j / TB + 1) * 4 * D;
+      for (int gi = lane; gi < ngrp; gi += 64) {
+        const int blk = gi / (4 * D), rem = gi - blk * 4 * D;
+        const int c = rem / D, d = rem - c * D;
+        u32x4_t* gp = reinterpret_cast<u32x4_t*>(pool + (size_t)blk * TB * D + ((size_t)c * D + d) * 16);
+        u32x4_t w = *gp;
+        const uint32_t fresh = s_nb[wv][d];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t re = requant4(w[q], s0, s);
+          uint32_t outw = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // byte e = 4q + i holds token r = 16 * (e / 4) + 4c + e % 4 = 16q + 4c + i
+            const int tok = blk * TB + 16 * q + 4 * c + i;
+            const uint32_t byte = tok < j ? (re >> (8 * i)) & 0xFFu
+                                : tok == j ? fresh : (w[q] >> (8 * i)) & 0xFFu;
+            outw |= byte << (8 * i);
+          }
+          w[q] = outw;
+        }
+        *gp = w;
+      }
+    }
+    if (lane == 0) *scale_p = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Debug gather: contiguous copy of each sequence's tokens, same addressing.
 // ---------------------------------------------------------------------------
 template <int KVT>
@@ -905,6 +1060,23 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   else if (a.kvt == KV_BF16) PKV_APPEND(KV_BF16);
   else PKV_APPEND(KV_FP8);
 #undef PKV_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_append_fp8(const AppendFp8Args& a, hipStream_t s) {
+  if (a.batch <= 0) return hipSuccess;
+  dim3 grid((unsigned)(((int64_t)a.batch * a.num_kv_heads + 3) / 4)), block(256);
+#define PKV_APPEND_FP8(BF, DD)                                                                     \
+  hipLaunchKernelGGL((append_fp8_kernel<BF, DD>), grid, block, 0, s, a.k_new, a.v_new, a.block_tables, \
+                     a.seq_lens, static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool),   \
+                     a.k_scales, a.v_scales, a.batch, a.max_pages, a.num_pages, a.num_kv_heads,      \
+                     a.page_size)
+  if (a.new_bf16) {
+    if (a.head_dim == 64) PKV_APPEND_FP8(true, 64); else PKV_APPEND_FP8(true, 128);
+  } else {
+    if (a.head_dim == 64) PKV_APPEND_FP8(false, 64); else PKV_APPEND_FP8(false, 128);
+  }
+#undef PKV_APPEND_FP8
   return hipGetLastError();
 }
 

@@ -124,3 +124,24 @@ def _step(**over):
                                        (dict(vn=F + 4), -6)])
 def test_step_rejects_bad_arguments(over, code):
     assert _step(**over) == code
+
+
+def _append_fp8(**over):
+    a = dict(k=F, v=F, ndt=1, bt=F, mp=4, sl=F, b=2, kp=F, vp=F, ks=F, vs=F, np_=8, hkv=2, d=128, p=64)
+    a.update(over)
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return pkv.lib().pkv_kv_append_fp8(vp(a["k"]), vp(a["v"]), a["ndt"], vp(a["bt"]), a["mp"], vp(a["sl"]),
+                                       a["b"], vp(a["kp"]), vp(a["vp"]), vp(a["ks"]), vp(a["vs"]), a["np_"],
+                                       a["hkv"], a["d"], a["p"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ks=0), -1), (dict(vs=0), -1), (dict(k=0), -1), (dict(ndt=2), -3), (dict(ndt=7), -3),
+    (dict(p=32), -2), (dict(d=96), -2), (dict(hkv=0), -2), (dict(kp=F + 4), -6), (dict(v=F + 2), -6),
+])
+def test_append_fp8_rejects_bad_arguments(over, code):
+    assert _append_fp8(**over) == code
+
+
+def test_append_fp8_batch_zero_is_a_noop():
+    assert _append_fp8(b=0, k=0, v=0, ks=0, vs=0) == 0

@@ -241,10 +241,11 @@ def test_split_merge_equals_unsplit(part):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_bf16", "inflight_bf16",
-                                  "long_splitkv_bf16", "fp8_kv"])
+                                  "long_splitkv_bf16", "fp8_kv", "inflight_fp8"])
 def test_c_and_numpy_oracles_agree(name):
     small = {"llama3_8b_bf16": dict(B=6), "inflight_bf16": dict(B=6, n_steps=2, max_len=3000),
-             "long_splitkv_bf16": dict(B=2, L=3000), "fp8_kv": dict(B=4)}
+             "long_splitkv_bf16": dict(B=2, L=3000), "fp8_kv": dict(B=4),
+             "inflight_fp8": dict(B=6, n_steps=2, max_len=3000)}
     wl = configs.CONFIGS[name](**small.get(name, {}))
     a, b = _oracles(wl)
     assert np.abs(a - b).max() < 1e-12

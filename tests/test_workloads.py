@@ -15,7 +15,8 @@ def _live_pages(wl, lens):
 
 @pytest.mark.parametrize("name,kw", [("tiny_fp32", {}), ("llama3_8b_bf16", dict(B=8)),
                                      ("inflight_bf16", dict(B=16, n_steps=16, max_len=4000)),
-                                     ("long_splitkv_bf16", dict(B=2, L=2048)), ("fp8_kv", dict(B=4))])
+                                     ("long_splitkv_bf16", dict(B=2, L=2048)), ("fp8_kv", dict(B=4)),
+                                     ("inflight_fp8", dict(B=16, n_steps=16, max_len=4000))])
 def test_deterministic_and_valid(name, kw):
     a = configs.CONFIGS[name](**kw)
     b = configs.CONFIGS[name](**kw)

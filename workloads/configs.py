@@ -70,6 +70,9 @@ class Workload:
     k_scales: Optional[np.ndarray] = None   # float32 [num_pages, Hkv]
     v_scales: Optional[np.ndarray] = None
     steps: List[Step] = field(default_factory=list)
+    # format of the steps' k_new / v_new rows: the cache format (copied into the
+    # pages), or bf16 rows for an fp8 cache (quantised on write)
+    new_dtype: Optional[str] = None
 
     @property
     def G(self) -> int:
@@ -287,6 +290,18 @@ def inflight_bf16(seed: int = 3, B: int = 256, n_steps: int = 16,
     use; a random half of them is freed; the B real sequences take their pages
     round-robin; the remaining dummies are freed.
     """
+    return _inflight("inflight_bf16", seed, B, n_steps, max_len, "bf16")
+
+
+def inflight_fp8(seed: int = 3, B: int = 256, n_steps: int = 16, max_len: int = 32768) -> Workload:
+    """The in-flight batch above (same seed, lengths, churn and draws) with an fp8
+    e4m3 cache: resident pages quantised with per-(page, kv head) scale amax/448,
+    and each step's new K/V rows given in bf16, to be quantised on write with
+    dynamic page scales (the cache format the fp8 append produces)."""
+    return _inflight("inflight_fp8", seed, B, n_steps, max_len, "fp8")
+
+
+def _inflight(name, seed, B, n_steps, max_len, kv_dtype) -> Workload:
     rng = np.random.default_rng(seed)
     P = 128
     L0 = lognormal_lengths(rng, B, 1024.0, 1.0, 1, max_len)
@@ -314,8 +329,9 @@ def inflight_bf16(seed: int = 3, B: int = 256, n_steps: int = 16,
     bt = np.full((B, max_pages), -1, dtype=np.int32)
     for b, t in enumerate(tables):
         bt[b, :len(t)] = t
-    wl = _assemble("inflight_bf16", seed, B, 32, 8, 128, P, NP, "bf16", "bf16", "bf16",
+    wl = _assemble(name, seed, B, 32, 8, 128, P, NP, kv_dtype, "bf16", "bf16",
                    np.float32(1.0 / math.sqrt(128)), 0, step_lens[-1], bt, pool_lens=L0)
+    wl.new_dtype = "bf16"
     for s in range(n_steps):
         r = _child(seed, 4, s)
         kn = r.standard_normal((B, 8, 128), dtype=np.float32)
@@ -376,4 +392,5 @@ CONFIGS = {
     "inflight_bf16": inflight_bf16,
     "long_splitkv_bf16": long_splitkv_bf16,
     "fp8_kv": fp8_kv,
+    "inflight_fp8": inflight_fp8,
 }
