@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "paged decode attention: KV HBM GB/s (fraction of peak) + seqs/s per layer"
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", "pkv_kernels.hip")
-WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "tiny_fp32"]
+WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "tiny_fp32"]
 
 
 def kernel_hash() -> str:
@@ -53,6 +53,11 @@ def parse():
     return ap.parse_args()
 
 
+def quantises_on_write(wl) -> bool:
+    """fp8 cache fed with wider new rows: the step appends through kv_append_fp8."""
+    return wl.kv_dtype == "fp8" and wl.new_dtype not in (None, "fp8")
+
+
 def alg_bytes(wl, seq_lens):
     """Bytes the method must move: (decode bytes, append bytes) for one step."""
     import numpy as np
@@ -65,7 +70,11 @@ def alg_bytes(wl, seq_lens):
     dec = kv + wl.B * wl.Hq * wl.D * (qb + ob) + int(pages.sum()) * 4 + wl.B * 4
     if wl.kv_dtype == "fp8":
         dec += int(pages.sum()) * wl.Hkv * 4 * 2
-    app = 2 * (wl.B * wl.Hkv * wl.D * eb * 2) + wl.B * 8
+    if quantises_on_write(wl):
+        # read the bf16 rows, write fp8 rows, read and write both page scales
+        app = wl.B * wl.Hkv * (2 * wl.D * 2 + 2 * wl.D * eb + 2 * 4 * 2) + wl.B * 8
+    else:
+        app = 2 * (wl.B * wl.Hkv * wl.D * eb * 2) + wl.B * 8
     return dec, app, kv
 
 
@@ -132,13 +141,21 @@ def cpu_baseline(wl, steps, seconds):
     import numpy as np
     from oracle import c_oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    from oracle import paged
     kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    ks = None if wl.k_scales is None else wl.k_scales.copy()
+    vs = None if wl.v_scales is None else wl.v_scales.copy()
     reps, kv_total, seqs, t0 = 0, 0, 0, time.perf_counter()
     while True:
         st = steps[reps % len(steps)]
-        c_oracle.append(st["k_new"], st["v_new"], wl.kv_dtype, wl.block_tables, st["seq_lens"], kp, vp, wl.P)
+        if quantises_on_write(wl):
+            paged.append_fp8_dynamic(st["k_new"], st["v_new"], wl.new_dtype, wl.block_tables, st["seq_lens"],
+                                     kp, vp, ks, vs, wl.P)
+        else:
+            c_oracle.append(st["k_new"], st["v_new"], wl.kv_dtype, wl.block_tables, st["seq_lens"], kp, vp,
+                            wl.P)
         c_oracle.decode(wl.q, wl.q_dtype, kp, vp, wl.kv_dtype, wl.block_tables, st["seq_lens"], wl.Hq,
-                        wl.P, wl.scale, wl.k_scales, wl.v_scales, nthreads=threads)
+                        wl.P, wl.scale, ks, vs, nthreads=threads)
         d, a, _ = alg_bytes(wl, st["seq_lens"])
         kv_total += d + a
         seqs += wl.B
@@ -152,7 +169,7 @@ def cpu_baseline(wl, steps, seconds):
                       f"(C oracle, {threads} threads), {el:.1f} s"}
 
 
-def diagnostics(pkv, wl, q, bt, kps, vps, ks, vs, dsteps, out, ws, step, i0, n=30):
+def diagnostics(pkv, wl, q, bt, kps, vps, kss, vss, dsteps, out, ws, step, i0, n=30):
     """Per-launch spread and the parts of a step, measured after the timed region.
 
     Each launch here is bracketed by its own event pair (whose packets add a few
@@ -179,12 +196,17 @@ def diagnostics(pkv, wl, q, bt, kps, vps, ks, vs, dsteps, out, ws, step, i0, n=3
         return us
 
     def app(i):
-        pkv.kv_append(s0["kn"], s0["vn"], wl.kv_dtype, bt, s0["sl"], kps[i % layers], vps[i % layers],
-                      wl.Hkv, wl.D, wl.P)
+        if quantises_on_write(wl):
+            pkv.kv_append_fp8(s0["kn"], s0["vn"], wl.new_dtype, bt, s0["sl"], kps[i % layers], vps[i % layers],
+                              kss[i % layers], vss[i % layers], wl.Hkv, wl.D, wl.P)
+        else:
+            pkv.kv_append(s0["kn"], s0["vn"], wl.kv_dtype, bt, s0["sl"], kps[i % layers], vps[i % layers],
+                          wl.Hkv, wl.D, wl.P)
 
     def dec(i):
         if wl.kv_dtype == "fp8":
-            pkv.paged_attn_decode_fp8(q, wl.q_dtype, kps[i % layers], vps[i % layers], ks, vs, bt, s0["sl"],
+            pkv.paged_attn_decode_fp8(q, wl.q_dtype, kps[i % layers], vps[i % layers], kss[i % layers],
+                                      vss[i % layers], bt, s0["sl"],
                                       wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws,
                                       wl.partition_tokens)
         else:
@@ -255,21 +277,31 @@ def main():
     bt = T(wl.block_tables)
     kps = [T(wl.k_pool) for _ in range(layers)]
     vps = [T(wl.v_pool) for _ in range(layers)]
-    ks = None if wl.k_scales is None else T(wl.k_scales)
-    vs = None if wl.v_scales is None else T(wl.v_scales)
+    # each cache copy has its own scales (an fp8 append may change them)
+    kss = [None if wl.k_scales is None else T(wl.k_scales) for _ in range(layers)]
+    vss = [None if wl.v_scales is None else T(wl.v_scales) for _ in range(layers)]
     dsteps = [{"sl": T(s["seq_lens"]), "kn": T(s["k_new"]), "vn": T(s["v_new"])} for s in steps]
     odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
     out = torch.empty((wl.B, wl.Hq, wl.D), dtype=odt, device=dev)
     ws = torch.zeros(pkv.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    quant = quantises_on_write(wl)
+
     def step(i):
-        """One decode iteration of one layer: append + attention in one decode_step call."""
+        """One decode iteration of one layer: append + attention, in one decode_step
+        call; an fp8 cache fed bf16 rows quantises them on write first
+        (kv_append_fp8), then decodes."""
         s = dsteps[i % len(dsteps)]
-        kp, vp = kps[i % layers], vps[i % layers]
-        pkv.decode_step(q, wl.q_dtype, s["kn"], s["vn"], kp, vp, wl.kv_dtype, bt, s["sl"], wl.Hq, wl.Hkv,
-                        wl.D, wl.P, wl.scale, out, wl.out_dtype, ws, k_scales=ks, v_scales=vs,
-                        partition_tokens=wl.partition_tokens)
+        kp, vp, ks, vs = kps[i % layers], vps[i % layers], kss[i % layers], vss[i % layers]
+        if quant:
+            pkv.kv_append_fp8(s["kn"], s["vn"], wl.new_dtype, bt, s["sl"], kp, vp, ks, vs, wl.Hkv, wl.D, wl.P)
+            pkv.paged_attn_decode_fp8(q, wl.q_dtype, kp, vp, ks, vs, bt, s["sl"], wl.Hq, wl.Hkv, wl.D, wl.P,
+                                      wl.scale, out, wl.out_dtype, ws, wl.partition_tokens)
+        else:
+            pkv.decode_step(q, wl.q_dtype, s["kn"], s["vn"], kp, vp, wl.kv_dtype, bt, s["sl"], wl.Hq,
+                            wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws, k_scales=ks, v_scales=vs,
+                            partition_tokens=wl.partition_tokens)
 
     for i in range(args.warmup):
         step(i)
@@ -290,7 +322,7 @@ def main():
     dec_mean = evs.elapsed_ms(0) / args.steps
     evs.close()
 
-    diag = diagnostics(pkv, wl, q, bt, kps, vps, ks, vs, dsteps, out, ws, step, args.warmup + args.steps)
+    diag = diagnostics(pkv, wl, q, bt, kps, vps, kss, vss, dsteps, out, ws, step, args.warmup + args.steps)
 
     step_bytes, kv_bytes = 0, 0
     for i in range(args.steps):
@@ -320,13 +352,17 @@ def main():
                    "head_dim": wl.D, "page_size": wl.P,
                    "mean_seq_len": float(np.mean(steps[0]["seq_lens"])),
                    "partition_tokens": wl.partition_tokens, "layers_rotated": layers,
-                   "step": "decode_step: kv_append fused into paged decode (split kernel + LSE merge kernel)"},
+                   "step": ("kv_append_fp8 (quantise on write, dynamic page scales) then fp8 paged decode"
+                            if quant else
+                            "decode_step: kv_append fused into paged decode (split kernel + LSE merge kernel)")},
         "seqs_per_s_per_layer": round(wl.B / (ms_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(kv_bytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_step launch (decode_split_kernel + decode_merge_kernel)",
+                     "kernel": ("kv_append_fp8 + paged_attn_decode_fp8 (append_fp8_kernel + decode_split_kernel"
+                                " + decode_merge_kernel)" if quant else
+                                "decode_step launch (decode_split_kernel + decode_merge_kernel)"),
                      "call_ms_mean": round(dec_mean, 5), "alg_bytes_per_call": int(step_bytes)},
     }
     rec["diagnostics"] = diag

@@ -113,8 +113,9 @@ int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype,
  * j = t % P of page pg = block_tables[b][t / P], and for each kv head g, for K
  * and V separately, with x = the new row widened to fp32 and a = max |x|:
  *   j == 0 (first token of the page): s = a / 448 (1 if a == 0);
- *   j > 0, s0 = scales[pg][g]: s = s0 if a / s0 <= 448; otherwise s = a / 448
- *     and every earlier slot of the page is re-encoded as enc((dec(byte) * s0) / s);
+ *   j > 0, s0 = scales[pg][g]: s = s0 if a / s0 <= 464 (the row's largest
+ *     element still rounds to +-448, no clipping); otherwise s = a / 448 and
+ *     every earlier slot of the page is re-encoded as enc((dec(byte) * s0) / s);
  *   the new row is stored as enc(x / s); scales[pg][g] = s.
  * Each division and product is one fp32 operation rounded to nearest even;
  * enc is e4m3 round-to-nearest-even saturating at +-448; dec is exact.  So

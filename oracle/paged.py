@@ -173,12 +173,16 @@ def merge_partials(o, lse):
 # yololab page ("FP8 與極致量化") gives FP8 as the way to halve the bandwidth a
 # model needs.  Applied here where new K/V data enter the fp8 cache.  Reading
 # (the pages fix no granularity or update rule): one fp32 scale per (page, kv
-# head), real value = decoded byte * scale, scale = amax / 448 of the tokens
-# written so far; the scale only grows, and when it grows the page's earlier
-# tokens are re-encoded under the new one.  Every step below is one fp32
-# operation rounded to nearest even, so the result is a unique byte image.
+# head), real value = decoded byte * scale, set to amax / 448 by the page's
+# first token; a later token keeps the scale if its largest element still
+# rounds to a finite code without clipping (|x| / scale <= 464, the midpoint
+# between 448 and the next binade step, which rounds down to 448), otherwise
+# the scale grows to its amax / 448 and the page's earlier tokens are
+# re-encoded under it.  Every step below is one fp32 operation rounded to
+# nearest even, so the result is a unique byte image.
 
 E4M3_FINITE_MAX = 448.0
+E4M3_NO_CLIP = 464.0        # largest |x| / scale that still rounds to +-448
 
 
 def e4m3_encode(x: np.ndarray) -> np.ndarray:
@@ -208,7 +212,8 @@ def append_fp8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, 
     and each kv head g, separately for K and V with x = the new row widened to
     fp32 and a = max |x|:
       j == 0 (first token of the page): s = a / 448, or 1 when a == 0;
-      j > 0, s0 = the page's current scale: if a / s0 <= 448 then s = s0;
+      j > 0, s0 = the page's current scale: if a / s0 <= 464 (the row's largest
+        element rounds to +-448 or less, no clipping) then s = s0;
         otherwise s = a / 448 and every earlier slot j' < j is re-encoded:
         byte' = enc((dec(byte) * s0) / s);
       the new token: byte = enc(x / s); the page scale becomes s.
@@ -240,7 +245,7 @@ def append_fp8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, 
                     s = f32(a / c448) if a > 0 else f32(1)
                 else:
                     s0 = f32(scales[pg, g])
-                    if f32(a / s0) <= c448:
+                    if f32(a / s0) <= f32(E4M3_NO_CLIP):
                         s = s0
                     else:
                         s = f32(a / c448)

@@ -797,8 +797,9 @@ __global__ __launch_bounds__(256) void append_kernel(
 // One wave per (sequence, kv head); K, then V, each with its own scale:
 // a = max |x| of the new row (widened to fp32);
 //   slot j == 0 (first token of the page): s = a / 448 (1 if a == 0);
-//   else, s0 = the page's scale: s = s0 if a / s0 <= 448, otherwise
-//   s = a / 448 and every earlier slot is re-encoded, enc((dec(byte) * s0) / s);
+//   else, s0 = the page's scale: s = s0 if a / s0 <= 464 (no clipping),
+//   otherwise s = a / 448 and every earlier slot is re-encoded,
+//   enc((dec(byte) * s0) / s);
 // the new row is stored as enc(x / s) and the page scale becomes s.
 // Every division and product is one correctly rounded fp32 operation.
 // ---------------------------------------------------------------------------
@@ -831,6 +832,100 @@ __device__ __forceinline__ uint32_t requant4(uint32_t w, float s0, float s) {
   return r;
 }
 
+// Scale decision for one row: returns the new scale; sets requant when the
+// page's earlier slots must be re-encoded.  A row fits the current scale while
+// its largest element rounds to +-448 without clipping: |x| / s0 <= 464, the
+// midpoint to the next binade step, which rounds down to 448.
+__device__ __forceinline__ float fp8_page_scale(float a, int j, float s0, bool& requant) {
+  requant = false;
+  if (j == 0) return a > 0.f ? a / 448.f : 1.f;
+  if (a / s0 <= 464.f) return s0;       // the row's largest element rounds to +-448 at most
+  requant = true;
+  return a / 448.f;
+}
+
+// A re-encode maps each old byte through enc((dec(byte) * s0) / s), a function
+// of the byte alone: the wave tabulates it once (4 codes per lane) in LDS and
+// then re-encodes by lookup.
+__device__ __forceinline__ uint32_t lut4(const uint8_t* lut, uint32_t w) {
+  return (uint32_t)lut[w & 0xFFu] | ((uint32_t)lut[(w >> 8) & 0xFFu] << 8) |
+         ((uint32_t)lut[(w >> 16) & 0xFFu] << 16) | ((uint32_t)lut[w >> 24] << 24);
+}
+
+// Re-encode slots [0, j) of a K chunk: 16-byte groups (16 dims of one token).
+// Each lane issues the loads of up to 16 groups before converting any, so a
+// page costs about one memory round trip per 1024 groups.
+template <int D>
+__device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uint8_t* lut, int lane) {
+  constexpr int GPL = 16;
+  const int ngrp = (D / 16) * j;
+  for (int base = 0; base < ngrp; base += 64 * GPL) {
+    u32x4_t w[GPL];
+    int off[GPL];
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int gi = min(base + lane + 64 * i, ngrp - 1);     // clamped: in-bounds, stored only if owned
+      const int c = gi / j, jj = gi - c * j;
+      off[i] = (c * P + jj) * 16;
+      w[i] = *reinterpret_cast<const u32x4_t*>(pool + off[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      if (base + lane + 64 * i < ngrp) {
+        u32x4_t r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[i][q]);
+        *reinterpret_cast<u32x4_t*>(pool + off[i]) = r;
+      }
+    }
+  }
+}
+
+// Re-encode a V chunk for a scale change at slot j: a 16-byte group holds 16
+// tokens of one dim from one 64-token block; blocks 0 .. j/64 are rewritten
+// group by group: tokens < j re-encoded, token j takes its new byte (nbj, from
+// LDS), later slots keep their bytes.
+template <int D>
+__device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* lut, const uint8_t* nbj,
+                                          int lane) {
+  constexpr int GPL = 16, TB = 64;
+  const int ngrp = (j / TB + 1) * 4 * D;
+  for (int base = 0; base < ngrp; base += 64 * GPL) {
+    u32x4_t w[GPL];
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int gi = min(base + lane + 64 * i, ngrp - 1);
+      const int blk = gi / (4 * D), rem = gi - blk * 4 * D;
+      w[i] = *reinterpret_cast<const u32x4_t*>(pool + (size_t)blk * TB * D + (size_t)rem * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int gi = base + lane + 64 * i;
+      if (gi < ngrp) {
+        const int blk = gi / (4 * D), rem = gi - blk * 4 * D;
+        const int c = rem / D, d = rem - c * D;
+        const uint32_t fresh = nbj[d];
+        u32x4_t r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t re = lut4(lut, w[i][q]);
+          uint32_t outw = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // byte 4q + e of the group holds token 16q + 4c + e of block blk
+            const int tok = blk * TB + 16 * q + 4 * c + e;
+            const uint32_t byte = tok < j ? (re >> (8 * e)) & 0xFFu
+                                : tok == j ? fresh : (w[i][q] >> (8 * e)) & 0xFFu;
+            outw |= byte << (8 * e);
+          }
+          r[q] = outw;
+        }
+        *reinterpret_cast<u32x4_t*>(pool + (size_t)blk * TB * D + (size_t)rem * 16) = r;
+      }
+    }
+  }
+}
+
 template <bool IN_BF16, int D>
 __global__ __launch_bounds__(256) void append_fp8_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new,
@@ -838,13 +933,24 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(
     uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool,
     float* __restrict__ kscales, float* __restrict__ vscales, int B, int MP, int NP, int Hkv, int P) {
   constexpr int NPL = D / 64;           // new-row elements per lane (consecutive dims)
-  constexpr int TB = 64;                // V block of the fp8 layout, tokens
-  __shared__ uint8_t s_nb[4][D];        // the new row's encoded bytes (V pass of a re-encode)
+  __shared__ uint8_t s_nb[4][D];        // the new V row's bytes (V pass of a re-encode)
+  __shared__ uint32_t s_lut[4][2][64];  // re-encode tables, K and V (256 codes each)
   const int wv = uniform(threadIdx.x >> 6);
   const int bg = uniform(blockIdx.x * 4 + wv);
   if (bg >= B * Hkv) return;
   const int lane = threadIdx.x & 63;
   const int b = bg / Hkv, g = bg - b * Hkv;
+  const int d0 = lane * NPL;
+  // the new rows do not depend on the table: their loads go first
+  const size_t row = ((size_t)b * Hkv + g) * D + (size_t)d0;
+  float xk[NPL], xv[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    xk[i] = IN_BF16 ? fbits((uint32_t)static_cast<const uint16_t*>(k_new)[row + i] << 16)
+                    : static_cast<const float*>(k_new)[row + i];
+    xv[i] = IN_BF16 ? fbits((uint32_t)static_cast<const uint16_t*>(v_new)[row + i] << 16)
+                    : static_cast<const float*>(v_new)[row + i];
+  }
   const int L = uniform(((const_i32_ptr)seq_lens)[b]);
   if (L <= 0) return;
   const int t = L - 1, pgi = t / P, j = t - pgi * P;
@@ -852,97 +958,66 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(
   const int pg = uniform(((const_i32_ptr)bt)[(size_t)b * MP + pgi]);
   if ((unsigned)pg >= (unsigned)NP) return;
   const size_t ch = chunk_elem(pg, g, Hkv, P, D);        // byte offset (1-byte elements)
-  const size_t row = ((size_t)b * Hkv + g) * D + (size_t)lane * NPL;
-  const int d0 = lane * NPL;
-
-#pragma unroll 1
-  for (int which = 0; which < 2; ++which) {
-    const void* src = which ? v_new : k_new;
-    uint8_t* pool = (which ? vpool : kpool) + ch;
-    float* scale_p = (which ? vscales : kscales) + (size_t)pg * Hkv + g;
-    float x[NPL];
+  const size_t si = (size_t)pg * Hkv + g;
+  float sk0 = 1.f, sv0 = 1.f;
+  if (j > 0) {                           // both scales in one round trip
+    sk0 = kscales[si];
+    sv0 = vscales[si];
+  }
+  float ak = 0.f, av = 0.f;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      x[i] = IN_BF16 ? fbits((uint32_t)static_cast<const uint16_t*>(src)[row + i] << 16)
-                     : static_cast<const float*>(src)[row + i];
-    float a = 0.f;
+  for (int i = 0; i < NPL; ++i) {
+    ak = fmaxf(ak, fabsf(xk[i]));
+    av = fmaxf(av, fabsf(xv[i]));
+  }
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) a = fmaxf(a, fabsf(x[i]));
+  for (int o = 32; o >= 1; o >>= 1) {
+    ak = fmaxf(ak, __shfl_xor(ak, o));
+    av = fmaxf(av, __shfl_xor(av, o));
+  }
+  ak = fbits(uniform((int)ubits(ak)));
+  av = fbits(uniform((int)ubits(av)));
+  sk0 = fbits(uniform((int)ubits(sk0)));
+  sv0 = fbits(uniform((int)ubits(sv0)));
+  bool rk, rv;
+  const float sk = fp8_page_scale(ak, j, sk0, rk);
+  const float sv = fp8_page_scale(av, j, sv0, rv);
+  uint32_t nbk[NPL], nbv[NPL];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-    a = fbits(uniform((int)ubits(a)));
-    float s;
-    bool requant = false;
-    float s0 = 1.f;
-    if (j == 0) {
-      s = a > 0.f ? a / 448.f : 1.f;
-    } else {
-      s0 = fbits(uniform((int)ubits(*scale_p)));
-      if (a / s0 <= 448.f) {
-        s = s0;
-      } else {
-        s = a / 448.f;
-        requant = true;
-      }
-    }
-    uint32_t nb[NPL];
+  for (int i = 0; i < NPL; ++i) {
+    nbk[i] = e4m3_encode(xk[i] / sk);
+    nbv[i] = e4m3_encode(xv[i] / sv);
+  }
+  uint8_t* kp = kpool + ch;
+  uint8_t* vp = vpool + ch;
+  const uint8_t* lutk = reinterpret_cast<const uint8_t*>(s_lut[wv][0]);
+  const uint8_t* lutv = reinterpret_cast<const uint8_t*>(s_lut[wv][1]);
+  if (rk || rv) {
+    const uint32_t codes = (uint32_t)(4 * lane) * 0x01010101u + 0x03020100u;   // 4 codes per lane
+    if (rk) s_lut[wv][0][lane] = requant4(codes, sk0, sk);
+    if (rv) s_lut[wv][1][lane] = requant4(codes, sv0, sv);
+    __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
+  }
+  if (rk) requant_k<D>(kp, j, P, lutk, lane);
+  // the new K token's dims d0.. are consecutive bytes of one group (disjoint
+  // from the re-encoded slots)
+  uint8_t* kt = kp + k_elem<16>(j, d0, P);
+  if (NPL == 2)
+    *reinterpret_cast<uint16_t*>(kt) = (uint16_t)(nbk[0] | (nbk[NPL - 1] << 8));
+  else
+    *kt = (uint8_t)nbk[0];
+  if (rv) {
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) nb[i] = e4m3_encode(x[i] / s);
-
-    if (which == 0) {
-      // K: earlier slots are whole 16-byte groups (16 dims of one token)
-      if (requant) {
-        const int ngrp = (D / 16) * j;
-        for (int gi = lane; gi < ngrp; gi += 64) {
-          const int c = gi / j, jj = gi - c * j;
-          u32x4_t* gp = reinterpret_cast<u32x4_t*>(pool + ((size_t)c * P + jj) * 16);
-          u32x4_t w = *gp;
+    for (int i = 0; i < NPL; ++i) s_nb[wv][d0 + i] = (uint8_t)nbv[i];
+    __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
+    requant_v<D>(vp, j, lutv, s_nb[wv], lane);
+  } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) w[q] = requant4(w[q], s0, s);
-          *gp = w;
-        }
-      }
-      // the new token's dims d0.. are consecutive bytes of one group
-      uint8_t* kp = pool + k_elem<16>(j, d0, P);
-      if (NPL == 2)
-        *reinterpret_cast<uint16_t*>(kp) = (uint16_t)(nb[0] | (nb[NPL - 1] << 8));
-      else
-        *kp = (uint8_t)nb[0];
-    } else if (!requant) {
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) pool[v_elem<16>(j, d0 + i, D)] = (uint8_t)nb[i];
-    } else {
-      // V: a 16-byte group holds 16 tokens of one dim from one 64-token block;
-      // rewrite blocks 0 .. j/64 group by group: tokens < j re-encoded, token j
-      // takes the new byte, later slots keep their bytes.
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) s_nb[wv][d0 + i] = (uint8_t)nb[i];
-      __builtin_amdgcn_wave_barrier();   // one wave's LDS operations complete in order
-      const int ngrp = (j / TB + 1) * 4 * D;
-      for (int gi = lane; gi < ngrp; gi += 64) {
-        const int blk = gi / (4 * D), rem = gi - blk * 4 * D;
-        const int c = rem / D, d = rem - c * D;
-        u32x4_t* gp = reinterpret_cast<u32x4_t*>(pool + (size_t)blk * TB * D + ((size_t)c * D + d) * 16);
-        u32x4_t w = *gp;
-        const uint32_t fresh = s_nb[wv][d];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t re = requant4(w[q], s0, s);
-          uint32_t outw = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // byte e = 4q + i holds token r = 16 * (e / 4) + 4c + e % 4 = 16q + 4c + i
-            const int tok = blk * TB + 16 * q + 4 * c + i;
-            const uint32_t byte = tok < j ? (re >> (8 * i)) & 0xFFu
-                                : tok == j ? fresh : (w[q] >> (8 * i)) & 0xFFu;
-            outw |= byte << (8 * i);
-          }
-          w[q] = outw;
-        }
-        *gp = w;
-      }
-    }
-    if (lane == 0) *scale_p = s;
+    for (int i = 0; i < NPL; ++i) vp[v_elem<16>(j, d0 + i, D)] = (uint8_t)nbv[i];
+  }
+  if (lane == 0) {
+    kscales[si] = sk;
+    vscales[si] = sv;
   }
 }
 

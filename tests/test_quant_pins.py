@@ -234,3 +234,37 @@ def test_k_and_v_scales_move_independently():
     assert np.array_equal(ks, ks0, equal_nan=True) and vs[0, 0] > ks[0, 0]
     koff, _ = paged._offsets(P, D, "fp8")
     assert np.array_equal(kp[0, 0, koff[0]], k0[0, 0, koff[0]])
+
+
+def test_no_clip_threshold_keeps_the_scale_up_to_464():
+    """A row whose largest element lands in (448, 464] under the page scale still
+    rounds to +-448 without clipping: the scale stays; just above 464 it grows."""
+    Hkv, D, P = 1, 64, 64
+    bt = np.array([[0]], dtype=np.int32)
+    for ratio, grows in ((448.0, False), (456.0, False), (464.0, False), (464.0 * (1 + 2 ** -20), True),
+                         (470.0, True)):
+        kp, vp, ks, vs = empty_fp8(1, Hkv, P, D)
+        first = np.zeros((1, 1, D), F32)
+        first[0, 0, 0] = 56.0                                     # scale exactly 1/8
+        paged.append_fp8_dynamic(first, first, "f32", bt, np.array([1], np.int32), kp, vp, ks, vs, P)
+        second = np.zeros((1, 1, D), F32)
+        second[0, 0, 1] = F32(ratio / 8)
+        paged.append_fp8_dynamic(second, second, "f32", bt, np.array([2], np.int32), kp, vp, ks, vs, P)
+        assert (ks[0, 0] != F32(0.125)) == grows, ratio
+        if not grows:
+            assert stored_row(kp, P, D, 0, 0, 1, "k")[1] == 0x7E
+            assert stored_row(kp, P, D, 0, 0, 0, "k")[0] == 0x7E       # untouched
+
+
+def test_repeating_the_row_that_set_the_scale_never_regrows_it():
+    """a / fp32(a / 448) can round just above 448; the no-clip rule keeps the scale."""
+    rng = np.random.default_rng(9)
+    Hkv, D, P = 1, 64, 64
+    bt = np.array([[0]], dtype=np.int32)
+    for _ in range(50):
+        kp, vp, ks, vs = empty_fp8(1, Hkv, P, D)
+        x = (rng.standard_normal((1, 1, D)) * 3).astype(F32)
+        paged.append_fp8_dynamic(x, x, "f32", bt, np.array([1], np.int32), kp, vp, ks, vs, P)
+        s1 = ks[0, 0]
+        paged.append_fp8_dynamic(x, x, "f32", bt, np.array([2], np.int32), kp, vp, ks, vs, P)
+        assert ks[0, 0] == s1
