@@ -15,7 +15,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "pkv_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
-DT = {"f32": 0, "bf16": 1, "fp8": 2}
+DT = {"f32": 0, "bf16": 1, "fp8": 2, "i8": 3}
 
 _lib = None
 

@@ -20,7 +20,7 @@ import math
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "i8": 1}
 
 
 # ---------------------------------------------------------------- decoding ----
@@ -60,6 +60,8 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
         return bf16_to_f64(x)
     if dtype == "fp8":
         return e4m3_to_f64(x)
+    if dtype == "i8":                       # two's complement bytes
+        return np.asarray(x).view(np.int8).astype(np.float64)
     raise ValueError(dtype)
 
 
@@ -115,7 +117,7 @@ def decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens, Hq, P, 
             continue
         k, v, pages = gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b)
         kf, vf = widen(k, kv_dtype), widen(v, kv_dtype)
-        if kv_dtype == "fp8":
+        if kv_dtype in ("fp8", "i8"):
             kf = kf * np.asarray(k_scales, np.float64)[pages].T[:, :, None]
             vf = vf * np.asarray(v_scales, np.float64)[pages].T[:, :, None]
         for g in range(Hkv):
@@ -202,30 +204,54 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
 
 
-def append_fp8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
-                       k_scales, v_scales, P):
-    """In place: token L-1 of each sequence into its fp8 page, with the page scale
-    kept at amax / 448 of the page's tokens (K and V each on their own).
+def int8_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> symmetric int8 byte: round to the nearest integer, a tie going
+    to the even one, then clamp to [-127, 127] (-128 is not used)."""
+    q = np.clip(np.rint(np.asarray(x, dtype=np.float32).astype(np.float64)), -127, 127)
+    return q.astype(np.int8).view(np.uint8)
+
+
+def int8_to_f64(codes: np.ndarray) -> np.ndarray:
+    return np.asarray(codes, dtype=np.uint8).view(np.int8).astype(np.float64)
+
+
+# Per format: (largest code value, largest |x| / scale that still rounds into
+# range without clipping, encoder, exact decoder).  int8 rounds 127.5 to 128
+# (ties to even), which clamps to 127: still within half a step, so 127.5 is
+# the no-clip bound there, as 464 (the midpoint above 448) is for e4m3.
+DYNAMIC_FORMATS = {
+    "fp8": (448.0, 464.0, lambda y: e4m3_encode(y), e4m3_to_f64),
+    "i8": (127.0, 127.5, lambda y: int8_encode(y), int8_to_f64),
+}
+
+
+def append_dynamic(fmt, k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
+                   k_scales, v_scales, P):
+    """In place: token L-1 of each sequence into its one-byte page (fmt "fp8" or
+    "i8"), with the page scale kept at amax / QMAX of the page's tokens (K and V
+    each on their own); QMAX = 448 for fp8, 127 for int8.
 
     For each b with L = seq_lens[b] >= 1, t = L - 1, page pg = block_tables[b, t//P]
     (a table index or page id out of range skips the sequence), slot j = t % P,
     and each kv head g, separately for K and V with x = the new row widened to
     fp32 and a = max |x|:
-      j == 0 (first token of the page): s = a / 448, or 1 when a == 0;
-      j > 0, s0 = the page's current scale: if a / s0 <= 464 (the row's largest
-        element rounds to +-448 or less, no clipping) then s = s0;
-        otherwise s = a / 448 and every earlier slot j' < j is re-encoded:
+      j == 0 (first token of the page): s = a / QMAX, or 1 when a == 0;
+      j > 0, s0 = the page's current scale: if a / s0 <= NOCLIP (the row's
+        largest element rounds to the largest code or less, no clipping:
+        464 for fp8, 127.5 for int8) then s = s0;
+        otherwise s = a / QMAX and every earlier slot j' < j is re-encoded:
         byte' = enc((dec(byte) * s0) / s);
       the new token: byte = enc(x / s); the page scale becomes s.
     Arithmetic is fp32 (each division and product rounded to nearest even);
-    enc is e4m3_encode, dec the exact e4m3 value.
+    enc is the format's encoder, dec its exact value.
     """
+    qmax, noclip, enc, dec = DYNAMIC_FORMATS[fmt]
     NP, Hkv, PD = k_pool.shape
     D = PD // P
     MP = np.asarray(block_tables).shape[1]
-    koff, voff = _offsets(P, D, "fp8")
+    koff, voff = _offsets(P, D, "fp8")          # one-byte layout
     f32 = np.float32
-    c448 = f32(E4M3_FINITE_MAX)
+    cmax, cnoclip = f32(qmax), f32(noclip)
     for b in range(len(seq_lens)):
         L = int(seq_lens[b])
         if L <= 0:
@@ -242,15 +268,29 @@ def append_fp8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, 
                 x = widen(np.asarray(new)[b, g], new_dtype).astype(np.float32)   # exact
                 a = f32(np.abs(x).max())
                 if j == 0:
-                    s = f32(a / c448) if a > 0 else f32(1)
+                    s = f32(a / cmax) if a > 0 else f32(1)
                 else:
                     s0 = f32(scales[pg, g])
-                    if f32(a / s0) <= f32(E4M3_NO_CLIP):
+                    if f32(a / s0) <= cnoclip:
                         s = s0
                     else:
-                        s = f32(a / c448)
+                        s = f32(a / cmax)
                         idx = off[:j]                                          # [j, D]
-                        real = e4m3_to_f64(pool[pg, g, idx]).astype(np.float32) * s0
-                        pool[pg, g, idx] = e4m3_encode(real.astype(np.float32) / s)
-                pool[pg, g, off[j]] = e4m3_encode(x / s)
+                        real = dec(pool[pg, g, idx]).astype(np.float32) * s0
+                        pool[pg, g, idx] = enc(real.astype(np.float32) / s)
+                pool[pg, g, off[j]] = enc(x / s)
                 scales[pg, g] = s
+
+
+def append_fp8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
+                       k_scales, v_scales, P):
+    """append_dynamic for an fp8 e4m3 cache (QMAX 448, no-clip bound 464)."""
+    append_dynamic("fp8", k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
+                   k_scales, v_scales, P)
+
+
+def append_int8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
+                        k_scales, v_scales, P):
+    """append_dynamic for a symmetric int8 cache (QMAX 127, no-clip bound 127.5)."""
+    append_dynamic("i8", k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
+                   k_scales, v_scales, P)

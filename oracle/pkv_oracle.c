@@ -21,8 +21,8 @@
  *     v_t = dec(V[page(t)][g][slot(t)][:]) * sV(page(t), g)
  *     s_t = scale * sum_d q[b][h][d] * k_t[d]
  *     out[b][h][:] = sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s)
- *   with out = 0 when L = 0.  dec() widens fp32, bf16 or fp8-e4m3 exactly;
- *   sK, sV are the per-(page, kv head) fp32 scales for fp8 and 1 otherwise.
+ *   with out = 0 when L = 0.  dec() widens fp32, bf16, fp8-e4m3 or int8 exactly;
+ *   sK, sV are the per-(page, kv head) fp32 scales for fp8 and int8, 1 otherwise.
  *   Everything after decoding is fp64, with libm exp.
  *
  * Byte layout of one (page, kv head) chunk of P tokens x D elements
@@ -38,9 +38,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_I8 = 3 };
 
-static int elem_bytes(int dt) { return dt == ORC_F32 ? 4 : dt == ORC_BF16 ? 2 : dt == ORC_FP8 ? 1 : 0; }
+static int elem_bytes(int dt) {
+  return dt == ORC_F32 ? 4 : dt == ORC_BF16 ? 2 : (dt == ORC_FP8 || dt == ORC_I8) ? 1 : 0;
+}
 
 /* bf16: the top half of a binary32. */
 double orc_bf16_to_f64(uint16_t bits) {
@@ -67,6 +69,7 @@ static double load_elem(const void* base, int dt, int64_t idx) {
   switch (dt) {
     case ORC_F32: return (double)((const float*)base)[idx];
     case ORC_BF16: return orc_bf16_to_f64(((const uint16_t*)base)[idx]);
+    case ORC_I8: return (double)((const int8_t*)base)[idx];   /* two's complement byte */
     default: return orc_e4m3_to_f64(((const uint8_t*)base)[idx]);
   }
 }

@@ -27,6 +27,8 @@ def _torch_widen(x, dtype):
         return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float64)
     if dtype == "bf16":
         return torch.from_numpy(np.asarray(x, np.uint16).view(np.int16).copy()).view(torch.bfloat16).to(torch.float64)
+    if dtype == "i8":
+        return torch.from_numpy(np.asarray(x, np.uint8).copy()).view(torch.int8).to(torch.float64)
     return torch.from_numpy(np.asarray(x, np.uint8).copy()).view(torch.float8_e4m3fn).to(torch.float64)
 
 
@@ -41,7 +43,7 @@ def _sdpa_reference(wl):
             continue
         k, v, ks, vs = configs.seq_tokens(wl.seed, b, L, Hkv, D, wl.kv_dtype, P)
         kt, vt = _torch_widen(k, wl.kv_dtype), _torch_widen(v, wl.kv_dtype)      # [L, Hkv, D]
-        if wl.kv_dtype == "fp8":
+        if wl.kv_dtype in ("fp8", "i8"):
             kt = kt * torch.from_numpy(np.repeat(ks, P, 0)[:L]).to(torch.float64)[:, :, None]
             vt = vt * torch.from_numpy(np.repeat(vs, P, 0)[:L]).to(torch.float64)[:, :, None]
         G = Hq // Hkv
@@ -66,6 +68,7 @@ SMALL = [
     dict(seed=12, lens=[3, 32, 33, 70], Hq=8, Hkv=2, D=32, P=32, kv_dtype="bf16"),
     dict(seed=13, lens=[1, 63, 64, 65, 130], Hq=4, Hkv=1, D=32, P=64, kv_dtype="fp8"),
     dict(seed=14, lens=[0, 7, 129], Hq=6, Hkv=3, D=16, P=128, kv_dtype="bf16"),
+    dict(seed=15, lens=[2, 64, 65, 200], Hq=8, Hkv=2, D=32, P=64, kv_dtype="i8"),
 ]
 
 
@@ -241,17 +244,19 @@ def test_split_merge_equals_unsplit(part):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_bf16", "inflight_bf16",
-                                  "long_splitkv_bf16", "fp8_kv", "inflight_fp8"])
+                                  "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "int8_kv", "inflight_int8"])
 def test_c_and_numpy_oracles_agree(name):
     small = {"llama3_8b_bf16": dict(B=6), "inflight_bf16": dict(B=6, n_steps=2, max_len=3000),
              "long_splitkv_bf16": dict(B=2, L=3000), "fp8_kv": dict(B=4),
-             "inflight_fp8": dict(B=6, n_steps=2, max_len=3000)}
+             "inflight_fp8": dict(B=6, n_steps=2, max_len=3000), "int8_kv": dict(B=4),
+             "inflight_int8": dict(B=6, n_steps=2, max_len=3000)}
     wl = configs.CONFIGS[name](**small.get(name, {}))
     a, b = _oracles(wl)
     assert np.abs(a - b).max() < 1e-12
 
 
-@pytest.mark.parametrize("kv_dtype,P", [("f32", 16), ("bf16", 32), ("bf16", 64), ("fp8", 64), ("fp8", 128)])
+@pytest.mark.parametrize("kv_dtype,P", [("f32", 16), ("bf16", 32), ("bf16", 64), ("fp8", 64), ("fp8", 128),
+                                        ("i8", 64)])
 def test_append_reproduces_packed_pool(kv_dtype, P):
     """Appending tokens one at a time (both oracles) rebuilds the generator's pool bytes."""
     wl = configs.custom(seed=21, lens=[1, P - 1, P, P + 1, 2 * P + 3], Hq=4, Hkv=2, D=32, P=P,
@@ -273,7 +278,7 @@ def test_append_reproduces_packed_pool(kv_dtype, P):
         assert np.array_equal(vp.view(np.uint8), wl.v_pool.view(np.uint8))
 
 
-@pytest.mark.parametrize("kv_dtype,P", [("f32", 16), ("bf16", 64), ("fp8", 64)])
+@pytest.mark.parametrize("kv_dtype,P", [("f32", 16), ("bf16", 64), ("fp8", 64), ("i8", 64)])
 def test_gather_returns_logical_tokens(kv_dtype, P):
     wl = configs.custom(seed=22, lens=[2, P, 3 * P - 1], Hq=2, Hkv=2, D=32, P=P, kv_dtype=kv_dtype)
     ko, vo = c_oracle.gather(wl.k_pool, wl.v_pool, kv_dtype, wl.block_tables, wl.seq_lens, P, 0)

@@ -1,4 +1,4 @@
-"""Pins of the oracle's fp8 encoder and of its dynamic-scale fp8 append.
+"""Pins of the oracle's fp8 and int8 encoders and of its dynamic-scale appends.
 
 The encoder is checked against torch's float8_e4m3fn conversion (round to
 nearest even; torch turns values past 464 into NaN, so the saturation rule is
@@ -268,3 +268,91 @@ def test_repeating_the_row_that_set_the_scale_never_regrows_it():
         s1 = ks[0, 0]
         paged.append_fp8_dynamic(x, x, "f32", bt, np.array([2], np.int32), kp, vp, ks, vs, P)
         assert ks[0, 0] == s1
+
+
+# ------------------------------------------------------------------ int8 ----
+
+def test_int8_encode_matches_torch_round_and_clamp():
+    x = all_bf16_as_f32()
+    m = np.isfinite(x) & (np.abs(x) < 1e4)
+    ties = (np.arange(-130, 130) + 0.5).astype(F32)
+    y = np.concatenate([x[m], ties, np.nextafter(ties, F32(np.inf)), np.nextafter(ties, F32(-np.inf))])
+    ref = torch.clamp(torch.round(torch.from_numpy(y)), -127, 127).to(torch.int8).numpy().view(np.uint8)
+    assert np.array_equal(paged.int8_encode(y), ref)
+    assert np.array_equal(paged.int8_encode(y), codec.int8_encode(y))
+
+
+def test_int8_first_token_sets_scale_and_hits_127():
+    rng = np.random.default_rng(20)
+    Hkv, D, P = 2, 128, 64
+    kp, vp, ks, vs = empty_fp8(2, Hkv, P, D)
+    x = one_token(rng, Hkv, D, 2.0)
+    bt = np.array([[1]], dtype=np.int32)
+    paged.append_int8_dynamic(x, x, "f32", bt, np.array([1], np.int32), kp, vp, ks, vs, P)
+    for g in range(Hkv):
+        a = F32(np.abs(x[0, g]).max())
+        assert ks[1, g] == F32(a / F32(127))
+        row = stored_row(kp, P, D, 1, g, 0, "k").view(np.int8)
+        assert abs(int(row[int(np.argmax(np.abs(x[0, g])))])) == 127
+        back = row.astype(np.float64) * float(ks[1, g])
+        assert np.all(np.abs(back - x[0, g]) <= 0.5 * float(ks[1, g]) * (1 + 1e-6))
+
+
+def test_int8_token_by_token_equals_one_shot():
+    rng = np.random.default_rng(21)
+    Hkv, D, P = 2, 64, 64
+    L = 2 * P - 3
+    x = rng.standard_normal((L, Hkv, D)).astype(F32)
+    for p0 in range(0, L, P):
+        x[p0, :, 7] = -9.0
+    kb, ksc = configs.quantize_int8_pages(x, P)
+    kp, vp, ks, vs = empty_fp8(3, Hkv, P, D)
+    bt = np.array([[2, 0]], dtype=np.int32)
+    for t in range(L):
+        paged.append_int8_dynamic(x[t:t + 1], x[t:t + 1], "f32", bt, np.array([t + 1], np.int32),
+                                  kp, vp, ks, vs, P)
+    kidx = layout.k_chunk_index(P, D, "i8")
+    for i, pg in enumerate((2, 0)):
+        n = min(P, L - i * P)
+        for g in range(Hkv):
+            assert np.array_equal(kp[pg, g, kidx[:n]], kb[i * P:i * P + n, g])
+        assert np.array_equal(ks[pg], ksc[i])
+
+
+def test_int8_no_clip_bound_and_doubling():
+    """Scale 1/2 from a first token of amax 63.5; a row reaching 127.5 * s keeps it
+    (its top element rounds to 128 and clamps to 127, half a step); above, the
+    scale grows; doubling the scale halves each code, ties to even."""
+    Hkv, D, P = 1, 64, 64
+    bt = np.array([[0]], dtype=np.int32)
+    for top, grows in ((63.75, False), (63.75 * (1 + 2 ** -20), True)):
+        kp, vp, ks, vs = empty_fp8(1, Hkv, P, D)
+        first = np.zeros((1, 1, D), F32)
+        first[0, 0, :] = (np.arange(D) - 31).astype(F32) / 2           # codes -62 .. 64 ... and 63.5 max
+        first[0, 0, 0] = F32(63.5)
+        paged.append_int8_dynamic(first, first, "f32", bt, np.array([1], np.int32), kp, vp, ks, vs, P)
+        assert ks[0, 0] == F32(0.5)
+        old = stored_row(kp, P, D, 0, 0, 0, "k").view(np.int8).astype(np.int64)
+        second = np.zeros((1, 1, D), F32)
+        second[0, 0, 3] = F32(top)
+        paged.append_int8_dynamic(second, second, "f32", bt, np.array([2], np.int32), kp, vp, ks, vs, P)
+        assert (ks[0, 0] != F32(0.5)) == grows
+        new = stored_row(kp, P, D, 0, 0, 0, "k").view(np.int8).astype(np.int64)
+        if not grows:
+            assert np.array_equal(new, old)
+            assert stored_row(kp, P, D, 0, 0, 1, "k").view(np.int8)[3] == 127
+    kp, vp, ks, vs = empty_fp8(1, Hkv, P, D)
+    first = np.zeros((1, 1, D), F32)
+    first[0, 0, :] = (np.arange(D) - 32).astype(F32) / 2
+    first[0, 0, 0] = F32(63.5)
+    paged.append_int8_dynamic(first, first, "f32", bt, np.array([1], np.int32), kp, vp, ks, vs, P)
+    old = stored_row(kp, P, D, 0, 0, 0, "k").view(np.int8).astype(np.int64)
+    second = np.zeros((1, 1, D), F32)
+    second[0, 0, 5] = F32(127.0)                                      # scale 1 = twice 1/2
+    paged.append_int8_dynamic(second, second, "f32", bt, np.array([2], np.int32), kp, vp, ks, vs, P)
+    assert ks[0, 0] == F32(1.0)
+    new = stored_row(kp, P, D, 0, 0, 0, "k").view(np.int8).astype(np.int64)
+    half = old / 2
+    want = np.where(half == np.floor(half), half, np.where(np.floor(half) % 2 == 0, np.floor(half),
+                                                             np.floor(half) + 1))
+    assert np.array_equal(new, want.astype(np.int64))

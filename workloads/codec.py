@@ -83,3 +83,13 @@ def e4m3_page_scales(x: np.ndarray) -> np.float32:
     if amax == 0:
         return np.float32(1.0)
     return np.float32(amax / np.float32(E4M3_MAX))
+
+
+def int8_encode(y: np.ndarray) -> np.ndarray:
+    """Encode float32 values as symmetric int8 bytes (two's complement):
+    nearest integer, half to even (numpy rint), clamped to [-127, 127]."""
+    q = np.rint(np.asarray(y, dtype=np.float32))
+    return np.clip(q, -127, 127).astype(np.int8).view(np.uint8)
+
+
+INT8_MAX = np.float32(127.0)

@@ -18,8 +18,9 @@ regenerated on its own:
 * new K/V of decode step s: ``[seed, 4, s]`` -> k_new then v_new, [B, Hkv, D] each
 
 All draws are float32 standard normals, scaled where a workload says so, then
-stored as fp32, bf16 (nearest-even) or fp8 e4m3 with one fp32 scale per
-(page, kv head) equal to amax/448 over the valid tokens of that page.
+stored as fp32, bf16 (nearest-even), fp8 e4m3 or symmetric int8 with one fp32
+scale per (page, kv head) equal to amax/448 (fp8) or amax/127 (int8) over the
+valid tokens of that page.
 """
 from __future__ import annotations
 
@@ -57,7 +58,7 @@ class Workload:
     P: int
     num_pages: int
     max_pages: int
-    kv_dtype: str                 # "f32" | "bf16" | "fp8"
+    kv_dtype: str                 # "f32" | "bf16" | "fp8" | "i8"
     q_dtype: str                  # "f32" | "bf16"
     out_dtype: str                # "f32" | "bf16"
     scale: np.float32
@@ -135,13 +136,32 @@ def quantize_fp8_pages(x: np.ndarray, P: int):
     return codec.e4m3_encode(y), scales
 
 
+def quantize_int8_pages(x: np.ndarray, P: int):
+    """x: [L, Hkv, D] fp32 -> (int8 bytes [L, Hkv, D], scales [npages, Hkv]).
+
+    Each (logical page, head) gets scale = fp32(amax/127) over its valid tokens
+    (1.0 if that block is all zero); bytes = rint(fp32(x / scale)) clamped to +-127.
+    """
+    L, Hkv, D = x.shape
+    npg = -(-L // P)
+    padded = np.zeros((npg * P, Hkv, D), dtype=np.float32)
+    padded[:L] = x
+    amax = np.abs(padded).reshape(npg, P, Hkv, D).max(axis=(1, 3))
+    scales = np.where(amax == 0, np.float32(1.0),
+                      (amax / codec.INT8_MAX).astype(np.float32)).astype(np.float32)
+    per_tok = np.repeat(scales, P, axis=0)[:L]
+    y = (x / per_tok[:, :, None]).astype(np.float32)
+    return codec.int8_encode(y), scales
+
+
 def seq_tokens(seed: int, b: int, L: int, Hkv: int, D: int, kv_dtype: str, P: int):
     """Logical K, V (stored format) and, for fp8, logical-page scales of sequence b."""
     kf = draw_seq_f32(seed, 2, b, L, Hkv, D)
     vf = draw_seq_f32(seed, 3, b, L, Hkv, D)
-    if kv_dtype == "fp8":
-        k, ks = quantize_fp8_pages(kf, P)
-        v, vs = quantize_fp8_pages(vf, P)
+    if kv_dtype in ("fp8", "i8"):
+        quant = quantize_fp8_pages if kv_dtype == "fp8" else quantize_int8_pages
+        k, ks = quant(kf, P)
+        v, vs = quant(vf, P)
         return k, v, ks, vs
     return _store(kf, kv_dtype), _store(vf, kv_dtype), None, None
 
@@ -229,7 +249,7 @@ def _assemble(name, seed, B, Hq, Hkv, D, P, num_pages, kv_dtype, q_dtype, out_dt
     kidx = layout.k_chunk_index(P, D, kv_dtype)
     vidx = layout.v_chunk_index(P, D, kv_dtype)
     ks = vs = None
-    if kv_dtype == "fp8":
+    if kv_dtype in ("fp8", "i8"):
         ks = np.full((num_pages, Hkv), np.nan, dtype=np.float32)
         vs = np.full((num_pages, Hkv), np.nan, dtype=np.float32)
     def fill(b):
@@ -238,7 +258,7 @@ def _assemble(name, seed, B, Hq, Hkv, D, P, num_pages, kv_dtype, q_dtype, out_dt
         k, v, kls, vls = seq_tokens(seed, b, n, Hkv, D, kv_dtype, P)
         layout.pack_sequence(kpool, pages, k, P, kidx, kv_dtype)
         layout.pack_sequence(vpool, pages, v, P, vidx, kv_dtype)
-        if kv_dtype == "fp8" and len(pages):
+        if kv_dtype in ("fp8", "i8") and len(pages):
             ks[pages] = kls
             vs[pages] = vls
 
@@ -355,7 +375,22 @@ def long_splitkv_bf16(seed: int = 4, B: int = 8, L: int = 131072) -> Workload:
                      np.float32(1.0 / math.sqrt(128)), 512, Ls, bt, q_mult=3.0)
 
 
-def fp8_kv(seed: int = 5, B: int = 128) -> Workload:
+def inflight_int8(seed: int = 3, B: int = 256, n_steps: int = 16, max_len: int = 32768) -> Workload:
+    """The in-flight batch with a symmetric int8 cache (per-(page, kv head) scale
+    amax/127) and bf16 new rows, quantised on write with dynamic page scales."""
+    return _inflight("inflight_int8", seed, B, n_steps, max_len, "i8")
+
+
+def int8_kv(seed: int = 5, B: int = 128) -> Workload:
+    """The fp8 workload's shape and draws (B 128, lengths uniform in [1024, 8192],
+    32/8 heads, D 128, pages of 64) with a symmetric int8 cache, scale amax/127
+    per (page, kv head); q bf16, out bf16."""
+    wl = fp8_kv(seed, B, kv_dtype="i8")
+    wl.name = "int8_kv"
+    return wl
+
+
+def fp8_kv(seed: int = 5, B: int = 128, kv_dtype: str = "fp8") -> Workload:
     """fp8 e4m3 cache: B 128, lengths uniform in [1024, 8192], 32/8 heads, D 128,
     pages of 64, per-(page, kv head) scale amax/448; q bf16, out bf16."""
     rng = np.random.default_rng(seed)
@@ -364,7 +399,7 @@ def fp8_kv(seed: int = 5, B: int = 128) -> Workload:
     need = int(pages_needed(L, P).sum())
     NP = int(math.ceil(1.25 * need))
     bt = place_permuted(rng, L, P, NP, max_pages=8192 // P)
-    return _assemble("fp8_kv", seed, B, 32, 8, 128, P, NP, "fp8", "bf16", "bf16",
+    return _assemble("fp8_kv", seed, B, 32, 8, 128, P, NP, kv_dtype, "bf16", "bf16",
                      np.float32(1.0 / math.sqrt(128)), 0, L, bt)
 
 
@@ -393,4 +428,6 @@ CONFIGS = {
     "long_splitkv_bf16": long_splitkv_bf16,
     "fp8_kv": fp8_kv,
     "inflight_fp8": inflight_fp8,
+    "int8_kv": int8_kv,
+    "inflight_int8": inflight_int8,
 }

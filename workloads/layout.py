@@ -22,10 +22,11 @@ from __future__ import annotations
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
-NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
-# Poison for slots that hold no token: a quiet NaN in each storage format.
-POISON = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "i8": 1}
+NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "i8": np.uint8}
+# Poison for slots that hold no token: a quiet NaN in each storage format;
+# int8 has no NaN, so its poison is -128, a code the quantiser never writes.
+POISON = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F), "i8": np.uint8(0x80)}
 
 
 def elems_per_16b(kv_dtype: str) -> int:
