@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "paged decode attention: KV HBM GB/s (fraction of peak) + seqs/s per layer"
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", "pkv_kernels.hip")
-WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "tiny_fp32"]
+WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "int8_kv",
+             "inflight_int8", "tiny_fp32"]
+SCALED = ("fp8", "i8")          # one-byte caches with per-(page, kv head) scales
 
 
 def kernel_hash() -> str:
@@ -54,21 +56,30 @@ def parse():
 
 
 def quantises_on_write(wl) -> bool:
-    """fp8 cache fed with wider new rows: the step appends through kv_append_fp8."""
-    return wl.kv_dtype == "fp8" and wl.new_dtype not in (None, "fp8")
+    """One-byte cache fed with wider new rows: the step appends through
+    kv_append_fp8 / kv_append_int8 (quantise on write)."""
+    return wl.kv_dtype in SCALED and wl.new_dtype not in (None, wl.kv_dtype)
+
+
+def decode_fn(pkv, kv_dtype):
+    return {"fp8": pkv.paged_attn_decode_fp8, "i8": pkv.paged_attn_decode_int8}[kv_dtype]
+
+
+def append_quant_fn(pkv, kv_dtype):
+    return {"fp8": pkv.kv_append_fp8, "i8": pkv.kv_append_int8}[kv_dtype]
 
 
 def alg_bytes(wl, seq_lens):
     """Bytes the method must move: (decode bytes, append bytes) for one step."""
     import numpy as np
-    eb = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8": 1, "i8": 1}[wl.kv_dtype]
     qb = 4 if wl.q_dtype == "f32" else 2
     ob = 4 if wl.out_dtype == "f32" else 2
     L = seq_lens.astype(np.int64)
     pages = (L + wl.P - 1) // wl.P
     kv = int(L.sum()) * wl.Hkv * wl.D * eb * 2
     dec = kv + wl.B * wl.Hq * wl.D * (qb + ob) + int(pages.sum()) * 4 + wl.B * 4
-    if wl.kv_dtype == "fp8":
+    if wl.kv_dtype in SCALED:
         dec += int(pages.sum()) * wl.Hkv * 4 * 2
     if quantises_on_write(wl):
         # read the bf16 rows, write fp8 rows, read and write both page scales
@@ -149,8 +160,8 @@ def cpu_baseline(wl, steps, seconds):
     while True:
         st = steps[reps % len(steps)]
         if quantises_on_write(wl):
-            paged.append_fp8_dynamic(st["k_new"], st["v_new"], wl.new_dtype, wl.block_tables, st["seq_lens"],
-                                     kp, vp, ks, vs, wl.P)
+            paged.append_dynamic(wl.kv_dtype, st["k_new"], st["v_new"], wl.new_dtype, wl.block_tables,
+                                 st["seq_lens"], kp, vp, ks, vs, wl.P)
         else:
             c_oracle.append(st["k_new"], st["v_new"], wl.kv_dtype, wl.block_tables, st["seq_lens"], kp, vp,
                             wl.P)
@@ -197,16 +208,17 @@ def diagnostics(pkv, wl, q, bt, kps, vps, kss, vss, dsteps, out, ws, step, i0, n
 
     def app(i):
         if quantises_on_write(wl):
-            pkv.kv_append_fp8(s0["kn"], s0["vn"], wl.new_dtype, bt, s0["sl"], kps[i % layers], vps[i % layers],
-                              kss[i % layers], vss[i % layers], wl.Hkv, wl.D, wl.P)
+            append_quant_fn(pkv, wl.kv_dtype)(s0["kn"], s0["vn"], wl.new_dtype, bt, s0["sl"], kps[i % layers],
+                                              vps[i % layers], kss[i % layers], vss[i % layers], wl.Hkv, wl.D,
+                                              wl.P)
         else:
             pkv.kv_append(s0["kn"], s0["vn"], wl.kv_dtype, bt, s0["sl"], kps[i % layers], vps[i % layers],
                           wl.Hkv, wl.D, wl.P)
 
     def dec(i):
-        if wl.kv_dtype == "fp8":
-            pkv.paged_attn_decode_fp8(q, wl.q_dtype, kps[i % layers], vps[i % layers], kss[i % layers],
-                                      vss[i % layers], bt, s0["sl"],
+        if wl.kv_dtype in SCALED:
+            decode_fn(pkv, wl.kv_dtype)(q, wl.q_dtype, kps[i % layers], vps[i % layers], kss[i % layers],
+                                        vss[i % layers], bt, s0["sl"],
                                       wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws,
                                       wl.partition_tokens)
         else:
@@ -257,7 +269,7 @@ def main():
     if wl.steps:
         steps = [{"seq_lens": s.seq_lens, "k_new": s.k_new, "v_new": s.v_new} for s in wl.steps]
     else:
-        eb_dt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[wl.kv_dtype]
+        eb_dt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "i8": np.uint8}[wl.kv_dtype]
         if wl.kv_dtype == "f32":
             kn = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
             vn = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
@@ -267,8 +279,10 @@ def main():
             vf = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
             if wl.kv_dtype == "bf16":
                 kn, vn = codec.f32_to_bf16_bits(kf), codec.f32_to_bf16_bits(vf)
-            else:                       # bytes at a typical quantised magnitude
+            elif wl.kv_dtype == "fp8":  # bytes at a typical quantised magnitude
                 kn, vn = codec.e4m3_encode(kf * 100), codec.e4m3_encode(vf * 100)
+            else:
+                kn, vn = codec.int8_encode(kf * 30), codec.int8_encode(vf * 30)
         steps = [{"seq_lens": wl.seq_lens.copy(), "k_new": kn.astype(eb_dt), "v_new": vn.astype(eb_dt)}]
 
     pool_bytes = wl.k_pool.nbytes + wl.v_pool.nbytes
@@ -295,9 +309,10 @@ def main():
         s = dsteps[i % len(dsteps)]
         kp, vp, ks, vs = kps[i % layers], vps[i % layers], kss[i % layers], vss[i % layers]
         if quant:
-            pkv.kv_append_fp8(s["kn"], s["vn"], wl.new_dtype, bt, s["sl"], kp, vp, ks, vs, wl.Hkv, wl.D, wl.P)
-            pkv.paged_attn_decode_fp8(q, wl.q_dtype, kp, vp, ks, vs, bt, s["sl"], wl.Hq, wl.Hkv, wl.D, wl.P,
-                                      wl.scale, out, wl.out_dtype, ws, wl.partition_tokens)
+            append_quant_fn(pkv, wl.kv_dtype)(s["kn"], s["vn"], wl.new_dtype, bt, s["sl"], kp, vp, ks, vs,
+                                              wl.Hkv, wl.D, wl.P)
+            decode_fn(pkv, wl.kv_dtype)(q, wl.q_dtype, kp, vp, ks, vs, bt, s["sl"], wl.Hq, wl.Hkv, wl.D, wl.P,
+                                        wl.scale, out, wl.out_dtype, ws, wl.partition_tokens)
         else:
             pkv.decode_step(q, wl.q_dtype, s["kn"], s["vn"], kp, vp, wl.kv_dtype, bt, s["sl"], wl.Hq,
                             wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws, k_scales=ks, v_scales=vs,
@@ -346,13 +361,14 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8e4m3 (kv) / bf16 (q, out)", "f32": "f32"}[wl.kv_dtype],
+        "dtype": {"bf16": "bf16", "fp8": "fp8e4m3 (kv) / bf16 (q, out)", "i8": "int8 (kv) / bf16 (q, out)",
+                  "f32": "f32"}[wl.kv_dtype],
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled pages)",
         "config": {"workload": args.workload, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "page_size": wl.P,
                    "mean_seq_len": float(np.mean(steps[0]["seq_lens"])),
                    "partition_tokens": wl.partition_tokens, "layers_rotated": layers,
-                   "step": ("kv_append_fp8 (quantise on write, dynamic page scales) then fp8 paged decode"
+                   "step": ("quantising append (dynamic page scales) then one-byte paged decode"
                             if quant else
                             "decode_step: kv_append fused into paged decode (split kernel + LSE merge kernel)")},
         "seqs_per_s_per_layer": round(wl.B / (ms_step * 1e-3), 1),
@@ -360,8 +376,8 @@ def main():
         "kv_bytes_per_step": int(kv_bytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("kv_append_fp8 + paged_attn_decode_fp8 (append_fp8_kernel + decode_split_kernel"
-                                " + decode_merge_kernel)" if quant else
+                     "kernel": ("quantising append + one-byte paged decode (append_quant_kernel + "
+                                "decode_split_kernel + decode_merge_kernel)" if quant else
                                 "decode_step launch (decode_split_kernel + decode_merge_kernel)"),
                      "call_ms_mean": round(dec_mean, 5), "alg_bytes_per_call": int(step_bytes)},
     }

@@ -41,21 +41,23 @@
  *                ceil(L_b / P) are never read (may be -1).
  *   seq_lens     int32 [B]; number of tokens of sequence b in the cache,
  *                INCLUDING the token appended this step.  0 is allowed.
- *   k_scales, v_scales  fp32 [NP][Hkv], fp8 cache only: stored value times
- *                scale is the real value, one scale per (page, kv head).
+ *   k_scales, v_scales  fp32 [NP][Hkv], fp8 and int8 caches only: stored
+ *                value times scale is the real value, one scale per
+ *                (page, kv head).  int8 elements are two's complement bytes
+ *                in [-127, 127].
  *   k_pool, v_pool      NP * Hkv chunks, one per (page, kv head), each holding
  *                P * D elements; chunk (pg, g) starts at element
  *                (pg * Hkv + g) * P * D.
  *
  * Layout inside one chunk.  Let E = 16 / (element bytes) (fp32 4, bf16 8,
- * fp8 16) and TB = 4 * E.  For token slot j in [0, P) and dimension d:
+ * fp8 and int8 16) and TB = 4 * E.  For token slot j in [0, P) and dimension d:
  *   K (j, d) at element ((d / E) * P + j) * E + d % E
  *   V (j, d) at element blk * TB * D + (c * D + d) * E + e, where
  *            blk = j / TB, r = j % TB, c = (r % 16) / 4, e = 4 * (r / 16) + r % 4
  * i.e. each 16-byte group holds E consecutive dimensions of one token for K,
  * and E tokens of one dimension for V, arranged so that a 64-lane wavefront
  * reading one 16-byte group per lane receives matrix-core operand fragments
- * directly.  P must be a multiple of TB (fp32: 16, bf16: 32, fp8: 64).
+ * directly.  P must be a multiple of TB (fp32: 16, bf16: 32, fp8 and int8: 64).
  * ---------------------------------------------------------------------------
  */
 #ifndef PKV_H
@@ -68,7 +70,7 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2, PKV_INT8 = 3 } pkv_dtype;
 
 /* Return codes.  0 is success; every failure is negative and leaves all device
  * memory untouched (arguments are checked before anything is launched). */
@@ -91,7 +93,7 @@ enum {
  * bit for bit for every kv head g.  Sequences with L_b <= 0 are skipped.
  *
  * kv_dtype: element type of k_new/v_new and of the pools (any pkv_dtype; fp8
- *   bytes are copied as given).
+ *   and int8 bytes are copied as given, already quantised with the page's scale).
  * Writes only the addressed slots of k_pool/v_pool.  Two sequences must not
  * address the same slot in one call (the writes would race).  A page id
  * outside [0, num_pages), or t / P >= max_pages_per_seq, skips that sequence.
@@ -137,6 +139,26 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype,
                       void* k_pool, void* v_pool, float* k_scales, float* v_scales,
                       int num_pages, int num_kv_heads, int head_dim, int page_size,
                       void* stream);
+
+/* kv_append_int8 - pkv_kv_append_fp8 for a symmetric int8 cache.
+ *
+ * The solosoft.dev page ("TensorRT-LLM：NVIDIA 的開源最佳化 LLM 推論函式庫")
+ * lists INT8 among the supported quantisation formats in its FAQ, and its
+ * performance and memory figures give INT8 half the memory of FP16 and a
+ * higher throughput; here INT8 is the cache format, with the same dynamic
+ * per-(page, kv head)
+ * scales as the fp8 append and QMAX = 127: the first token of a page sets
+ * s = a / 127 (1 if a == 0); a later row keeps the scale while a / s0 <= 127.5
+ * (its largest element rounds to 128 at most, clamped to 127: within half a
+ * step), else s = a / 127 and earlier slots are re-encoded; enc(y) = y rounded
+ * to the nearest integer (ties to even) and clamped to [-127, 127].
+ * Same arguments, contract and errors as pkv_kv_append_fp8. */
+int pkv_kv_append_int8(const void* k_new, const void* v_new, pkv_dtype new_dtype,
+                       const int32_t* block_tables, int max_pages_per_seq,
+                       const int32_t* seq_lens, int batch,
+                       void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                       int num_pages, int num_kv_heads, int head_dim, int page_size,
+                       void* stream);
 
 /* Bytes of scratch that pkv_paged_attn_decode / pkv_paged_attn_decode_fp8 need
  * for these sizes on the current HIP device (0 if the sizes are invalid).
@@ -197,10 +219,25 @@ int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype,
                               void* out, pkv_dtype out_dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_attn_decode_int8 - as pkv_paged_attn_decode_fp8 for a symmetric int8
+ * cache: bytes are two's complement integers, real value = byte * scale.
+ * Integers of at most 8 significant bits widen to bf16 exactly; scales are
+ * folded in as for fp8; accumulation is fp32.  q is BF16; out is BF16 or F32.
+ * Same sizes and errors as pkv_paged_attn_decode_fp8. */
+int pkv_paged_attn_decode_int8(const void* q, pkv_dtype q_dtype,
+                               const void* k_pool, const void* v_pool,
+                               const float* k_scales, const float* v_scales,
+                               const int32_t* block_tables, int max_pages_per_seq,
+                               const int32_t* seq_lens, int batch, int num_pages,
+                               int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                               float scale, int partition_tokens,
+                               void* out, pkv_dtype out_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* decode_step - one whole decode iteration of the cache for one layer: the
  * append of pkv_kv_append followed by the attention of pkv_paged_attn_decode
- * (or of pkv_paged_attn_decode_fp8 when kv_dtype is FP8_E4M3), with no launch
- * of its own for the append.
+ * (or of pkv_paged_attn_decode_fp8 / _int8 when kv_dtype is FP8_E4M3 / INT8),
+ * with no launch of its own for the append.
  *
  * The first page's "runtime execution model" has each iteration's attention
  * both update and read the cache pages.  Here the wavefront of the split
@@ -209,8 +246,8 @@ int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype,
  * slot's old contents, and the merge kernel, which runs after it on the
  * stream, stores them into the page slot.  Results equal pkv_kv_append then decode with the same
  * seq_lens (the pool bytes exactly; out up to the rounding order).
- * k_scales / v_scales: required for FP8_E4M3 (k_new / v_new are then bytes
- * already quantised with that page's scale), ignored otherwise.
+ * k_scales / v_scales: required for FP8_E4M3 and INT8 (k_new / v_new are then
+ * bytes already quantised with that page's scale), ignored otherwise.
  * Same sizes, dtypes, workspace and errors as the decode entry points, plus
  * PKV_E_NULL for a NULL k_new / v_new.  A sequence whose slot L_b - 1 lies on
  * a bad page id stores nothing and gets NaN rows. */

@@ -40,7 +40,9 @@ int check_align(std::initializer_list<const void*> ptrs) {
   return PKV_OK;
 }
 
-bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3; }
+bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3 || d == PKV_INT8; }
+// One-byte formats carry per-(page, kv head) scales.
+bool scaled_dtype(int d) { return d == PKV_FP8_E4M3 || d == PKV_INT8; }
 
 // Shared size checks for every entry point that reads the pools.
 int check_pool_shape(int kv_dtype, int max_pages, int batch, int num_pages, int num_kv_heads,
@@ -133,6 +135,28 @@ int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
   return PKV_OK;
 }
 
+int append_quant(int kv_dtype, const void* k_new, const void* v_new, pkv_dtype new_dtype,
+                 const int32_t* block_tables, int max_pages_per_seq, const int32_t* seq_lens, int batch,
+                 void* k_pool, void* v_pool, float* k_scales, float* v_scales, int num_pages, int num_kv_heads,
+                 int head_dim, int page_size, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && (!k_new || !v_new || !block_tables || !seq_lens || !k_pool || !v_pool || !k_scales ||
+                    !v_scales))
+    return fail(PKV_E_NULL, "a required pointer is NULL");
+  int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
+  if (rc) return rc;
+  if (new_dtype != PKV_BF16 && new_dtype != PKV_F32)
+    return fail(PKV_E_DTYPE, "new-row dtype %d unsupported (bf16 or f32)", new_dtype);
+  if (batch == 0) return PKV_OK;
+  if ((rc = check_align({k_new, v_new, k_pool, v_pool}))) return rc;
+  pkv::AppendQuantArgs a{k_new,  v_new,    kv_dtype, new_dtype == PKV_BF16, block_tables, seq_lens,
+                         k_pool, v_pool,   k_scales, v_scales,              batch,        max_pages_per_seq,
+                         num_pages, num_kv_heads, head_dim, page_size};
+  hipError_t e = pkv::launch_append_quant(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantising append launch");
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,23 +209,16 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype,
                       int max_pages_per_seq, const int32_t* seq_lens, int batch, void* k_pool, void* v_pool,
                       float* k_scales, float* v_scales, int num_pages, int num_kv_heads, int head_dim,
                       int page_size, void* stream) {
-  g_last_error.clear();
-  if (batch > 0 && (!k_new || !v_new || !block_tables || !seq_lens || !k_pool || !v_pool || !k_scales ||
-                    !v_scales))
-    return fail(PKV_E_NULL, "a required pointer is NULL");
-  int rc = check_pool_shape(PKV_FP8_E4M3, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim,
-                            page_size);
-  if (rc) return rc;
-  if (new_dtype != PKV_BF16 && new_dtype != PKV_F32)
-    return fail(PKV_E_DTYPE, "new-row dtype %d unsupported (bf16 or f32)", new_dtype);
-  if (batch == 0) return PKV_OK;
-  if ((rc = check_align({k_new, v_new, k_pool, v_pool}))) return rc;
-  pkv::AppendFp8Args a{k_new,    v_new,    new_dtype == PKV_BF16, block_tables, seq_lens,
-                       k_pool,   v_pool,   k_scales,              v_scales,     batch,
-                       max_pages_per_seq, num_pages, num_kv_heads, head_dim, page_size};
-  hipError_t e = pkv::launch_append_fp8(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "fp8 append launch");
-  return PKV_OK;
+  return append_quant(PKV_FP8_E4M3, k_new, v_new, new_dtype, block_tables, max_pages_per_seq, seq_lens, batch,
+                      k_pool, v_pool, k_scales, v_scales, num_pages, num_kv_heads, head_dim, page_size, stream);
+}
+
+int pkv_kv_append_int8(const void* k_new, const void* v_new, pkv_dtype new_dtype, const int32_t* block_tables,
+                       int max_pages_per_seq, const int32_t* seq_lens, int batch, void* k_pool, void* v_pool,
+                       float* k_scales, float* v_scales, int num_pages, int num_kv_heads, int head_dim,
+                       int page_size, void* stream) {
+  return append_quant(PKV_INT8, k_new, v_new, new_dtype, block_tables, max_pages_per_seq, seq_lens, batch,
+                      k_pool, v_pool, k_scales, v_scales, num_pages, num_kv_heads, head_dim, page_size, stream);
 }
 
 int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
@@ -211,8 +228,8 @@ int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype, const void* k_pool, 
                           int partition_tokens, void* out, pkv_dtype out_dtype, void* workspace,
                           size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (kv_dtype == PKV_FP8_E4M3)
-    return fail(PKV_E_DTYPE, "fp8 cache: use pkv_paged_attn_decode_fp8 (it carries the scales)");
+  if (scaled_dtype(kv_dtype))
+    return fail(PKV_E_DTYPE, "fp8 / int8 cache: use pkv_paged_attn_decode_fp8 / _int8 (they carry the scales)");
   return run_decode(q, q_dtype, k_pool, v_pool, kv_dtype, nullptr, nullptr, block_tables, max_pages_per_seq,
                     seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
                     partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
@@ -231,6 +248,19 @@ int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype, const void* k_po
                     page_size, scale, partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
 }
 
+int pkv_paged_attn_decode_int8(const void* q, pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
+                               const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                               int max_pages_per_seq, const int32_t* seq_lens, int batch, int num_pages,
+                               int num_q_heads, int num_kv_heads, int head_dim, int page_size, float scale,
+                               int partition_tokens, void* out, pkv_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "int8 scales are NULL");
+  return run_decode(q, q_dtype, k_pool, v_pool, PKV_INT8, k_scales, v_scales, block_tables, max_pages_per_seq,
+                    seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
+                    partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
 int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_new, void* k_pool,
                     void* v_pool, pkv_dtype kv_dtype, const float* k_scales, const float* v_scales,
                     const int32_t* block_tables, int max_pages_per_seq, const int32_t* seq_lens, int batch,
@@ -243,8 +273,8 @@ int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const v
     const int rc = check_align({k_new, v_new});
     if (rc) return rc;
   }
-  if (kv_dtype == PKV_FP8_E4M3) {
-    if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 scales are NULL");
+  if (scaled_dtype(kv_dtype)) {
+    if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 / int8 scales are NULL");
   } else {
     k_scales = v_scales = nullptr;
   }

@@ -8,7 +8,7 @@
 
 namespace pkv {
 
-enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_INT8 = 3 };
 
 // Tokens per 16-byte V group block (and per decode step): 4 * (16 / element bytes).
 inline int v_block_tokens(int kvt) { return kvt == KV_F32 ? 16 : kvt == KV_BF16 ? 32 : 64; }
@@ -24,9 +24,10 @@ inline size_t partials_bytes(int cus, int G, int D) {
   return (b + 255) & ~(size_t)255;
 }
 
-struct AppendFp8Args {
+struct AppendQuantArgs {
   const void* k_new;
   const void* v_new;
+  int kvt;                  // KV_FP8 or KV_INT8: the one-byte format written
   bool new_bf16;            // rows are bf16 (else fp32)
   const int32_t* block_tables;
   const int32_t* seq_lens;
@@ -78,7 +79,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
-hipError_t launch_append_fp8(const AppendFp8Args& a, hipStream_t s);
+// Quantising append into a one-byte cache (fp8 or int8) with dynamic page scales.
+hipError_t launch_append_quant(const AppendQuantArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 // Launches the decode kernel and the log-sum-exp merge kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

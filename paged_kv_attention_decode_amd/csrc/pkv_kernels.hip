@@ -52,6 +52,7 @@ template <int KVT> struct Kv;
 template <> struct Kv<KV_F32> { static constexpr int EB = 4; typedef uint32_t elem_t; };
 template <> struct Kv<KV_BF16> { static constexpr int EB = 2; typedef uint16_t elem_t; };
 template <> struct Kv<KV_FP8> { static constexpr int EB = 1; typedef uint8_t elem_t; };
+template <> struct Kv<KV_INT8> { static constexpr int EB = 1; typedef uint8_t elem_t; };
 
 // ---------------------------------------------------------------------------
 // Chunk addressing shared by every kernel.  A (page, kv head) chunk holds P
@@ -132,8 +133,19 @@ __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
   r.y = pack_hi16(b.x, b.y);
   return r;
 }
-__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  const u32x2_t a = fp8x4_to_bf16x4(w0), b = fp8x4_to_bf16x4(w1);
+// Four int8 bytes -> four bf16 (exact: |v| <= 128 has at most 8 significant
+// bits).  Each signed-byte conversion is one instruction (a sign-extending byte
+// select on the int -> float convert).
+__device__ __forceinline__ u32x2_t i8x4_to_bf16x4(uint32_t w) {
+  const float a = (float)(int8_t)w, b = (float)(int8_t)(w >> 8);
+  const float c = (float)(int8_t)(w >> 16), d = (float)((int32_t)w >> 24);
+  return u32x2_t{pack_hi16(a, b), pack_hi16(c, d)};
+}
+// Eight one-byte cache elements (fp8 e4m3 or int8) -> a bf16x8 MFMA operand.
+template <int KVT>
+__device__ __forceinline__ u32x4_t byte8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const u32x2_t a = KVT == KV_FP8 ? fp8x4_to_bf16x4(w0) : i8x4_to_bf16x4(w0);
+  const u32x2_t b = KVT == KV_FP8 ? fp8x4_to_bf16x4(w1) : i8x4_to_bf16x4(w1);
   return u32x4_t{a.x, a.y, b.x, b.y};
 }
 
@@ -276,7 +288,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   constexpr int NSUB = TS / 16;     // 16-token QK^T tiles per step
   constexpr int NKK = D / (4 * E);  // K groups per lane per 16-token tile
   constexpr int NDT = D / 16;       // 16-dim PV tiles
-  constexpr int NQ = KVT == KV_FP8 ? 2 * NKK : NKK;
+  constexpr bool BYTE = EB == 1;       // fp8 or int8 cache: scaled, widened to bf16
+  constexpr int NQ = BYTE ? 2 * NKK : NKK;
 
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, c4 = lane >> 4;
@@ -468,7 +481,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     bool bad = (unsigned)page >= (unsigned)NP;
     int pg_ld = bad ? 0 : page;
     float ksc = 1.f, vsc = 1.f;
-    if constexpr (KVT == KV_FP8) {
+    if constexpr (BYTE) {
       ksc = kscales[(size_t)pg_ld * Hkv + g];
       vsc = vscales[(size_t)pg_ld * Hkv + g];
     }
@@ -553,8 +566,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
           } else if constexpr (KVT == KV_BF16) {
             acc = mfma_bf16(kr[sub][kk], qop(kk), acc);
           } else {
-            acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][0], kr[sub][kk][1]), qop(2 * kk), acc);
-            acc = mfma_bf16(fp8x8_to_bf16x8(kr[sub][kk][2], kr[sub][kk][3]), qop(2 * kk + 1), acc);
+            acc = mfma_bf16(byte8_to_bf16x8<KVT>(kr[sub][kk][0], kr[sub][kk][1]), qop(2 * kk), acc);
+            acc = mfma_bf16(byte8_to_bf16x8<KVT>(kr[sub][kk][2], kr[sub][kk][3]), qop(2 * kk + 1), acc);
           }
         }
 #pragma unroll
@@ -562,7 +575,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       }
       if constexpr (!LAST) {
         load_k(pg_ld_n, j_n);
-        if constexpr (KVT == KV_FP8) {
+        if constexpr (BYTE) {
           ksc = kscales[(size_t)pg_ld_n * Hkv + g];
           vsc = vscales[(size_t)pg_ld_n * Hkv + g];
         }
@@ -639,8 +652,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         split_probs(p[2], p[3], vmul, ph[1], pl[1]);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const u32x4_t a0 = fp8x8_to_bf16x8(vr[dt][0], vr[dt][1]);
-          const u32x4_t a1 = fp8x8_to_bf16x8(vr[dt][2], vr[dt][3]);
+          const u32x4_t a0 = byte8_to_bf16x8<KVT>(vr[dt][0], vr[dt][1]);
+          const u32x4_t a1 = byte8_to_bf16x8<KVT>(vr[dt][2], vr[dt][3]);
           O[dt] = mfma_bf16(a0, ph[0], O[dt]);
           O[dt] = mfma_bf16(a0, pl[0], O[dt]);
           O[dt] = mfma_bf16(a1, ph[1], O[dt]);
@@ -792,13 +805,15 @@ __global__ __launch_bounds__(256) void append_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// fp8 append with dynamic page scales (quantise on write).
+// One-byte appends (fp8 e4m3 or int8) with dynamic page scales (quantise on
+// write).  QMAX = 448 (fp8) or 127 (int8); NOCLIP = 464 or 127.5, the largest
+// |x| / scale whose encoding is the largest code without clipping.
 //
-// One wave per (sequence, kv head); K, then V, each with its own scale:
+// One wave per (sequence, kv head); K and V each with their own scale:
 // a = max |x| of the new row (widened to fp32);
-//   slot j == 0 (first token of the page): s = a / 448 (1 if a == 0);
-//   else, s0 = the page's scale: s = s0 if a / s0 <= 464 (no clipping),
-//   otherwise s = a / 448 and every earlier slot is re-encoded,
+//   slot j == 0 (first token of the page): s = a / QMAX (1 if a == 0);
+//   else, s0 = the page's scale: s = s0 if a / s0 <= NOCLIP,
+//   otherwise s = a / QMAX and every earlier slot is re-encoded,
 //   enc((dec(byte) * s0) / s);
 // the new row is stored as enc(x / s) and the page scale becomes s.
 // Every division and product is one correctly rounded fp32 operation.
@@ -818,30 +833,57 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | (uint32_t)(8 * (e + 6) + k);
 }
 
-// Four e4m3 bytes of a word re-encoded under a new scale: enc((dec(byte) * s0) / s).
+// fp32 -> symmetric int8 byte: nearest integer, ties to even, clamped to +-127.
+__device__ __forceinline__ uint32_t int8_encode(float x) {
+  const float r = fminf(fmaxf(rintf(x), -127.f), 127.f);
+  return (uint32_t)(int)r & 0xFFu;
+}
+
+template <int KVT> struct ByteFmt;
+template <> struct ByteFmt<KV_FP8> {
+  static constexpr float QMAX = 448.f, NOCLIP = 464.f;
+  __device__ static uint32_t enc(float y) { return e4m3_encode(y); }
+  __device__ static void dec4(uint32_t w, float (&v)[4]) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+  }
+};
+template <> struct ByteFmt<KV_INT8> {
+  static constexpr float QMAX = 127.f, NOCLIP = 127.5f;
+  __device__ static uint32_t enc(float y) { return int8_encode(y); }
+  __device__ static void dec4(uint32_t w, float (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(uint8_t)(w >> (8 * i));
+  }
+};
+
+// Four bytes of a word re-encoded under a new scale: enc((dec(byte) * s0) / s).
+template <int KVT>
 __device__ __forceinline__ uint32_t requant4(uint32_t w, float s0, float s) {
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  const float v[4] = {a.x, a.y, b.x, b.y};
+  float v[4];
+  ByteFmt<KVT>::dec4(w, v);
   uint32_t r = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float real = v[i] * s0;        // rounded product, then a rounded quotient
-    r |= e4m3_encode(real / s) << (8 * i);
+    r |= ByteFmt<KVT>::enc(real / s) << (8 * i);
   }
   return r;
 }
 
 // Scale decision for one row: returns the new scale; sets requant when the
 // page's earlier slots must be re-encoded.  A row fits the current scale while
-// its largest element rounds to +-448 without clipping: |x| / s0 <= 464, the
-// midpoint to the next binade step, which rounds down to 448.
-__device__ __forceinline__ float fp8_page_scale(float a, int j, float s0, bool& requant) {
+// its largest element encodes to the largest code without clipping:
+// |x| / s0 <= NOCLIP (fp8: 464, the midpoint above 448, rounds down to 448;
+// int8: 127.5 rounds to 128 and clamps to 127, still within half a step).
+template <int KVT>
+__device__ __forceinline__ float page_scale(float a, int j, float s0, bool& requant) {
   requant = false;
-  if (j == 0) return a > 0.f ? a / 448.f : 1.f;
-  if (a / s0 <= 464.f) return s0;       // the row's largest element rounds to +-448 at most
+  if (j == 0) return a > 0.f ? a / ByteFmt<KVT>::QMAX : 1.f;
+  if (a / s0 <= ByteFmt<KVT>::NOCLIP) return s0;
   requant = true;
-  return a / 448.f;
+  return a / ByteFmt<KVT>::QMAX;
 }
 
 // A re-encode maps each old byte through enc((dec(byte) * s0) / s), a function
@@ -926,8 +968,8 @@ __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* l
   }
 }
 
-template <bool IN_BF16, int D>
-__global__ __launch_bounds__(256) void append_fp8_kernel(
+template <int KVT, bool IN_BF16, int D>
+__global__ __launch_bounds__(256) void append_quant_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
     uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool,
@@ -980,13 +1022,13 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(
   sk0 = fbits(uniform((int)ubits(sk0)));
   sv0 = fbits(uniform((int)ubits(sv0)));
   bool rk, rv;
-  const float sk = fp8_page_scale(ak, j, sk0, rk);
-  const float sv = fp8_page_scale(av, j, sv0, rv);
+  const float sk = page_scale<KVT>(ak, j, sk0, rk);
+  const float sv = page_scale<KVT>(av, j, sv0, rv);
   uint32_t nbk[NPL], nbv[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
-    nbk[i] = e4m3_encode(xk[i] / sk);
-    nbv[i] = e4m3_encode(xv[i] / sv);
+    nbk[i] = ByteFmt<KVT>::enc(xk[i] / sk);
+    nbv[i] = ByteFmt<KVT>::enc(xv[i] / sv);
   }
   uint8_t* kp = kpool + ch;
   uint8_t* vp = vpool + ch;
@@ -994,8 +1036,8 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(
   const uint8_t* lutv = reinterpret_cast<const uint8_t*>(s_lut[wv][1]);
   if (rk || rv) {
     const uint32_t codes = (uint32_t)(4 * lane) * 0x01010101u + 0x03020100u;   // 4 codes per lane
-    if (rk) s_lut[wv][0][lane] = requant4(codes, sk0, sk);
-    if (rv) s_lut[wv][1][lane] = requant4(codes, sv0, sv);
+    if (rk) s_lut[wv][0][lane] = requant4<KVT>(codes, sk0, sk);
+    if (rv) s_lut[wv][1][lane] = requant4<KVT>(codes, sv0, sv);
     __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
   }
   if (rk) requant_k<D>(kp, j, P, lutk, lane);
@@ -1083,6 +1125,7 @@ decode_fn_t pick_decode(int kvt, int D, bool ob) {
   PKV_PICK(KV_F32)
   PKV_PICK(KV_BF16)
   PKV_PICK(KV_FP8)
+  PKV_PICK(KV_INT8)
 #undef PKV_PICK
   return nullptr;
 }
@@ -1133,25 +1176,32 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
                      a.head_dim, a.page_size)
   if (a.kvt == KV_F32) PKV_APPEND(KV_F32);
   else if (a.kvt == KV_BF16) PKV_APPEND(KV_BF16);
-  else PKV_APPEND(KV_FP8);
+  else PKV_APPEND(KV_FP8);          // any one-byte format (fp8, int8): a byte copy
 #undef PKV_APPEND
   return hipGetLastError();
 }
 
-hipError_t launch_append_fp8(const AppendFp8Args& a, hipStream_t s) {
+hipError_t launch_append_quant(const AppendQuantArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
   dim3 grid((unsigned)(((int64_t)a.batch * a.num_kv_heads + 3) / 4)), block(256);
-#define PKV_APPEND_FP8(BF, DD)                                                                     \
-  hipLaunchKernelGGL((append_fp8_kernel<BF, DD>), grid, block, 0, s, a.k_new, a.v_new, a.block_tables, \
-                     a.seq_lens, static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool),   \
-                     a.k_scales, a.v_scales, a.batch, a.max_pages, a.num_pages, a.num_kv_heads,      \
-                     a.page_size)
-  if (a.new_bf16) {
-    if (a.head_dim == 64) PKV_APPEND_FP8(true, 64); else PKV_APPEND_FP8(true, 128);
-  } else {
-    if (a.head_dim == 64) PKV_APPEND_FP8(false, 64); else PKV_APPEND_FP8(false, 128);
+#define PKV_APPEND_Q(K, BF, DD)                                                                     \
+  hipLaunchKernelGGL((append_quant_kernel<K, BF, DD>), grid, block, 0, s, a.k_new, a.v_new,          \
+                     a.block_tables, a.seq_lens, static_cast<uint8_t*>(a.k_pool),                    \
+                     static_cast<uint8_t*>(a.v_pool), a.k_scales, a.v_scales, a.batch, a.max_pages,  \
+                     a.num_pages, a.num_kv_heads, a.page_size)
+#define PKV_APPEND_QK(K)                                                                            \
+  if (a.new_bf16) {                                                                                 \
+    if (a.head_dim == 64) PKV_APPEND_Q(K, true, 64); else PKV_APPEND_Q(K, true, 128);               \
+  } else {                                                                                          \
+    if (a.head_dim == 64) PKV_APPEND_Q(K, false, 64); else PKV_APPEND_Q(K, false, 128);             \
   }
-#undef PKV_APPEND_FP8
+  if (a.kvt == KV_INT8) {
+    PKV_APPEND_QK(KV_INT8)
+  } else {
+    PKV_APPEND_QK(KV_FP8)
+  }
+#undef PKV_APPEND_QK
+#undef PKV_APPEND_Q
   return hipGetLastError();
 }
 
@@ -1164,7 +1214,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
                      a.head_dim, a.page_size)
   if (a.kvt == KV_F32) PKV_GATHER(KV_F32);
   else if (a.kvt == KV_BF16) PKV_GATHER(KV_BF16);
-  else PKV_GATHER(KV_FP8);
+  else PKV_GATHER(KV_FP8);          // any one-byte format
 #undef PKV_GATHER
   return hipGetLastError();
 }

@@ -52,10 +52,32 @@ def test_fp8_codes_exhaustive_through_decode():
     assert np.array_equal(got[ok], ref[ok])
 
 
+def test_int8_codes_exhaustive_through_decode():
+    """Single-token sequences return their value row: all 256 int8 codes, scale 1
+    (-128 included, though the quantiser never writes it)."""
+    D, P = 128, 64
+    codes = np.arange(256, dtype=np.uint8).reshape(2, 1, 1, D)
+    kp = layout.empty_pool(4, 1, P, D, "i8")
+    vp = layout.empty_pool(4, 1, P, D, "i8")
+    bt = np.array([[1], [3]], np.int32)
+    for b in range(2):
+        layout.pack_sequence(kp, bt[b], np.zeros((1, 1, D), np.uint8), P, layout.k_chunk_index(P, D, "i8"), "i8")
+        layout.pack_sequence(vp, bt[b], codes[b, :1], P, layout.v_chunk_index(P, D, "i8"), "i8")
+    ones = np.ones((4, 1), np.float32)
+    q = codec.f32_to_bf16_bits(np.ones((2, 1, D), np.float32))
+    out = torch.empty((2, 1, D), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(pkv.decode_workspace_bytes(2, 1, 1, D), dtype=torch.uint8, device="cuda")
+    pkv.paged_attn_decode_int8(dev_tensor(q), "bf16", dev_tensor(kp), dev_tensor(vp), dev_tensor(ones),
+                               dev_tensor(ones), dev_tensor(bt), dev_tensor(np.array([1, 1], np.int32)),
+                               1, 1, D, P, 0.1, out, "f32", ws)
+    got = out.cpu().numpy().astype(np.float64).reshape(256)
+    assert np.array_equal(got, np.arange(256, dtype=np.uint8).view(np.int8).astype(np.float64))
+
+
 # ------------------------------------------------------------- append/gather ----
 
 APPEND_CASES = [("f32", 16, 64), ("bf16", 32, 128), ("bf16", 64, 128), ("bf16", 128, 64),
-                ("fp8", 64, 128), ("fp8", 128, 64)]
+                ("fp8", 64, 128), ("fp8", 128, 64), ("i8", 64, 128)]
 
 
 @pytest.mark.parametrize("kv_dtype,P,D", APPEND_CASES)
@@ -130,6 +152,9 @@ EDGE = [
     dict(seed=53, lens=[1, 2, 3, 4, 5] * 400, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16"),
     dict(seed=54, lens=[100, 4097], Hq=12, Hkv=4, D=128, P=64, kv_dtype="fp8", partition_tokens=128),
     dict(seed=57, lens=[1, 2, 3, 4, 5] * 400, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16", out_dtype="f32"),
+    dict(seed=58, lens=[1, 63, 64, 65, 1000], Hq=32, Hkv=8, D=128, P=64, kv_dtype="i8"),
+    dict(seed=59, lens=[64, 200, 1300], Hq=16, Hkv=4, D=64, P=128, kv_dtype="i8", out_dtype="f32"),
+    dict(seed=60, lens=[0, 100, 4097], Hq=12, Hkv=4, D=128, P=64, kv_dtype="i8", partition_tokens=128),
 ]
 
 
@@ -249,6 +274,7 @@ STEP_CASES = [
     dict(seed=73, lens=[1, 63, 64, 65, 129, 700], Hq=32, Hkv=8, D=128, P=64, kv_dtype="fp8"),
     dict(seed=74, lens=[0, 128, 129, 5000], Hq=64, Hkv=8, D=128, P=128, kv_dtype="bf16", partition_tokens=512),
     dict(seed=75, lens=[1, 2, 3, 4, 5] * 100, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16", out_dtype="f32"),
+    dict(seed=77, lens=[1, 63, 64, 65, 129, 700], Hq=32, Hkv=8, D=128, P=64, kv_dtype="i8"),
 ]
 
 
@@ -313,6 +339,10 @@ def test_config_llama3_8b_bf16():
 
 def test_config_fp8_kv():
     _decode_vs_oracle(configs.fp8_kv(), "fp8_kv")
+
+
+def test_config_int8_kv():
+    _decode_vs_oracle(configs.int8_kv(), "int8_kv")
 
 
 def test_config_inflight_16_steps():

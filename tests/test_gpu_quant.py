@@ -1,7 +1,8 @@
-"""GPU parity of the fp8 append with dynamic page scales (pkv_kv_append_fp8).
+"""GPU parity of the one-byte appends with dynamic page scales
+(pkv_kv_append_fp8, pkv_kv_append_int8).
 
 Every case runs the HIP kernel through the C ABI and the oracle
-(oracle.paged.append_fp8_dynamic) on the same inputs, step after step, and
+(oracle.paged.append_dynamic) on the same inputs, step after step, and
 requires the pools and the scales to be equal bit for bit after every step;
 decode over the resulting cache is then checked against the oracle's decode
 within the fp8 tolerance.
@@ -18,6 +19,11 @@ from tests._helpers import DeviceWorkload, check_close, dev_tensor, gpu_out, hos
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
+FMTS = ["fp8", "i8"]
+
+
+def gpu_append(fmt, *args):
+    (pkv.kv_append_fp8 if fmt == "fp8" else pkv.kv_append_int8)(*args)
 
 
 def _rows(rng, B, Hkv, D, new_dtype):
@@ -48,8 +54,9 @@ CASES = [  # (D, P, new_dtype, steps)
 ]
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("D,P,new_dtype,steps", CASES, ids=lambda v: str(v))
-def test_append_fp8_bit_exact_every_step(D, P, new_dtype, steps):
+def test_append_bit_exact_every_step(fmt, D, P, new_dtype, steps):
     rng = np.random.default_rng(100 + D + P)
     B, Hkv, MP = 7, 2, 2
     NP = B * MP + 3
@@ -69,14 +76,15 @@ def test_append_fp8_bit_exact_every_step(D, P, new_dtype, steps):
         if s % 17 == 5:
             lens[4] = MP * P + 1         # a call past the end of the table: skipped
         x, y = _rows(rng, B, Hkv, D, new_dtype), _rows(rng, B, Hkv, D, new_dtype)
-        pkv.kv_append_fp8(dev_tensor(x), dev_tensor(y), new_dtype, bt_d, dev_tensor(lens), kp_d, vp_d,
-                          ks_d, vs_d, Hkv, D, P)
-        paged.append_fp8_dynamic(x, y, new_dtype, bt, lens, kp, vp, ks, vs, P)
+        gpu_append(fmt, dev_tensor(x), dev_tensor(y), new_dtype, bt_d, dev_tensor(lens), kp_d, vp_d,
+                   ks_d, vs_d, Hkv, D, P)
+        paged.append_dynamic(fmt, x, y, new_dtype, bt, lens, kp, vp, ks, vs, P)
         torch.cuda.synchronize()
         _compare(kp_d, vp_d, ks_d, vs_d, kp, vp, ks, vs, f"step {s}")
 
 
-def test_append_fp8_grows_at_every_slot():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_append_grows_at_every_slot(fmt):
     """One sequence, each new token larger than the last: the scale grows on every
     append, so every slot position re-encodes all earlier ones."""
     rng = np.random.default_rng(7)
@@ -92,14 +100,15 @@ def test_append_fp8_grows_at_every_slot():
         x[0, 0, t % D] = 10 * 1.05 ** t                    # a new maximum every time
         y = (-x).astype(F32)
         lens = np.array([t + 1], np.int32)
-        pkv.kv_append_fp8(dev_tensor(x), dev_tensor(y), "f32", dev_tensor(bt), dev_tensor(lens), kp_d, vp_d,
-                          ks_d, vs_d, Hkv, D, P)
-        paged.append_fp8_dynamic(x, y, "f32", bt, lens, kp, vp, ks, vs, P)
+        gpu_append(fmt, dev_tensor(x), dev_tensor(y), "f32", dev_tensor(bt), dev_tensor(lens), kp_d, vp_d,
+                   ks_d, vs_d, Hkv, D, P)
+        paged.append_dynamic(fmt, x, y, "f32", bt, lens, kp, vp, ks, vs, P)
     torch.cuda.synchronize()
     _compare(kp_d, vp_d, ks_d, vs_d, kp, vp, ks, vs, "growing")
 
 
-def test_append_fp8_matches_one_shot_generator_pages():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_append_matches_one_shot_generator_pages(fmt):
     """Token-by-token GPU appends with the page amax on each page's first token
     reproduce the generator's one-shot per-page quantisation."""
     rng = np.random.default_rng(8)
@@ -110,8 +119,9 @@ def test_append_fp8_matches_one_shot_generator_pages():
     for p0 in range(0, L, P):
         xk[p0, :, 3] = 12.0
         xv[p0, :, 9] = -11.0
-    kb, ksc = configs.quantize_fp8_pages(xk, P)
-    vb, vsc = configs.quantize_fp8_pages(xv, P)
+    quant = configs.quantize_fp8_pages if fmt == "fp8" else configs.quantize_int8_pages
+    kb, ksc = quant(xk, P)
+    vb, vsc = quant(xv, P)
     pages = np.array([4, 0, 2], np.int32)
     NP = 5
     kp_d = dev_tensor(np.full((NP, Hkv, P * D), 0x7F, np.uint8))
@@ -120,10 +130,10 @@ def test_append_fp8_matches_one_shot_generator_pages():
     vs_d = dev_tensor(np.full((NP, Hkv), np.nan, F32))
     bt_d = dev_tensor(pages.reshape(1, -1))
     for t in range(L):
-        pkv.kv_append_fp8(dev_tensor(xk[t:t + 1]), dev_tensor(xv[t:t + 1]), "f32", bt_d,
-                          dev_tensor(np.array([t + 1], np.int32)), kp_d, vp_d, ks_d, vs_d, Hkv, D, P)
+        gpu_append(fmt, dev_tensor(xk[t:t + 1]), dev_tensor(xv[t:t + 1]), "f32", bt_d,
+                   dev_tensor(np.array([t + 1], np.int32)), kp_d, vp_d, ks_d, vs_d, Hkv, D, P)
     torch.cuda.synchronize()
-    kidx, vidx = layout.k_chunk_index(P, D, "fp8"), layout.v_chunk_index(P, D, "fp8")
+    kidx, vidx = layout.k_chunk_index(P, D, fmt), layout.v_chunk_index(P, D, fmt)
     kp = kp_d.cpu().numpy()
     vp = vp_d.cpu().numpy()
     for i, pg in enumerate(pages):
@@ -135,7 +145,7 @@ def test_append_fp8_matches_one_shot_generator_pages():
     assert np.array_equal(vs_d.cpu().numpy()[pages], vsc)
 
 
-def test_append_fp8_errors():
+def test_append_quant_errors():
     x = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device="cuda")
     bt = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
     sl = torch.ones(2, dtype=torch.int32, device="cuda")
@@ -147,19 +157,23 @@ def test_append_fp8_errors():
     with pytest.raises(pkv.PkvError) as e:
         pkv.kv_append_fp8(x, x, "bf16", bt, sl, pool, pool.clone(), sc, sc.clone(), 2, 128, 32)
     assert e.value.code == -2
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.kv_append_int8(x, x, "i8", bt, sl, pool, pool.clone(), sc, sc.clone(), 2, 128, 64)
+    assert e.value.code == -3
 
 
-def _inflight_fp8_run(B, n_steps, max_len, decode_every, pools_every=True):
-    wl = configs.inflight_fp8(B=B, n_steps=n_steps, max_len=max_len)
+def _inflight_quant_run(fmt, B, n_steps, max_len, decode_every, pools_every=True):
+    gen = configs.inflight_fp8 if fmt == "fp8" else configs.inflight_int8
+    wl = gen(B=B, n_steps=n_steps, max_len=max_len)
     dw = DeviceWorkload(wl)
     kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
     ks, vs = wl.k_scales.copy(), wl.v_scales.copy()
     for s, st in enumerate(wl.steps):
         sl = dev_tensor(st.seq_lens)
-        pkv.kv_append_fp8(dev_tensor(st.k_new), dev_tensor(st.v_new), "bf16", dw.bt, sl, dw.k_pool,
-                          dw.v_pool, dw.ks, dw.vs, wl.Hkv, wl.D, wl.P)
-        paged.append_fp8_dynamic(st.k_new, st.v_new, "bf16", wl.block_tables, st.seq_lens, kp, vp, ks, vs,
-                                 wl.P)
+        gpu_append(fmt, dev_tensor(st.k_new), dev_tensor(st.v_new), "bf16", dw.bt, sl, dw.k_pool,
+                   dw.v_pool, dw.ks, dw.vs, wl.Hkv, wl.D, wl.P)
+        paged.append_dynamic(fmt, st.k_new, st.v_new, "bf16", wl.block_tables, st.seq_lens, kp, vp, ks, vs,
+                             wl.P)
         torch.cuda.synchronize()
         if pools_every or s == n_steps - 1:
             _compare(dw.k_pool, dw.v_pool, dw.ks, dw.vs, kp, vp, ks, vs, f"step {s}")
@@ -169,14 +183,16 @@ def _inflight_fp8_run(B, n_steps, max_len, decode_every, pools_every=True):
         if decode_every or s == n_steps - 1:
             out = gpu_out(dw.decode(seq_lens=sl))
             wl_now = configs.Workload(**{**wl.__dict__, "k_scales": ks, "v_scales": vs})
-            check_close(out, oracle_decode(wl_now, kp, vp, st.seq_lens), "fp8", f"decode after step {s}")
+            check_close(out, oracle_decode(wl_now, kp, vp, st.seq_lens), fmt, f"decode after step {s}")
 
 
-def test_config_inflight_fp8_reduced_every_step():
-    _inflight_fp8_run(B=16, n_steps=16, max_len=4000, decode_every=True)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_config_inflight_quant_reduced_every_step(fmt):
+    _inflight_quant_run(fmt, B=16, n_steps=16, max_len=4000, decode_every=True)
 
 
-def test_config_inflight_fp8_full():
-    """The in-flight batch with an fp8 cache: 16 quantise-on-write steps; scales
-    bit-exact after every step, pools after the last one, then decode."""
-    _inflight_fp8_run(B=256, n_steps=16, max_len=32768, decode_every=False, pools_every=False)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_config_inflight_quant_full(fmt):
+    """The in-flight batch with a one-byte cache: 16 quantise-on-write steps;
+    scales bit-exact after every step, pools after the last one, then decode."""
+    _inflight_quant_run(fmt, B=256, n_steps=16, max_len=32768, decode_every=False, pools_every=False)
