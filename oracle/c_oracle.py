@@ -15,7 +15,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "pkv_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
-DT = {"f32": 0, "bf16": 1, "fp8": 2, "i8": 3}
+DT = {"f32": 0, "bf16": 1, "fp8": 2, "i8": 3, "i4": 4}
 
 _lib = None
 
@@ -69,6 +69,8 @@ def decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens, Hq, P, 
     bt, sl = _c(block_tables, np.int32), _c(seq_lens, np.int32)
     ks, vs = _c(k_scales, np.float32), _c(v_scales, np.float32)
     NP, Hkv, PD = k_pool.shape
+    if kv_dtype == "i4":                    # two elements per byte
+        PD *= 2
     D = PD // P
     B = len(sl)
     out = np.zeros((B, Hq, D), dtype=np.float64)
@@ -89,6 +91,8 @@ def append(k_new, v_new, kv_dtype, block_tables, seq_lens, k_pool, v_pool, P):
     kn, vn = _c(k_new), _c(v_new)
     bt, sl = _c(block_tables, np.int32), _c(seq_lens, np.int32)
     NP, Hkv, PD = k_pool.shape
+    if kv_dtype == "i4":                    # pools hold two elements per byte
+        PD *= 2
     rc = lib().orc_append(_p(kn), _p(vn), DT[kv_dtype], _p(bt), bt.shape[1], _p(sl), len(sl),
                           _p(k_pool), _p(v_pool), NP, Hkv, PD // P, P)
     if rc:
@@ -100,10 +104,13 @@ def gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, fill):
     k_pool, v_pool = _c(k_pool), _c(v_pool)
     bt, sl = _c(block_tables, np.int32), _c(seq_lens, np.int32)
     NP, Hkv, PD = k_pool.shape
+    if kv_dtype == "i4":                    # two elements per byte, rows packed too
+        PD *= 2
     D = PD // P
     rows = bt.shape[1] * P
-    ko = np.full((len(sl), Hkv, rows, D), fill, dtype=k_pool.dtype)
-    vo = np.full((len(sl), Hkv, rows, D), fill, dtype=k_pool.dtype)
+    row_len = D // 2 if kv_dtype == "i4" else D
+    ko = np.full((len(sl), Hkv, rows, row_len), fill, dtype=k_pool.dtype)
+    vo = np.full((len(sl), Hkv, rows, row_len), fill, dtype=k_pool.dtype)
     rc = lib().orc_gather(_p(k_pool), _p(v_pool), DT[kv_dtype], _p(bt), bt.shape[1], _p(sl),
                           len(sl), NP, Hkv, D, P, _p(ko), _p(vo))
     if rc:

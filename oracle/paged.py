@@ -20,7 +20,44 @@ import math
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "i8": 1}
+ELEM_BITS = {"f32": 32, "bf16": 16, "fp8": 8, "i8": 8, "i4": 4}
+SCALED = ("fp8", "i8", "i4")      # formats with per-(page, kv head) scales
+
+
+def pool_elems(pool: np.ndarray, kv_dtype: str) -> int:
+    """Elements per (page, kv head) chunk of a pool array (int4: two per byte)."""
+    return pool.shape[-1] * (2 if kv_dtype == "i4" else 1)
+
+
+def read_elems(pool: np.ndarray, idx, kv_dtype: str) -> np.ndarray:
+    """Stored elements pool[..., idx] by element index (int4: the nibble codes)."""
+    if kv_dtype != "i4":
+        return pool[idx]
+    *lead, e = idx
+    b = pool[tuple(lead) + (e // 2,)]
+    return ((b >> (4 * (e % 2))) & 0xF).astype(np.uint8)
+
+
+def write_elems(pool: np.ndarray, idx, vals, kv_dtype: str) -> None:
+    """pool[..., idx] = vals by element index (int4: nibble codes, the byte's other
+    nibble kept).  For int4 the even elements are written first, then the odd
+    ones: each byte holds one of each, so neither pass assigns a byte twice."""
+    if kv_dtype != "i4":
+        pool[idx] = vals
+        return
+    *lead, e = idx
+    e = np.asarray(e)
+    shape = np.broadcast(*lead, e).shape
+    vals = np.broadcast_to(np.asarray(vals, dtype=np.uint8) & 0xF, shape)
+    full = [np.broadcast_to(np.asarray(x), shape) for x in lead] + [np.broadcast_to(e, shape)]
+    for parity in (0, 1):
+        m = full[-1] % 2 == parity
+        sel = tuple(x[m] for x in full[:-1]) + (full[-1][m] // 2,)
+        old = pool[sel]
+        if parity == 0:
+            pool[sel] = (old & 0xF0) | vals[m]
+        else:
+            pool[sel] = (old & 0x0F) | (vals[m] << 4)
 
 
 # ---------------------------------------------------------------- decoding ----
@@ -62,6 +99,9 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
         return e4m3_to_f64(x)
     if dtype == "i8":                       # two's complement bytes
         return np.asarray(x).view(np.int8).astype(np.float64)
+    if dtype == "i4":                       # two's complement nibble codes
+        c = np.asarray(x, dtype=np.int64) & 0xF
+        return ((c ^ 8) - 8).astype(np.float64)
     raise ValueError(dtype)
 
 
@@ -69,7 +109,7 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def _offsets(P: int, D: int, kv_dtype: str):
     """Element offsets inside one (page, head) chunk, as [P, D] arrays (K, V)."""
-    E = 16 // ELEM_BYTES[kv_dtype]
+    E = 128 // ELEM_BITS[kv_dtype]
     TB = 4 * E
     j = np.arange(P).reshape(P, 1)
     d = np.arange(D).reshape(1, D)
@@ -81,8 +121,8 @@ def _offsets(P: int, D: int, kv_dtype: str):
 
 def gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b):
     """Stored K, V elements of sequence b in logical order: [Hkv, L, D] each."""
-    NP, Hkv, PD = k_pool.shape
-    D = PD // P
+    NP, Hkv = k_pool.shape[:2]
+    D = pool_elems(k_pool, kv_dtype) // P
     L = max(int(seq_lens[b]), 0)
     koff, voff = _offsets(P, D, kv_dtype)
     t = np.arange(L)
@@ -90,8 +130,9 @@ def gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b):
     if L and (pages.min() < 0 or pages.max() >= NP):
         raise IndexError("page id out of range")
     slot = t % P
-    k = k_pool[pages[None, :, None], np.arange(Hkv)[:, None, None], koff[slot][None, :, :]]
-    v = v_pool[pages[None, :, None], np.arange(Hkv)[:, None, None], voff[slot][None, :, :]]
+    hh = np.arange(Hkv)[:, None, None]
+    k = read_elems(k_pool, (pages[None, :, None], hh, koff[slot][None, :, :]), kv_dtype)
+    v = read_elems(v_pool, (pages[None, :, None], hh, voff[slot][None, :, :]), kv_dtype)
     return k, v, pages
 
 
@@ -107,8 +148,8 @@ def decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens, Hq, P, 
            k_scales=None, v_scales=None, batches=None):
     """fp64 [B, Hq, D] outputs (rows of sequences not in ``batches`` stay zero)."""
     B = len(seq_lens)
-    NP, Hkv, PD = k_pool.shape
-    D = PD // P
+    NP, Hkv = k_pool.shape[:2]
+    D = pool_elems(k_pool, kv_dtype) // P
     G = Hq // Hkv
     out = np.zeros((B, Hq, D), dtype=np.float64)
     qf = widen(q, q_dtype).reshape(B, Hq, D)
@@ -117,7 +158,7 @@ def decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens, Hq, P, 
             continue
         k, v, pages = gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b)
         kf, vf = widen(k, kv_dtype), widen(v, kv_dtype)
-        if kv_dtype in ("fp8", "i8"):
+        if kv_dtype in SCALED:
             kf = kf * np.asarray(k_scales, np.float64)[pages].T[:, :, None]
             vf = vf * np.asarray(v_scales, np.float64)[pages].T[:, :, None]
         for g in range(Hkv):
@@ -126,10 +167,14 @@ def decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens, Hq, P, 
 
 
 def append(k_new, v_new, kv_dtype, block_tables, seq_lens, k_pool, v_pool, P):
-    """In place: token L-1 of each sequence (L = seq_lens[b] >= 1) into its page slot."""
-    NP, Hkv, PD = k_pool.shape
-    D = PD // P
+    """In place: token L-1 of each sequence (L = seq_lens[b] >= 1) into its page slot.
+    int4 rows k_new[b][g] are packed (D/2 bytes, element 2i in the low nibble)."""
+    NP, Hkv = k_pool.shape[:2]
+    D = pool_elems(k_pool, kv_dtype) // P
     koff, voff = _offsets(P, D, kv_dtype)
+    if kv_dtype == "i4":
+        k_new = np.stack([np.asarray(k_new) & 0xF, np.asarray(k_new) >> 4], -1).reshape(len(seq_lens), Hkv, D)
+        v_new = np.stack([np.asarray(v_new) & 0xF, np.asarray(v_new) >> 4], -1).reshape(len(seq_lens), Hkv, D)
     for b in range(len(seq_lens)):
         L = int(seq_lens[b])
         if L <= 0:
@@ -138,8 +183,9 @@ def append(k_new, v_new, kv_dtype, block_tables, seq_lens, k_pool, v_pool, P):
         pg = int(block_tables[b][t // P])
         if not 0 <= pg < NP:
             raise IndexError("page id out of range")
-        k_pool[pg][:, koff[t % P]] = k_new[b]          # k_pool[pg] is a view
-        v_pool[pg][:, voff[t % P]] = v_new[b]
+        hh = np.arange(Hkv)[:, None]
+        write_elems(k_pool, (pg, hh, koff[t % P][None, :]), k_new[b], kv_dtype)
+        write_elems(v_pool, (pg, hh, voff[t % P][None, :]), v_new[b], kv_dtype)
 
 
 # ------------------------------------------------- split-KV partitions -------
@@ -219,17 +265,30 @@ def int8_to_f64(codes: np.ndarray) -> np.ndarray:
 # range without clipping, encoder, exact decoder).  int8 rounds 127.5 to 128
 # (ties to even), which clamps to 127: still within half a step, so 127.5 is
 # the no-clip bound there, as 464 (the midpoint above 448) is for e4m3.
+def int4_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> symmetric int4 nibble code: nearest integer, ties to even,
+    clamped to [-7, 7] (-8 is not used), as a two's complement nibble 0..15."""
+    q = np.clip(np.rint(np.asarray(x, dtype=np.float32).astype(np.float64)), -7, 7).astype(np.int64)
+    return (q & 0xF).astype(np.uint8)
+
+
+def int4_to_f64(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    return ((c ^ 8) - 8).astype(np.float64)
+
+
 DYNAMIC_FORMATS = {
     "fp8": (448.0, 464.0, lambda y: e4m3_encode(y), e4m3_to_f64),
     "i8": (127.0, 127.5, lambda y: int8_encode(y), int8_to_f64),
+    "i4": (7.0, 7.5, lambda y: int4_encode(y), int4_to_f64),
 }
 
 
 def append_dynamic(fmt, k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
                    k_scales, v_scales, P):
-    """In place: token L-1 of each sequence into its one-byte page (fmt "fp8" or
-    "i8"), with the page scale kept at amax / QMAX of the page's tokens (K and V
-    each on their own); QMAX = 448 for fp8, 127 for int8.
+    """In place: token L-1 of each sequence into its page (fmt "fp8", "i8" or
+    "i4"), with the page scale kept at amax / QMAX of the page's tokens (K and V
+    each on their own); QMAX = 448 for fp8, 127 for int8, 7 for int4.
 
     For each b with L = seq_lens[b] >= 1, t = L - 1, page pg = block_tables[b, t//P]
     (a table index or page id out of range skips the sequence), slot j = t % P,
@@ -238,7 +297,7 @@ def append_dynamic(fmt, k_new, v_new, new_dtype, block_tables, seq_lens, k_pool,
       j == 0 (first token of the page): s = a / QMAX, or 1 when a == 0;
       j > 0, s0 = the page's current scale: if a / s0 <= NOCLIP (the row's
         largest element rounds to the largest code or less, no clipping:
-        464 for fp8, 127.5 for int8) then s = s0;
+        464 for fp8, 127.5 for int8, 7.5 for int4) then s = s0;
         otherwise s = a / QMAX and every earlier slot j' < j is re-encoded:
         byte' = enc((dec(byte) * s0) / s);
       the new token: byte = enc(x / s); the page scale becomes s.
@@ -246,10 +305,10 @@ def append_dynamic(fmt, k_new, v_new, new_dtype, block_tables, seq_lens, k_pool,
     enc is the format's encoder, dec its exact value.
     """
     qmax, noclip, enc, dec = DYNAMIC_FORMATS[fmt]
-    NP, Hkv, PD = k_pool.shape
-    D = PD // P
+    NP, Hkv = k_pool.shape[:2]
+    D = pool_elems(k_pool, fmt) // P
     MP = np.asarray(block_tables).shape[1]
-    koff, voff = _offsets(P, D, "fp8")          # one-byte layout
+    koff, voff = _offsets(P, D, fmt)
     f32 = np.float32
     cmax, cnoclip = f32(qmax), f32(noclip)
     for b in range(len(seq_lens)):
@@ -276,9 +335,9 @@ def append_dynamic(fmt, k_new, v_new, new_dtype, block_tables, seq_lens, k_pool,
                     else:
                         s = f32(a / cmax)
                         idx = off[:j]                                          # [j, D]
-                        real = dec(pool[pg, g, idx]).astype(np.float32) * s0
-                        pool[pg, g, idx] = enc(real.astype(np.float32) / s)
-                pool[pg, g, off[j]] = enc(x / s)
+                        real = dec(read_elems(pool, (pg, g, idx), fmt)).astype(np.float32) * s0
+                        write_elems(pool, (pg, g, idx), enc(real.astype(np.float32) / s), fmt)
+                write_elems(pool, (pg, g, off[j]), enc(x / s), fmt)
                 scales[pg, g] = s
 
 
@@ -286,6 +345,13 @@ def append_fp8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, 
                        k_scales, v_scales, P):
     """append_dynamic for an fp8 e4m3 cache (QMAX 448, no-clip bound 464)."""
     append_dynamic("fp8", k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
+                   k_scales, v_scales, P)
+
+
+def append_int4_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
+                        k_scales, v_scales, P):
+    """append_dynamic for a symmetric int4 cache (QMAX 7, no-clip bound 7.5)."""
+    append_dynamic("i4", k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
                    k_scales, v_scales, P)
 
 

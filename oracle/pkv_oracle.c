@@ -21,12 +21,15 @@
  *     v_t = dec(V[page(t)][g][slot(t)][:]) * sV(page(t), g)
  *     s_t = scale * sum_d q[b][h][d] * k_t[d]
  *     out[b][h][:] = sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s)
- *   with out = 0 when L = 0.  dec() widens fp32, bf16, fp8-e4m3 or int8 exactly;
- *   sK, sV are the per-(page, kv head) fp32 scales for fp8 and int8, 1 otherwise.
+ *   with out = 0 when L = 0.  dec() widens fp32, bf16, fp8-e4m3, int8 or int4
+ *   exactly; sK, sV are the per-(page, kv head) fp32 scales for fp8, int8 and
+ *   int4, 1 otherwise.  int4 elements are two's complement nibbles, two per
+ *   byte, element 2i in the low nibble of byte i (of the chunk, or of a row of
+ *   k_new / v_new / the gather output).
  *   Everything after decoding is fp64, with libm exp.
  *
- * Byte layout of one (page, kv head) chunk of P tokens x D elements
- * (E = 16 / element bytes elements per 16-byte group, TB = 4E):
+ * Element layout of one (page, kv head) chunk of P tokens x D elements
+ * (E = elements per 16-byte group: 128 / element bits, TB = 4E):
  *   K (j, d): ((d / E) * P + j) * E + d % E
  *   V (j, d): blk = j / TB, r = j % TB, c = (r % 16) / 4,
  *             e = 4 * (r / 16) + r % 4  ->  blk*TB*D + (c*D + d)*E + e
@@ -38,10 +41,33 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_I8 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_I8 = 3, ORC_I4 = 4 };
 
-static int elem_bytes(int dt) {
-  return dt == ORC_F32 ? 4 : dt == ORC_BF16 ? 2 : (dt == ORC_FP8 || dt == ORC_I8) ? 1 : 0;
+static int elem_bits(int dt) {
+  return dt == ORC_F32 ? 32 : dt == ORC_BF16 ? 16 : (dt == ORC_FP8 || dt == ORC_I8) ? 8 : dt == ORC_I4 ? 4 : 0;
+}
+
+/* int4: nibble idx of a packed array (two's complement code 0..15). */
+static int get_nib(const void* base, int64_t idx) {
+  uint8_t byte = ((const uint8_t*)base)[idx >> 1];
+  return (idx & 1) ? byte >> 4 : byte & 15;
+}
+static void set_nib(void* base, int64_t idx, int code) {
+  uint8_t* p = (uint8_t*)base + (idx >> 1);
+  if (idx & 1)
+    *p = (uint8_t)((*p & 0x0F) | ((code & 15) << 4));
+  else
+    *p = (uint8_t)((*p & 0xF0) | (code & 15));
+}
+
+/* Copy one stored element (any format) from src[si] to dst[di]. */
+static void copy_elem(void* dst, int64_t di, const void* src, int64_t si, int bits) {
+  if (bits == 4) {
+    set_nib(dst, di, get_nib(src, si));
+  } else {
+    int eb = bits / 8;
+    memcpy((char*)dst + di * eb, (const char*)src + si * eb, (size_t)eb);
+  }
 }
 
 /* bf16: the top half of a binary32. */
@@ -70,6 +96,7 @@ static double load_elem(const void* base, int dt, int64_t idx) {
     case ORC_F32: return (double)((const float*)base)[idx];
     case ORC_BF16: return orc_bf16_to_f64(((const uint16_t*)base)[idx]);
     case ORC_I8: return (double)((const int8_t*)base)[idx];   /* two's complement byte */
+    case ORC_I4: return (double)((get_nib(base, idx) ^ 8) - 8);  /* two's complement nibble */
     default: return orc_e4m3_to_f64(((const uint8_t*)base)[idx]);
   }
 }
@@ -109,7 +136,7 @@ typedef struct {
 
 /* One (b, h) output row.  Returns 0, or -1 if a page id used is out of range. */
 static int one_row(const job_t* J, int b, int h, double* s_buf, double* acc) {
-  const int D = J->D, P = J->P, E = 16 / elem_bytes(J->kv_dtype);
+  const int D = J->D, P = J->P, E = 128 / elem_bits(J->kv_dtype);
   const int G = J->Hq / J->Hkv, g = h / G;
   const int L = J->seq_lens[b] > 0 ? J->seq_lens[b] : 0;
   double* o = J->out + ((int64_t)b * J->Hq + h) * D;
@@ -181,7 +208,7 @@ int orc_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
                const int32_t* pairs, int n_pairs, double* out, int nthreads) {
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return -2;
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 || page_size <= 0) return -2;
-  if (!elem_bytes(kv_dtype)) return -2;
+  if (!elem_bits(kv_dtype)) return -2;
   for (int b = 0; b < batch; ++b)
     if (seq_lens[b] > max_pages * page_size) return -2;
   if (nthreads < 1) nthreads = 1;
@@ -210,9 +237,9 @@ int orc_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
 int orc_append(const void* k_new, const void* v_new, int kv_dtype, const int32_t* block_tables,
                int max_pages, const int32_t* seq_lens, int batch, void* k_pool, void* v_pool,
                int num_pages, int num_kv_heads, int head_dim, int page_size) {
-  int eb = elem_bytes(kv_dtype);
-  if (!eb) return -2;
-  int E = 16 / eb, D = head_dim, P = page_size;
+  int bits = elem_bits(kv_dtype);
+  if (!bits) return -2;
+  int E = 128 / bits, D = head_dim, P = page_size;
   for (int b = 0; b < batch; ++b) {
     int L = seq_lens[b];
     if (L <= 0) continue;
@@ -225,10 +252,8 @@ int orc_append(const void* k_new, const void* v_new, int kv_dtype, const int32_t
       int64_t cbase = ((int64_t)pg * num_kv_heads + g) * P * D;
       int64_t src = ((int64_t)b * num_kv_heads + g) * D;
       for (int d = 0; d < D; ++d) {
-        memcpy((char*)k_pool + (cbase + k_off(j, d, P, E)) * eb,
-               (const char*)k_new + (src + d) * eb, (size_t)eb);
-        memcpy((char*)v_pool + (cbase + v_off(j, d, P, D, E)) * eb,
-               (const char*)v_new + (src + d) * eb, (size_t)eb);
+        copy_elem(k_pool, cbase + k_off(j, d, P, E), k_new, src + d, bits);
+        copy_elem(v_pool, cbase + v_off(j, d, P, D, E), v_new, src + d, bits);
       }
     }
   }
@@ -240,9 +265,9 @@ int orc_append(const void* k_new, const void* v_new, int kv_dtype, const int32_t
 int orc_gather(const void* k_pool, const void* v_pool, int kv_dtype, const int32_t* block_tables,
                int max_pages, const int32_t* seq_lens, int batch, int num_pages,
                int num_kv_heads, int head_dim, int page_size, void* k_out, void* v_out) {
-  int eb = elem_bytes(kv_dtype);
-  if (!eb) return -2;
-  int E = 16 / eb, D = head_dim, P = page_size;
+  int bits = elem_bits(kv_dtype);
+  if (!bits) return -2;
+  int E = 128 / bits, D = head_dim, P = page_size;
   int64_t rows = (int64_t)max_pages * P;
   for (int b = 0; b < batch; ++b) {
     int L = seq_lens[b];
@@ -255,10 +280,8 @@ int orc_gather(const void* k_pool, const void* v_pool, int kv_dtype, const int32
         int64_t cbase = ((int64_t)pg * num_kv_heads + g) * P * D;
         int64_t dst = (((int64_t)b * num_kv_heads + g) * rows + t) * D;
         for (int d = 0; d < D; ++d) {
-          memcpy((char*)k_out + (dst + d) * eb,
-                 (const char*)k_pool + (cbase + k_off(j, d, P, E)) * eb, (size_t)eb);
-          memcpy((char*)v_out + (dst + d) * eb,
-                 (const char*)v_pool + (cbase + v_off(j, d, P, D, E)) * eb, (size_t)eb);
+          copy_elem(k_out, dst + d, k_pool, cbase + k_off(j, d, P, E), bits);
+          copy_elem(v_out, dst + d, v_pool, cbase + v_off(j, d, P, D, E), bits);
         }
       }
     }

@@ -29,6 +29,8 @@ def _torch_widen(x, dtype):
         return torch.from_numpy(np.asarray(x, np.uint16).view(np.int16).copy()).view(torch.bfloat16).to(torch.float64)
     if dtype == "i8":
         return torch.from_numpy(np.asarray(x, np.uint8).copy()).view(torch.int8).to(torch.float64)
+    if dtype == "i4":   # nibble codes: shift the sign bit of the 4-bit code up to bit 7
+        return (torch.from_numpy((np.asarray(x, np.uint8) << 4).copy()).view(torch.int8) >> 4).to(torch.float64)
     return torch.from_numpy(np.asarray(x, np.uint8).copy()).view(torch.float8_e4m3fn).to(torch.float64)
 
 
@@ -43,7 +45,7 @@ def _sdpa_reference(wl):
             continue
         k, v, ks, vs = configs.seq_tokens(wl.seed, b, L, Hkv, D, wl.kv_dtype, P)
         kt, vt = _torch_widen(k, wl.kv_dtype), _torch_widen(v, wl.kv_dtype)      # [L, Hkv, D]
-        if wl.kv_dtype in ("fp8", "i8"):
+        if wl.kv_dtype in ("fp8", "i8", "i4"):
             kt = kt * torch.from_numpy(np.repeat(ks, P, 0)[:L]).to(torch.float64)[:, :, None]
             vt = vt * torch.from_numpy(np.repeat(vs, P, 0)[:L]).to(torch.float64)[:, :, None]
         G = Hq // Hkv
@@ -69,6 +71,7 @@ SMALL = [
     dict(seed=13, lens=[1, 63, 64, 65, 130], Hq=4, Hkv=1, D=32, P=64, kv_dtype="fp8"),
     dict(seed=14, lens=[0, 7, 129], Hq=6, Hkv=3, D=16, P=128, kv_dtype="bf16"),
     dict(seed=15, lens=[2, 64, 65, 200], Hq=8, Hkv=2, D=32, P=64, kv_dtype="i8"),
+    dict(seed=16, lens=[1, 128, 129, 300], Hq=8, Hkv=2, D=128, P=128, kv_dtype="i4"),
 ]
 
 
@@ -166,7 +169,7 @@ def test_output_within_value_range(spec):
             continue
         _, v, _, vs = configs.seq_tokens(wl.seed, b, L, wl.Hkv, wl.D, wl.kv_dtype, wl.P)
         vf = _torch_widen(v, wl.kv_dtype).numpy()
-        if wl.kv_dtype == "fp8":
+        if wl.kv_dtype in configs.SCALED:
             vf = vf * np.repeat(vs, wl.P, 0)[:L][:, :, None]
         for h in range(wl.Hq):
             g = h // wl.G
@@ -197,6 +200,8 @@ def test_poison_invariance(spec):
     a0, b0 = _oracles(wl)
     # overwrite every slot that holds no valid token with different garbage
     kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    if wl.kv_dtype == "i4":               # work on the nibble codes, repack below
+        kp, vp = layout.unpack_nibbles(kp), layout.unpack_nibbles(vp)
     valid_k = np.zeros(kp.shape, bool)
     valid_v = np.zeros(vp.shape, bool)
     ki, vi = layout.k_chunk_index(wl.P, wl.D, wl.kv_dtype), layout.v_chunk_index(wl.P, wl.D, wl.kv_dtype)
@@ -206,8 +211,12 @@ def test_poison_invariance(spec):
             valid_k[pg, :, ki[t % wl.P]] = True
             valid_v[pg, :, vi[t % wl.P]] = True
     junk = np.random.default_rng(7).integers(0, 255, kp.shape).astype(kp.dtype)
+    if wl.kv_dtype == "i4":
+        junk &= 0xF
     kp[~valid_k] = junk[~valid_k]
     vp[~valid_v] = junk[~valid_v]
+    if wl.kv_dtype == "i4":
+        kp, vp = layout.pack_nibbles(kp), layout.pack_nibbles(vp)
     a1 = paged.decode(wl.q, wl.q_dtype, kp, vp, wl.kv_dtype, wl.block_tables, wl.seq_lens, wl.Hq, wl.P, wl.scale, wl.k_scales, wl.v_scales)
     b1 = c_oracle.decode(wl.q, wl.q_dtype, kp, vp, wl.kv_dtype, wl.block_tables, wl.seq_lens, wl.Hq, wl.P, wl.scale, wl.k_scales, wl.v_scales)
     assert np.array_equal(a0, a1) and np.array_equal(b0, b1)
@@ -243,20 +252,27 @@ def test_split_merge_equals_unsplit(part):
     assert np.abs(paged.merge_partials(o, lse) - full).max() < 1e-12
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_bf16", "inflight_bf16",
-                                  "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "int8_kv", "inflight_int8"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16",
+                                  "fp8_kv", "inflight_fp8", "int8_kv", "inflight_int8", "int4_kv",
+                                  "inflight_int4"])
 def test_c_and_numpy_oracles_agree(name):
     small = {"llama3_8b_bf16": dict(B=6), "inflight_bf16": dict(B=6, n_steps=2, max_len=3000),
              "long_splitkv_bf16": dict(B=2, L=3000), "fp8_kv": dict(B=4),
              "inflight_fp8": dict(B=6, n_steps=2, max_len=3000), "int8_kv": dict(B=4),
-             "inflight_int8": dict(B=6, n_steps=2, max_len=3000)}
+             "inflight_int8": dict(B=6, n_steps=2, max_len=3000), "int4_kv": dict(B=4),
+             "inflight_int4": dict(B=6, n_steps=2, max_len=3000)}
     wl = configs.CONFIGS[name](**small.get(name, {}))
     a, b = _oracles(wl)
     assert np.abs(a - b).max() < 1e-12
 
 
+def _row(x, kv_dtype):
+    """A token row in the ABI's stored form (int4: packed two per byte)."""
+    return layout.pack_nibbles(x) if kv_dtype == "i4" else x
+
+
 @pytest.mark.parametrize("kv_dtype,P", [("f32", 16), ("bf16", 32), ("bf16", 64), ("fp8", 64), ("fp8", 128),
-                                        ("i8", 64)])
+                                        ("i8", 64), ("i4", 128), ("i4", 256)])
 def test_append_reproduces_packed_pool(kv_dtype, P):
     """Appending tokens one at a time (both oracles) rebuilds the generator's pool bytes."""
     wl = configs.custom(seed=21, lens=[1, P - 1, P, P + 1, 2 * P + 3], Hq=4, Hkv=2, D=32, P=P,
@@ -268,32 +284,34 @@ def test_append_reproduces_packed_pool(kv_dtype, P):
                 for b in range(wl.B)]
         for t in range(int(wl.seq_lens.max())):
             lens = np.where(wl.seq_lens > t, t + 1, 0).astype(np.int32)   # sequences still growing
-            kn = np.zeros((wl.B, wl.Hkv, wl.D), kp.dtype)
-            vn = np.zeros((wl.B, wl.Hkv, wl.D), kp.dtype)
+            rl = wl.D // 2 if kv_dtype == "i4" else wl.D
+            kn = np.zeros((wl.B, wl.Hkv, rl), kp.dtype)
+            vn = np.zeros((wl.B, wl.Hkv, rl), kp.dtype)
             for b in range(wl.B):
                 if lens[b]:
-                    kn[b], vn[b] = toks[b][0][t], toks[b][1][t]
+                    kn[b], vn[b] = _row(toks[b][0][t], kv_dtype), _row(toks[b][1][t], kv_dtype)
             impl(kn, vn, kv_dtype, wl.block_tables, lens, kp, vp, P)
         assert np.array_equal(kp.view(np.uint8), wl.k_pool.view(np.uint8))
         assert np.array_equal(vp.view(np.uint8), wl.v_pool.view(np.uint8))
 
 
-@pytest.mark.parametrize("kv_dtype,P", [("f32", 16), ("bf16", 64), ("fp8", 64), ("i8", 64)])
+@pytest.mark.parametrize("kv_dtype,P", [("f32", 16), ("bf16", 64), ("fp8", 64), ("i8", 64), ("i4", 128)])
 def test_gather_returns_logical_tokens(kv_dtype, P):
     wl = configs.custom(seed=22, lens=[2, P, 3 * P - 1], Hq=2, Hkv=2, D=32, P=P, kv_dtype=kv_dtype)
     ko, vo = c_oracle.gather(wl.k_pool, wl.v_pool, kv_dtype, wl.block_tables, wl.seq_lens, P, 0)
     for b in range(wl.B):
         L = int(wl.seq_lens[b])
         k, v, _, _ = configs.seq_tokens(wl.seed, b, L, wl.Hkv, wl.D, kv_dtype, P)
+        k, v = _row(k, kv_dtype), _row(v, kv_dtype)
         assert np.array_equal(ko[b, :, :L].view(np.uint8), k.transpose(1, 0, 2).copy().view(np.uint8))
         assert np.array_equal(vo[b, :, :L].view(np.uint8), v.transpose(1, 0, 2).copy().view(np.uint8))
         kn, vn, _ = paged.gather(wl.k_pool, wl.v_pool, kv_dtype, wl.block_tables, wl.seq_lens, P, b)
-        assert np.array_equal(kn.view(np.uint8), ko[b, :, :L].view(np.uint8))
-        assert np.array_equal(vn.view(np.uint8), vo[b, :, :L].view(np.uint8))
+        assert np.array_equal(_row(kn, kv_dtype).view(np.uint8), ko[b, :, :L].view(np.uint8))
+        assert np.array_equal(_row(vn, kv_dtype).view(np.uint8), vo[b, :, :L].view(np.uint8))
 
 
 def test_layout_offsets_are_permutations():
-    for dt, P in [("f32", 16), ("bf16", 32), ("bf16", 128), ("fp8", 64)]:
+    for dt, P in [("f32", 16), ("bf16", 32), ("bf16", 128), ("fp8", 64), ("i4", 128)]:
         for D in (64, 128):
             for idx in (layout.k_chunk_index(P, D, dt), layout.v_chunk_index(P, D, dt)):
                 assert np.array_equal(np.sort(idx.ravel()), np.arange(P * D))

@@ -356,3 +356,88 @@ def test_int8_no_clip_bound_and_doubling():
     want = np.where(half == np.floor(half), half, np.where(np.floor(half) % 2 == 0, np.floor(half),
                                                              np.floor(half) + 1))
     assert np.array_equal(new, want.astype(np.int64))
+
+
+# ------------------------------------------------------------------ int4 ----
+
+def test_int4_encode_matches_torch_round_and_clamp():
+    x = all_bf16_as_f32()
+    m = np.isfinite(x) & (np.abs(x) < 100)
+    ties = (np.arange(-10, 10) + 0.5).astype(F32)
+    y = np.concatenate([x[m], ties, np.nextafter(ties, F32(np.inf)), np.nextafter(ties, F32(-np.inf))])
+    ref = torch.clamp(torch.round(torch.from_numpy(y)), -7, 7).to(torch.int8).numpy().view(np.uint8) & 0xF
+    assert np.array_equal(paged.int4_encode(y), ref)
+    assert np.array_equal(paged.int4_encode(y), codec.int4_encode(y))
+    assert np.array_equal(paged.int4_to_f64(np.arange(16)), np.array([0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5,
+                                                                        -4, -3, -2, -1], np.float64))
+
+
+def empty_i4(NP, Hkv, P, D):
+    k = layout.empty_pool(NP, Hkv, P, D, "i4")
+    return k, k.copy(), np.full((NP, Hkv), np.nan, F32), np.full((NP, Hkv), np.nan, F32)
+
+
+def i4_row(pool, P, D, pg, g, j, which):
+    koff, voff = paged._offsets(P, D, "i4")
+    off = (koff if which == "k" else voff)[j]
+    return paged.int4_to_f64(paged.read_elems(pool, (pg, g, off), "i4")).astype(np.int64)
+
+
+def test_int4_first_token_and_token_by_token_equals_one_shot():
+    rng = np.random.default_rng(30)
+    Hkv, D, P = 2, 128, 128
+    L = 2 * P - 9
+    x = rng.standard_normal((L, Hkv, D)).astype(F32)
+    for p0 in range(0, L, P):
+        x[p0, :, 11] = 5.0
+    kb, ksc = configs.quantize_int4_pages(x, P)
+    kp, vp, ks, vs = empty_i4(3, Hkv, P, D)
+    bt = np.array([[1, 2]], dtype=np.int32)
+    for t in range(L):
+        paged.append_int4_dynamic(x[t:t + 1], x[t:t + 1], "f32", bt, np.array([t + 1], np.int32),
+                                  kp, vp, ks, vs, P)
+        if t == 0:
+            assert ks[1, 0] == F32(F32(5.0) / F32(7))
+            assert i4_row(kp, P, D, 1, 0, 0, "k")[11] == 7
+    kidx = layout.k_chunk_index(P, D, "i4")
+    for i, pg in enumerate((1, 2)):
+        n = min(P, L - i * P)
+        for g in range(Hkv):
+            got = paged.read_elems(kp, (pg, g, kidx[:n]), "i4")
+            assert np.array_equal(got, kb[i * P:i * P + n, g])
+        assert np.array_equal(ks[pg], ksc[i])
+
+
+def test_int4_no_clip_bound_and_doubling():
+    Hkv, D, P = 1, 128, 128
+    bt = np.array([[0]], dtype=np.int32)
+    for top, grows in ((7.5 * 0.5, False), (7.5 * 0.5 * (1 + 2 ** -20), True)):
+        kp, vp, ks, vs = empty_i4(1, Hkv, P, D)
+        first = np.zeros((1, 1, D), F32)
+        first[0, 0, :15] = (np.arange(15) - 7).astype(F32) / 2      # codes -7 .. 7 at scale 1/2
+        first[0, 0, 20] = F32(3.5)
+        paged.append_int4_dynamic(first, first, "f32", bt, np.array([1], np.int32), kp, vp, ks, vs, P)
+        assert ks[0, 0] == F32(0.5)
+        old = i4_row(kp, P, D, 0, 0, 0, "k")
+        second = np.zeros((1, 1, D), F32)
+        second[0, 0, 3] = F32(top)
+        paged.append_int4_dynamic(second, second, "f32", bt, np.array([2], np.int32), kp, vp, ks, vs, P)
+        assert (ks[0, 0] != F32(0.5)) == grows
+        if not grows:
+            assert np.array_equal(i4_row(kp, P, D, 0, 0, 0, "k"), old)
+            assert i4_row(kp, P, D, 0, 0, 1, "k")[3] == 7
+    kp, vp, ks, vs = empty_i4(1, Hkv, P, D)
+    first = np.zeros((1, 1, D), F32)
+    first[0, 0, :15] = (np.arange(15) - 7).astype(F32) / 2
+    first[0, 0, 20] = F32(3.5)
+    paged.append_int4_dynamic(first, first, "f32", bt, np.array([1], np.int32), kp, vp, ks, vs, P)
+    old = i4_row(kp, P, D, 0, 0, 0, "k")
+    second = np.zeros((1, 1, D), F32)
+    second[0, 0, 5] = F32(7.0)                                       # scale 1 = twice 1/2
+    paged.append_int4_dynamic(second, second, "f32", bt, np.array([2], np.int32), kp, vp, ks, vs, P)
+    assert ks[0, 0] == F32(1.0)
+    half = old / 2
+    want = np.where(half == np.floor(half), half, np.where(np.floor(half) % 2 == 0, np.floor(half),
+                                                             np.floor(half) + 1))
+    assert np.array_equal(i4_row(kp, P, D, 0, 0, 0, "k"), want.astype(np.int64))
+    assert np.array_equal(i4_row(vp, P, D, 0, 0, 0, "v"), want.astype(np.int64))

@@ -93,3 +93,13 @@ def int8_encode(y: np.ndarray) -> np.ndarray:
 
 
 INT8_MAX = np.float32(127.0)
+
+
+def int4_encode(y: np.ndarray) -> np.ndarray:
+    """Encode float32 values as symmetric int4 nibble codes (two's complement,
+    0..15, one per byte): nearest integer, half to even, clamped to [-7, 7]."""
+    q = np.clip(np.rint(np.asarray(y, dtype=np.float32)), -7, 7).astype(np.int8)
+    return (q.view(np.uint8) & 0xF).astype(np.uint8)
+
+
+INT4_MAX = np.float32(7.0)

@@ -58,7 +58,7 @@ class Workload:
     P: int
     num_pages: int
     max_pages: int
-    kv_dtype: str                 # "f32" | "bf16" | "fp8" | "i8"
+    kv_dtype: str                 # "f32" | "bf16" | "fp8" | "i8" | "i4"
     q_dtype: str                  # "f32" | "bf16"
     out_dtype: str                # "f32" | "bf16"
     scale: np.float32
@@ -82,8 +82,8 @@ class Workload:
     def kv_bytes(self, seq_lens: Optional[np.ndarray] = None) -> int:
         """Bytes of K and V that a decode over ``seq_lens`` must read."""
         L = self.seq_lens if seq_lens is None else seq_lens
-        eb = layout.ELEM_BYTES[self.kv_dtype]
-        return int(np.sum(L.astype(np.int64))) * self.Hkv * self.D * eb * 2
+        bits = layout.ELEM_BITS[self.kv_dtype]
+        return int(np.sum(L.astype(np.int64))) * self.Hkv * self.D * bits // 8 * 2
 
 
 # ----------------------------------------------------------------------------
@@ -154,12 +154,34 @@ def quantize_int8_pages(x: np.ndarray, P: int):
     return codec.int8_encode(y), scales
 
 
+def quantize_int4_pages(x: np.ndarray, P: int):
+    """x: [L, Hkv, D] fp32 -> (int4 nibble codes [L, Hkv, D], scales [npages, Hkv]).
+
+    Each (logical page, head) gets scale = fp32(amax/7) over its valid tokens
+    (1.0 if that block is all zero); codes = rint(fp32(x / scale)) clamped to +-7.
+    """
+    L, Hkv, D = x.shape
+    npg = -(-L // P)
+    padded = np.zeros((npg * P, Hkv, D), dtype=np.float32)
+    padded[:L] = x
+    amax = np.abs(padded).reshape(npg, P, Hkv, D).max(axis=(1, 3))
+    scales = np.where(amax == 0, np.float32(1.0),
+                      (amax / codec.INT4_MAX).astype(np.float32)).astype(np.float32)
+    per_tok = np.repeat(scales, P, axis=0)[:L]
+    y = (x / per_tok[:, :, None]).astype(np.float32)
+    return codec.int4_encode(y), scales
+
+
+QUANTIZERS = {"fp8": quantize_fp8_pages, "i8": quantize_int8_pages, "i4": quantize_int4_pages}
+SCALED = tuple(QUANTIZERS)
+
+
 def seq_tokens(seed: int, b: int, L: int, Hkv: int, D: int, kv_dtype: str, P: int):
     """Logical K, V (stored format) and, for fp8, logical-page scales of sequence b."""
     kf = draw_seq_f32(seed, 2, b, L, Hkv, D)
     vf = draw_seq_f32(seed, 3, b, L, Hkv, D)
-    if kv_dtype in ("fp8", "i8"):
-        quant = quantize_fp8_pages if kv_dtype == "fp8" else quantize_int8_pages
+    if kv_dtype in SCALED:
+        quant = QUANTIZERS[kv_dtype]
         k, ks = quant(kf, P)
         v, vs = quant(vf, P)
         return k, v, ks, vs
@@ -249,7 +271,7 @@ def _assemble(name, seed, B, Hq, Hkv, D, P, num_pages, kv_dtype, q_dtype, out_dt
     kidx = layout.k_chunk_index(P, D, kv_dtype)
     vidx = layout.v_chunk_index(P, D, kv_dtype)
     ks = vs = None
-    if kv_dtype in ("fp8", "i8"):
+    if kv_dtype in SCALED:
         ks = np.full((num_pages, Hkv), np.nan, dtype=np.float32)
         vs = np.full((num_pages, Hkv), np.nan, dtype=np.float32)
     def fill(b):
@@ -258,7 +280,7 @@ def _assemble(name, seed, B, Hq, Hkv, D, P, num_pages, kv_dtype, q_dtype, out_dt
         k, v, kls, vls = seq_tokens(seed, b, n, Hkv, D, kv_dtype, P)
         layout.pack_sequence(kpool, pages, k, P, kidx, kv_dtype)
         layout.pack_sequence(vpool, pages, v, P, vidx, kv_dtype)
-        if kv_dtype in ("fp8", "i8") and len(pages):
+        if kv_dtype in SCALED and len(pages):
             ks[pages] = kls
             vs[pages] = vls
 
@@ -381,6 +403,22 @@ def inflight_int8(seed: int = 3, B: int = 256, n_steps: int = 16, max_len: int =
     return _inflight("inflight_int8", seed, B, n_steps, max_len, "i8")
 
 
+def int4_kv(seed: int = 5, B: int = 128) -> Workload:
+    """The fp8 workload's lengths and draws (B 128, lengths uniform in [1024,
+    8192], 32/8 heads, D 128) with a symmetric int4 cache (scale amax/7 per
+    (page, kv head), two codes per byte) on pages of 128 tokens (int4 tiles are
+    128 tokens); q bf16, out bf16."""
+    wl = fp8_kv(seed, B, kv_dtype="i4", P=128)
+    wl.name = "int4_kv"
+    return wl
+
+
+def inflight_int4(seed: int = 3, B: int = 256, n_steps: int = 16, max_len: int = 32768) -> Workload:
+    """The in-flight batch with a symmetric int4 cache and bf16 new rows,
+    quantised on write with dynamic page scales (amax / 7)."""
+    return _inflight("inflight_int4", seed, B, n_steps, max_len, "i4")
+
+
 def int8_kv(seed: int = 5, B: int = 128) -> Workload:
     """The fp8 workload's shape and draws (B 128, lengths uniform in [1024, 8192],
     32/8 heads, D 128, pages of 64) with a symmetric int8 cache, scale amax/127
@@ -390,12 +428,11 @@ def int8_kv(seed: int = 5, B: int = 128) -> Workload:
     return wl
 
 
-def fp8_kv(seed: int = 5, B: int = 128, kv_dtype: str = "fp8") -> Workload:
+def fp8_kv(seed: int = 5, B: int = 128, kv_dtype: str = "fp8", P: int = 64) -> Workload:
     """fp8 e4m3 cache: B 128, lengths uniform in [1024, 8192], 32/8 heads, D 128,
     pages of 64, per-(page, kv head) scale amax/448; q bf16, out bf16."""
     rng = np.random.default_rng(seed)
     L = rng.integers(1024, 8192, size=B, endpoint=True).astype(np.int32)
-    P = 64
     need = int(pages_needed(L, P).sum())
     NP = int(math.ceil(1.25 * need))
     bt = place_permuted(rng, L, P, NP, max_pages=8192 // P)
@@ -430,4 +467,6 @@ CONFIGS = {
     "inflight_fp8": inflight_fp8,
     "int8_kv": int8_kv,
     "inflight_int8": inflight_int8,
+    "int4_kv": int4_kv,
+    "inflight_int4": inflight_int4,
 }
