@@ -32,8 +32,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "paged decode attention: KV HBM GB/s (fraction of peak) + seqs/s per layer"
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", "pkv_kernels.hip")
 WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "int8_kv",
-             "inflight_int8", "tiny_fp32"]
-SCALED = ("fp8", "i8")          # one-byte caches with per-(page, kv head) scales
+             "inflight_int8", "int4_kv", "inflight_int4", "tiny_fp32"]
+SCALED = ("fp8", "i8", "i4")    # caches of one byte or less, with per-(page, kv head) scales
+ELEM_BITS = {"f32": 32, "bf16": 16, "fp8": 8, "i8": 8, "i4": 4}
 
 
 def kernel_hash() -> str:
@@ -62,30 +63,31 @@ def quantises_on_write(wl) -> bool:
 
 
 def decode_fn(pkv, kv_dtype):
-    return {"fp8": pkv.paged_attn_decode_fp8, "i8": pkv.paged_attn_decode_int8}[kv_dtype]
+    return {"fp8": pkv.paged_attn_decode_fp8, "i8": pkv.paged_attn_decode_int8,
+            "i4": pkv.paged_attn_decode_int4}[kv_dtype]
 
 
 def append_quant_fn(pkv, kv_dtype):
-    return {"fp8": pkv.kv_append_fp8, "i8": pkv.kv_append_int8}[kv_dtype]
+    return {"fp8": pkv.kv_append_fp8, "i8": pkv.kv_append_int8, "i4": pkv.kv_append_int4}[kv_dtype]
 
 
 def alg_bytes(wl, seq_lens):
     """Bytes the method must move: (decode bytes, append bytes) for one step."""
     import numpy as np
-    eb = {"f32": 4, "bf16": 2, "fp8": 1, "i8": 1}[wl.kv_dtype]
+    bits = ELEM_BITS[wl.kv_dtype]
     qb = 4 if wl.q_dtype == "f32" else 2
     ob = 4 if wl.out_dtype == "f32" else 2
     L = seq_lens.astype(np.int64)
     pages = (L + wl.P - 1) // wl.P
-    kv = int(L.sum()) * wl.Hkv * wl.D * eb * 2
+    kv = int(L.sum()) * wl.Hkv * wl.D * bits // 8 * 2
     dec = kv + wl.B * wl.Hq * wl.D * (qb + ob) + int(pages.sum()) * 4 + wl.B * 4
     if wl.kv_dtype in SCALED:
         dec += int(pages.sum()) * wl.Hkv * 4 * 2
     if quantises_on_write(wl):
         # read the bf16 rows, write fp8 rows, read and write both page scales
-        app = wl.B * wl.Hkv * (2 * wl.D * 2 + 2 * wl.D * eb + 2 * 4 * 2) + wl.B * 8
+        app = wl.B * wl.Hkv * (2 * wl.D * 2 + 2 * wl.D * bits // 8 + 2 * 4 * 2) + wl.B * 8
     else:
-        app = 2 * (wl.B * wl.Hkv * wl.D * eb * 2) + wl.B * 8
+        app = 2 * (wl.B * wl.Hkv * wl.D * bits // 8 * 2) + wl.B * 8
     return dec, app, kv
 
 
@@ -269,7 +271,7 @@ def main():
     if wl.steps:
         steps = [{"seq_lens": s.seq_lens, "k_new": s.k_new, "v_new": s.v_new} for s in wl.steps]
     else:
-        eb_dt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "i8": np.uint8}[wl.kv_dtype]
+        eb_dt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "i8": np.uint8, "i4": np.uint8}[wl.kv_dtype]
         if wl.kv_dtype == "f32":
             kn = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
             vn = rng.standard_normal((wl.B, wl.Hkv, wl.D)).astype(np.float32)
@@ -281,8 +283,12 @@ def main():
                 kn, vn = codec.f32_to_bf16_bits(kf), codec.f32_to_bf16_bits(vf)
             elif wl.kv_dtype == "fp8":  # bytes at a typical quantised magnitude
                 kn, vn = codec.e4m3_encode(kf * 100), codec.e4m3_encode(vf * 100)
-            else:
+            elif wl.kv_dtype == "i8":
                 kn, vn = codec.int8_encode(kf * 30), codec.int8_encode(vf * 30)
+            else:                       # int4 rows, two codes per byte
+                from workloads import layout
+                kn = layout.pack_nibbles(codec.int4_encode(kf * 2))
+                vn = layout.pack_nibbles(codec.int4_encode(vf * 2))
         steps = [{"seq_lens": wl.seq_lens.copy(), "k_new": kn.astype(eb_dt), "v_new": vn.astype(eb_dt)}]
 
     pool_bytes = wl.k_pool.nbytes + wl.v_pool.nbytes
@@ -362,7 +368,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8e4m3 (kv) / bf16 (q, out)", "i8": "int8 (kv) / bf16 (q, out)",
-                  "f32": "f32"}[wl.kv_dtype],
+                  "i4": "int4 (kv) / bf16 (q, out)", "f32": "f32"}[wl.kv_dtype],
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled pages)",
         "config": {"workload": args.workload, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "page_size": wl.P,

@@ -41,23 +41,27 @@
  *                ceil(L_b / P) are never read (may be -1).
  *   seq_lens     int32 [B]; number of tokens of sequence b in the cache,
  *                INCLUDING the token appended this step.  0 is allowed.
- *   k_scales, v_scales  fp32 [NP][Hkv], fp8 and int8 caches only: stored
- *                value times scale is the real value, one scale per
+ *   k_scales, v_scales  fp32 [NP][Hkv], fp8, int8 and int4 caches only:
+ *                stored value times scale is the real value, one scale per
  *                (page, kv head).  int8 elements are two's complement bytes
- *                in [-127, 127].
+ *                in [-127, 127]; int4 elements are two's complement nibbles in
+ *                [-7, 7], two per byte, element 2i in the low nibble of byte i
+ *                (in the pools by element index within a chunk, and in k_new /
+ *                v_new rows, which are then D / 2 bytes).
  *   k_pool, v_pool      NP * Hkv chunks, one per (page, kv head), each holding
  *                P * D elements; chunk (pg, g) starts at element
  *                (pg * Hkv + g) * P * D.
  *
- * Layout inside one chunk.  Let E = 16 / (element bytes) (fp32 4, bf16 8,
- * fp8 and int8 16) and TB = 4 * E.  For token slot j in [0, P) and dimension d:
+ * Layout inside one chunk.  Let E = 128 / (element bits) (fp32 4, bf16 8,
+ * fp8 and int8 16, int4 32) and TB = 4 * E.  For token slot j in [0, P) and dimension d:
  *   K (j, d) at element ((d / E) * P + j) * E + d % E
  *   V (j, d) at element blk * TB * D + (c * D + d) * E + e, where
  *            blk = j / TB, r = j % TB, c = (r % 16) / 4, e = 4 * (r / 16) + r % 4
  * i.e. each 16-byte group holds E consecutive dimensions of one token for K,
  * and E tokens of one dimension for V, arranged so that a 64-lane wavefront
  * reading one 16-byte group per lane receives matrix-core operand fragments
- * directly.  P must be a multiple of TB (fp32: 16, bf16: 32, fp8 and int8: 64).
+ * directly.  P must be a multiple of TB (fp32: 16, bf16: 32, fp8 and int8: 64,
+ * int4: 128); an int4 cache needs D = 128.
  * ---------------------------------------------------------------------------
  */
 #ifndef PKV_H
@@ -70,7 +74,7 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2, PKV_INT8 = 3 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2, PKV_INT8 = 3, PKV_INT4 = 4 } pkv_dtype;
 
 /* Return codes.  0 is success; every failure is negative and leaves all device
  * memory untouched (arguments are checked before anything is launched). */
@@ -160,6 +164,18 @@ int pkv_kv_append_int8(const void* k_new, const void* v_new, pkv_dtype new_dtype
                        int num_pages, int num_kv_heads, int head_dim, int page_size,
                        void* stream);
 
+/* kv_append_int4 - pkv_kv_append_fp8 for a symmetric int4 cache: QMAX = 7,
+ * a later row keeps the page scale while a / s0 <= 7.5, enc(y) = y rounded to
+ * the nearest integer (ties to even) and clamped to [-7, 7], stored as a
+ * nibble.  The same solosoft.dev FAQ and figures list INT4 beside INT8.
+ * Same arguments, contract and errors as pkv_kv_append_fp8 (D = 128). */
+int pkv_kv_append_int4(const void* k_new, const void* v_new, pkv_dtype new_dtype,
+                       const int32_t* block_tables, int max_pages_per_seq,
+                       const int32_t* seq_lens, int batch,
+                       void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                       int num_pages, int num_kv_heads, int head_dim, int page_size,
+                       void* stream);
+
 /* Bytes of scratch that pkv_paged_attn_decode / pkv_paged_attn_decode_fp8 need
  * for these sizes on the current HIP device (0 if the sizes are invalid).
  * The workspace holds split-KV partial results (per-head running max, sum and
@@ -234,9 +250,24 @@ int pkv_paged_attn_decode_int8(const void* q, pkv_dtype q_dtype,
                                void* out, pkv_dtype out_dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_attn_decode_int4 - as pkv_paged_attn_decode_fp8 for a symmetric int4
+ * cache (D = 128, P a multiple of 128).  Codes n widen to bf16 as 136 + n
+ * exactly (an integer bit pattern, no conversion); 136 * (sum of q) is taken
+ * back out of each logit and 136 * (sum of the probabilities, as the products
+ * see them) out of each output.  Same sizes and errors as the fp8 entry. */
+int pkv_paged_attn_decode_int4(const void* q, pkv_dtype q_dtype,
+                               const void* k_pool, const void* v_pool,
+                               const float* k_scales, const float* v_scales,
+                               const int32_t* block_tables, int max_pages_per_seq,
+                               const int32_t* seq_lens, int batch, int num_pages,
+                               int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                               float scale, int partition_tokens,
+                               void* out, pkv_dtype out_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* decode_step - one whole decode iteration of the cache for one layer: the
  * append of pkv_kv_append followed by the attention of pkv_paged_attn_decode
- * (or of pkv_paged_attn_decode_fp8 / _int8 when kv_dtype is FP8_E4M3 / INT8),
+ * (or of pkv_paged_attn_decode_fp8 / _int8 / _int4 for those cache types),
  * with no launch of its own for the append.
  *
  * The first page's "runtime execution model" has each iteration's attention
@@ -246,8 +277,9 @@ int pkv_paged_attn_decode_int8(const void* q, pkv_dtype q_dtype,
  * slot's old contents, and the merge kernel, which runs after it on the
  * stream, stores them into the page slot.  Results equal pkv_kv_append then decode with the same
  * seq_lens (the pool bytes exactly; out up to the rounding order).
- * k_scales / v_scales: required for FP8_E4M3 and INT8 (k_new / v_new are then
- * bytes already quantised with that page's scale), ignored otherwise.
+ * k_scales / v_scales: required for FP8_E4M3, INT8 and INT4 (k_new / v_new are
+ * then already quantised with that page's scale; int4 rows packed), ignored
+ * otherwise.
  * Same sizes, dtypes, workspace and errors as the decode entry points, plus
  * PKV_E_NULL for a NULL k_new / v_new.  A sequence whose slot L_b - 1 lies on
  * a bad page id stores nothing and gets NaN rows. */

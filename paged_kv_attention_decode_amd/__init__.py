@@ -11,8 +11,8 @@ import ctypes
 
 from ._native import NativeLibraryMissing, lib  # noqa: F401
 
-F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
-_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "i8": INT8}
+F32, BF16, FP8_E4M3, INT8, INT4 = 0, 1, 2, 3, 4
+_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "i8": INT8, "i4": INT4}
 
 
 class PkvError(RuntimeError):
@@ -66,6 +66,18 @@ def kv_append_fp8(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_poo
         _stream(stream)))
 
 
+def kv_append_int4(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool, k_scales, v_scales,
+                   num_kv_heads, head_dim, page_size, stream=None):
+    """As kv_append_fp8 for a symmetric int4 cache (page scales amax / 7, two codes
+    per byte)."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("kv_append_int4", lib().pkv_kv_append_int4(
+        _ptr(k_new), _ptr(v_new), _code(new_dtype), _ptr(block_tables), MP, _ptr(seq_lens), B,
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), NP, num_kv_heads, head_dim, page_size,
+        _stream(stream)))
+
+
 def kv_append_int8(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool, k_scales, v_scales,
                    num_kv_heads, head_dim, page_size, stream=None):
     """As kv_append_fp8 for a symmetric int8 cache (page scales amax / 127)."""
@@ -101,6 +113,19 @@ def paged_attn_decode_fp8(q, q_dtype, k_pool, v_pool, k_scales, v_scales, block_
     B, MP = block_tables.shape
     NP = k_pool.shape[0]
     _check("paged_attn_decode_fp8", lib().pkv_paged_attn_decode_fp8(
+        _ptr(q), _code(q_dtype), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), MP, _ptr(seq_lens), B, NP, num_q_heads, num_kv_heads, head_dim,
+        page_size, float(scale), int(partition_tokens), _ptr(out), _code(out_dtype), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def paged_attn_decode_int4(q, q_dtype, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                           num_q_heads, num_kv_heads, head_dim, page_size, scale, out, out_dtype,
+                           workspace, partition_tokens=0, stream=None):
+    """As paged_attn_decode for a symmetric int4 cache with per-(page, kv head) scales."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("paged_attn_decode_int4", lib().pkv_paged_attn_decode_int4(
         _ptr(q), _code(q_dtype), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),
         _ptr(block_tables), MP, _ptr(seq_lens), B, NP, num_q_heads, num_kv_heads, head_dim,
         page_size, float(scale), int(partition_tokens), _ptr(out), _code(out_dtype), _ptr(workspace),

@@ -12,12 +12,15 @@ SIGNATURES = {
     "pkv_kv_append": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp]),
     "pkv_kv_append_fp8": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "pkv_kv_append_int8": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "pkv_kv_append_int4": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "pkv_paged_attn_decode": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i,
                                    _f, _i, _vp, _i, _vp, _sz, _vp]),
     "pkv_paged_attn_decode_fp8": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i,
                                        _i, _i, _f, _i, _vp, _i, _vp, _sz, _vp]),
     "pkv_paged_attn_decode_int8": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i,
+                                        _i, _i, _f, _i, _vp, _i, _vp, _sz, _vp]),
+    "pkv_paged_attn_decode_int4": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i,
                                         _i, _i, _f, _i, _vp, _i, _vp, _sz, _vp]),
     "pkv_decode_step": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i,
                              _i, _f, _i, _vp, _i, _vp, _sz, _vp]),

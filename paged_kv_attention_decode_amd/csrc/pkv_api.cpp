@@ -40,9 +40,11 @@ int check_align(std::initializer_list<const void*> ptrs) {
   return PKV_OK;
 }
 
-bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3 || d == PKV_INT8; }
-// One-byte formats carry per-(page, kv head) scales.
-bool scaled_dtype(int d) { return d == PKV_FP8_E4M3 || d == PKV_INT8; }
+bool valid_dtype(int d) {
+  return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3 || d == PKV_INT8 || d == PKV_INT4;
+}
+// Formats of one byte or less carry per-(page, kv head) scales.
+bool scaled_dtype(int d) { return d == PKV_FP8_E4M3 || d == PKV_INT8 || d == PKV_INT4; }
 
 // Shared size checks for every entry point that reads the pools.
 int check_pool_shape(int kv_dtype, int max_pages, int batch, int num_pages, int num_kv_heads,
@@ -54,6 +56,8 @@ int check_pool_shape(int kv_dtype, int max_pages, int batch, int num_pages, int 
                 max_pages, num_pages, num_kv_heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_E_SHAPE, "head_dim %d not supported (64 or 128)", head_dim);
+  if (kv_dtype == PKV_INT4 && head_dim != 128)
+    return fail(PKV_E_SHAPE, "int4 cache: head_dim %d not supported (128)", head_dim);
   const int tb = pkv::v_block_tokens(kv_dtype);
   if (page_size <= 0 || page_size > 1024 || page_size % tb)
     return fail(PKV_E_SHAPE, "page_size %d must be a positive multiple of %d and <= 1024", page_size, tb);
@@ -221,6 +225,14 @@ int pkv_kv_append_int8(const void* k_new, const void* v_new, pkv_dtype new_dtype
                       k_pool, v_pool, k_scales, v_scales, num_pages, num_kv_heads, head_dim, page_size, stream);
 }
 
+int pkv_kv_append_int4(const void* k_new, const void* v_new, pkv_dtype new_dtype, const int32_t* block_tables,
+                       int max_pages_per_seq, const int32_t* seq_lens, int batch, void* k_pool, void* v_pool,
+                       float* k_scales, float* v_scales, int num_pages, int num_kv_heads, int head_dim,
+                       int page_size, void* stream) {
+  return append_quant(PKV_INT4, k_new, v_new, new_dtype, block_tables, max_pages_per_seq, seq_lens, batch,
+                      k_pool, v_pool, k_scales, v_scales, num_pages, num_kv_heads, head_dim, page_size, stream);
+}
+
 int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
                           pkv_dtype kv_dtype, const int32_t* block_tables, int max_pages_per_seq,
                           const int32_t* seq_lens, int batch, int num_pages, int num_q_heads,
@@ -229,7 +241,7 @@ int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype, const void* k_pool, 
                           size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (scaled_dtype(kv_dtype))
-    return fail(PKV_E_DTYPE, "fp8 / int8 cache: use pkv_paged_attn_decode_fp8 / _int8 (they carry the scales)");
+    return fail(PKV_E_DTYPE, "fp8 / int8 / int4 cache: use the _fp8 / _int8 / _int4 entry (they carry the scales)");
   return run_decode(q, q_dtype, k_pool, v_pool, kv_dtype, nullptr, nullptr, block_tables, max_pages_per_seq,
                     seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
                     partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
@@ -246,6 +258,19 @@ int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype, const void* k_po
   return run_decode(q, q_dtype, k_pool, v_pool, PKV_FP8_E4M3, k_scales, v_scales, block_tables,
                     max_pages_per_seq, seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim,
                     page_size, scale, partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_int4(const void* q, pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
+                               const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                               int max_pages_per_seq, const int32_t* seq_lens, int batch, int num_pages,
+                               int num_q_heads, int num_kv_heads, int head_dim, int page_size, float scale,
+                               int partition_tokens, void* out, pkv_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "int4 scales are NULL");
+  return run_decode(q, q_dtype, k_pool, v_pool, PKV_INT4, k_scales, v_scales, block_tables, max_pages_per_seq,
+                    seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
+                    partition_tokens, out, out_dtype, workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_attn_decode_int8(const void* q, pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
@@ -274,7 +299,7 @@ int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const v
     if (rc) return rc;
   }
   if (scaled_dtype(kv_dtype)) {
-    if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 / int8 scales are NULL");
+    if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 / int8 / int4 scales are NULL");
   } else {
     k_scales = v_scales = nullptr;
   }

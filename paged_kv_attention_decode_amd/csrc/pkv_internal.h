@@ -8,11 +8,11 @@
 
 namespace pkv {
 
-enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_INT8 = 3 };
+enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_INT8 = 3, KV_INT4 = 4 };
 
-// Tokens per 16-byte V group block (and per decode step): 4 * (16 / element bytes).
-inline int v_block_tokens(int kvt) { return kvt == KV_F32 ? 16 : kvt == KV_BF16 ? 32 : 64; }
-inline int elem_bytes(int kvt) { return kvt == KV_F32 ? 4 : kvt == KV_BF16 ? 2 : 1; }
+inline int elem_bits(int kvt) { return kvt == KV_F32 ? 32 : kvt == KV_BF16 ? 16 : kvt == KV_INT4 ? 4 : 8; }
+// Tokens per V block (and per decode step): 4 * E, E = elements per 16-byte group.
+inline int v_block_tokens(int kvt) { return 4 * (128 / elem_bits(kvt)); }
 
 // Upper bound on decode wavefronts per compute unit; sizes the partial-result
 // workspace together with the device's compute-unit count.
@@ -27,7 +27,7 @@ inline size_t partials_bytes(int cus, int G, int D) {
 struct AppendQuantArgs {
   const void* k_new;
   const void* v_new;
-  int kvt;                  // KV_FP8 or KV_INT8: the one-byte format written
+  int kvt;                  // KV_FP8, KV_INT8 or KV_INT4: the format written
   bool new_bf16;            // rows are bf16 (else fp32)
   const int32_t* block_tables;
   const int32_t* seq_lens;

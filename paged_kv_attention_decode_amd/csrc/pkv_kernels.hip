@@ -48,11 +48,40 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// Element width in bits; elem_t is the storage word of one element (int4: a
+// byte holding two, the even element in the low nibble).
 template <int KVT> struct Kv;
-template <> struct Kv<KV_F32> { static constexpr int EB = 4; typedef uint32_t elem_t; };
-template <> struct Kv<KV_BF16> { static constexpr int EB = 2; typedef uint16_t elem_t; };
-template <> struct Kv<KV_FP8> { static constexpr int EB = 1; typedef uint8_t elem_t; };
-template <> struct Kv<KV_INT8> { static constexpr int EB = 1; typedef uint8_t elem_t; };
+template <> struct Kv<KV_F32> { static constexpr int BITS = 32; typedef uint32_t elem_t; };
+template <> struct Kv<KV_BF16> { static constexpr int BITS = 16; typedef uint16_t elem_t; };
+template <> struct Kv<KV_FP8> { static constexpr int BITS = 8; typedef uint8_t elem_t; };
+template <> struct Kv<KV_INT8> { static constexpr int BITS = 8; typedef uint8_t elem_t; };
+template <> struct Kv<KV_INT4> { static constexpr int BITS = 4; typedef uint8_t elem_t; };
+// Byte offset of element index x (element indices of int4 chunks are even
+// wherever a whole byte is addressed).
+template <int KVT>
+__device__ __forceinline__ size_t elem_byte(size_t x) { return x * Kv<KVT>::BITS / 8; }
+// Element x of an array of stored elements, as its code (int4: the nibble).
+template <int KVT>
+__device__ __forceinline__ uint32_t get_code(const void* base, size_t x) {
+  typedef typename Kv<KVT>::elem_t T;
+  if constexpr (Kv<KVT>::BITS == 4)
+    return ((uint32_t)static_cast<const uint8_t*>(base)[x >> 1] >> (4 * (x & 1))) & 0xFu;
+  else
+    return static_cast<const T*>(base)[x];
+}
+// Store element x (int4: read-modify-write of its byte; no other thread may
+// write the same byte concurrently).
+template <int KVT>
+__device__ __forceinline__ void put_code(void* base, size_t x, uint32_t c) {
+  typedef typename Kv<KVT>::elem_t T;
+  if constexpr (Kv<KVT>::BITS == 4) {
+    uint8_t* p = static_cast<uint8_t*>(base) + (x >> 1);
+    const int sh = 4 * (int)(x & 1);
+    *p = (uint8_t)((*p & ~(0xF << sh)) | ((c & 0xFu) << sh));
+  } else {
+    static_cast<T*>(base)[x] = (T)c;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Chunk addressing shared by every kernel.  A (page, kv head) chunk holds P
@@ -116,6 +145,11 @@ __device__ __forceinline__ u32x2_t split_pair(float a, float b) {
   const float rb = b - fbits(ubits(b) & 0xffff0000u);
   return u32x2_t{pack_hi16(a, b), pack_hi16(ra, rb)};
 }
+// As split_probs, and adds to sum the exact value hi + lo of all eight.
+__device__ __forceinline__ float split_sum(float a) {
+  const float hi = fbits(ubits(a) & 0xffff0000u);
+  return hi + fbits(ubits(a - hi) & 0xffff0000u);
+}
 // Probabilities of two 16-token tiles (8 per lane) as hi and lo bf16x8 operands.
 __device__ __forceinline__ void split_probs(const float (&x)[4], const float (&y)[4], float mul,
                                            u32x4_t& hi, u32x4_t& lo) {
@@ -141,6 +175,23 @@ __device__ __forceinline__ u32x2_t i8x4_to_bf16x4(uint32_t w) {
   const float c = (float)(int8_t)(w >> 16), d = (float)((int32_t)w >> 24);
   return u32x2_t{pack_hi16(a, b), pack_hi16(c, d)};
 }
+// Eight int4 codes (one word, element 2i in the low nibble of byte i) -> a
+// bf16x8 operand holding 136 + n for each code n in [-8, 7]: with u = n + 8,
+// the bf16 pattern 0x4300 | u is exactly 128 + u.  Each pair of elements
+// (byte i) goes into one word with two integer instructions.  Products against
+// this operand carry 136 * (sum of the other operand), which callers subtract.
+__device__ __forceinline__ u32x4_t nib8_to_bf16x8(uint32_t w) {
+  const uint32_t u = w ^ 0x88888888u;
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = (u >> (8 * i)) & 0xFFu;        // (u_2i, u_2i+1)
+    r[i] = ((b | (b << 12)) & 0x000F000Fu) | 0x43004300u;
+  }
+  return r;
+}
+constexpr float INT4_BIAS = 136.f;
+
 // Eight one-byte cache elements (fp8 e4m3 or int8) -> a bf16x8 MFMA operand.
 template <int KVT>
 __device__ __forceinline__ u32x4_t byte8_to_bf16x8(uint32_t w0, uint32_t w1) {
@@ -282,14 +333,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens, void* __restrict__ out_,
     float* __restrict__ partials, int4* __restrict__ descs, int B, int MP, int NP, int Hq, int Hkv,
     int G, int P, int PT, int Wmax, float scale_log2) {
-  constexpr int EB = Kv<KVT>::EB;
-  constexpr int E = 16 / EB;        // elements per 16-byte group
+  constexpr int BITS = Kv<KVT>::BITS;
+  constexpr int E = 128 / BITS;     // elements per 16-byte group
   constexpr int TS = 4 * E;         // tokens per step (= V block)
   constexpr int NSUB = TS / 16;     // 16-token QK^T tiles per step
   constexpr int NKK = D / (4 * E);  // K groups per lane per 16-token tile
   constexpr int NDT = D / 16;       // 16-dim PV tiles
-  constexpr bool BYTE = EB == 1;       // fp8 or int8 cache: scaled, widened to bf16
-  constexpr int NQ = BYTE ? 2 * NKK : NKK;
+  constexpr bool I4 = KVT == KV_INT4;
+  constexpr bool SCALED = BITS <= 8;   // fp8, int8, int4: per-page scales, widened to bf16
+  constexpr int NCH = I4 ? 4 : SCALED ? 2 : 1;   // bf16x8 operands per 16-byte group
+  constexpr int NQ = NCH * NKK;
+  static_assert(NKK >= 1, "head_dim too small for this element width");
 
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, c4 = lane >> 4;
@@ -297,7 +351,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int wv = uniform(threadIdx.x >> 6);
   const int w = uniform(blockIdx.x * 4 + wv);
   // per-wave LDS slots: the step entry's new K and V rows, the query operand
-  __shared__ __attribute__((aligned(16))) uint8_t s_new[4][2 * D * Kv<KVT>::EB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_new[4][2 * D * BITS / 8];
   __shared__ u32x4_t s_q[4][NQ][64];
 
   // ---- this wave's unit range -------------------------------------------------
@@ -419,9 +473,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       const uint16_t* q = static_cast<const uint16_t*>(q_) + ((size_t)b * Hq + h) * D;
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
-        // bf16 cache: group kk covers dims 8*(c4+4kk) .. +8.
-        // fp8 cache: group kk covers dims 16*(c4+4kk) .. +16, split in two halves.
-        const int d0 = KVT == KV_BF16 ? 8 * (c4 + 4 * i) : 16 * (c4 + 4 * (i >> 1)) + 8 * (i & 1);
+        // group kk covers dims E*(c4+4kk) .. +E, taken 8 at a time (one bf16x8
+        // operand per chunk; E = 8 for bf16, 16 for fp8 / int8, 32 for int4).
+        const int d0 = E * (c4 + 4 * (i / NCH)) + 8 * (i % NCH);
         qv_ld[i] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + d0)) : u32x4_t{0, 0, 0, 0};
       }
     }
@@ -430,10 +484,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // step entry: the segment that ends the sequence reads the new token row;
     // it is parked in this wave's LDS slot once the first tile's loads are out.
     const bool has_new = k_new != nullptr && tok1 == Lb;
-    constexpr int NEWCH = D * EB / 16;              // 16-byte chunks per K (or V) row
+    constexpr int NEWCH = D * BITS / 128;           // 16-byte chunks per K (or V) row
     u32x4_t new_chunk = {0, 0, 0, 0};
     if (has_new && lane < 2 * NEWCH) {
-      const size_t nrow = (((size_t)b * Hkv + g) * D) * EB;
+      const size_t nrow = elem_byte<KVT>(((size_t)b * Hkv + g) * D);
       const uint8_t* src = lane < NEWCH ? static_cast<const uint8_t*>(k_new) + nrow
                                         : static_cast<const uint8_t*>(v_new) + nrow - NEWCH * 16;
       new_chunk = ld16(src + lane * 16);
@@ -443,6 +497,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = NEG_INF, l = 0.f;
+    // int4: the widened operands are 136 + n; lp accumulates, like l, the sum
+    // of the probabilities exactly as the PV products see them, and qsum is the
+    // head's sum of query values, so that the bias comes back out exactly.
+    float lp = 0.f, qsum = 0.f;
+    if constexpr (I4) {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          qsum += fbits(qv_ld[i][x] << 16) + fbits(qv_ld[i][x] & 0xffff0000u);
+      qsum += __shfl_xor(qsum, 16);
+      qsum += __shfl_xor(qsum, 32);
+    }
 
     // Loop state is wave-uniform; readfirstlane lets the compiler keep it in
     // scalar registers, so page ids come from scalar loads (lgkmcnt) that do
@@ -460,18 +527,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // An invalid page id marks the segment bad (NaN result); page 0 is read instead.
     u32x4_t kr[NSUB][NKK], vr[NDT];
     auto load_k = [&](int pg, int j) {
-      const uint8_t* kc = kpool + chunk_elem(pg, g, Hkv, P, D) * EB;
+      const uint8_t* kc = kpool + elem_byte<KVT>(chunk_elem(pg, g, Hkv, P, D));
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
-          kr[sub][kk] = ld16_stream(kc + (uint32_t)(k_elem<E>(j + 16 * sub + r16, (c4 + 4 * kk) * E, P) * EB));
+          kr[sub][kk] = ld16_stream(kc + (uint32_t)elem_byte<KVT>(k_elem<E>(j + 16 * sub + r16, (c4 + 4 * kk) * E, P)));
     };
     auto load_v = [&](int pg, int j) {
-      const uint8_t* vc = vpool + chunk_elem(pg, g, Hkv, P, D) * EB;
+      const uint8_t* vc = vpool + elem_byte<KVT>(chunk_elem(pg, g, Hkv, P, D));
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        vr[dt] = ld16_stream(vc + (uint32_t)(v_elem<E>(j + 4 * c4, dt * 16 + r16, D) * EB));
+        vr[dt] = ld16_stream(vc + (uint32_t)elem_byte<KVT>(v_elem<E>(j + 4 * c4, dt * 16 + r16, D)));
     };
     int page = page_of(pgi);
     // step entry: the wave that writes (b, g)'s descriptor also looks up the
@@ -481,7 +548,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     bool bad = (unsigned)page >= (unsigned)NP;
     int pg_ld = bad ? 0 : page;
     float ksc = 1.f, vsc = 1.f;
-    if constexpr (BYTE) {
+    if constexpr (SCALED) {
       ksc = kscales[(size_t)pg_ld * Hkv + g];
       vsc = vscales[(size_t)pg_ld * Hkv + g];
     }
@@ -534,12 +601,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             }
           }
           if (c4 == c_t) {
-            const int kw = (e_t * EB) >> 2, sh = ((e_t * EB) & 3) * 8;
-            const uint32_t msk = (uint32_t)((1ull << (8 * EB)) - 1ull) << sh;
+            const int kw = (e_t * BITS) >> 5, sh = (e_t * BITS) & 31;
+            const uint32_t msk = (uint32_t)((1ull << BITS) - 1ull) << sh;
             const T* vrow = reinterpret_cast<const T*>(s_new[wv] + NEWCH * 16);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-              const uint32_t bits = (uint32_t)vrow[dt * 16 + r16] << sh;
+              const int dd = dt * 16 + r16;
+              const uint32_t code = I4 ? ((uint32_t)vrow[dd >> 1] >> (4 * (dd & 1))) & 0xFu : (uint32_t)vrow[dd];
+              const uint32_t bits = code << sh;
 #pragma unroll
               for (int x = 0; x < 4; ++x) {
                 const uint32_t mx = x == kw ? msk : 0u;
@@ -565,17 +634,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             }
           } else if constexpr (KVT == KV_BF16) {
             acc = mfma_bf16(kr[sub][kk], qop(kk), acc);
+          } else if constexpr (I4) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc = mfma_bf16(nib8_to_bf16x8(kr[sub][kk][c]), qop(4 * kk + c), acc);
           } else {
             acc = mfma_bf16(byte8_to_bf16x8<KVT>(kr[sub][kk][0], kr[sub][kk][1]), qop(2 * kk), acc);
             acc = mfma_bf16(byte8_to_bf16x8<KVT>(kr[sub][kk][2], kr[sub][kk][3]), qop(2 * kk + 1), acc);
           }
+        }
+        if constexpr (I4) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] -= INT4_BIAS * qsum;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[sub][i] = acc[i] * kmul;
       }
       if constexpr (!LAST) {
         load_k(pg_ld_n, j_n);
-        if constexpr (BYTE) {
+        if constexpr (SCALED) {
           ksc = kscales[(size_t)pg_ld_n * Hkv + g];
           vsc = vscales[(size_t)pg_ld_n * Hkv + g];
         }
@@ -589,15 +665,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               if (t + 16 * sub + 4 * c4 + i >= tok1) s[sub][i] = NEG_INF;
+          // per element of the lane's V group (element e holds token
+          // 16 * (e / 4) + 4 * c4 + e % 4 of the step)
           u32x4_t keep;
+          constexpr int FIELD = BITS < 8 ? BITS : 8;     // mask granularity: bytes, or nibbles
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             uint32_t msk = 0;
 #pragma unroll
-            for (int byte = 0; byte < 4; ++byte) {
-              const int e = (4 * k + byte) / EB;
+            for (int f = 0; f < 32 / FIELD; ++f) {
+              const int e = (32 * k + FIELD * f) / BITS;
               const int tok = t + 16 * (e >> 2) + 4 * c4 + (e & 3);
-              if (tok < tok1) msk |= 0xffu << (8 * byte);
+              if (tok < tok1) msk |= ((1u << FIELD) - 1u) << (FIELD * f);
             }
             keep[k] = msk;
           }
@@ -626,6 +705,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
           lsum += p[sub][i];
         }
       l = l * alpha + lsum;
+      if constexpr (I4) lp *= alpha;
       if (__ballot(mnew > m)) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
@@ -645,6 +725,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         for (int dt = 0; dt < NDT; ++dt) {
           O[dt] = mfma_bf16(vr[dt], ph, O[dt]);
           O[dt] = mfma_bf16(vr[dt], pl, O[dt]);
+        }
+      } else if constexpr (I4) {
+        u32x4_t ph[4], pl[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          split_probs(p[2 * c], p[2 * c + 1], vmul, ph[c], pl[c]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lp += split_sum(p[2 * c][i] * vmul) + split_sum(p[2 * c + 1][i] * vmul);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const u32x4_t a = nib8_to_bf16x8(vr[dt][c]);
+            O[dt] = mfma_bf16(a, ph[c], O[dt]);
+            O[dt] = mfma_bf16(a, pl[c], O[dt]);
+          }
         }
       } else {
         u32x4_t ph[2], pl[2];
@@ -676,6 +773,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // ---- finish the segment ------------------------------------------------------
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
+    if constexpr (I4) {
+      float lpt = lp + __shfl_xor(lp, 16);
+      lpt += __shfl_xor(lpt, 32);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) O[dt] -= INT4_BIAS * lpt;
+    }
     const float qnan = __builtin_nanf("");
     if (complete) {
       if (hv) {
@@ -730,8 +833,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int4* __restrict__ descs, const float* __restrict__ partials, void* __restrict__ out_, int B,
     int Hq, int Hkv, int G, int D, int nchunk, const void* __restrict__ k_new, const void* __restrict__ v_new,
     void* __restrict__ kpool, void* __restrict__ vpool, int NP, int P) {
-  typedef typename Kv<KVT>::elem_t T;
-  constexpr int EB = Kv<KVT>::EB, E = 16 / EB;
+  constexpr int E = 128 / Kv<KVT>::BITS;
   // wave-uniform (the compiler cannot tell that threadIdx.x >> 6 is)
   const int wi = uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int bg = wi / nchunk, chunk = wi - bg * nchunk;
@@ -748,9 +850,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   u32x4_t kgrp = {0, 0, 0, 0};
   uint32_t vv[2] = {0, 0};                // one element each, kept unpacked
   if (app) {
-    kgrp = ld16(static_cast<const uint8_t*>(k_new) + (nrow + (size_t)min(lane, ngrp - 1) * E) * EB);
+    kgrp = ld16(static_cast<const uint8_t*>(k_new) + elem_byte<KVT>(nrow + (size_t)min(lane, ngrp - 1) * E));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) vv[i] = static_cast<const T*>(v_new)[nrow + min(lane + 64 * i, D - 1)];
+    for (int i = 0; i < 2; ++i) vv[i] = get_code<KVT>(v_new, nrow + min(lane + 64 * i, D - 1));
   }
   // descriptor of (b, g), written by the split kernel in this call: first
   // contributing wave, contributors, slot of the first, sequence length
@@ -768,11 +870,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int j = (L - 1) % P;
     const size_t ch = chunk_elem(d.z, g, Hkv, P, D);
     if (lane < ngrp)
-      *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(kpool) + (ch + k_elem<E>(j, lane * E, P)) * EB) = kgrp;
+      *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(kpool) + elem_byte<KVT>(ch + k_elem<E>(j, lane * E, P))) = kgrp;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i) {                 // each dim's V element lies in its own byte
       const int dd = lane + 64 * i;
-      if (dd < D) static_cast<T*>(vpool)[ch + v_elem<E>(j, dd, D)] = (T)vv[i];
+      if (dd < D) put_code<KVT>(vpool, ch + v_elem<E>(j, dd, D), vv[i]);
     }
   }
 }
@@ -785,8 +887,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
     void* __restrict__ kpool, void* __restrict__ vpool, int MP, int NP, int Hkv, int D, int P) {
-  typedef typename Kv<KVT>::elem_t T;
-  constexpr int E = 16 / Kv<KVT>::EB;
+  constexpr int E = 128 / Kv<KVT>::BITS;
   const int b = blockIdx.x;
   const int L = seq_lens[b];
   if (L <= 0) return;
@@ -794,13 +895,18 @@ __global__ __launch_bounds__(256) void append_kernel(
   if (pgi >= MP) return;
   const int page = bt[(size_t)b * MP + pgi];
   if ((unsigned)page >= (unsigned)NP) return;
-  const T* kn = static_cast<const T*>(k_new) + (size_t)b * Hkv * D;
-  const T* vn = static_cast<const T*>(v_new) + (size_t)b * Hkv * D;
-  for (int x = threadIdx.x; x < Hkv * D; x += blockDim.x) {
+  // Each thread copies a pair of dims (d even): an int4 K pair is one byte of
+  // the pool, and its V elements lie in two different bytes, so no byte is
+  // written by two threads.
+  const size_t row0 = (size_t)b * Hkv * D;
+  for (int x = 2 * threadIdx.x; x < Hkv * D; x += 2 * blockDim.x) {
     const int g = x / D, d = x - g * D;
     const size_t ch = chunk_elem(page, g, Hkv, P, D);
-    static_cast<T*>(kpool)[ch + k_elem<E>(j, d, P)] = kn[x];
-    static_cast<T*>(vpool)[ch + v_elem<E>(j, d, D)] = vn[x];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      put_code<KVT>(kpool, ch + k_elem<E>(j, d + i, P), get_code<KVT>(k_new, row0 + x + i));
+      put_code<KVT>(vpool, ch + v_elem<E>(j, d + i, D), get_code<KVT>(v_new, row0 + x + i));
+    }
   }
 }
 
@@ -857,17 +963,36 @@ template <> struct ByteFmt<KV_INT8> {
     for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(uint8_t)(w >> (8 * i));
   }
 };
+// int4: codes are two's complement nibbles; symmetric, clamped to +-7.
+template <> struct ByteFmt<KV_INT4> {
+  static constexpr float QMAX = 7.f, NOCLIP = 7.5f;
+  __device__ static uint32_t enc(float y) {
+    const float r = fminf(fmaxf(rintf(y), -7.f), 7.f);
+    return (uint32_t)(int)r & 0xFu;
+  }
+  __device__ static float dec(uint32_t c) { return (float)(int)((c & 0xFu) ^ 8u) - 8.f; }
+};
 
-// Four bytes of a word re-encoded under a new scale: enc((dec(byte) * s0) / s).
+// One element re-encoded under a new scale: enc((dec(code) * s0) / s), the
+// product and the quotient each rounded once.
+template <int KVT>
+__device__ __forceinline__ uint32_t requant1(float v, float s0, float s) {
+  const float real = v * s0;
+  return ByteFmt<KVT>::enc(real / s);
+}
+// Four bytes of a word re-encoded (int4: both nibbles of each byte).
 template <int KVT>
 __device__ __forceinline__ uint32_t requant4(uint32_t w, float s0, float s) {
-  float v[4];
-  ByteFmt<KVT>::dec4(w, v);
   uint32_t r = 0;
+  if constexpr (KVT == KV_INT4) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float real = v[i] * s0;        // rounded product, then a rounded quotient
-    r |= ByteFmt<KVT>::enc(real / s) << (8 * i);
+    for (int i = 0; i < 8; ++i)
+      r |= requant1<KVT>(ByteFmt<KVT>::dec(w >> (4 * i)), s0, s) << (4 * i);
+  } else {
+    float v[4];
+    ByteFmt<KVT>::dec4(w, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r |= requant1<KVT>(v[i], s0, s) << (8 * i);
   }
   return r;
 }
@@ -897,10 +1022,11 @@ __device__ __forceinline__ uint32_t lut4(const uint8_t* lut, uint32_t w) {
 // Re-encode slots [0, j) of a K chunk: 16-byte groups (16 dims of one token).
 // Each lane issues the loads of up to 16 groups before converting any, so a
 // page costs about one memory round trip per 1024 groups.
-template <int D>
+template <int KVT, int D>
 __device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uint8_t* lut, int lane) {
   constexpr int GPL = 16;
-  const int ngrp = (D / 16) * j;
+  constexpr int GPT = D * Kv<KVT>::BITS / 128;       // 16-byte groups per token
+  const int ngrp = GPT * j;
   for (int base = 0; base < ngrp; base += 64 * GPL) {
     u32x4_t w[GPL];
     int off[GPL];
@@ -923,14 +1049,15 @@ __device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uin
   }
 }
 
-// Re-encode a V chunk for a scale change at slot j: a 16-byte group holds 16
-// tokens of one dim from one 64-token block; blocks 0 .. j/64 are rewritten
-// group by group: tokens < j re-encoded, token j takes its new byte (nbj, from
-// LDS), later slots keep their bytes.
-template <int D>
+// Re-encode a V chunk for a scale change at slot j: a 16-byte group holds E
+// tokens of one dim from one TB = 4E token block; blocks 0 .. j/TB are
+// rewritten group by group: tokens < j re-encoded, token j takes its new code
+// (nbj, from LDS), later slots keep theirs.
+template <int KVT, int D>
 __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* lut, const uint8_t* nbj,
                                           int lane) {
-  constexpr int GPL = 16, TB = 64;
+  constexpr int BITS = Kv<KVT>::BITS, E = 128 / BITS;
+  constexpr int GPL = 16, TB = 4 * E, BLK = TB * D * BITS / 8;   // bytes per V block
   const int ngrp = (j / TB + 1) * 4 * D;
   for (int base = 0; base < ngrp; base += 64 * GPL) {
     u32x4_t w[GPL];
@@ -938,7 +1065,7 @@ __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* l
     for (int i = 0; i < GPL; ++i) {
       const int gi = min(base + lane + 64 * i, ngrp - 1);
       const int blk = gi / (4 * D), rem = gi - blk * 4 * D;
-      w[i] = *reinterpret_cast<const u32x4_t*>(pool + (size_t)blk * TB * D + (size_t)rem * 16);
+      w[i] = *reinterpret_cast<const u32x4_t*>(pool + (size_t)blk * BLK + (size_t)rem * 16);
     }
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
@@ -952,17 +1079,20 @@ __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* l
         for (int q = 0; q < 4; ++q) {
           const uint32_t re = lut4(lut, w[i][q]);
           uint32_t outw = 0;
+          constexpr int PW = 32 / BITS;                  // elements per word
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // byte 4q + e of the group holds token 16q + 4c + e of block blk
-            const int tok = blk * TB + 16 * q + 4 * c + e;
-            const uint32_t byte = tok < j ? (re >> (8 * e)) & 0xFFu
-                                : tok == j ? fresh : (w[i][q] >> (8 * e)) & 0xFFu;
-            outw |= byte << (8 * e);
+          for (int x = 0; x < PW; ++x) {
+            // element e of the group holds token 16 * (e / 4) + 4c + e % 4 of block blk
+            const int e = PW * q + x;
+            const int tok = blk * TB + 16 * (e >> 2) + 4 * c + (e & 3);
+            constexpr uint32_t M = (1u << BITS) - 1u;
+            const uint32_t code = tok < j ? (re >> (BITS * x)) & M
+                                : tok == j ? fresh : (w[i][q] >> (BITS * x)) & M;
+            outw |= code << (BITS * x);
           }
           r[q] = outw;
         }
-        *reinterpret_cast<u32x4_t*>(pool + (size_t)blk * TB * D + (size_t)rem * 16) = r;
+        *reinterpret_cast<u32x4_t*>(pool + (size_t)blk * BLK + (size_t)rem * 16) = r;
       }
     }
   }
@@ -999,7 +1129,7 @@ __global__ __launch_bounds__(256) void append_quant_kernel(
   if (pgi >= MP) return;
   const int pg = uniform(((const_i32_ptr)bt)[(size_t)b * MP + pgi]);
   if ((unsigned)pg >= (unsigned)NP) return;
-  const size_t ch = chunk_elem(pg, g, Hkv, P, D);        // byte offset (1-byte elements)
+  const size_t ch = chunk_elem(pg, g, Hkv, P, D);        // element offset of the chunk
   const size_t si = (size_t)pg * Hkv + g;
   float sk0 = 1.f, sv0 = 1.f;
   if (j > 0) {                           // both scales in one round trip
@@ -1030,8 +1160,8 @@ __global__ __launch_bounds__(256) void append_quant_kernel(
     nbk[i] = ByteFmt<KVT>::enc(xk[i] / sk);
     nbv[i] = ByteFmt<KVT>::enc(xv[i] / sv);
   }
-  uint8_t* kp = kpool + ch;
-  uint8_t* vp = vpool + ch;
+  uint8_t* kp = kpool + elem_byte<KVT>(ch);
+  uint8_t* vp = vpool + elem_byte<KVT>(ch);
   const uint8_t* lutk = reinterpret_cast<const uint8_t*>(s_lut[wv][0]);
   const uint8_t* lutv = reinterpret_cast<const uint8_t*>(s_lut[wv][1]);
   if (rk || rv) {
@@ -1040,11 +1170,14 @@ __global__ __launch_bounds__(256) void append_quant_kernel(
     if (rv) s_lut[wv][1][lane] = requant4<KVT>(codes, sv0, sv);
     __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
   }
-  if (rk) requant_k<D>(kp, j, P, lutk, lane);
-  // the new K token's dims d0.. are consecutive bytes of one group (disjoint
-  // from the re-encoded slots)
-  uint8_t* kt = kp + k_elem<16>(j, d0, P);
-  if (NPL == 2)
+  constexpr int E = 128 / Kv<KVT>::BITS;
+  if (rk) requant_k<KVT, D>(kp, j, P, lutk, lane);
+  // the new K token's dims d0.. are consecutive elements of one group
+  // (disjoint from the re-encoded slots): two bytes, or one int4 byte
+  uint8_t* kt = kp + elem_byte<KVT>(k_elem<E>(j, d0, P));
+  if constexpr (KVT == KV_INT4)
+    *kt = (uint8_t)(nbk[0] | (nbk[NPL - 1] << 4));
+  else if constexpr (NPL == 2)
     *reinterpret_cast<uint16_t*>(kt) = (uint16_t)(nbk[0] | (nbk[NPL - 1] << 8));
   else
     *kt = (uint8_t)nbk[0];
@@ -1052,10 +1185,10 @@ __global__ __launch_bounds__(256) void append_quant_kernel(
 #pragma unroll
     for (int i = 0; i < NPL; ++i) s_nb[wv][d0 + i] = (uint8_t)nbv[i];
     __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
-    requant_v<D>(vp, j, lutv, s_nb[wv], lane);
+    requant_v<KVT, D>(vp, j, lutv, s_nb[wv], lane);
   } else {
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) vp[v_elem<16>(j, d0 + i, D)] = (uint8_t)nbv[i];
+    for (int i = 0; i < NPL; ++i) put_code<KVT>(vp, v_elem<E>(j, d0 + i, D), nbv[i]);   // own bytes
   }
   if (lane == 0) {
     kscales[si] = sk;
@@ -1071,8 +1204,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const void* __restrict__ kpool, const void* __restrict__ vpool,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
     void* __restrict__ k_out, void* __restrict__ v_out, int MP, int NP, int Hkv, int D, int P) {
-  typedef typename Kv<KVT>::elem_t T;
-  constexpr int E = 16 / Kv<KVT>::EB;
+  constexpr int E = 128 / Kv<KVT>::BITS;
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int L = seq_lens[b];
@@ -1085,14 +1217,17 @@ __global__ __launch_bounds__(256) void gather_kernel(
   }
   if (!__syncthreads_and(ok)) return;
   const size_t rows = (size_t)MP * P;
-  T* ko = static_cast<T*>(k_out) + ((size_t)b * Hkv + g) * rows * D;
-  T* vo = static_cast<T*>(v_out) + ((size_t)b * Hkv + g) * rows * D;
-  for (size_t x = threadIdx.x; x < (size_t)L * D; x += blockDim.x) {
+  const size_t o0 = ((size_t)b * Hkv + g) * rows * D;
+  // a pair of dims per thread (one output byte for int4)
+  for (size_t x = 2 * threadIdx.x; x < (size_t)L * D; x += 2 * blockDim.x) {
     const int t = (int)(x / D), d = (int)(x - (size_t)t * D);
     const int pgi = t / P, j = t - pgi * P;
     const size_t ch = chunk_elem(bt[(size_t)b * MP + pgi], g, Hkv, P, D);
-    ko[x] = static_cast<const T*>(kpool)[ch + k_elem<E>(j, d, P)];
-    vo[x] = static_cast<const T*>(vpool)[ch + v_elem<E>(j, d, D)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      put_code<KVT>(k_out, o0 + x + i, get_code<KVT>(kpool, ch + k_elem<E>(j, d + i, P)));
+      put_code<KVT>(v_out, o0 + x + i, get_code<KVT>(vpool, ch + v_elem<E>(j, d + i, D)));
+    }
   }
 }
 
@@ -1127,6 +1262,8 @@ decode_fn_t pick_decode(int kvt, int D, bool ob) {
   PKV_PICK(KV_FP8)
   PKV_PICK(KV_INT8)
 #undef PKV_PICK
+  // int4: 32-dim groups need D = 128 (one group per lane row)
+  if (kvt == KV_INT4 && D == 128) return ob ? decode_fn<KV_INT4, 128, true>() : decode_fn<KV_INT4, 128, false>();
   return nullptr;
 }
 
@@ -1176,6 +1313,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
                      a.head_dim, a.page_size)
   if (a.kvt == KV_F32) PKV_APPEND(KV_F32);
   else if (a.kvt == KV_BF16) PKV_APPEND(KV_BF16);
+  else if (a.kvt == KV_INT4) PKV_APPEND(KV_INT4);
   else PKV_APPEND(KV_FP8);          // any one-byte format (fp8, int8): a byte copy
 #undef PKV_APPEND
   return hipGetLastError();
@@ -1197,6 +1335,8 @@ hipError_t launch_append_quant(const AppendQuantArgs& a, hipStream_t s) {
   }
   if (a.kvt == KV_INT8) {
     PKV_APPEND_QK(KV_INT8)
+  } else if (a.kvt == KV_INT4) {
+    PKV_APPEND_QK(KV_INT4)
   } else {
     PKV_APPEND_QK(KV_FP8)
   }
@@ -1214,6 +1354,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
                      a.head_dim, a.page_size)
   if (a.kvt == KV_F32) PKV_GATHER(KV_F32);
   else if (a.kvt == KV_BF16) PKV_GATHER(KV_BF16);
+  else if (a.kvt == KV_INT4) PKV_GATHER(KV_INT4);
   else PKV_GATHER(KV_FP8);          // any one-byte format
 #undef PKV_GATHER
   return hipGetLastError();
@@ -1257,7 +1398,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (a.out_bf16) PKV_MERGE(KV_F32, true); else PKV_MERGE(KV_F32, false);
   } else if (a.kvt == KV_BF16) {
     if (a.out_bf16) PKV_MERGE(KV_BF16, true); else PKV_MERGE(KV_BF16, false);
-  } else {
+  } else if (a.kvt == KV_INT4) {
+    if (a.out_bf16) PKV_MERGE(KV_INT4, true); else PKV_MERGE(KV_INT4, false);
+  } else {            // any one-byte format (the append is a byte copy)
     if (a.out_bf16) PKV_MERGE(KV_FP8, true); else PKV_MERGE(KV_FP8, false);
   }
 #undef PKV_MERGE

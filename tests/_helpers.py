@@ -14,7 +14,8 @@ from oracle import c_oracle
 # fp8 e4m3 cache: max-abs <= 3e-2 (mean-abs reported).
 # int8 cache (no spec figure): its values widen to bf16 exactly and take
 # the bf16 path's arithmetic, so the bf16 bounds apply.
-TOL = {"f32": (1e-2, 1e-3), "bf16": (1e-2, 1e-3), "fp8": (3e-2, None), "i8": (1e-2, 1e-3)}
+TOL = {"f32": (1e-2, 1e-3), "bf16": (1e-2, 1e-3), "fp8": (3e-2, None), "i8": (1e-2, 1e-3), "i4": (1e-2, 1e-3)}
+DECODE_SCALED = {"fp8": "paged_attn_decode_fp8", "i8": "paged_attn_decode_int8", "i4": "paged_attn_decode_int4"}
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
@@ -51,8 +52,8 @@ class DeviceWorkload:
         sl = self.sl if seq_lens is None else seq_lens
         pt = wl.partition_tokens if partition_tokens is None else partition_tokens
         out = self.out if out is None else out
-        if wl.kv_dtype in ("fp8", "i8"):
-            fn = pkv.paged_attn_decode_fp8 if wl.kv_dtype == "fp8" else pkv.paged_attn_decode_int8
+        if wl.kv_dtype in DECODE_SCALED:
+            fn = getattr(pkv, DECODE_SCALED[wl.kv_dtype])
             fn(self.q, wl.q_dtype, self.k_pool, self.v_pool, self.ks, self.vs, self.bt, sl, wl.Hq, wl.Hkv,
                wl.D, wl.P, wl.scale, out, wl.out_dtype, self.ws, pt)
         else:

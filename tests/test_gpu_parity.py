@@ -74,10 +74,31 @@ def test_int8_codes_exhaustive_through_decode():
     assert np.array_equal(got, np.arange(256, dtype=np.uint8).view(np.int8).astype(np.float64))
 
 
+def test_int4_codes_exhaustive_through_decode():
+    """Single-token sequences return their value row: all 16 int4 codes (each
+    dim of the row holds code d % 16), scale 1: exact values -8 .. 7."""
+    D, P = 128, 128
+    codes = (np.arange(D) % 16).astype(np.uint8).reshape(1, 1, D)
+    kp = layout.empty_pool(3, 1, P, D, "i4")
+    vp = layout.empty_pool(3, 1, P, D, "i4")
+    bt = np.array([[2]], np.int32)
+    layout.pack_sequence(kp, bt[0], np.zeros((1, 1, D), np.uint8), P, layout.k_chunk_index(P, D, "i4"), "i4")
+    layout.pack_sequence(vp, bt[0], codes, P, layout.v_chunk_index(P, D, "i4"), "i4")
+    ones = np.ones((3, 1), np.float32)
+    q = codec.f32_to_bf16_bits(np.ones((1, 1, D), np.float32))
+    out = torch.empty((1, 1, D), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(pkv.decode_workspace_bytes(1, 1, 1, D), dtype=torch.uint8, device="cuda")
+    pkv.paged_attn_decode_int4(dev_tensor(q), "bf16", dev_tensor(kp), dev_tensor(vp), dev_tensor(ones),
+                               dev_tensor(ones), dev_tensor(bt), dev_tensor(np.array([1], np.int32)),
+                               1, 1, D, P, 0.1, out, "f32", ws)
+    got = out.cpu().numpy().astype(np.float64).reshape(D)
+    assert np.array_equal(got, ((codes.reshape(D).astype(np.int64) ^ 8) - 8).astype(np.float64))
+
+
 # ------------------------------------------------------------- append/gather ----
 
 APPEND_CASES = [("f32", 16, 64), ("bf16", 32, 128), ("bf16", 64, 128), ("bf16", 128, 64),
-                ("fp8", 64, 128), ("fp8", 128, 64), ("i8", 64, 128)]
+                ("fp8", 64, 128), ("fp8", 128, 64), ("i8", 64, 128), ("i4", 128, 128), ("i4", 256, 128)]
 
 
 @pytest.mark.parametrize("kv_dtype,P,D", APPEND_CASES)
@@ -99,8 +120,9 @@ def test_append_bit_exact(kv_dtype, P, D):
     for step in range(2):
         lens = np.array([x + step + 1 for x in lens0], np.int32)
         lens[0] = 0 if step == 0 else lens[0]        # a sequence that does not append this step
-        kn = rng.integers(0, 255, (wl.B, wl.Hkv, D * layout.ELEM_BYTES[kv_dtype]), dtype=np.uint8)
-        vn = rng.integers(0, 255, (wl.B, wl.Hkv, D * layout.ELEM_BYTES[kv_dtype]), dtype=np.uint8)
+        row_bytes = D * layout.ELEM_BITS[kv_dtype] // 8
+        kn = rng.integers(0, 255, (wl.B, wl.Hkv, row_bytes), dtype=np.uint8)
+        vn = rng.integers(0, 255, (wl.B, wl.Hkv, row_bytes), dtype=np.uint8)
         kn = kn.view(layout.NP_DTYPE[kv_dtype])
         vn = vn.view(layout.NP_DTYPE[kv_dtype])
         pkv.kv_append(dev_tensor(kn), dev_tensor(vn), kv_dtype, bt, dev_tensor(lens), dk, dv, wl.Hkv, D, P)
@@ -114,8 +136,9 @@ def test_append_bit_exact(kv_dtype, P, D):
 def test_gather_bit_exact(kv_dtype, P, D):
     wl = configs.custom(seed=32, lens=[1, P, P + 1, 3 * P - 1, 0], Hq=4, Hkv=2, D=D, P=P, kv_dtype=kv_dtype)
     dw = DeviceWorkload(wl)
-    fill = layout.POISON[kv_dtype]
-    ko = torch.empty((wl.B, wl.Hkv, wl.max_pages * P, D), dtype=dw.k_pool.dtype, device="cuda")
+    fill = 0x88 if kv_dtype == "i4" else layout.POISON[kv_dtype]
+    row = D // 2 if kv_dtype == "i4" else D              # int4 rows are packed
+    ko = torch.empty((wl.B, wl.Hkv, wl.max_pages * P, row), dtype=dw.k_pool.dtype, device="cuda")
     vo = torch.empty_like(ko)
     ko.view(torch.uint8).fill_(0xAB)
     vo.view(torch.uint8).fill_(0xAB)
@@ -155,6 +178,10 @@ EDGE = [
     dict(seed=58, lens=[1, 63, 64, 65, 1000], Hq=32, Hkv=8, D=128, P=64, kv_dtype="i8"),
     dict(seed=59, lens=[64, 200, 1300], Hq=16, Hkv=4, D=64, P=128, kv_dtype="i8", out_dtype="f32"),
     dict(seed=60, lens=[0, 100, 4097], Hq=12, Hkv=4, D=128, P=64, kv_dtype="i8", partition_tokens=128),
+    dict(seed=61, lens=[1, 127, 128, 129, 1000], Hq=32, Hkv=8, D=128, P=128, kv_dtype="i4"),
+    dict(seed=62, lens=[64, 300, 1300], Hq=16, Hkv=4, D=128, P=256, kv_dtype="i4", out_dtype="f32"),
+    dict(seed=63, lens=[0, 100, 4097], Hq=64, Hkv=8, D=128, P=128, kv_dtype="i4", partition_tokens=512,
+         q_mult=3.0),
 ]
 
 
@@ -275,6 +302,7 @@ STEP_CASES = [
     dict(seed=74, lens=[0, 128, 129, 5000], Hq=64, Hkv=8, D=128, P=128, kv_dtype="bf16", partition_tokens=512),
     dict(seed=75, lens=[1, 2, 3, 4, 5] * 100, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16", out_dtype="f32"),
     dict(seed=77, lens=[1, 63, 64, 65, 129, 700], Hq=32, Hkv=8, D=128, P=64, kv_dtype="i8"),
+    dict(seed=78, lens=[1, 127, 128, 129, 257, 700], Hq=32, Hkv=8, D=128, P=128, kv_dtype="i4"),
 ]
 
 
@@ -289,7 +317,8 @@ def test_step_equals_append_then_decode(spec):
     ki, vi = layout.k_chunk_index(wl.P, wl.D, wl.kv_dtype), layout.v_chunk_index(wl.P, wl.D, wl.kv_dtype)
     kp = layout.empty_pool(wl.num_pages, wl.Hkv, wl.P, wl.D, wl.kv_dtype)
     vp = layout.empty_pool(wl.num_pages, wl.Hkv, wl.P, wl.D, wl.kv_dtype)
-    knew = np.zeros((wl.B, wl.Hkv, wl.D), layout.NP_DTYPE[wl.kv_dtype])
+    i4 = wl.kv_dtype == "i4"
+    knew = np.zeros((wl.B, wl.Hkv, wl.D // 2 if i4 else wl.D), layout.NP_DTYPE[wl.kv_dtype])
     vnew = np.zeros_like(knew)
     for b in range(wl.B):
         n = int(lens_now[b])
@@ -298,7 +327,8 @@ def test_step_equals_append_then_decode(spec):
         layout.pack_sequence(kp, pages, k[:int(lens_prev[b])], wl.P, ki, wl.kv_dtype)
         layout.pack_sequence(vp, pages, v[:int(lens_prev[b])], wl.P, vi, wl.kv_dtype)
         if n:
-            knew[b], vnew[b] = k[n - 1], v[n - 1]
+            knew[b] = layout.pack_nibbles(k[n - 1]) if i4 else k[n - 1]
+            vnew[b] = layout.pack_nibbles(v[n - 1]) if i4 else v[n - 1]
     wl.k_pool, wl.v_pool = kp, vp
     dw = DeviceWorkload(wl)
     out = gpu_out(dw.step(dev_tensor(knew), dev_tensor(vnew), dw.sl))
@@ -343,6 +373,10 @@ def test_config_fp8_kv():
 
 def test_config_int8_kv():
     _decode_vs_oracle(configs.int8_kv(), "int8_kv")
+
+
+def test_config_int4_kv():
+    _decode_vs_oracle(configs.int4_kv(), "int4_kv")
 
 
 def test_config_inflight_16_steps():

@@ -19,11 +19,17 @@ from tests._helpers import DeviceWorkload, check_close, dev_tensor, gpu_out, hos
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
-FMTS = ["fp8", "i8"]
+FMTS = ["fp8", "i8", "i4"]
+APPEND_FN = {"fp8": "kv_append_fp8", "i8": "kv_append_int8", "i4": "kv_append_int4"}
 
 
 def gpu_append(fmt, *args):
-    (pkv.kv_append_fp8 if fmt == "fp8" else pkv.kv_append_int8)(*args)
+    getattr(pkv, APPEND_FN[fmt])(*args)
+
+
+def empty_pools(fmt, NP, Hkv, P, D):
+    kp = layout.empty_pool(NP, Hkv, P, D, fmt)
+    return kp, kp.copy(), np.full((NP, Hkv), np.nan, F32), np.full((NP, Hkv), np.nan, F32)
 
 
 def _rows(rng, B, Hkv, D, new_dtype):
@@ -46,16 +52,14 @@ def _compare(kp_dev, vp_dev, ks_dev, vs_dev, kp, vp, ks, vs, what):
     assert np.array_equal(host_bytes(vs_dev), vs.reshape(-1).view(np.uint8)), f"{what}: V scales"
 
 
-CASES = [  # (D, P, new_dtype, steps)
-    (128, 128, "bf16", 140),
-    (64, 64, "f32", 75),
-    (128, 64, "bf16", 80),
-    (64, 128, "bf16", 135),
-]
+CASES = [  # (fmt, D, P, new_dtype, steps)
+    (fmt, D, P, nd, st) for fmt in ("fp8", "i8")
+    for (D, P, nd, st) in ((128, 128, "bf16", 140), (64, 64, "f32", 75), (128, 64, "bf16", 80),
+                           (64, 128, "bf16", 135))
+] + [("i4", 128, 128, "bf16", 140), ("i4", 128, 256, "f32", 270)]
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("D,P,new_dtype,steps", CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("fmt,D,P,new_dtype,steps", CASES, ids=lambda v: str(v))
 def test_append_bit_exact_every_step(fmt, D, P, new_dtype, steps):
     rng = np.random.default_rng(100 + D + P)
     B, Hkv, MP = 7, 2, 2
@@ -65,10 +69,7 @@ def test_append_bit_exact_every_step(fmt, D, P, new_dtype, steps):
     bt[5, 1] = -1                       # sequence 5 runs onto a missing page after P tokens
     bt[6, 1] = NP + 7                   # sequence 6 onto a page id out of range
     start = np.array([0, 0, 3, 10, P - 2, 1, 2])    # step at which each sequence starts
-    kp = np.full((NP, Hkv, P * D), 0x7F, np.uint8)
-    vp = kp.copy()
-    ks = np.full((NP, Hkv), np.nan, F32)
-    vs = ks.copy()
+    kp, vp, ks, vs = empty_pools(fmt, NP, Hkv, P, D)
     kp_d, vp_d, ks_d, vs_d = (dev_tensor(a) for a in (kp, vp, ks, vs))
     bt_d = dev_tensor(bt)
     for s in range(steps):
@@ -90,10 +91,7 @@ def test_append_grows_at_every_slot(fmt):
     rng = np.random.default_rng(7)
     B, Hkv, D, P = 1, 1, 128, 128
     bt = np.array([[2]], np.int32)
-    kp = np.full((3, Hkv, P * D), 0x7F, np.uint8)
-    vp = kp.copy()
-    ks = np.full((3, Hkv), np.nan, F32)
-    vs = ks.copy()
+    kp, vp, ks, vs = empty_pools(fmt, 3, Hkv, P, D)
     kp_d, vp_d, ks_d, vs_d = (dev_tensor(a) for a in (kp, vp, ks, vs))
     for t in range(P):
         x = (rng.standard_normal((1, 1, D)) * 1.05 ** t).astype(F32)
@@ -112,22 +110,18 @@ def test_append_matches_one_shot_generator_pages(fmt):
     """Token-by-token GPU appends with the page amax on each page's first token
     reproduce the generator's one-shot per-page quantisation."""
     rng = np.random.default_rng(8)
-    Hkv, D, P = 2, 128, 64
+    Hkv, D, P = 2, 128, 64 if fmt != "i4" else 128
     L = 3 * P - 5
     xk = rng.standard_normal((L, Hkv, D)).astype(F32)
     xv = rng.standard_normal((L, Hkv, D)).astype(F32)
     for p0 in range(0, L, P):
         xk[p0, :, 3] = 12.0
         xv[p0, :, 9] = -11.0
-    quant = configs.quantize_fp8_pages if fmt == "fp8" else configs.quantize_int8_pages
-    kb, ksc = quant(xk, P)
-    vb, vsc = quant(xv, P)
+    kb, ksc = configs.QUANTIZERS[fmt](xk, P)
+    vb, vsc = configs.QUANTIZERS[fmt](xv, P)
     pages = np.array([4, 0, 2], np.int32)
     NP = 5
-    kp_d = dev_tensor(np.full((NP, Hkv, P * D), 0x7F, np.uint8))
-    vp_d = dev_tensor(np.full((NP, Hkv, P * D), 0x7F, np.uint8))
-    ks_d = dev_tensor(np.full((NP, Hkv), np.nan, F32))
-    vs_d = dev_tensor(np.full((NP, Hkv), np.nan, F32))
+    kp_d, vp_d, ks_d, vs_d = (dev_tensor(a) for a in empty_pools(fmt, NP, Hkv, P, D))
     bt_d = dev_tensor(pages.reshape(1, -1))
     for t in range(L):
         gpu_append(fmt, dev_tensor(xk[t:t + 1]), dev_tensor(xv[t:t + 1]), "f32", bt_d,
@@ -139,8 +133,8 @@ def test_append_matches_one_shot_generator_pages(fmt):
     for i, pg in enumerate(pages):
         n = min(P, L - i * P)
         for g in range(Hkv):
-            assert np.array_equal(kp[pg, g, kidx[:n]], kb[i * P:i * P + n, g])
-            assert np.array_equal(vp[pg, g, vidx[:n]], vb[i * P:i * P + n, g])
+            assert np.array_equal(paged.read_elems(kp, (pg, g, kidx[:n]), fmt), kb[i * P:i * P + n, g])
+            assert np.array_equal(paged.read_elems(vp, (pg, g, vidx[:n]), fmt), vb[i * P:i * P + n, g])
     assert np.array_equal(ks_d.cpu().numpy()[pages], ksc)
     assert np.array_equal(vs_d.cpu().numpy()[pages], vsc)
 
@@ -163,7 +157,7 @@ def test_append_quant_errors():
 
 
 def _inflight_quant_run(fmt, B, n_steps, max_len, decode_every, pools_every=True):
-    gen = configs.inflight_fp8 if fmt == "fp8" else configs.inflight_int8
+    gen = {"fp8": configs.inflight_fp8, "i8": configs.inflight_int8, "i4": configs.inflight_int4}[fmt]
     wl = gen(B=B, n_steps=n_steps, max_len=max_len)
     dw = DeviceWorkload(wl)
     kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
