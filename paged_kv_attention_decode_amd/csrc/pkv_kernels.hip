@@ -145,11 +145,6 @@ __device__ __forceinline__ u32x2_t split_pair(float a, float b) {
   const float rb = b - fbits(ubits(b) & 0xffff0000u);
   return u32x2_t{pack_hi16(a, b), pack_hi16(ra, rb)};
 }
-// As split_probs, and adds to sum the exact value hi + lo of all eight.
-__device__ __forceinline__ float split_sum(float a) {
-  const float hi = fbits(ubits(a) & 0xffff0000u);
-  return hi + fbits(ubits(a - hi) & 0xffff0000u);
-}
 // Probabilities of two 16-token tiles (8 per lane) as hi and lo bf16x8 operands.
 __device__ __forceinline__ void split_probs(const float (&x)[4], const float (&y)[4], float mul,
                                            u32x4_t& hi, u32x4_t& lo) {
@@ -157,6 +152,17 @@ __device__ __forceinline__ void split_probs(const float (&x)[4], const float (&y
   const u32x2_t c = split_pair(y[0] * mul, y[1] * mul), d = split_pair(y[2] * mul, y[3] * mul);
   hi = u32x4_t{a.x, b.x, c.x, d.x};
   lo = u32x4_t{a.y, b.y, c.y, d.y};
+}
+// As split_probs, with the two tiles interleaved: word i holds x[i] and y[i]
+// (the slot order of the int4 operands below).
+__device__ __forceinline__ void split_probs_zip(const float (&x)[4], const float (&y)[4], float mul,
+                                               u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x2_t a = split_pair(x[i] * mul, y[i] * mul);
+    hi[i] = a.x;
+    lo[i] = a.y;
+  }
 }
 // Four fp8 e4m3 bytes -> four bf16 (exact: every e4m3 value is a bf16 value).
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
@@ -175,20 +181,24 @@ __device__ __forceinline__ u32x2_t i8x4_to_bf16x4(uint32_t w) {
   const float c = (float)(int8_t)(w >> 16), d = (float)((int32_t)w >> 24);
   return u32x2_t{pack_hi16(a, b), pack_hi16(c, d)};
 }
-// Eight int4 codes (one word, element 2i in the low nibble of byte i) -> a
-// bf16x8 operand holding 136 + n for each code n in [-8, 7]: with u = n + 8,
-// the bf16 pattern 0x4300 | u is exactly 128 + u.  Each pair of elements
-// (byte i) goes into one word with two integer instructions.  Products against
-// this operand carry 136 * (sum of the other operand), which callers subtract.
+// Eight int4 codes (one word, element k in nibble k: element 2i in the low
+// nibble of byte i) -> a bf16x8 operand holding 136 + n for each code n in
+// [-8, 7]: with u = n + 8 (the code with its top bit flipped), the bf16 pattern
+// 0x4300 | u is exactly 128 + u.  Nibbles i and 4 + i lie 16 bits apart, so
+// one shift and one and-xor (which also flips the top bits) give both: slot
+// order (e0, e4, e1, e5, e2, e6, e3, e7).  The other operand of each product
+// is laid out in that order, and products carry 136 * (sum of the other
+// operand), which callers subtract.
 __device__ __forceinline__ u32x4_t nib8_to_bf16x8(uint32_t w) {
-  const uint32_t u = w ^ 0x88888888u;
   u32x4_t r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t b = (u >> (8 * i)) & 0xFFu;        // (u_2i, u_2i+1)
-    r[i] = ((b | (b << 12)) & 0x000F000Fu) | 0x43004300u;
-  }
+  for (int i = 0; i < 4; ++i) r[i] = ((w >> (4 * i)) & 0x000F000Fu) ^ 0x43084308u;
   return r;
+}
+// Eight bf16 values (natural order) reordered to the slot order above.
+__device__ __forceinline__ u32x4_t zip_halves(u32x4_t x) {
+  return u32x4_t{__builtin_amdgcn_perm(x[2], x[0], 0x05040100u), __builtin_amdgcn_perm(x[2], x[0], 0x07060302u),
+                 __builtin_amdgcn_perm(x[3], x[1], 0x05040100u), __builtin_amdgcn_perm(x[3], x[1], 0x07060302u)};
 }
 constexpr float INT4_BIAS = 136.f;
 
@@ -477,6 +487,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         // operand per chunk; E = 8 for bf16, 16 for fp8 / int8, 32 for int4).
         const int d0 = E * (c4 + 4 * (i / NCH)) + 8 * (i % NCH);
         qv_ld[i] = hv ? ld16(reinterpret_cast<const uint8_t*>(q + d0)) : u32x4_t{0, 0, 0, 0};
+        if constexpr (I4) qv_ld[i] = zip_halves(qv_ld[i]);
       }
     }
     auto qop = [&](int i) -> u32x4_t { return s_q[wv][i][lane]; };
@@ -497,10 +508,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = NEG_INF, l = 0.f;
-    // int4: the widened operands are 136 + n; lp accumulates, like l, the sum
-    // of the probabilities exactly as the PV products see them, and qsum is the
+    // int4: the widened operands are 136 + n; LP accumulates, like l, the sum
+    // of the probabilities exactly as the PV products see them (a product with
+    // an all-ones operand: every entry holds the column's sum), and qsum is the
     // head's sum of query values, so that the bias comes back out exactly.
-    float lp = 0.f, qsum = 0.f;
+    f32x4_t LP = {0.f, 0.f, 0.f, 0.f};
+    float qsum = 0.f;
     if constexpr (I4) {
 #pragma unroll
       for (int i = 0; i < NQ; ++i)
@@ -705,10 +718,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
           lsum += p[sub][i];
         }
       l = l * alpha + lsum;
-      if constexpr (I4) lp *= alpha;
       if (__ballot(mnew > m)) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+        if constexpr (I4) LP *= alpha;
       }
       m = mnew;
 
@@ -728,11 +741,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         }
       } else if constexpr (I4) {
         u32x4_t ph[4], pl[4];
+        const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          split_probs(p[2 * c], p[2 * c + 1], vmul, ph[c], pl[c]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lp += split_sum(p[2 * c][i] * vmul) + split_sum(p[2 * c + 1][i] * vmul);
+          split_probs_zip(p[2 * c], p[2 * c + 1], vmul, ph[c], pl[c]);
+          LP = mfma_bf16(ones, ph[c], LP);
+          LP = mfma_bf16(ones, pl[c], LP);
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -774,10 +788,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     if constexpr (I4) {
-      float lpt = lp + __shfl_xor(lp, 16);
-      lpt += __shfl_xor(lpt, 32);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[dt] -= INT4_BIAS * lpt;
+      for (int dt = 0; dt < NDT; ++dt) O[dt] -= INT4_BIAS * LP[0];
     }
     const float qnan = __builtin_nanf("");
     if (complete) {
@@ -1373,8 +1385,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   // tile is 128 * D bytes in every dtype), i.e. one wave per SIMD at D = 128.
   // More waves than that do not raise the streaming rate: two waves on one
   // SIMD issue in age order, so the second one starts late and finishes last,
-  // stretching the tail of the launch.
-  const int Wmax = cus * std::min(waves_per_cu(fn, dev), 512 / a.head_dim);
+  // stretching the tail of the launch.  int4 is the exception: its tile is
+  // half the bytes and four times the widening work of a bf16 one, so the
+  // second wave on each SIMD hides ALU time rather than adding loads in flight.
+  const int tile_waves = a.kvt == KV_INT4 ? 1024 : 512;
+  const int Wmax = cus * std::min(waves_per_cu(fn, dev), tile_waves / a.head_dim);
   const int G = a.num_q_heads / a.num_kv_heads;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   dim3 grid((Wmax + 3) / 4), block(256);
