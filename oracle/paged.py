@@ -1,4 +1,5 @@
-"""numpy fp64 oracle for paged decode attention (vectorised twin of pkv_oracle.c).
+"""numpy fp64 oracle for paged decode attention (vectorised twin of pkv_oracle.c),
+the quantising appends, and causal chunked prefill over the same pages.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU baseline, never by the product path.  It shares no code with
@@ -360,3 +361,80 @@ def append_int8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool,
     """append_dynamic for a symmetric int8 cache (QMAX 127, no-clip bound 127.5)."""
     append_dynamic("i8", k_new, v_new, new_dtype, block_tables, seq_lens, k_pool, v_pool,
                    k_scales, v_scales, P)
+
+
+# ------------------------------------------------------ chunked prefill -------
+#
+# Source: the concept page's "key performance parameters" section: with paged
+# attention the context is processed in parallel over many tokens at once (the
+# compute that sets the first-token latency), beside the decode iterations of
+# its "runtime execution model" section that read and update the same pages.
+# Reading (the pages give no formula or interface): sequence b brings a chunk
+# of C_b new tokens whose K/V rows are written into its pages first, so
+# seq_lens[b] = L_b counts them; chunk token i sits at position p = L_b - C_b + i
+# and attends to the cached tokens 0..p (causal).  q and the output hold the
+# chunks back to back, rows cu_q[b] .. cu_q[b+1] for sequence b.  A position
+# below zero (C_b > L_b) attends to nothing and gives zeros, as L = 0 does for
+# decode.
+
+def prefill(q, q_dtype, cu_q, k_pool, v_pool, kv_dtype, block_tables, seq_lens, Hq, P, scale,
+            batches=None):
+    """fp64 [T, Hq, D] outputs of causal chunked prefill over the paged cache."""
+    cu = np.asarray(cu_q, dtype=np.int64)
+    B = len(seq_lens)
+    T = int(cu[-1])
+    NP, Hkv = k_pool.shape[:2]
+    D = pool_elems(k_pool, kv_dtype) // P
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    qf = widen(q, q_dtype).reshape(T, Hq, D)
+    for b in (range(B) if batches is None else batches):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        C, L = r1 - r0, int(seq_lens[b])
+        if C <= 0 or L <= 0:
+            continue
+        pos = L - C + np.arange(C)                          # position of each chunk token
+        allowed = np.arange(L)[None, :] <= pos[:, None]      # [C, L] causal mask
+        live = pos >= 0
+        k, v, _ = gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b)
+        kf, vf = widen(k, kv_dtype), widen(v, kv_dtype)
+        for g in range(Hkv):
+            qg = qf[r0:r1, g * G:(g + 1) * G]                # [C, G, D]
+            s = float(scale) * np.einsum("cgd,ld->cgl", qg, kf[g])
+            s = np.where(allowed[:, None, :], s, -np.inf)
+            m = np.where(live[:, None, None], s.max(axis=2, keepdims=True), 0.0)
+            with np.errstate(invalid="ignore"):
+                w = np.where(allowed[:, None, :], np.exp(s - m), 0.0)
+            den = w.sum(axis=2, keepdims=True)
+            o = np.einsum("cgl,ld->cgd", w, vf[g]) / np.where(live[:, None, None], den, 1.0)
+            out[r0:r1, g * G:(g + 1) * G] = np.where(live[:, None, None], o, 0.0)
+    return out
+
+
+def append_chunk(k_new, v_new, kv_dtype, cu_new, block_tables, seq_lens, k_pool, v_pool, P):
+    """In place: rows cu_new[b] .. cu_new[b+1] of k_new / v_new ([T, Hkv, D] stored
+    elements; int4 rows packed, D/2 bytes) into positions L_b - C_b + i of
+    sequence b.  A sequence whose chunk does not fit (C_b > L_b, or L_b beyond its
+    page-table row) is skipped; a page id out of range raises."""
+    cu = np.asarray(cu_new, dtype=np.int64)
+    NP, Hkv = k_pool.shape[:2]
+    D = pool_elems(k_pool, kv_dtype) // P
+    MP = np.asarray(block_tables).shape[1]
+    koff, voff = _offsets(P, D, kv_dtype)
+    if kv_dtype == "i4":
+        T = len(k_new)
+        k_new = np.stack([np.asarray(k_new) & 0xF, np.asarray(k_new) >> 4], -1).reshape(T, Hkv, D)
+        v_new = np.stack([np.asarray(v_new) & 0xF, np.asarray(v_new) >> 4], -1).reshape(T, Hkv, D)
+    hh = np.arange(Hkv)[:, None]
+    for b in range(len(seq_lens)):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        C, L = r1 - r0, int(seq_lens[b])
+        if C <= 0 or C > L or L > MP * P:
+            continue
+        for i in range(C):
+            t = L - C + i
+            pg = int(block_tables[b][t // P])
+            if not 0 <= pg < NP:
+                raise IndexError("page id out of range")
+            write_elems(k_pool, (pg, hh, koff[t % P][None, :]), k_new[r0 + i], kv_dtype)
+            write_elems(v_pool, (pg, hh, voff[t % P][None, :]), v_new[r0 + i], kv_dtype)

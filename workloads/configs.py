@@ -470,3 +470,116 @@ CONFIGS = {
     "int4_kv": int4_kv,
     "inflight_int4": inflight_int4,
 }
+
+
+# ----------------------------------------------------------------------------
+# Chunked prefill
+# ----------------------------------------------------------------------------
+#
+# A batch of sequences that each bring a chunk of C_b new tokens on top of
+# L_b - C_b cached ones: the pools hold the cached tokens, k_new / v_new the
+# chunk's rows (tokens L_b - C_b .. L_b - 1 of the same per-sequence draws, so
+# appending them gives the pool of all L_b tokens), q one row per chunk token
+# from child stream [seed, 5].  Rows of all chunks are packed back to back;
+# cu_q[b] .. cu_q[b+1] are sequence b's.
+
+
+@dataclass
+class PrefillWorkload:
+    name: str
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    P: int
+    num_pages: int
+    max_pages: int
+    kv_dtype: str                 # "f32" | "bf16"
+    q_dtype: str
+    out_dtype: str
+    scale: np.float32
+    seq_lens: np.ndarray          # int32 [B], cached tokens + chunk
+    chunk_lens: np.ndarray        # int32 [B]
+    cu_q: np.ndarray              # int32 [B + 1]
+    block_tables: np.ndarray      # int32 [B, max_pages]
+    q: np.ndarray                 # [T, Hq, D] stored format
+    k_pool: np.ndarray            # cached tokens only
+    v_pool: np.ndarray
+    k_new: np.ndarray             # [T, Hkv, D] stored format, the chunks' rows
+    v_new: np.ndarray
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_q[-1])
+
+    def attended(self) -> int:
+        """(query token, key token) pairs the causal chunks attend to, per head."""
+        L = self.seq_lens.astype(np.int64)
+        C = self.chunk_lens.astype(np.int64)
+        first = np.maximum(L - C + 1, 0)           # keys seen by the chunk's first row
+        return int(np.sum(C * first + C * (C - 1) // 2))
+
+    def flops(self) -> int:
+        """2 flops per multiply-add of q.k and of p.v, per attended pair and head."""
+        return 4 * self.attended() * self.Hq * self.D
+
+    def kv_bytes(self) -> int:
+        """K and V bytes of all L_b tokens (each read at least once)."""
+        bits = layout.ELEM_BITS[self.kv_dtype]
+        return int(np.sum(self.seq_lens.astype(np.int64))) * self.Hkv * self.D * bits // 8 * 2
+
+
+def prefill_case(name: str, seed: int, ctx_lens, chunk_lens, Hq: int, Hkv: int, D: int, P: int,
+                 kv_dtype: str = "bf16", out_dtype: Optional[str] = None, slack: float = 1.25,
+                 q_mult: float = 1.0, extra_table_cols: int = 0) -> PrefillWorkload:
+    """Sequences with ``ctx_lens`` cached tokens and chunks of ``chunk_lens``."""
+    if kv_dtype not in ("f32", "bf16"):
+        raise ValueError("chunked prefill workloads are fp32 or bf16")
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx_lens, dtype=np.int32)
+    C = np.asarray(chunk_lens, dtype=np.int32)
+    L = (ctx + C).astype(np.int32)
+    B = len(L)
+    need = int(pages_needed(L, P).sum())
+    NP = max(1, int(math.ceil(slack * need)))
+    mp = max(1, int(pages_needed(L, P).max()) if B else 1) + extra_table_cols
+    bt = place_permuted(rng, L, P, NP, max_pages=mp)
+    q_dtype = "f32" if kv_dtype == "f32" else "bf16"
+    sc = np.float32(1.0 / math.sqrt(D))
+    base = _assemble(name, seed, B, Hq, Hkv, D, P, NP, kv_dtype, q_dtype, out_dtype or q_dtype,
+                     sc, 0, L, bt, pool_lens=ctx)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(C)
+    T = int(cu[-1])
+    qf = _child(seed, 5).standard_normal((T, Hq, D), dtype=np.float32)
+    if q_mult != 1.0:
+        qf = qf * np.float32(q_mult)
+    kn = np.zeros((T, Hkv, D), dtype=np.float32)
+    vn = np.zeros((T, Hkv, D), dtype=np.float32)
+    for b in range(B):
+        n = int(L[b])
+        kn[cu[b]:cu[b + 1]] = draw_seq_f32(seed, 2, b, n, Hkv, D)[ctx[b]:]
+        vn[cu[b]:cu[b + 1]] = draw_seq_f32(seed, 3, b, n, Hkv, D)[ctx[b]:]
+    return PrefillWorkload(name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, D=D, P=P, num_pages=NP,
+                           max_pages=bt.shape[1], kv_dtype=kv_dtype, q_dtype=q_dtype,
+                           out_dtype=base.out_dtype, scale=sc, seq_lens=L, chunk_lens=C, cu_q=cu,
+                           block_tables=bt, q=_store(qf, q_dtype), k_pool=base.k_pool,
+                           v_pool=base.v_pool, k_new=_store(kn, kv_dtype), v_new=_store(vn, kv_dtype))
+
+
+def chunked_prefill_bf16(seed: int = 6, B: int = 16, chunk: int = 512) -> PrefillWorkload:
+    """Llama-3-8B-shaped chunked prefill: 16 sequences, each a 512-token chunk on
+    top of U{0..7680} cached tokens, 32/8 heads, D 128, pages of 64, bf16."""
+    rng = np.random.default_rng([seed, 0])
+    ctx = rng.integers(0, 7680, size=B, endpoint=True).astype(np.int32)
+    return prefill_case("chunked_prefill_bf16", seed, ctx, np.full(B, chunk, np.int32), 32, 8, 128, 64)
+
+
+PREFILL_CONFIGS = {
+    "chunked_prefill_bf16": chunked_prefill_bf16,
+}
