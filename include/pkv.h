@@ -293,6 +293,61 @@ int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const v
                     void* out, pkv_dtype out_dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* kv_append_chunk - write a chunk of new K/V tokens per sequence into its pages.
+ *
+ * The paged store of the first page ("key mechanisms", after the page-table
+ * lookup of "compile-time graph optimization") for the context tokens that its
+ * "key performance parameters" section processes many at a time.  Sequence b
+ * owns rows cu_new[b] .. cu_new[b+1] - 1 of k_new / v_new ([total_new][Hkv][D]
+ * elements of kv_dtype, int4 rows packed two per byte): C_b = cu_new[b+1] -
+ * cu_new[b] tokens that take positions L_b - C_b .. L_b - 1 (seq_lens counts
+ * them), each copied bit for bit to slot t % P of page block_tables[b][t / P].
+ *
+ * cu_new: int32 [batch + 1] device array, non-decreasing, cu_new[batch] <=
+ *   total_new.  kv_dtype: any pkv_dtype (fp8 / int8 / int4 bytes copied as
+ *   given).  Writes only the addressed slots.  Sequences must not share slots.
+ * A sequence with C_b <= 0 is untouched; one whose chunk does not fit (C_b >
+ * L_b, L_b > max_pages_per_seq * P, or rows outside [0, total_new)) is skipped,
+ * and so is a token whose page id lies outside [0, num_pages).
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (as pkv_kv_append, and total_new < 0),
+ * PKV_E_DTYPE, PKV_E_ALIGN, PKV_E_HIP. */
+int pkv_kv_append_chunk(const void* k_new, const void* v_new, pkv_dtype kv_dtype,
+                        const int32_t* cu_new, int total_new,
+                        const int32_t* block_tables, int max_pages_per_seq,
+                        const int32_t* seq_lens, int batch,
+                        void* k_pool, void* v_pool, int num_pages,
+                        int num_kv_heads, int head_dim, int page_size, void* stream);
+
+/* paged_prefill - causal attention of a chunk of query tokens per sequence
+ * over the paged cache (chunked prefill).
+ *
+ * The first page's "key performance parameters" section has paged attention
+ * process the context in parallel over many tokens; its "runtime execution
+ * model" has the same pages read and updated by the decode iterations.  With
+ * G = num_q_heads / num_kv_heads and C_b = cu_q[b+1] - cu_q[b], row
+ * r = cu_q[b] + i of q is chunk token i of sequence b at position
+ * p = L_b - C_b + i (its K/V already in the pages, e.g. by
+ * pkv_kv_append_chunk); for each query head h (kv head h / G):
+ *   out[r][h][:] = sum_{t <= p} softmax_t(scale * q[r][h] . k_t) v_t.
+ * A row with p < 0 (C_b > L_b) gets zeros.
+ *
+ * q: bf16 [total_q][num_q_heads][head_dim]; out: bf16 or fp32, same shape;
+ * cu_q: int32 [batch + 1] device array, non-decreasing, cu_q[batch] <= total_q
+ * (rows of a sequence with a decreasing or out-of-range pair are not written);
+ * kv_dtype must be BF16.  Pool layout and sizes as for decode.  Writes only the
+ * rows of out that belong to a sequence.  No workspace.  A key position whose
+ * page id lies outside [0, num_pages) (or past the table row) makes every row
+ * of that (sequence, kv head) block NaN.
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (as decode, total_q < 0, G > 256),
+ * PKV_E_DTYPE (kv not bf16, q not bf16, out not bf16 / fp32), PKV_E_ALIGN,
+ * PKV_E_HIP. */
+int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int total_q,
+                      const void* k_pool, const void* v_pool, pkv_dtype kv_dtype,
+                      const int32_t* block_tables, int max_pages_per_seq,
+                      const int32_t* seq_lens, int batch, int num_pages,
+                      int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                      float scale, void* out, pkv_dtype out_dtype, void* stream);
+
 /* debug_gather - copy each sequence's cached tokens out of the pages into
  * contiguous rows, through the same page-table lookup and chunk addressing
  * the decode kernels use (for bit-exact tests of that address path).

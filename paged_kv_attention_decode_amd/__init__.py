@@ -159,6 +159,29 @@ def decode_step(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, block_tables
         _stream(stream)))
 
 
+def kv_append_chunk(k_new, v_new, kv_dtype, cu_new, block_tables, seq_lens, k_pool, v_pool,
+                    num_kv_heads, head_dim, page_size, stream=None):
+    """Write each sequence's chunk of new tokens (rows cu_new[b] .. cu_new[b+1] of
+    k_new / v_new) into positions seq_lens[b] - C_b .. seq_lens[b] - 1."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("kv_append_chunk", lib().pkv_kv_append_chunk(
+        _ptr(k_new), _ptr(v_new), _code(kv_dtype), _ptr(cu_new), int(k_new.shape[0]), _ptr(block_tables), MP,
+        _ptr(seq_lens), B, _ptr(k_pool), _ptr(v_pool), NP, num_kv_heads, head_dim, page_size, _stream(stream)))
+
+
+def paged_prefill(q, q_dtype, cu_q, k_pool, v_pool, kv_dtype, block_tables, seq_lens,
+                  num_q_heads, num_kv_heads, head_dim, page_size, scale, out, out_dtype, stream=None):
+    """Causal attention of each sequence's chunk of query rows (rows cu_q[b] ..
+    cu_q[b+1] of q) over its pages (bf16 cache)."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("paged_prefill", lib().pkv_paged_prefill(
+        _ptr(q), _code(q_dtype), _ptr(cu_q), int(q.shape[0]), _ptr(k_pool), _ptr(v_pool), _code(kv_dtype),
+        _ptr(block_tables), MP, _ptr(seq_lens), B, NP, num_q_heads, num_kv_heads, head_dim, page_size,
+        float(scale), _ptr(out), _code(out_dtype), _stream(stream)))
+
+
 def debug_gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, num_kv_heads, head_dim,
                  page_size, k_out, v_out, stream=None):
     """Copy cached tokens to contiguous [B, Hkv, MP*P, D] rows (tests of the address path)."""

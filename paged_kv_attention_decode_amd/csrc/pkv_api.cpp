@@ -209,6 +209,55 @@ int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype, cons
   return PKV_OK;
 }
 
+int pkv_kv_append_chunk(const void* k_new, const void* v_new, pkv_dtype kv_dtype, const int32_t* cu_new,
+                        int total_new, const int32_t* block_tables, int max_pages_per_seq, const int32_t* seq_lens,
+                        int batch, void* k_pool, void* v_pool, int num_pages, int num_kv_heads, int head_dim,
+                        int page_size, void* stream) {
+  g_last_error.clear();
+  if (total_new < 0) return fail(PKV_E_SHAPE, "total_new %d < 0", total_new);
+  if (batch > 0 && (!cu_new || !block_tables || !seq_lens || !k_pool || !v_pool))
+    return fail(PKV_E_NULL, "a required pointer is NULL");
+  if (batch > 0 && total_new > 0 && (!k_new || !v_new)) return fail(PKV_E_NULL, "k_new / v_new is NULL");
+  int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
+  if (rc) return rc;
+  if (batch == 0 || total_new == 0) return PKV_OK;
+  if ((rc = check_align({k_new, v_new, k_pool, v_pool}))) return rc;
+  pkv::AppendChunkArgs a{k_new, v_new, cu_new, total_new, block_tables, seq_lens, k_pool, v_pool,
+                         (int)kv_dtype, batch, max_pages_per_seq, num_pages, num_kv_heads, head_dim, page_size};
+  hipError_t e = pkv::launch_append_chunk(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "chunk append launch");
+  return PKV_OK;
+}
+
+int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int total_q, const void* k_pool,
+                      const void* v_pool, pkv_dtype kv_dtype, const int32_t* block_tables, int max_pages_per_seq,
+                      const int32_t* seq_lens, int batch, int num_pages, int num_q_heads, int num_kv_heads,
+                      int head_dim, int page_size, float scale, void* out, pkv_dtype out_dtype, void* stream) {
+  g_last_error.clear();
+  if (total_q < 0) return fail(PKV_E_SHAPE, "total_q %d < 0", total_q);
+  if (batch > 0 && (!cu_q || !block_tables || !seq_lens || !k_pool || !v_pool))
+    return fail(PKV_E_NULL, "a required pointer is NULL");
+  if (batch > 0 && total_q > 0 && (!q || !out)) return fail(PKV_E_NULL, "q / out is NULL");
+  int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
+  if (rc) return rc;
+  if (kv_dtype != PKV_BF16) return fail(PKV_E_DTYPE, "chunked prefill reads a bf16 cache (kv dtype %d)", kv_dtype);
+  if (q_dtype != PKV_BF16) return fail(PKV_E_DTYPE, "chunked prefill takes bf16 queries (q dtype %d)", q_dtype);
+  if (out_dtype != PKV_BF16 && out_dtype != PKV_F32)
+    return fail(PKV_E_DTYPE, "out dtype %d not supported (bf16 or fp32)", out_dtype);
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(PKV_E_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  if (num_q_heads / num_kv_heads > 256)
+    return fail(PKV_E_SHAPE, "group size %d > 256", num_q_heads / num_kv_heads);
+  if (batch == 0 || total_q == 0) return PKV_OK;
+  if ((rc = check_align({q, k_pool, v_pool, out}))) return rc;
+  pkv::PrefillArgs a{q, cu_q, total_q, k_pool, v_pool, block_tables, seq_lens, out, out_dtype == PKV_BF16,
+                     batch, max_pages_per_seq, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale};
+  hipError_t e = pkv::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return PKV_OK;
+}
+
 int pkv_kv_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype, const int32_t* block_tables,
                       int max_pages_per_seq, const int32_t* seq_lens, int batch, void* k_pool, void* v_pool,
                       float* k_scales, float* v_scales, int num_pages, int num_kv_heads, int head_dim,

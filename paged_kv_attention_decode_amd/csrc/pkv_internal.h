@@ -78,7 +78,39 @@ struct DecodeArgs {
   float scale;
 };
 
+// Chunk append: rows cu_new[b] .. cu_new[b+1] of k_new / v_new ([total][Hkv][D])
+// into positions L_b - C_b .. L_b - 1 of sequence b.
+struct AppendChunkArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* cu_new;
+  int total;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* k_pool;
+  void* v_pool;
+  int kvt, batch, max_pages, num_pages, num_kv_heads, head_dim, page_size;
+};
+
+// Causal chunked prefill over a bf16 cache: q and out are [total_q][Hq][D],
+// rows cu_q[b] .. cu_q[b+1] belong to sequence b.
+struct PrefillArgs {
+  const void* q;            // bf16
+  const int32_t* cu_q;
+  int total_q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* out;
+  bool out_bf16;
+  int batch, max_pages, num_pages, num_q_heads, num_kv_heads, head_dim, page_size;
+  float scale;
+};
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_chunk(const AppendChunkArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 // Quantising append into a one-byte cache (fp8 or int8) with dynamic page scales.
 hipError_t launch_append_quant(const AppendQuantArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);

@@ -39,230 +39,9 @@
 #include <type_traits>
 
 #include "pkv_internal.h"
+#include "pkv_device.h"
 
 namespace pkv {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-// Element width in bits; elem_t is the storage word of one element (int4: a
-// byte holding two, the even element in the low nibble).
-template <int KVT> struct Kv;
-template <> struct Kv<KV_F32> { static constexpr int BITS = 32; typedef uint32_t elem_t; };
-template <> struct Kv<KV_BF16> { static constexpr int BITS = 16; typedef uint16_t elem_t; };
-template <> struct Kv<KV_FP8> { static constexpr int BITS = 8; typedef uint8_t elem_t; };
-template <> struct Kv<KV_INT8> { static constexpr int BITS = 8; typedef uint8_t elem_t; };
-template <> struct Kv<KV_INT4> { static constexpr int BITS = 4; typedef uint8_t elem_t; };
-// Byte offset of element index x (element indices of int4 chunks are even
-// wherever a whole byte is addressed).
-template <int KVT>
-__device__ __forceinline__ size_t elem_byte(size_t x) { return x * Kv<KVT>::BITS / 8; }
-// Element x of an array of stored elements, as its code (int4: the nibble).
-template <int KVT>
-__device__ __forceinline__ uint32_t get_code(const void* base, size_t x) {
-  typedef typename Kv<KVT>::elem_t T;
-  if constexpr (Kv<KVT>::BITS == 4)
-    return ((uint32_t)static_cast<const uint8_t*>(base)[x >> 1] >> (4 * (x & 1))) & 0xFu;
-  else
-    return static_cast<const T*>(base)[x];
-}
-// Store element x (int4: read-modify-write of its byte; no other thread may
-// write the same byte concurrently).
-template <int KVT>
-__device__ __forceinline__ void put_code(void* base, size_t x, uint32_t c) {
-  typedef typename Kv<KVT>::elem_t T;
-  if constexpr (Kv<KVT>::BITS == 4) {
-    uint8_t* p = static_cast<uint8_t*>(base) + (x >> 1);
-    const int sh = 4 * (int)(x & 1);
-    *p = (uint8_t)((*p & ~(0xF << sh)) | ((c & 0xFu) << sh));
-  } else {
-    static_cast<T*>(base)[x] = (T)c;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Chunk addressing shared by every kernel.  A (page, kv head) chunk holds P
-// tokens x D elements; E = 16 / element bytes; V blocks hold TB = 4E tokens.
-// ---------------------------------------------------------------------------
-template <int E>
-__device__ __forceinline__ int k_elem(int j, int d, int P) {
-  return ((d / E) * P + j) * E + (d % E);
-}
-template <int E>
-__device__ __forceinline__ int v_elem(int j, int d, int D) {
-  constexpr int TB = 4 * E;
-  const int blk = j / TB, r = j % TB;
-  const int c = (r & 15) >> 2, e = 4 * (r >> 4) + (r & 3);
-  return blk * TB * D + (c * D + d) * E + e;
-}
-__device__ __forceinline__ size_t chunk_elem(int page, int g, int Hkv, int P, int D) {
-  return ((size_t)page * (size_t)Hkv + (size_t)g) * (size_t)P * (size_t)D;
-}
-
-// ---------------------------------------------------------------------------
-// Wave-level helpers (64 lanes)
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int x = __shfl_up(v, o);
-    if (lane >= o) v += x;
-  }
-  return v;
-}
-typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ float fbits(uint32_t u) { return __builtin_bit_cast(float, u); }
-__device__ __forceinline__ uint32_t ubits(float f) { return __builtin_bit_cast(uint32_t, f); }
-
-// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = ubits(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-// Upper halves of two fp32 words packed as (lo, hi) bf16 pair = truncation.
-__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
-  return __builtin_amdgcn_perm(ubits(hi), ubits(lo), 0x07060302u);
-}
-// p = hi + lo with hi, lo bf16 (truncated): ~16 significant bits of p.
-__device__ __forceinline__ u32x2_t split_pair(float a, float b) {
-  const float ra = a - fbits(ubits(a) & 0xffff0000u);
-  const float rb = b - fbits(ubits(b) & 0xffff0000u);
-  return u32x2_t{pack_hi16(a, b), pack_hi16(ra, rb)};
-}
-// Probabilities of two 16-token tiles (8 per lane) as hi and lo bf16x8 operands.
-__device__ __forceinline__ void split_probs(const float (&x)[4], const float (&y)[4], float mul,
-                                           u32x4_t& hi, u32x4_t& lo) {
-  const u32x2_t a = split_pair(x[0] * mul, x[1] * mul), b = split_pair(x[2] * mul, x[3] * mul);
-  const u32x2_t c = split_pair(y[0] * mul, y[1] * mul), d = split_pair(y[2] * mul, y[3] * mul);
-  hi = u32x4_t{a.x, b.x, c.x, d.x};
-  lo = u32x4_t{a.y, b.y, c.y, d.y};
-}
-// As split_probs, with the two tiles interleaved: word i holds x[i] and y[i]
-// (the slot order of the int4 operands below).
-__device__ __forceinline__ void split_probs_zip(const float (&x)[4], const float (&y)[4], float mul,
-                                               u32x4_t& hi, u32x4_t& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x2_t a = split_pair(x[i] * mul, y[i] * mul);
-    hi[i] = a.x;
-    lo[i] = a.y;
-  }
-}
-// Four fp8 e4m3 bytes -> four bf16 (exact: every e4m3 value is a bf16 value).
-__device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  u32x2_t r;
-  r.x = pack_hi16(a.x, a.y);
-  r.y = pack_hi16(b.x, b.y);
-  return r;
-}
-// Four int8 bytes -> four bf16 (exact: |v| <= 128 has at most 8 significant
-// bits).  Each signed-byte conversion is one instruction (a sign-extending byte
-// select on the int -> float convert).
-__device__ __forceinline__ u32x2_t i8x4_to_bf16x4(uint32_t w) {
-  const float a = (float)(int8_t)w, b = (float)(int8_t)(w >> 8);
-  const float c = (float)(int8_t)(w >> 16), d = (float)((int32_t)w >> 24);
-  return u32x2_t{pack_hi16(a, b), pack_hi16(c, d)};
-}
-// Eight int4 codes (one word, element k in nibble k: element 2i in the low
-// nibble of byte i) -> a bf16x8 operand holding 136 + n for each code n in
-// [-8, 7]: with u = n + 8 (the code with its top bit flipped), the bf16 pattern
-// 0x4300 | u is exactly 128 + u.  Nibbles i and 4 + i lie 16 bits apart, so
-// one shift and one and-xor (which also flips the top bits) give both: slot
-// order (e0, e4, e1, e5, e2, e6, e3, e7).  The other operand of each product
-// is laid out in that order, and products carry 136 * (sum of the other
-// operand), which callers subtract.
-__device__ __forceinline__ u32x4_t nib8_to_bf16x8(uint32_t w) {
-  u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = ((w >> (4 * i)) & 0x000F000Fu) ^ 0x43084308u;
-  return r;
-}
-// Eight bf16 values (natural order) reordered to the slot order above.
-__device__ __forceinline__ u32x4_t zip_halves(u32x4_t x) {
-  return u32x4_t{__builtin_amdgcn_perm(x[2], x[0], 0x05040100u), __builtin_amdgcn_perm(x[2], x[0], 0x07060302u),
-                 __builtin_amdgcn_perm(x[3], x[1], 0x05040100u), __builtin_amdgcn_perm(x[3], x[1], 0x07060302u)};
-}
-constexpr float INT4_BIAS = 136.f;
-
-// Eight one-byte cache elements (fp8 e4m3 or int8) -> a bf16x8 MFMA operand.
-template <int KVT>
-__device__ __forceinline__ u32x4_t byte8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  const u32x2_t a = KVT == KV_FP8 ? fp8x4_to_bf16x4(w0) : i8x4_to_bf16x4(w0);
-  const u32x2_t b = KVT == KV_FP8 ? fp8x4_to_bf16x4(w1) : i8x4_to_bf16x4(w1);
-  return u32x4_t{a.x, a.y, b.x, b.y};
-}
-
-__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ u32x4_t ld16(const uint8_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
-// Streaming load for K/V: each byte is read exactly once per call, so mark it
-// nontemporal and keep it from displacing other lines in L2 and the MALL.
-__device__ __forceinline__ u32x4_t ld16_stream(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
-
-// ---------------------------------------------------------------------------
-// Work split.  Units are (b, g, range) in b-major, then g, then range order;
-// range r of (b, g) covers tokens [r*PT, min(L_b, (r+1)*PT)).  With T units and
-// at most Wmax waves, k = ceil(T / Wmax) and W = ceil(T / k) waves get work;
-// wave w owns units [floor(w*T/W), floor((w+1)*T/W)).
-// ---------------------------------------------------------------------------
-struct Split {
-  int64_t T;
-  int64_t W;
-};
-__device__ __forceinline__ Split make_split(int64_t T, int Wmax) {
-  Split s;
-  s.T = T;
-  const int64_t k = (T + Wmax - 1) / Wmax;
-  s.W = T > 0 ? (T + k - 1) / k : 0;
-  return s;
-}
-__device__ __forceinline__ int64_t range_begin(const Split& s, int64_t w) { return w * s.T / s.W; }
-// The wave whose range contains unit idx.
-__device__ __forceinline__ int64_t wave_of(const Split& s, int64_t idx) {
-  return ((idx + 1) * s.W - 1) / s.T;
-}
-__device__ __forceinline__ int ranges_of(int L, int PT) { return L > 0 ? (L + PT - 1) / PT : 0; }
-
-// Store 4 consecutive outputs.
-template <bool OUT_BF16>
-__device__ __forceinline__ void store_out4(void* out_, size_t idx, f32x4_t v) {
-  if (OUT_BF16) {
-    u32x2_t p;
-    p.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-    p.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out_) + idx) = p;
-  } else {
-    *reinterpret_cast<f32x4_t*>(static_cast<float*>(out_) + idx) = v;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the n partial ranges of one (b, g) for 256 of its G*D

@@ -145,3 +145,51 @@ def test_append_fp8_rejects_bad_arguments(over, code):
 
 def test_append_fp8_batch_zero_is_a_noop():
     assert _append_fp8(b=0, k=0, v=0, ks=0, vs=0) == 0
+
+
+def _append_chunk(**over):
+    a = dict(k=F, v=F, dt=1, cu=F, tot=100, bt=F, mp=4, sl=F, b=2, kp=F, vp=F, np_=8, hkv=2, d=128, p=64)
+    a.update(over)
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return pkv.lib().pkv_kv_append_chunk(vp(a["k"]), vp(a["v"]), a["dt"], vp(a["cu"]), a["tot"], vp(a["bt"]),
+                                         a["mp"], vp(a["sl"]), a["b"], vp(a["kp"]), vp(a["vp"]), a["np_"],
+                                         a["hkv"], a["d"], a["p"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(cu=0), -1), (dict(k=0), -1), (dict(tot=-1), -2), (dict(d=96), -2), (dict(p=48), -2),
+    (dict(dt=9), -3), (dict(k=F + 4), -6),
+])
+def test_append_chunk_rejects_bad_arguments(over, code):
+    assert _append_chunk(**over) == code
+    assert pkv.lib().pkv_last_error()
+
+
+def test_append_chunk_empty_is_a_noop():
+    assert _append_chunk(b=0, k=0, v=0, cu=0) == 0
+    assert _append_chunk(tot=0, k=0, v=0) == 0
+
+
+def _prefill(**over):
+    a = dict(q=F, qdt=1, cu=F, tot=100, kp=F, vp=F, kvdt=1, bt=F, mp=4, sl=F, b=2, np_=8, hq=8, hkv=2, d=128,
+             p=64, scale=0.1, out=F, odt=1)
+    a.update(over)
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return pkv.lib().pkv_paged_prefill(vp(a["q"]), a["qdt"], vp(a["cu"]), a["tot"], vp(a["kp"]), vp(a["vp"]),
+                                       a["kvdt"], vp(a["bt"]), a["mp"], vp(a["sl"]), a["b"], a["np_"], a["hq"],
+                                       a["hkv"], a["d"], a["p"], a["scale"], vp(a["out"]), a["odt"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), -1), (dict(cu=0), -1), (dict(out=0), -1), (dict(tot=-1), -2), (dict(hq=7), -2),
+    (dict(hq=1024, hkv=2), -2), (dict(d=96), -2), (dict(kvdt=0, p=16), -3), (dict(kvdt=2), -3),
+    (dict(qdt=0), -3), (dict(odt=2), -3), (dict(q=F + 2), -6), (dict(out=F + 8), -6),
+])
+def test_prefill_rejects_bad_arguments(over, code):
+    assert _prefill(**over) == code
+    assert pkv.lib().pkv_last_error()
+
+
+def test_prefill_empty_is_a_noop():
+    assert _prefill(b=0, q=0, out=0, cu=0) == 0
+    assert _prefill(tot=0, q=0, out=0) == 0

@@ -1,0 +1,210 @@
+"""GPU parity of chunked prefill: pkv_kv_append_chunk (bit-exact against
+oracle.paged.append_chunk) and pkv_paged_prefill (against oracle.paged.prefill
+at the bf16 tolerance), through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_decode_amd as pkv
+from oracle import paged
+from workloads import codec, configs, layout
+from tests._helpers import check_close, dev_tensor, gpu_out, host_bytes
+
+pytestmark = pytest.mark.gpu
+
+
+def _up(wl):
+    return {k: dev_tensor(getattr(wl, k)) for k in ("q", "cu_q", "block_tables", "seq_lens", "k_pool", "v_pool",
+                                                    "k_new", "v_new")}
+
+
+def _gpu_append_chunk(wl, d, seq_lens=None, cu=None, bt=None):
+    pkv.kv_append_chunk(d["k_new"], d["v_new"], wl.kv_dtype, d["cu_q"] if cu is None else cu,
+                        d["block_tables"] if bt is None else bt, d["seq_lens"] if seq_lens is None else seq_lens,
+                        d["k_pool"], d["v_pool"], wl.Hkv, wl.D, wl.P)
+
+
+def _gpu_prefill(wl, d, out_dtype=None, seq_lens=None, bt=None):
+    odt = out_dtype or wl.out_dtype
+    out = torch.full((wl.T, wl.Hq, wl.D), 7.0, dtype=torch.bfloat16 if odt == "bf16" else torch.float32,
+                     device="cuda")
+    pkv.paged_prefill(d["q"], wl.q_dtype, d["cu_q"], d["k_pool"], d["v_pool"], wl.kv_dtype,
+                      d["block_tables"] if bt is None else bt, d["seq_lens"] if seq_lens is None else seq_lens,
+                      wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, odt)
+    torch.cuda.synchronize()
+    return gpu_out(out)
+
+
+def _full_pools(wl):
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    paged.append_chunk(wl.k_new, wl.v_new, wl.kv_dtype, wl.cu_q, wl.block_tables, wl.seq_lens, kp, vp, wl.P)
+    return kp, vp
+
+
+def _quantised_case(fmt, seed, ctx, chunk, Hq, Hkv, D, P):
+    """A chunk workload whose cache and rows are stored in ``fmt`` (bytes as the
+    generator's page quantiser writes them; the append copies them as given)."""
+    wl = configs.prefill_case("q", seed, ctx, chunk, Hq, Hkv, D, P, kv_dtype="f32" if fmt == "f32" else "bf16")
+    L = wl.seq_lens
+    bits = layout.ELEM_BITS[fmt]
+    kp = layout.empty_pool(wl.num_pages, Hkv, P, D, fmt)
+    vp = layout.empty_pool(wl.num_pages, Hkv, P, D, fmt)
+    kidx, vidx = layout.k_chunk_index(P, D, fmt), layout.v_chunk_index(P, D, fmt)
+    T = wl.T
+    rowb = D * bits // 8
+    kn = np.zeros((T, Hkv, rowb), np.uint8) if fmt != "f32" else np.zeros((T, Hkv, D), np.float32)
+    vn = kn.copy()
+    for b in range(wl.B):
+        n = int(L[b])
+        kf = configs.draw_seq_f32(wl.seed, 2, b, n, Hkv, D)
+        vf = configs.draw_seq_f32(wl.seed, 3, b, n, Hkv, D)
+        if fmt == "f32":
+            k, v = kf, vf
+        else:
+            k, _ = configs.QUANTIZERS[fmt](kf, P)
+            v, _ = configs.QUANTIZERS[fmt](vf, P)
+        c0 = int(ctx[b])
+        pages = wl.block_tables[b, :-(-c0 // P)] if c0 else np.zeros(0, np.int32)
+        layout.pack_sequence(kp, pages, k[:c0], P, kidx, fmt)
+        layout.pack_sequence(vp, pages, v[:c0], P, vidx, fmt)
+        rk, rv = k[c0:], v[c0:]
+        if fmt == "i4":
+            rk, rv = layout.pack_nibbles(rk), layout.pack_nibbles(rv)
+        kn[wl.cu_q[b]:wl.cu_q[b + 1]] = rk
+        vn[wl.cu_q[b]:wl.cu_q[b + 1]] = rv
+    wl.kv_dtype, wl.k_pool, wl.v_pool, wl.k_new, wl.v_new = fmt, kp, vp, kn, vn
+    return wl
+
+
+APPEND_CASES = [  # (fmt, D, P)
+    ("bf16", 128, 64), ("bf16", 64, 32), ("f32", 64, 16), ("fp8", 128, 64), ("i8", 64, 64), ("i4", 128, 128),
+]
+
+
+@pytest.mark.parametrize("fmt,D,P", APPEND_CASES, ids=lambda v: str(v))
+def test_append_chunk_bit_exact(fmt, D, P):
+    ctx = [0, 3, 130, 17, 250, 0]
+    chunk = [1, 200, 2, 0, 61, 129]
+    wl = _quantised_case(fmt, 40 + D + P, ctx, chunk, 4, 2, D, P) if fmt != "bf16" else \
+        configs.prefill_case("a", 40 + D + P, ctx, chunk, 4, 2, D, P)
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    torch.cuda.synchronize()
+    kp, vp = _full_pools(wl)
+    assert np.array_equal(host_bytes(d["k_pool"]), kp.reshape(-1).view(np.uint8))
+    assert np.array_equal(host_bytes(d["v_pool"]), vp.reshape(-1).view(np.uint8))
+
+
+def test_append_chunk_skips_what_does_not_fit():
+    wl = configs.prefill_case("a", 51, [0, 5, 40, 17], [7, 1, 33, 16], 4, 2, 64, 32)
+    d = _up(wl)
+    lens = wl.seq_lens.copy()
+    lens[0] = 3                                    # chunk of 7 > L = 3
+    lens[2] = wl.max_pages * wl.P + 1              # beyond the table row
+    bt = wl.block_tables.copy()
+    L3 = int(lens[3])
+    bt[3, :-(-L3 // wl.P)] = wl.num_pages + 5      # every page of sequence 3 out of range
+    _gpu_append_chunk(wl, d, seq_lens=dev_tensor(lens), bt=dev_tensor(bt))
+    torch.cuda.synchronize()
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    cu2 = np.zeros_like(wl.cu_q)
+    cu2[1:] = np.cumsum([wl.chunk_lens[b] if b == 1 else 0 for b in range(wl.B)])
+    sel = np.arange(wl.cu_q[1], wl.cu_q[2])
+    paged.append_chunk(wl.k_new[sel], wl.v_new[sel], "bf16", cu2, wl.block_tables, lens, kp, vp, wl.P)
+    assert np.array_equal(host_bytes(d["k_pool"]), kp.reshape(-1).view(np.uint8))
+    assert np.array_equal(host_bytes(d["v_pool"]), vp.reshape(-1).view(np.uint8))
+
+
+PREFILL_CASES = [  # (ctx, chunk, Hq, Hkv, D, P)
+    ([0, 5, 100, 300], [1, 70, 33, 130], 8, 2, 128, 64),        # G 4, ragged, several tiles and pages
+    ([64, 0, 31], [64, 257, 97], 2, 2, 64, 32),                   # G 1: blocks of 256 tokens
+    ([200, 9], [45, 300], 16, 2, 128, 128),                       # G 8
+    ([33, 0], [80, 19], 4, 2, 64, 64),                            # G 2
+    ([100], [40], 32, 2, 128, 64),                                # G 16
+    ([70, 1], [90, 130], 6, 2, 128, 32),                          # G 3: padding rows in every block
+    ([0, 0, 0], [1, 2, 300], 8, 2, 128, 64),                      # pure prefill (no cached tokens)
+]
+
+
+@pytest.mark.parametrize("ctx,chunk,Hq,Hkv,D,P", PREFILL_CASES, ids=lambda v: str(v))
+def test_prefill_matches_oracle(ctx, chunk, Hq, Hkv, D, P):
+    wl = configs.prefill_case("p", 60 + Hq + D + P, ctx, chunk, Hq, Hkv, D, P)
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    got = _gpu_prefill(wl, d)
+    kp, vp = _full_pools(wl)
+    ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                        wl.scale)
+    check_close(got, ref, "bf16", "prefill", out_rounding=True)
+
+
+def test_prefill_fp32_output_and_large_logits():
+    wl = configs.prefill_case("p", 71, [150, 20], [70, 90], 8, 2, 128, 64, out_dtype="f32", q_mult=3.0)
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    got = _gpu_prefill(wl, d, out_dtype="f32")
+    kp, vp = _full_pools(wl)
+    ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                        wl.scale)
+    check_close(got, ref, "bf16", "prefill f32 out")
+
+
+def test_prefill_rows_without_keys_zero_and_other_rows_untouched():
+    wl = configs.prefill_case("p", 72, [0, 10, 0], [20, 0, 30], 8, 2, 64, 32)
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    kp, vp = _full_pools(wl)
+    lens = wl.seq_lens.copy()
+    lens[0] = 12                                   # chunk of 20 over 12 keys: rows 0..7 at p < 0
+    got = _gpu_prefill(wl, d, seq_lens=dev_tensor(lens))
+    ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, lens, wl.Hq, wl.P, wl.scale)
+    assert np.all(got[:8] == 0)
+    check_close(got, ref, "bf16", "prefill p < 0", out_rounding=True)
+
+
+def test_prefill_bad_page_gives_nan_rows_of_that_head_block_only():
+    wl = configs.prefill_case("p", 73, [40, 50], [30, 20], 8, 2, 64, 32)
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    kp, vp = _full_pools(wl)
+    bt = wl.block_tables.copy()
+    bt[1, 0] = wl.num_pages + 3                    # sequence 1's first page id out of range
+    got = _gpu_prefill(wl, d, bt=dev_tensor(bt))
+    r0, r1 = int(wl.cu_q[1]), int(wl.cu_q[2])
+    assert np.all(np.isnan(got[r0:r1]))
+    ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                        wl.scale, batches=[0])
+    check_close(got[:r0], ref[:r0], "bf16", "prefill other sequence", out_rounding=True)
+
+
+def test_prefill_padding_rows_not_written():
+    """Rows of out outside every sequence's range keep their contents."""
+    wl = configs.prefill_case("p", 74, [10, 20], [5, 7], 8, 2, 64, 32)
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    cu = wl.cu_q.copy()
+    cu[0] = cu[1] = 5                              # sequence 0 given no rows: rows 0..4 belong to nobody
+    d["cu_q"] = dev_tensor(cu)
+    got = _gpu_prefill(wl, d)
+    assert np.all(got[:5] == 7.0)
+    assert np.isfinite(got[5:]).all() and not np.all(got[5:] == 7.0)
+
+
+def test_config_chunked_prefill_sampled_sequences():
+    """The full chunked-prefill workload in the launch the benchmark times; two
+    sequences (the shortest and the longest cached context) checked against the
+    oracle, every row finite."""
+    wl = configs.chunked_prefill_bf16()
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    got = _gpu_prefill(wl, d)
+    assert np.isfinite(got).all()
+    ctx = wl.seq_lens - wl.chunk_lens
+    picks = [int(np.argmin(ctx)), int(np.argmax(ctx))]
+    kp = host_bytes(d["k_pool"]).view(np.uint16).reshape(wl.k_pool.shape)
+    vp = host_bytes(d["v_pool"]).view(np.uint16).reshape(wl.v_pool.shape)
+    ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                        wl.scale, batches=picks)
+    for b in picks:
+        r0, r1 = int(wl.cu_q[b]), int(wl.cu_q[b + 1])
+        check_close(got[r0:r1], ref[r0:r1], "bf16", f"sequence {b}", out_rounding=True)
