@@ -32,7 +32,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "paged decode attention: KV HBM GB/s (fraction of peak) + seqs/s per layer"
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", "pkv_kernels.hip")
 WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "int8_kv",
-             "inflight_int8", "int4_kv", "inflight_int4", "tiny_fp32"]
+             "inflight_int8", "int4_kv", "inflight_int4", "tiny_fp32", "chunked_prefill_bf16"]
+PREFILL_METRIC = "paged chunked prefill attention: TFLOP/s (causal pairs, algorithmic)"
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA peak
 SCALED = ("fp8", "i8", "i4")    # caches of one byte or less, with per-(page, kv head) scales
 ELEM_BITS = {"f32": 32, "bf16": 16, "fp8": 8, "i8": 8, "i4": 4}
 
@@ -182,6 +184,111 @@ def cpu_baseline(wl, steps, seconds):
                       f"(C oracle, {threads} threads), {el:.1f} s"}
 
 
+def cpu_baseline_prefill(wl, seconds):
+    """The fp64 numpy oracle on this host: whole sequences (shortest cached context
+    first) until the time budget is spent; flops counted as for the GPU."""
+    import numpy as np
+    from oracle import paged
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    t0 = time.perf_counter()
+    paged.append_chunk(wl.k_new, wl.v_new, wl.kv_dtype, wl.cu_q, wl.block_tables, wl.seq_lens, kp, vp, wl.P)
+    ctx = wl.seq_lens - wl.chunk_lens
+    flops, done = 0, []
+    for b in np.argsort(ctx, kind="stable"):
+        paged.prefill(wl.q, wl.q_dtype, wl.cu_q, kp, vp, wl.kv_dtype, wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                      wl.scale, batches=[int(b)])
+        L, C = int(wl.seq_lens[b]), int(wl.chunk_lens[b])
+        flops += 4 * wl.Hq * wl.D * (C * (L - C + 1) + C * (C - 1) // 2)
+        done.append(int(b))
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"chunk append + fp64 prefill of {len(done)} of {wl.B} sequences (shortest cached "
+                      f"context first; numpy einsum, one thread), {el:.1f} s"}
+
+
+def bench_prefill(args):
+    """One chunked-prefill step of one layer: kv_append_chunk of every sequence's
+    chunk, then causal prefill attention of its query rows over the pages."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_decode_amd as pkv
+    from workloads import configs
+
+    wl = configs.PREFILL_CONFIGS[args.workload]()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def T(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    pool_bytes = wl.k_pool.nbytes + wl.v_pool.nbytes
+    layers = args.layers or max(1, min(8, math.ceil(2.0e9 / pool_bytes)))
+    q, cu, bt, sl = T(wl.q), T(wl.cu_q), T(wl.block_tables), T(wl.seq_lens)
+    kn, vn = T(wl.k_new), T(wl.v_new)
+    kps = [T(wl.k_pool) for _ in range(layers)]
+    vps = [T(wl.v_pool) for _ in range(layers)]
+    out = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def append(i):
+        pkv.kv_append_chunk(kn, vn, wl.kv_dtype, cu, bt, sl, kps[i % layers], vps[i % layers], wl.Hkv, wl.D, wl.P)
+
+    def attend(i):
+        pkv.paged_prefill(q, wl.q_dtype, cu, kps[i % layers], vps[i % layers], wl.kv_dtype, bt, sl, wl.Hq, wl.Hkv,
+                          wl.D, wl.P, wl.scale, out, wl.out_dtype)
+
+    for i in range(args.warmup):
+        append(i)
+        attend(i)
+    evs = DeviceEvents(2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs.record(0)
+    for i in range(args.steps):
+        append(args.warmup + i)
+        attend(args.warmup + i)
+    evs.record(1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    # the prefill kernel alone (the dominant kernel), K launches back to back
+    evs.record(2)
+    for i in range(args.steps):
+        attend(args.warmup + i)
+    evs.record(3)
+    torch.cuda.synchronize()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    step_ev = evs.elapsed_ms(0) / args.steps
+    pre_ms = evs.elapsed_ms(1) / args.steps
+    evs.close()
+    flops = wl.flops()
+    tfs = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (pre_ms * 1e-3) / 1e12
+    rec = {
+        "metric": PREFILL_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled pages)",
+        "config": {"workload": args.workload, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.D, "page_size": wl.P, "chunk_tokens": int(wl.T),
+                   "mean_cached_context": float(np.mean(wl.seq_lens - wl.chunk_lens)), "layers_rotated": layers,
+                   "step": "kv_append_chunk of every chunk, then causal paged prefill attention"},
+        "flops_per_step": int(flops), "kv_bytes_per_step": int(wl.kv_bytes()),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "call_ms_mean": round(pre_ms, 5),
+                     "alg_flops_per_call": int(flops)},
+        "diagnostics": {"step_ms_events": round(step_ev, 5), "append_chunk_ms": round(step_ev - pre_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def diagnostics(pkv, wl, q, bt, kps, vps, kss, vss, dsteps, out, ws, step, i0, n=30):
     """Per-launch spread and the parts of a step, measured after the timed region.
 
@@ -254,6 +361,9 @@ def main():
     import paged_kv_attention_decode_amd as pkv
     from workloads import configs
 
+    if args.workload in configs.PREFILL_CONFIGS:
+        bench_prefill(args)
+        return
     gen = configs.CONFIGS[args.workload]
     wl = gen()
     dev = torch.device("cuda:0")

@@ -2,32 +2,58 @@
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["pkv_kernels.hip", "pkv_prefill.hip", "pkv_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# source -> extra flags.  The prefill kernel's MFMA accumulators (64 query rows
+# x D outputs per wave) take the vector-register form: in the accumulation
+# registers, the rare rescale of the running output made the compiler copy every
+# accumulator out and back around its branch on every tile.
+SOURCES = {
+    "pkv_kernels.hip": [],
+    "pkv_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "pkv_api.cpp": [],
+}
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source of the library; always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
-    if verbose:
-        print(" ".join(cmd))
-    os.replace(tmp, LIB)
+    """Compile every HIP/C++ source of the library (always) and link it."""
+    tmpdir = tempfile.mkdtemp(prefix="pkv_build_")
+    try:
+        inc = ["-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
+        procs, objs = [], []
+        for src, extra in SOURCES.items():
+            obj = os.path.join(tmpdir, src + ".o")
+            cmd = [HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd))
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+            objs.append(obj)
+        for cmd, p in procs:
+            out, err = p.communicate()
+            if p.returncode != 0:
+                raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + out + err)
+        tmp = LIB + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd))
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

@@ -247,8 +247,8 @@ int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads)
     return fail(PKV_E_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
                 num_kv_heads);
-  if (num_q_heads / num_kv_heads > 256)
-    return fail(PKV_E_SHAPE, "group size %d > 256", num_q_heads / num_kv_heads);
+  if (num_q_heads / num_kv_heads > 128)
+    return fail(PKV_E_SHAPE, "group size %d > 128", num_q_heads / num_kv_heads);
   if (batch == 0 || total_q == 0) return PKV_OK;
   if ((rc = check_align({q, k_pool, v_pool, out}))) return rc;
   pkv::PrefillArgs a{q, cu_q, total_q, k_pool, v_pool, block_tables, seq_lens, out, out_dtype == PKV_BF16,

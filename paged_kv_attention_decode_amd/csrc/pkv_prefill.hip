@@ -12,19 +12,31 @@
 // Design for gfx950
 // -----------------
 // * Query rows are (chunk token, head of the kv group) pairs.  A workgroup of
-//   four waves owns one (sequence, kv head, block of 256/G chunk tokens); each
-//   wave holds 64 rows as four 16-column N tiles of the QK^T and PV MFMAs, the
-//   query operand in registers for the whole kv range.
-// * K and V come straight from the pages into MFMA operand registers, as in
-//   decode (the page layout puts each 16-byte group where a lane needs it), one
-//   32-token tile ahead; every K or V operand feeds four MFMAs (one per N tile).
-//   The workgroups of a kv head g are blockIdx = g (mod Hkv), so with eight kv
-//   heads all readers of one head's pages run on one XCD and share its L2.
+//   four waves owns one (sequence, kv head, block of 128/G chunk tokens); each
+//   wave holds 32 rows as two 16-column N tiles of the QK^T and PV MFMAs, with
+//   its query operand in registers.  That keeps a wave within 256 registers, so
+//   two workgroups share a CU and each SIMD runs two waves: one wave's softmax
+//   (VALU, cross-lane exchanges) overlaps the other's MFMAs.
+// * K and V tiles are fetched once per workgroup with direct global -> LDS
+//   loads (the page layout puts each 16-byte group where a lane needs it, so a
+//   fetching lane's group is exactly some lane's MFMA operand), double buffered
+//   one 32-token tile ahead, and read by all four waves; every K or V operand
+//   feeds four MFMAs (one per N tile).  The workgroups of a kv head g are
+//   blockIdx = g (mod Hkv), so with eight kv heads all readers of one head's
+//   pages run on one XCD and share its L2.
 // * Workgroups holding the later (longer-range) blocks of a sequence are
 //   dispatched first.
 // * S^T = K Q^T leaves four tokens of one query row per lane, which is the
 //   B-operand layout of O^T += V^T P^T: probabilities never cross lanes.  They
-//   enter the MFMA as one bf16 value (round to nearest even).
+//   enter the MFMA as one bf16 value (round to nearest even); the row sums come
+//   from one more MFMA against an all-ones operand, i.e. from the same bf16
+//   values the PV products use.
+// * Online softmax with a lazy reference: p = 2^(s - m) against a reference m
+//   that moves (rescaling O and the row sum) only when a tile's maximum exceeds
+//   it by more than 8, so p <= 256 and the rescale, which reads and writes
+//   every accumulator, runs a few times per row instead of on most early tiles.
+//   The softmax scale (log2 e folded in) enters through one fma per score;
+//   a negative scale is folded into the sign of q.
 // * Only tiles that reach past a wave's first row position apply the causal
 //   mask; V elements of tokens at or past the wave's last position + 1 are
 //   zeroed (they may be unwritten slots).
@@ -33,6 +45,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <type_traits>
 
 #include "pkv_internal.h"
@@ -41,11 +54,33 @@
 namespace pkv {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
 // Two fp32 -> packed bf16 pair (round to nearest even), element a low.
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
   return __builtin_bit_cast(uint32_t, r);
+}
+
+// v *= a element by element, each product written back into its own register
+// (a plain multiply inside a rarely taken branch makes the compiler give the
+// products new registers and copy every accumulator on the common path).
+__device__ __forceinline__ void scale_in_place(f32x4_t& v, float a) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = v[i];
+    asm("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(a));
+    v[i] = x;
+  }
+}
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one MFMA column):
+// the 16-lane row swap pairs rows 0-1 and 2-3, the 32-lane swap the halves.
+__device__ __forceinline__ float colmax4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(ubits(x), ubits(x), false, false);
+  const float y = fmaxf(fbits(a[0]), fbits(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(ubits(y), ubits(y), false, false);
+  return fmaxf(fbits(c[0]), fbits(c[1]));
 }
 
 // ---------------------------------------------------------------------------
@@ -91,23 +126,43 @@ __global__ __launch_bounds__(256) void append_chunk_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Prefill attention, bf16 cache.  TPW = 256 / G chunk tokens per workgroup;
-// row rho (0..255) of a workgroup is chunk token qb * TPW + rho / G and head
+// Prefill attention, bf16 cache.  TPW = 128 / G chunk tokens per workgroup;
+// row rho (0..127) of a workgroup is chunk token qb * TPW + rho / G and head
 // rho % G of kv group g (rows at or past TPW * G are padding).  Wave wv owns
-// rows 64 wv .. 64 wv + 63; N tile nt holds rows 64 wv + 16 nt + (0..15).
+// rows 32 wv .. 32 wv + 31; N tile nt holds rows 32 wv + 16 nt + (0..15).
+//
+// K/V tiles of 32 tokens are staged in LDS, NBUF buffers deep: a tile is NOP
+// operand slices of 64 lanes x 16 bytes (K slice (sub, kk) is what lane l of
+// the QK^T MFMA needs as its A operand for 16-token sub-tile sub and k step kk;
+// V slice dt the A operand of PV for dims 16 dt ..), each fetched by one wave
+// with a direct global -> LDS load (lane l's 16 bytes land at slot l).  Every
+// wave then reads the slices as its own operands.  Tiles are fetched NBUF - 1
+// ahead, so a fetch has that many tiles of compute to arrive.  One barrier per
+// tile: before it each wave waits for its own slices of tile i (its later
+// fetches may stay in flight) and for its own LDS reads; after it, tile i is
+// complete and no wave still reads buffer (i - 1) mod NBUF, which the fetch of
+// tile i + NBUF - 1 then fills.  Every wave runs every iteration (fetches and
+// barrier), computing only tiles below its own kv_end.
 // ---------------------------------------------------------------------------
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ cu, int total_q,
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, void* __restrict__ out_, int B, int MP, int NP, int Hq, int Hkv,
-    int G, int TPW, int P, float scale_log2) {
+    int G, int TPW, int P, float scale_log2, uint32_t q_sign) {
   constexpr int E = 8;              // bf16 elements per 16-byte group
   constexpr int TS = 32;            // tokens per tile (one V block)
-  constexpr int NKK = D / 32;       // K groups per lane per 16-token sub-tile
+  constexpr int NKK = D / 32;       // k steps of the QK^T MFMA
   constexpr int NDT = D / 16;       // 16-dim PV tiles
-  constexpr int NT = 4;             // 16-row N tiles per wave
+  constexpr int NT = 2;             // 16-row N tiles per wave
+  constexpr int NKOP = 2 * NKK;     // K slices per tile
+  constexpr int NOP = NKOP + NDT;   // K and V slices per tile (16 at D = 128)
+  constexpr int OPW = NOP / 4;      // slices each wave fetches
+  constexpr float TH = 8.f;         // reference lag allowed before a rescale (log2 units)
+  constexpr int NBUF = 4;           // K/V tile buffers (prefetch distance NBUF - 1)
   const float NEG_INF = -__builtin_inff();
+
+  __shared__ u32x4_t s_kv[NBUF][NOP][64];      // K/V tiles
 
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, c4 = lane >> 4;
@@ -115,7 +170,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int g = uniform((int)(blockIdx.x % (unsigned)Hkv));
   const int unit = uniform((int)(blockIdx.x / (unsigned)Hkv));
 
-  // ---- (sequence, token block) of this workgroup --------------------------------
+  // ---- (sequence, token block) of this workgroup (same in every wave) ---------
   // blocks of sequence b: ceil(C_b / TPW); units are numbered in sequence order,
   // and within a sequence from the last block to the first.
   int b = -1, qb = 0;
@@ -142,7 +197,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       run = uniform(__builtin_amdgcn_readlane(incl, 63));
     }
   }
-  if (b < 0) return;
+  if (b < 0) return;                           // the whole workgroup: no unit
   b = uniform(b);
   qb = uniform(qb);
   const int r0 = uniform(cu[b]);
@@ -150,32 +205,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int L = uniform(seq_lens[b]);
   const int ctx = L - C;                       // position of chunk token 0
 
-  // ---- this wave's rows ----------------------------------------------------------
-  const int rows = TPW * G;                    // real rows of the workgroup
+  // ---- rows and key ranges -------------------------------------------------------
+  const int rows = TPW * G;                    // real rows of the workgroup (before C)
   const int tok_base = qb * TPW;
-  const int rho_w0 = 64 * wv;
-  if (rho_w0 >= rows || tok_base + rho_w0 / G >= C) return;      // no real row in this wave
-  const int rho_last = min(rho_w0 + 63, rows - 1);
-  const int tok_last = min(C - 1, tok_base + rho_last / G);
+  const int tok_wg_last = min(C - 1, tok_base + (rows - 1) / G);
+  const int kv_end_wg = max(ctx + tok_wg_last + 1, 0);           // keys any wave needs
+  const int rho_w0 = 16 * NT * wv;
+  const bool has_rows = rho_w0 < rows && tok_base + rho_w0 / G < C;
+  const int tok_last = min(C - 1, tok_base + min(rho_w0 + 16 * NT - 1, rows - 1) / G);
   const int pos_first = ctx + tok_base + rho_w0 / G;             // smallest row position
-  const int kv_end = max(ctx + tok_last + 1, 0);                 // keys 0 .. kv_end - 1
+  const int kv_end = has_rows ? max(ctx + tok_last + 1, 0) : 0;  // keys this wave needs
 
-  u32x4_t Q[NT][NKK];
   int pos_n[NT];                // position of this lane's row in each N tile (-1: none)
-  size_t orow[NT];              // output row offset (elements) of this lane's row
-  bool store_n[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  u32x4_t Q[NT][NKK];           // query operands (B of QK^T)
+  auto out_row = [&](int nt) -> int64_t {
     const int rho = rho_w0 + 16 * nt + r16;
     const int tok = tok_base + rho / G, h = rho % G;
-    const bool real = rho < rows && tok < C;
-    store_n[nt] = real;
-    pos_n[nt] = real ? max(ctx + tok, -1) : -1;
-    orow[nt] = real ? ((size_t)(r0 + tok) * Hq + (size_t)g * G + h) * D : 0;
+    if (rho >= rows || tok >= C) return -1;
+    return ((int64_t)(r0 + tok) * Hq + (int64_t)g * G + h) * D;
+  };
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t orow = out_row(nt);
+    const int tok = tok_base + (rho_w0 + 16 * nt + r16) / G;
+    pos_n[nt] = orow >= 0 ? max(ctx + tok, -1) : -1;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      Q[nt][kk] = real ? ld16(reinterpret_cast<const uint8_t*>(q + orow[nt] + 8 * c4 + 32 * kk))
-                       : u32x4_t{0, 0, 0, 0};
+      Q[nt][kk] = orow >= 0 ? ld16(reinterpret_cast<const uint8_t*>(q + orow + 8 * c4 + 32 * kk)) ^ q_sign
+                            : u32x4_t{0, 0, 0, 0};
   }
 
   f32x4_t O[NDT][NT];
@@ -183,165 +240,201 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) O[dt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[NT], l[NT];
+  // m: the softmax reference per row (scaled, log2 domain); Ls: row sums of p
+  // (every entry of Ls[nt] holds its column's sum).
+  float m[NT];
+  f32x4_t Ls[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = NEG_INF;
-    l[nt] = 0.f;
+    Ls[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
   const const_i32_ptr btrow = (const_i32_ptr)(bt + (size_t)b * MP);
-  auto page_of = [&](int idx) -> int {
-    idx = uniform(idx);
-    const int v = btrow[idx < MP ? idx : MP - 1];
-    return idx < MP ? v : -1;
+  // Wave wv fetches slices wv, wv + 4, ...: the first OPW / 2 are K slices, the
+  // rest V slices.  A slice's lane offset inside a page chunk is linear in the
+  // tile's token offset j (K: 16 bytes per token; V: 2 D bytes per token, j a
+  // multiple of 32), so it is computed once here and the fetch adds a
+  // wave-uniform base.
+  static_assert(NKOP % 4 == 0 && NDT % 4 == 0, "K and V slices must split evenly over four waves");
+  uint32_t sl_off[OPW];
+#pragma unroll
+  for (int o = 0; o < OPW; ++o) {
+    const int op = wv + 4 * o;
+    if (o < OPW / 2) {
+      const int sub = op / NKK, kk = op % NKK;
+      sl_off[o] = 2u * (uint32_t)k_elem<E>(16 * sub + r16, (c4 + 4 * kk) * E, P);
+    } else {
+      sl_off[o] = 2u * (uint32_t)v_elem<E>(4 * c4, (op - NKOP) * 16 + r16, D);
+    }
+  }
+  // Next tile to fetch: page index and token offset in it.  Returns whether its
+  // page id is bad (page 0 is read instead).
+  int f_pgi = 0, f_j = 0;
+  auto fetch_next = [&](int buf) -> bool {
+    const int page = f_pgi < MP ? btrow[f_pgi] : -1;
+    const bool badp = (unsigned)page >= (unsigned)NP;
+    const size_t ch = 2 * chunk_elem(badp ? 0 : page, g, Hkv, P, D);
+    const uint8_t* kc = kpool + ch + 16 * f_j;
+    const uint8_t* vc = vpool + ch + 2 * D * f_j;
+#pragma unroll
+    for (int o = 0; o < OPW; ++o) {
+      const uint8_t* src = (o < OPW / 2 ? kc : vc) + sl_off[o];
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)&s_kv[buf][wv + 4 * o][0], 16,
+                                       0, 0);
+    }
+    f_j += TS;
+    if (f_j == P) {
+      f_j = 0;
+      ++f_pgi;
+    }
+    return badp;
   };
-  u32x4_t kr[2][NKK], vr[NDT];
-  auto load_k = [&](int pg, int j) {
-    const uint8_t* kc = kpool + 2 * chunk_elem(pg, g, Hkv, P, D);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        kr[sub][kk] = ld16(kc + 2u * (uint32_t)k_elem<E>(j + 16 * sub + r16, (c4 + 4 * kk) * E, P));
-  };
-  auto load_v = [&](int pg, int j) {
-    const uint8_t* vc = vpool + 2 * chunk_elem(pg, g, Hkv, P, D);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      vr[dt] = ld16(vc + 2u * (uint32_t)v_elem<E>(j + 4 * c4, dt * 16 + r16, D));
+  auto slice = [&](int buf, int op) -> u32x4_t {
+    return *(volatile lds_u32x4_t*)(&s_kv[buf][op][lane]);
   };
 
-  bool bad = false;
-  if (kv_end > 0) {
-    int pgi = 0, j0 = 0;
-    int page = page_of(0);
-    bad = (unsigned)page >= (unsigned)NP;
-    load_k(bad ? 0 : page, 0);
-    load_v(bad ? 0 : page, 0);
-
-    auto tile = [&](const int t, auto last_tag) {
-      constexpr bool LAST = decltype(last_tag)::value;
-      int pgi_n = pgi, j_n = j0, page_n = page;
-      if constexpr (!LAST) {
-        j_n = j0 + TS;
-        if (j_n == P) {
-          j_n = 0;
-          ++pgi_n;
-        }
-        page_n = page_of(pgi_n);
+  // One tile from buffer buf.  MASK: the tile reaches past the wave's first row
+  // position (causal mask); LAST: the wave's final tile (V of keys at or past
+  // kv_end zeroed: they may be unwritten slots).
+  auto tile = [&](const int t, const int buf, auto mask_tag, auto last_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool LAST = decltype(last_tag)::value;
+    // ---- S^T = K Q^T: rows = 16 tokens, columns = query rows (unscaled) ------
+    f32x4_t acc[2][NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc[0][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc[1][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4_t k0 = slice(buf, kk), k1 = slice(buf, NKK + kk);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[0][nt] = mfma_bf16(k0, Q[nt][kk], acc[0][nt]);
+        acc[1][nt] = mfma_bf16(k1, Q[nt][kk], acc[1][nt]);
       }
-      const bool bad_n = (unsigned)page_n >= (unsigned)NP;
-      const int pg_ld_n = bad_n ? 0 : page_n;
-
-      // ---- S^T = K Q^T: rows = 16 tokens, columns = query rows ----------------
-      float s[2][NT][4];
+    }
+    // ---- online softmax per row (log2 domain, lazy reference) -----------------
+    // Unmasked scores are finite, so a column with any unmasked score has a
+    // finite reference after its first tile; masked scores (-inf) get p = 0.
+    u32x4_t pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float s[2][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[0][i] = acc[0][nt][i];
+        s[1][i] = acc[1][nt][i];
+      }
+      if constexpr (MASK) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t + 16 * sub + 4 * c4 + i > pos_n[nt]) s[sub][i] = NEG_INF;
+      }
+      float tmax = NEG_INF;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[sub][i]);
+      tmax = colmax4(tmax);
+      const float tm = tmax == NEG_INF ? NEG_INF : tmax * scale_log2;
+      const bool grow = tm > m[nt] + TH;
+      const float mref = grow ? tm : m[nt];
+      if (__ballot(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m[nt] - mref) : 1.f;
 #pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) acc = mfma_bf16(kr[sub][kk], Q[nt][kk], acc);
+        for (int dt = 0; dt < NDT; ++dt) scale_in_place(O[dt][nt], alpha);
+        scale_in_place(Ls[nt], alpha);
+      }
+      m[nt] = mref;
+      float p[2][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[sub][nt][i] = acc[i] * scale_log2;
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][i], scale_log2, -mref));
+          if (MASK && s[sub][i] == NEG_INF) p[sub][i] = 0.f;
         }
-      if constexpr (!LAST) load_k(pg_ld_n, j_n);
-
-      // ---- causal mask (tiles reaching past the wave's first row) -------------
-      if (t + TS - 1 > pos_first) {
+      pb[nt] = u32x4_t{pack_bf16_rne(p[0][0], p[0][1]), pack_bf16_rne(p[0][2], p[0][3]),
+                       pack_bf16_rne(p[1][0], p[1][1]), pack_bf16_rne(p[1][2], p[1][3])};
+      Ls[nt] = mfma_bf16(ones, pb[nt], Ls[nt]);
+    }
+    // keys at or past kv_end: zero their V elements (element e of a lane's
+    // group is token 16 (e / 4) + 4 c4 + e % 4)
+    u32x4_t keep = {~0u, ~0u, ~0u, ~0u};
+    if constexpr (LAST) {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+      for (int w = 0; w < 4; ++w) {
+        uint32_t msk = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tau = t + 16 * sub + 4 * c4 + i;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              if (tau > pos_n[nt]) s[sub][nt][i] = NEG_INF;
-          }
-      }
-      if constexpr (LAST) {
-        // keys at or past kv_end may be unwritten slots: zero their V elements
-        // (element e of a lane's group is token 16 (e / 4) + 4 c4 + e % 4)
-        if (t + TS > kv_end) {
-          u32x4_t keep;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            uint32_t msk = 0;
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-              const int e = 2 * w + f;
-              if (t + 16 * (e >> 2) + 4 * c4 + (e & 3) < kv_end) msk |= 0xFFFFu << (16 * f);
-            }
-            keep[w] = msk;
-          }
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) vr[dt] &= keep;
+        for (int f = 0; f < 2; ++f) {
+          const int e = 2 * w + f;
+          if (t + 16 * (e >> 2) + 4 * c4 + (e & 3) < kv_end) msk |= 0xFFFFu << (16 * f);
         }
+        keep[w] = msk;
       }
+    }
+    // ---- O^T += V^T P^T: rows = 16 dims, columns = query rows -------------------
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      u32x4_t vv = slice(buf, NKOP + dt);
+      if constexpr (LAST) vv &= keep;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma_bf16(vv, pb[nt], O[dt][nt]);
+    }
+  };
 
-      // ---- online softmax per query row (log2 domain) --------------------------
-      u32x4_t pb[NT];
+  // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0, expcnt 6:4 left at
+  // its maximum, lgkmcnt 11:8 = 0): all LDS reads done and at most n vector
+  // memory operations (this wave's later fetches) outstanding
+  constexpr int WAIT_V0 = 0x70, WAIT_V1 = 0x70 | OPW, WAIT_V2 = 0x70 | (2 * OPW);
+  static_assert(2 * OPW < 16 && NBUF == 4, "waitcnt immediates assume fetches of < 8 loads, 3 ahead");
+  bool bad = false;
+  const int ntiles = (kv_end_wg + TS - 1) / TS;
+  if (ntiles > 0) {
+    uint32_t bad_bits = 0;                     // bit i % 32: tile i's page id is bad
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float tmax = NEG_INF;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[sub][nt][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m[nt], tmax);
-        const float msafe = mnew == NEG_INF ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m[nt] - msafe);
-        float p[2][4], lsum = 0.f;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[sub][i] = __builtin_amdgcn_exp2f(s[sub][nt][i] - msafe);
-            lsum += p[sub][i];
-          }
-        l[nt] = l[nt] * alpha + lsum;
-        if (__ballot(mnew > m[nt])) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) O[dt][nt] *= alpha;
-        }
-        m[nt] = mnew;
-        pb[nt] = u32x4_t{pack_bf16_rne(p[0][0], p[0][1]), pack_bf16_rne(p[0][2], p[0][3]),
-                         pack_bf16_rne(p[1][0], p[1][1]), pack_bf16_rne(p[1][2], p[1][3])};
+    for (int i = 0; i < NBUF - 1; ++i)
+      if (i < ntiles && fetch_next(i)) bad_bits |= 1u << i;
+    for (int it = 0; it < ntiles; ++it) {
+      const int buf = it % NBUF;
+      // this wave's slices of tile `it` have landed (later tiles may be in flight)
+      const int later = min(ntiles - 1 - it, NBUF - 2);
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(WAIT_V2);
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(WAIT_V1);
+      else __builtin_amdgcn_s_waitcnt(WAIT_V0);
+      __builtin_amdgcn_s_barrier();
+      const int nf = it + NBUF - 1;
+      if (nf < ntiles && fetch_next(nf % NBUF)) bad_bits |= 1u << (nf & 31);
+      const int t = it * TS;
+      if (t < kv_end) {
+        bad |= (bad_bits >> (it & 31)) & 1u;
+        if (t + TS >= kv_end) tile(t, buf, std::true_type{}, std::true_type{});
+        else if (t + TS - 1 > pos_first) tile(t, buf, std::true_type{}, std::false_type{});
+        else tile(t, buf, std::false_type{}, std::false_type{});
       }
-
-      // ---- O^T += V^T P^T: rows = 16 dims, columns = query rows -----------------
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma_bf16(vr[dt], pb[nt], O[dt][nt]);
-      if constexpr (!LAST) {
-        load_v(pg_ld_n, j_n);
-        bad |= bad_n;
-        page = page_n;
-        pgi = pgi_n;
-        j0 = j_n;
-      }
-    };
-
-    int t = 0;
-    for (; t + TS < kv_end; t += TS) tile(t, std::false_type{});
-    tile(t, std::true_type{});
+      bad_bits &= ~(1u << (it & 31));
+    }
   }
 
   // ---- normalise and store ---------------------------------------------------------
   const float qnan = __builtin_nanf("");
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float lt = l[nt] + __shfl_xor(l[nt], 16);
-    lt += __shfl_xor(lt, 32);
-    if (!store_n[nt]) continue;
+    const float lt = Ls[nt][0];
+    const int64_t orow = out_row(nt);
+    if (orow < 0) continue;
     // rows with no key (position < 0) give zeros; a bad page id gives NaN
     const float inv = bad ? qnan : (pos_n[nt] < 0 ? 0.f : 1.f / lt);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) store_out4<OUT_BF16>(out_, orow[nt] + dt * 16 + 4 * c4, O[dt][nt] * inv);
+    for (int dt = 0; dt < NDT; ++dt)
+      store_out4<OUT_BF16>(out_, (size_t)orow + dt * 16 + 4 * c4, O[dt][nt] * inv);
   }
 }
 
@@ -363,19 +456,22 @@ hipError_t launch_append_chunk(const AppendChunkArgs& a, hipStream_t s) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.batch <= 0 || a.total_q <= 0) return hipSuccess;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int TPW = 256 / G;                       // chunk tokens per workgroup (G <= 256)
+  const int TPW = 128 / G;                       // chunk tokens per workgroup (G <= 128)
   // every sequence's blocks: at most total_q / TPW full ones plus one partial each
   const int64_t units = ((int64_t)a.total_q + TPW - 1) / TPW + a.batch;
   const int64_t blocks = units * a.num_kv_heads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const float scale_log2 = a.scale * 1.4426950408889634f;
+  // a negative scale is applied as a sign flip of q (exact), so the kernel's
+  // scale is never negative
+  const float scale_log2 = fabsf(a.scale) * 1.4426950408889634f;
+  const uint32_t q_sign = std::signbit(a.scale) ? 0x80008000u : 0u;
   dim3 grid((unsigned)blocks), block(256);
 #define PKV_PREFILL(DD, OB)                                                                          \
   hipLaunchKernelGGL((prefill_kernel<DD, OB>), grid, block, 0, s, static_cast<const uint16_t*>(a.q),  \
                      a.cu_q, a.total_q, static_cast<const uint8_t*>(a.k_pool),                         \
                      static_cast<const uint8_t*>(a.v_pool), a.block_tables, a.seq_lens, a.out,        \
                      a.batch, a.max_pages, a.num_pages, a.num_q_heads, a.num_kv_heads, G, TPW,        \
-                     a.page_size, scale_log2)
+                     a.page_size, scale_log2, q_sign)
   if (a.head_dim == 128) {
     if (a.out_bf16) PKV_PREFILL(128, true); else PKV_PREFILL(128, false);
   } else if (a.head_dim == 64) {
