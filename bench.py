@@ -30,7 +30,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "paged decode attention: KV HBM GB/s (fraction of peak) + seqs/s per layer"
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", "pkv_kernels.hip")
+CSRC = os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc")
+# sources a kernel's machine code depends on (a stored counter profile counts
+# only while they are unchanged)
+DECODE_SRCS = ("pkv_kernels.hip", "pkv_device.h", "pkv_internal.h")
+PREFILL_SRCS = ("pkv_prefill.hip", "pkv_device.h", "pkv_internal.h")
 WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "int8_kv",
              "inflight_int8", "int4_kv", "inflight_int4", "tiny_fp32", "chunked_prefill_bf16"]
 PREFILL_METRIC = "paged chunked prefill attention: TFLOP/s (causal pairs, algorithmic)"
@@ -39,9 +43,12 @@ SCALED = ("fp8", "i8", "i4")    # caches of one byte or less, with per-(page, kv
 ELEM_BITS = {"f32": 32, "bf16": 16, "fp8": 8, "i8": 8, "i4": 4}
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_hash(srcs=DECODE_SRCS) -> str:
+    h = hashlib.sha256()
+    for name in srcs:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -268,6 +275,13 @@ def bench_prefill(args):
     flops = wl.flops()
     tfs = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (pre_ms * 1e-3) / 1e12
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"prefill_{args.workload}_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256_16") == kernel_hash(PREFILL_SRCS):
+            traffic = tr.get("hbm_bytes_per_prefill_call")
     rec = {
         "metric": PREFILL_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -279,7 +293,7 @@ def bench_prefill(args):
                    "step": "kv_append_chunk of every chunk, then causal paged prefill attention"},
         "flops_per_step": int(flops), "kv_bytes_per_step": int(wl.kv_bytes()),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic,
                      "kernel": "prefill_kernel", "call_ms_mean": round(pre_ms, 5),
                      "alg_flops_per_call": int(flops)},
         "diagnostics": {"step_ms_events": round(step_ev, 5), "append_chunk_ms": round(step_ev - pre_ms, 5)},
