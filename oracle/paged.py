@@ -438,3 +438,50 @@ def append_chunk(k_new, v_new, kv_dtype, cu_new, block_tables, seq_lens, k_pool,
                 raise IndexError("page id out of range")
             write_elems(k_pool, (pg, hh, koff[t % P][None, :]), k_new[r0 + i], kv_dtype)
             write_elems(v_pool, (pg, hh, voff[t % P][None, :]), v_new[r0 + i], kv_dtype)
+
+
+# ------------------------------------------------ device page allocation ------
+#
+# Source: the concept page's "key mechanisms" section takes pages from a shared
+# pool as a sequence grows, and its "runtime execution model" section has
+# finished requests return their pages for reuse.  Reading (the pages give no
+# data structure): the free pages form a stack (free_pages[0 .. count - 1],
+# top at count - 1).  alloc: in sequence order, every sequence whose last token
+# L_b - 1 opens a page (L_b >= 1, (L_b - 1) % P == 0, within its table row)
+# and whose entry for that page is empty (negative) takes the top page into
+# block_tables[b][(L_b - 1) / P]; once the stack is empty the remaining
+# requests keep their -1.  (A sequence that did not grow this step already
+# holds its page and takes none.)  release: in sequence order, every
+# marked sequence pushes the ids in the first ceil(L_b / P) entries of its row
+# (ids in [0, num_pages) only) and sets those entries to -1; pushes beyond the
+# stack's capacity are dropped.
+
+def alloc_pages(seq_lens, block_tables, free_pages, count, P):
+    """In place on block_tables and free_pages; returns the new count."""
+    MP = block_tables.shape[1]
+    for b, L in enumerate(np.asarray(seq_lens)):
+        L = int(L)
+        if L < 1 or (L - 1) % P != 0 or (L - 1) // P >= MP or block_tables[b, (L - 1) // P] >= 0:
+            continue
+        if count > 0:
+            count -= 1
+            block_tables[b, (L - 1) // P] = free_pages[count]
+    return count
+
+
+def release_pages(release, seq_lens, block_tables, free_pages, count, capacity, num_pages, P):
+    """In place; returns the new count."""
+    MP = block_tables.shape[1]
+    for b, r in enumerate(np.asarray(release)):
+        if not r:
+            continue
+        L = int(seq_lens[b])
+        n = min(max(-(-L // P), 0), MP)
+        for i in range(n):
+            pg = int(block_tables[b, i])
+            if 0 <= pg < num_pages:
+                if count < capacity:
+                    free_pages[count] = pg
+                    count += 1
+            block_tables[b, i] = -1
+    return count
