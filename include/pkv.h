@@ -348,6 +348,41 @@ int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int
                       int num_q_heads, int num_kv_heads, int head_dim, int page_size,
                       float scale, void* out, pkv_dtype out_dtype, void* stream);
 
+/* alloc_pages - give every sequence the page its newest token opens, from a
+ * free-page stack in device memory (no host round trip per step).
+ *
+ * The first page's "key mechanisms" section takes pages from a shared pool as a
+ * sequence grows.  free_pages[0 .. *free_count - 1] is the stack (top at
+ * *free_count - 1); capacity is free_pages' length.  In sequence order, each b
+ * with L_b >= 1, (L_b - 1) % P == 0, (L_b - 1) / P < max_pages_per_seq and a
+ * negative entry block_tables[b][(L_b - 1) / P] takes the top page into that
+ * entry (so a sequence that did not grow this step takes nothing); when the
+ * stack runs out the remaining entries stay negative.  *free_count is updated.
+ * Call it with the step's seq_lens before the append (pkv_kv_append or
+ * pkv_decode_step), which then writes into the new page.
+ * seq_lens, block_tables, free_pages, free_count: device int32 arrays
+ * ([batch], [batch][max_pages_per_seq], [capacity], [1]).  A *free_count
+ * outside [0, capacity] is clamped.  Calls on one stack must not overlap.
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (batch < 0; max_pages_per_seq, page_size or
+ * capacity <= 0), PKV_E_HIP. */
+int pkv_alloc_pages(const int32_t* seq_lens, int batch, int32_t* block_tables,
+                    int max_pages_per_seq, int page_size,
+                    const int32_t* free_pages, int32_t* free_count, int capacity, void* stream);
+
+/* release_pages - return the pages of finished sequences to the stack.
+ *
+ * The first page's "runtime execution model" has finished requests release
+ * their KV pages for reuse.  In sequence order, each b with release[b] != 0
+ * pushes the ids in [0, num_pages) among the first ceil(L_b / P) entries of its
+ * row (at most max_pages_per_seq) onto the stack and sets those entries to -1;
+ * pushes past capacity are dropped.  *free_count is updated.
+ * release: device int32 [batch]; other arguments as for pkv_alloc_pages.
+ * Errors: as pkv_alloc_pages, plus PKV_E_NULL for release and PKV_E_SHAPE
+ * for num_pages <= 0. */
+int pkv_release_pages(const int32_t* release, const int32_t* seq_lens, int batch,
+                      int32_t* block_tables, int max_pages_per_seq, int page_size, int num_pages,
+                      int32_t* free_pages, int32_t* free_count, int capacity, void* stream);
+
 /* debug_gather - copy each sequence's cached tokens out of the pages into
  * contiguous rows, through the same page-table lookup and chunk addressing
  * the decode kernels use (for bit-exact tests of that address path).

@@ -182,6 +182,23 @@ def paged_prefill(q, q_dtype, cu_q, k_pool, v_pool, kv_dtype, block_tables, seq_
         float(scale), _ptr(out), _code(out_dtype), _stream(stream)))
 
 
+def alloc_pages(seq_lens, block_tables, page_size, free_pages, free_count, stream=None):
+    """Give each sequence the page its newest token opens, from the device free-page
+    stack free_pages[0 .. free_count[0] - 1] (updated in place)."""
+    B, MP = block_tables.shape
+    _check("alloc_pages", lib().pkv_alloc_pages(
+        _ptr(seq_lens), B, _ptr(block_tables), MP, page_size, _ptr(free_pages), _ptr(free_count),
+        int(free_pages.numel()), _stream(stream)))
+
+
+def release_pages(release, seq_lens, block_tables, page_size, num_pages, free_pages, free_count, stream=None):
+    """Push the pages of sequences marked in ``release`` back onto the stack."""
+    B, MP = block_tables.shape
+    _check("release_pages", lib().pkv_release_pages(
+        _ptr(release), _ptr(seq_lens), B, _ptr(block_tables), MP, page_size, num_pages, _ptr(free_pages),
+        _ptr(free_count), int(free_pages.numel()), _stream(stream)))
+
+
 def debug_gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, num_kv_heads, head_dim,
                  page_size, k_out, v_out, stream=None):
     """Copy cached tokens to contiguous [B, Hkv, MP*P, D] rows (tests of the address path)."""

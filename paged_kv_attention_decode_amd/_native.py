@@ -27,6 +27,8 @@ SIGNATURES = {
     "pkv_kv_append_chunk": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp]),
     "pkv_paged_prefill": (_i, [_vp, _i, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _f,
                                _vp, _i, _vp]),
+    "pkv_alloc_pages": (_i, [_vp, _i, _vp, _i, _i, _vp, _vp, _i, _vp]),
+    "pkv_release_pages": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _i, _vp]),
     "pkv_debug_gather": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "pkv_strerror": (ctypes.c_char_p, [_i]),
     "pkv_last_error": (ctypes.c_char_p, []),

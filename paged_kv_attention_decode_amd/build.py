@@ -16,13 +16,14 @@ FLAGS = [
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# source -> extra flags.  The prefill kernel's MFMA accumulators (64 query rows
-# x D outputs per wave) take the vector-register form: in the accumulation
-# registers, the rare rescale of the running output made the compiler copy every
-# accumulator out and back around its branch on every tile.
+# source -> extra flags.  The prefill kernel's MFMA accumulators take the
+# vector-register form: left in the accumulation registers, the rare rescale of
+# the running output made the compiler copy accumulators out and back around
+# its branch on every tile.
 SOURCES = {
     "pkv_kernels.hip": [],
     "pkv_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "pkv_pages.hip": [],
     "pkv_api.cpp": [],
 }
 

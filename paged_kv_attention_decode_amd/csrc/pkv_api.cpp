@@ -258,6 +258,48 @@ int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int
   return PKV_OK;
 }
 
+namespace {
+int check_pages(const void* seq_lens, int batch, const void* block_tables, int max_pages, int page_size,
+                const void* free_pages, const void* free_count, int capacity) {
+  if (batch < 0) return fail(PKV_E_SHAPE, "batch %d < 0", batch);
+  if (max_pages <= 0 || page_size <= 0 || capacity <= 0)
+    return fail(PKV_E_SHAPE, "max_pages_per_seq %d, page_size %d, capacity %d must be > 0", max_pages, page_size,
+                capacity);
+  if (!free_pages || !free_count) return fail(PKV_E_NULL, "free_pages / free_count is NULL");
+  if (batch > 0 && (!seq_lens || !block_tables)) return fail(PKV_E_NULL, "seq_lens / block_tables is NULL");
+  return PKV_OK;
+}
+}  // namespace
+
+int pkv_alloc_pages(const int32_t* seq_lens, int batch, int32_t* block_tables, int max_pages_per_seq, int page_size,
+                    const int32_t* free_pages, int32_t* free_count, int capacity, void* stream) {
+  g_last_error.clear();
+  int rc = check_pages(seq_lens, batch, block_tables, max_pages_per_seq, page_size, free_pages, free_count, capacity);
+  if (rc) return rc;
+  if (batch == 0) return PKV_OK;
+  pkv::PageArgs a{nullptr, seq_lens, block_tables, const_cast<int32_t*>(free_pages), free_count, batch,
+                  max_pages_per_seq, page_size, 0, capacity};
+  hipError_t e = pkv::launch_alloc_pages(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "page allocation launch");
+  return PKV_OK;
+}
+
+int pkv_release_pages(const int32_t* release, const int32_t* seq_lens, int batch, int32_t* block_tables,
+                      int max_pages_per_seq, int page_size, int num_pages, int32_t* free_pages, int32_t* free_count,
+                      int capacity, void* stream) {
+  g_last_error.clear();
+  int rc = check_pages(seq_lens, batch, block_tables, max_pages_per_seq, page_size, free_pages, free_count, capacity);
+  if (rc) return rc;
+  if (num_pages <= 0) return fail(PKV_E_SHAPE, "num_pages %d must be > 0", num_pages);
+  if (batch > 0 && !release) return fail(PKV_E_NULL, "release is NULL");
+  if (batch == 0) return PKV_OK;
+  pkv::PageArgs a{release, seq_lens, block_tables, free_pages, free_count, batch, max_pages_per_seq, page_size,
+                  num_pages, capacity};
+  hipError_t e = pkv::launch_release_pages(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "page release launch");
+  return PKV_OK;
+}
+
 int pkv_kv_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype, const int32_t* block_tables,
                       int max_pages_per_seq, const int32_t* seq_lens, int batch, void* k_pool, void* v_pool,
                       float* k_scales, float* v_scales, int num_pages, int num_kv_heads, int head_dim,

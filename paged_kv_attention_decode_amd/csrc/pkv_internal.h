@@ -108,6 +108,18 @@ struct PrefillArgs {
   float scale;
 };
 
+// Device page allocation: a free-page stack free_pages[0 .. *free_count - 1].
+struct PageArgs {
+  const int32_t* release;   // release only: nonzero marks a finished sequence
+  const int32_t* seq_lens;
+  int32_t* block_tables;
+  int32_t* free_pages;
+  int32_t* free_count;      // one int32 in device memory
+  int batch, max_pages, page_size, num_pages, capacity;
+};
+
+hipError_t launch_alloc_pages(const PageArgs& a, hipStream_t s);
+hipError_t launch_release_pages(const PageArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_chunk(const AppendChunkArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);

@@ -193,3 +193,26 @@ def test_prefill_rejects_bad_arguments(over, code):
 def test_prefill_empty_is_a_noop():
     assert _prefill(b=0, q=0, out=0, cu=0) == 0
     assert _prefill(tot=0, q=0, out=0) == 0
+
+
+def _alloc(**over):
+    a = dict(sl=F, b=2, bt=F, mp=4, p=64, fp=F, fc=F, cap=16)
+    a.update(over)
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return pkv.lib().pkv_alloc_pages(vp(a["sl"]), a["b"], vp(a["bt"]), a["mp"], a["p"], vp(a["fp"]), vp(a["fc"]),
+                                     a["cap"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(fp=0), -1), (dict(fc=0), -1), (dict(sl=0), -1), (dict(b=-1), -2), (dict(mp=0), -2), (dict(p=0), -2),
+    (dict(cap=0), -2),
+])
+def test_alloc_pages_rejects_bad_arguments(over, code):
+    assert _alloc(**over) == code
+
+
+def test_release_pages_rejects_bad_arguments():
+    L = pkv.lib()
+    assert L.pkv_release_pages(None, F, 2, F, 4, 64, 8, F, F, 16, None) == -1
+    assert L.pkv_release_pages(F, F, 2, F, 4, 64, 0, F, F, 16, None) == -2
+    assert _alloc(b=0, sl=0, bt=0) == 0
