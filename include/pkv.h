@@ -338,7 +338,8 @@ int pkv_kv_append_chunk(const void* k_new, const void* v_new, pkv_dtype kv_dtype
  * rows of out that belong to a sequence.  No workspace.  A key position whose
  * page id lies outside [0, num_pages) (or past the table row) makes every row
  * of that (sequence, kv head) block NaN.
- * Errors: PKV_E_NULL, PKV_E_SHAPE (as decode, total_q < 0, G > 128),
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (as decode, total_q < 0, G > 128, a page of
+ * all kv heads of 4 GiB or more),
  * PKV_E_DTYPE (kv not bf16, q not bf16, out not bf16 / fp32), PKV_E_ALIGN,
  * PKV_E_HIP. */
 int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int total_q,

@@ -249,6 +249,9 @@ int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int
                 num_kv_heads);
   if (num_q_heads / num_kv_heads > 128)
     return fail(PKV_E_SHAPE, "group size %d > 128", num_q_heads / num_kv_heads);
+  if ((uint64_t)num_kv_heads * page_size * head_dim * 2 >= (1ull << 32))
+    return fail(PKV_E_SHAPE, "a page of all kv heads (%d x %d x %d bf16) must be below 4 GiB", num_kv_heads,
+                page_size, head_dim);
   if (batch == 0 || total_q == 0) return PKV_OK;
   if ((rc = check_align({q, k_pool, v_pool, out}))) return rc;
   pkv::PrefillArgs a{q, cu_q, total_q, k_pool, v_pool, block_tables, seq_lens, out, out_dtype == PKV_BF16,

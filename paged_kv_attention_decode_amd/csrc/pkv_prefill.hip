@@ -14,14 +14,18 @@
 // * Query rows are (chunk token, head of the kv group) pairs.  A workgroup of
 //   four waves owns one (sequence, kv head, block of 128/G chunk tokens); each
 //   wave holds 32 rows as two 16-column N tiles of the QK^T and PV MFMAs, with
-//   its query operand in registers.  That keeps a wave within 256 registers, so
-//   two workgroups share a CU and each SIMD runs two waves: one wave's softmax
-//   (VALU, cross-lane exchanges) overlaps the other's MFMAs.
+//   its query operand in registers.  A wave needs 168 registers and a
+//   workgroup 48 KiB of LDS, so three workgroups share a CU and each SIMD runs
+//   three waves: one wave's softmax (VALU, cross-lane exchanges, exp) overlaps
+//   the others' MFMAs.  Every tile runs through one body (masking steps are
+//   small uniform branches): with a copy of the body per tile kind the
+//   compiler kept the output accumulators in two register sets and copied
+//   them on every tile.
 // * K and V tiles are fetched once per workgroup with direct global -> LDS
 //   loads (the page layout puts each 16-byte group where a lane needs it, so a
-//   fetching lane's group is exactly some lane's MFMA operand), double buffered
-//   one 32-token tile ahead, and read by all four waves; every K or V operand
-//   feeds four MFMAs (one per N tile).  The workgroups of a kv head g are
+//   fetching lane's group is exactly some lane's MFMA operand), three buffers
+//   deep, two 32-token tiles ahead, and read by all four waves; every K or V
+//   operand feeds two MFMAs (one per N tile).  The workgroups of a kv head g are
 //   blockIdx = g (mod Hkv), so with eight kv heads all readers of one head's
 //   pages run on one XCD and share its L2.
 // * Workgroups holding the later (longer-range) blocks of a sequence are
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(256) void append_chunk_kernel(
 // barrier), computing only tiles below its own kv_end.
 // ---------------------------------------------------------------------------
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ cu, int total_q,
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, void* __restrict__ out_, int B, int MP, int NP, int Hq, int Hkv,
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NOP = NKOP + NDT;   // K and V slices per tile (16 at D = 128)
   constexpr int OPW = NOP / 4;      // slices each wave fetches
   constexpr float TH = 8.f;         // reference lag allowed before a rescale (log2 units)
-  constexpr int NBUF = 4;           // K/V tile buffers (prefetch distance NBUF - 1)
+  constexpr int NBUF = 3;           // K/V tile buffers (prefetch distance NBUF - 1)
   const float NEG_INF = -__builtin_inff();
 
   __shared__ u32x4_t s_kv[NBUF][NOP][64];      // K/V tiles
@@ -272,12 +276,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Next tile to fetch: page index and token offset in it.  Returns whether its
   // page id is bad (page 0 is read instead).
   int f_pgi = 0, f_j = 0;
+  // bytes per page (all kv heads; below 2^32, checked at the boundary) and from
+  // a page to kv head g's chunk
+  const uint32_t page_bytes = uniform((uint32_t)(Hkv * P * D * 2));
+  const uint8_t* kg = kpool + (size_t)g * P * D * 2;
+  const uint8_t* vg = vpool + (size_t)g * P * D * 2;
   auto fetch_next = [&](int buf) -> bool {
     const int page = f_pgi < MP ? btrow[f_pgi] : -1;
     const bool badp = (unsigned)page >= (unsigned)NP;
-    const size_t ch = 2 * chunk_elem(badp ? 0 : page, g, Hkv, P, D);
-    const uint8_t* kc = kpool + ch + 16 * f_j;
-    const uint8_t* vc = vpool + ch + 2 * D * f_j;
+    const uint64_t ch = (uint64_t)(uint32_t)(badp ? 0 : page) * page_bytes;
+    const uint8_t* kc = kg + ch + 16 * f_j;
+    const uint8_t* vc = vg + ch + 2 * D * f_j;
 #pragma unroll
     for (int o = 0; o < OPW; ++o) {
       const uint8_t* src = (o < OPW / 2 ? kc : vc) + sl_off[o];
@@ -296,12 +305,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return *(volatile lds_u32x4_t*)(&s_kv[buf][op][lane]);
   };
 
-  // One tile from buffer buf.  MASK: the tile reaches past the wave's first row
-  // position (causal mask); LAST: the wave's final tile (V of keys at or past
-  // kv_end zeroed: they may be unwritten slots).
-  auto tile = [&](const int t, const int buf, auto mask_tag, auto last_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool LAST = decltype(last_tag)::value;
+  // One tile from buffer buf.  masked (wave-uniform): the tile reaches past the
+  // wave's first row position (causal mask); last: the wave's final tile (V of
+  // keys at or past kv_end zeroed: they may be unwritten slots).  One body for
+  // every tile: the mask steps are small uniform branches, so the output
+  // accumulators never cross a branch of their own.
+  auto tile = [&](const int t, const int buf, const bool masked, const bool last) {
     // ---- S^T = K Q^T: rows = 16 tokens, columns = query rows (unscaled) ------
     f32x4_t acc[2][NT];
 #pragma unroll
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         s[0][i] = acc[0][nt][i];
         s[1][i] = acc[1][nt][i];
       }
-      if constexpr (MASK) {
+      if (masked) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -357,10 +366,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][i], scale_log2, -mref));
-          if (MASK && s[sub][i] == NEG_INF) p[sub][i] = 0.f;
-        }
+        for (int i = 0; i < 4; ++i) p[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][i], scale_log2, -mref));
+      if (masked) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (s[sub][i] == NEG_INF) p[sub][i] = 0.f;
+      }
       pb[nt] = u32x4_t{pack_bf16_rne(p[0][0], p[0][1]), pack_bf16_rne(p[0][2], p[0][3]),
                        pack_bf16_rne(p[1][0], p[1][1]), pack_bf16_rne(p[1][2], p[1][3])};
       Ls[nt] = mfma_bf16(ones, pb[nt], Ls[nt]);
@@ -368,7 +381,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // keys at or past kv_end: zero their V elements (element e of a lane's
     // group is token 16 (e / 4) + 4 c4 + e % 4)
     u32x4_t keep = {~0u, ~0u, ~0u, ~0u};
-    if constexpr (LAST) {
+    if (last) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t msk = 0;
@@ -383,8 +396,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- O^T += V^T P^T: rows = 16 dims, columns = query rows -------------------
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      u32x4_t vv = slice(buf, NKOP + dt);
-      if constexpr (LAST) vv &= keep;
+      const u32x4_t vv = slice(buf, NKOP + dt) & keep;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma_bf16(vv, pb[nt], O[dt][nt]);
     }
@@ -394,7 +406,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // its maximum, lgkmcnt 11:8 = 0): all LDS reads done and at most n vector
   // memory operations (this wave's later fetches) outstanding
   constexpr int WAIT_V0 = 0x70, WAIT_V1 = 0x70 | OPW, WAIT_V2 = 0x70 | (2 * OPW);
-  static_assert(2 * OPW < 16 && NBUF == 4, "waitcnt immediates assume fetches of < 8 loads, 3 ahead");
+  static_assert(2 * OPW < 16 && NBUF >= 2 && NBUF <= 4, "waitcnt immediates assume < 16 loads, <= 3 tiles ahead");
   bool bad = false;
   const int ntiles = (kv_end_wg + TS - 1) / TS;
   if (ntiles > 0) {
@@ -415,9 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int t = it * TS;
       if (t < kv_end) {
         bad |= (bad_bits >> (it & 31)) & 1u;
-        if (t + TS >= kv_end) tile(t, buf, std::true_type{}, std::true_type{});
-        else if (t + TS - 1 > pos_first) tile(t, buf, std::true_type{}, std::false_type{});
-        else tile(t, buf, std::false_type{}, std::false_type{});
+        tile(t, buf, t + TS - 1 > pos_first, t + TS >= kv_end);
       }
       bad_bits &= ~(1u << (it & 31));
     }
