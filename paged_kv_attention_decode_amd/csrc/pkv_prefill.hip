@@ -42,8 +42,9 @@
 //   The softmax scale (log2 e folded in) enters through one fma per score;
 //   a negative scale is folded into the sign of q.
 // * Only tiles that reach past a wave's first row position apply the causal
-//   mask; V elements of tokens at or past the wave's last position + 1 are
-//   zeroed (they may be unwritten slots).
+//   mask; V elements of slots at or past the sequence end L (unwritten, may
+//   hold anything) are zeroed in LDS by the waves that fetched them, once, when
+//   the sequence's last tile arrives.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -306,11 +307,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   };
 
   // One tile from buffer buf.  masked (wave-uniform): the tile reaches past the
-  // wave's first row position (causal mask); last: the wave's final tile (V of
-  // keys at or past kv_end zeroed: they may be unwritten slots).  One body for
-  // every tile: the mask steps are small uniform branches, so the output
-  // accumulators never cross a branch of their own.
-  auto tile = [&](const int t, const int buf, const bool masked, const bool last) {
+  // wave's first row position (causal mask).  One body for every tile: the mask
+  // steps are small uniform branches, so the output accumulators never cross a
+  // branch of their own.  Keys past a row's position get p = 0; V of slots at or
+  // past L (which may hold anything) was zeroed in LDS when the tile arrived.
+  auto tile = [&](const int t, const int buf, const bool masked) {
     // ---- S^T = K Q^T: rows = 16 tokens, columns = query rows (unscaled) ------
     f32x4_t acc[2][NT];
 #pragma unroll
@@ -378,25 +379,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                        pack_bf16_rne(p[1][0], p[1][1]), pack_bf16_rne(p[1][2], p[1][3])};
       Ls[nt] = mfma_bf16(ones, pb[nt], Ls[nt]);
     }
-    // keys at or past kv_end: zero their V elements (element e of a lane's
-    // group is token 16 (e / 4) + 4 c4 + e % 4)
-    u32x4_t keep = {~0u, ~0u, ~0u, ~0u};
-    if (last) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t msk = 0;
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int e = 2 * w + f;
-          if (t + 16 * (e >> 2) + 4 * c4 + (e & 3) < kv_end) msk |= 0xFFFFu << (16 * f);
-        }
-        keep[w] = msk;
-      }
-    }
     // ---- O^T += V^T P^T: rows = 16 dims, columns = query rows -------------------
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const u32x4_t vv = slice(buf, NKOP + dt) & keep;
+      const u32x4_t vv = slice(buf, NKOP + dt);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma_bf16(vv, pb[nt], O[dt][nt]);
     }
@@ -421,13 +407,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       if (later >= 2) __builtin_amdgcn_s_waitcnt(WAIT_V2);
       else if (later == 1) __builtin_amdgcn_s_waitcnt(WAIT_V1);
       else __builtin_amdgcn_s_waitcnt(WAIT_V0);
+      if (it * TS + TS > L) {
+        // The tile holds slots at or past L, which may hold anything: each wave
+        // zeroes the V elements of those slots in the slices it fetched (element
+        // e of a lane's group is token 16 (e / 4) + 4 c4 + e % 4), so no 0 * NaN
+        // reaches the products, and waits for its writes before the barrier.
+        u32x4_t keep;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t msk = 0;
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const int e = 2 * w + f;
+            if (it * TS + 16 * (e >> 2) + 4 * c4 + (e & 3) < L) msk |= 0xFFFFu << (16 * f);
+          }
+          keep[w] = msk;
+        }
+#pragma unroll
+        for (int o = OPW / 2; o < OPW; ++o) {
+          volatile lds_u32x4_t* slot = (volatile lds_u32x4_t*)(&s_kv[buf][wv + 4 * o][lane]);
+          *slot = *slot & keep;
+        }
+        __builtin_amdgcn_s_waitcnt(WAIT_V0);
+      }
       __builtin_amdgcn_s_barrier();
       const int nf = it + NBUF - 1;
       if (nf < ntiles && fetch_next(nf % NBUF)) bad_bits |= 1u << (nf & 31);
       const int t = it * TS;
       if (t < kv_end) {
         bad |= (bad_bits >> (it & 31)) & 1u;
-        tile(t, buf, t + TS - 1 > pos_first, t + TS >= kv_end);
+        tile(t, buf, t + TS - 1 > pos_first);
       }
       bad_bits &= ~(1u << (it & 31));
     }
