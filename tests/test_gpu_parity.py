@@ -259,14 +259,16 @@ def test_partition_choice_within_tolerance():
 
 def test_workspace_reuse_across_calls():
     """One workspace (filled with junk first) serves successive calls of different
-    lengths; stale descriptors from earlier calls must not leak into later ones."""
+    lengths and range sizes; stale descriptors and partials from earlier calls
+    must not leak into later ones."""
     big = configs.custom(seed=66, lens=[4096] * 4, Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16")
     dw = DeviceWorkload(big)
     dw.ws.fill_(0x5A)
-    for lens in ([3000, 17, 900, 4096], [100, 0, 2500, 1], [4096, 4096, 4096, 4096], [0, 5, 0, 64]):
+    for lens, pt in (([3000, 17, 900, 4096], 0), ([100, 0, 2500, 1], 512), ([4096, 4096, 4096, 4096], 0),
+                     ([0, 5, 0, 64], 0), ([4096, 1, 4095, 2], 4096), ([3000, 17, 900, 4096], 128)):
         sl = np.array(lens, np.int32)
-        out = gpu_out(dw.decode(seq_lens=dev_tensor(sl)))
-        check_close(out, oracle_decode(big, seq_lens=sl), "bf16", f"lens {lens}")
+        out = gpu_out(dw.decode(seq_lens=dev_tensor(sl), partition_tokens=pt))
+        check_close(out, oracle_decode(big, seq_lens=sl), "bf16", f"lens {lens} partition {pt}")
 
 
 def test_bad_page_id_gives_nan_row():
