@@ -10,10 +10,11 @@ import torch
 import paged_kv_attention_decode_amd as pkv
 from oracle import c_oracle
 
-# Spec tolerances: bf16/fp32 cache: max-abs <= 1e-2 and mean-abs <= 1e-3;
-# fp8 e4m3 cache: max-abs <= 3e-2 (mean-abs reported).
-# int8 cache (no spec figure): its values widen to bf16 exactly and take
-# the bf16 path's arithmetic, so the bf16 bounds apply.
+# Parity bounds of the decode output against the fp64 oracle: bf16/fp32 cache:
+# max-abs <= 1e-2 and mean-abs <= 1e-3; fp8 e4m3 cache: max-abs <= 3e-2
+# (mean-abs reported).  int8 and int4 caches (no stated figure): their values
+# widen to bf16 exactly and take the bf16 path's arithmetic, so the bf16
+# bounds apply.
 TOL = {"f32": (1e-2, 1e-3), "bf16": (1e-2, 1e-3), "fp8": (3e-2, None), "i8": (1e-2, 1e-3), "i4": (1e-2, 1e-3)}
 DECODE_SCALED = {"fp8": "paged_attn_decode_fp8", "i8": "paged_attn_decode_int8", "i4": "paged_attn_decode_int4"}
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -97,7 +98,7 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
 
 def check_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = "",
                 out_rounding: bool = False):
-    """Element-wise comparison at the benchmark spec's tolerance; returns (max, mean).
+    """Element-wise comparison at the parity bounds above; returns (max, mean).
 
     With ``out_rounding`` (bf16 outputs of large magnitude in edge-case tests),
     each element may additionally differ by the half-ulp that storing the exact
