@@ -11,6 +11,7 @@
 namespace pkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -131,6 +132,18 @@ __device__ __forceinline__ void split_probs_zip(const float (&x)[4], const float
     hi[i] = a.x;
     lo[i] = a.y;
   }
+}
+// Two fp32 -> packed bf16 pair (round to nearest even), element a low.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+// As split_probs_zip with one bf16 per probability (round to nearest even).
+__device__ __forceinline__ u32x4_t probs_zip_bf16(const float (&x)[4], const float (&y)[4], float mul) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16_rne(x[i] * mul, y[i] * mul);
+  return r;
 }
 // Four fp8 e4m3 bytes -> four bf16 (exact: every e4m3 value is a bf16 value).
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {

@@ -302,6 +302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       qsum += __shfl_xor(qsum, 16);
       qsum += __shfl_xor(qsum, 32);
     }
+    const float nbias = -INT4_BIAS * qsum;
 
     // Loop state is wave-uniform; readfirstlane lets the compiler keep it in
     // scalar registers, so page ids come from scalar loads (lgkmcnt) that do
@@ -317,20 +318,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       return idx < MP ? v : -1;
     };
     // An invalid page id marks the segment bad (NaN result); page 0 is read instead.
+    // Byte addresses of a lane's 16-byte groups in the page layout, for a tile
+    // starting at slot j (a multiple of the V block):
+    //   K token j + 16 sub + r16, dims E (c4 + 4 kk) ..:
+    //     chunk + 16 j + 64 P kk + 16 (P c4 + r16) + 256 sub
+    //   V tokens j + 4 c4 .., dim 16 dt + r16:
+    //     chunk + j D BITS / 8 + 16 (D c4 + r16) + 256 dt
+    // i.e. a wave-uniform base, one per-lane offset and a constant, which the
+    // loads take as a base register pair + immediate offsets.
     u32x4_t kr[NSUB][NKK], vr[NDT];
+    const uint32_t k_lane = (uint32_t)(16 * (P * c4 + r16));
+    const uint32_t v_lane = (uint32_t)(16 * (D * c4 + r16));
     auto load_k = [&](int pg, int j) {
-      const uint8_t* kc = kpool + elem_byte<KVT>(chunk_elem(pg, g, Hkv, P, D));
+      const uint8_t* kc = kpool + elem_byte<KVT>(chunk_elem(pg, g, Hkv, P, D)) + 16 * (size_t)j;
 #pragma unroll
-      for (int sub = 0; sub < NSUB; ++sub)
+      for (int kk = 0; kk < NKK; ++kk) {
+        const uint8_t* kb = kc + (size_t)(64 * P * kk) + k_lane;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          kr[sub][kk] = ld16_stream(kc + (uint32_t)elem_byte<KVT>(k_elem<E>(j + 16 * sub + r16, (c4 + 4 * kk) * E, P)));
+        for (int sub = 0; sub < NSUB; ++sub) kr[sub][kk] = ld16_stream(kb + 256 * sub);
+      }
     };
     auto load_v = [&](int pg, int j) {
-      const uint8_t* vc = vpool + elem_byte<KVT>(chunk_elem(pg, g, Hkv, P, D));
+      const uint8_t* vb = vpool + elem_byte<KVT>(chunk_elem(pg, g, Hkv, P, D)) + (size_t)j * (D * BITS / 8) + v_lane;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        vr[dt] = ld16_stream(vc + (uint32_t)elem_byte<KVT>(v_elem<E>(j + 4 * c4, dt * 16 + r16, D)));
+      for (int dt = 0; dt < NDT; ++dt) vr[dt] = ld16_stream(vb + 256 * dt);
     };
     int page = page_of(pgi);
     // step entry: the wave that writes (b, g)'s descriptor also looks up the
@@ -415,7 +426,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       float s[NSUB][4];
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        // int4: the products start from -136 * (sum of q), which takes the
+        // bias of the widened codes out inside the accumulation
+        f32x4_t acc = {nbias, nbias, nbias, nbias};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           if constexpr (KVT == KV_F32) {
@@ -433,10 +446,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             acc = mfma_bf16(byte8_to_bf16x8<KVT>(kr[sub][kk][0], kr[sub][kk][1]), qop(2 * kk), acc);
             acc = mfma_bf16(byte8_to_bf16x8<KVT>(kr[sub][kk][2], kr[sub][kk][3]), qop(2 * kk + 1), acc);
           }
-        }
-        if constexpr (I4) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] -= INT4_BIAS * qsum;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[sub][i] = acc[i] * kmul;
@@ -519,22 +528,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
           O[dt] = mfma_bf16(vr[dt], pl, O[dt]);
         }
       } else if constexpr (I4) {
-        u32x4_t ph[4], pl[4];
+        // int4 values carry 4 bits: the probabilities enter as one bf16 each
+        // (round to nearest even, 8 significant bits), far finer than the data.
+        u32x4_t pb[4];
         const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          split_probs_zip(p[2 * c], p[2 * c + 1], vmul, ph[c], pl[c]);
-          LP = mfma_bf16(ones, ph[c], LP);
-          LP = mfma_bf16(ones, pl[c], LP);
+          pb[c] = probs_zip_bf16(p[2 * c], p[2 * c + 1], vmul);
+          LP = mfma_bf16(ones, pb[c], LP);
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const u32x4_t a = nib8_to_bf16x8(vr[dt][c]);
-            O[dt] = mfma_bf16(a, ph[c], O[dt]);
-            O[dt] = mfma_bf16(a, pl[c], O[dt]);
-          }
+          for (int c = 0; c < 4; ++c) O[dt] = mfma_bf16(nib8_to_bf16x8(vr[dt][c]), pb[c], O[dt]);
         }
       } else {
         u32x4_t ph[2], pl[2];

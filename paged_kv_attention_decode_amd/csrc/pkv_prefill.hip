@@ -58,14 +58,7 @@
 
 namespace pkv {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-
-// Two fp32 -> packed bf16 pair (round to nearest even), element a low.
-__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
-  const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
-  return __builtin_bit_cast(uint32_t, r);
-}
 
 // v *= a element by element, each product written back into its own register
 // (a plain multiply inside a rarely taken branch makes the compiler give the
