@@ -350,14 +350,51 @@ def diagnostics(pkv, wl, q, bt, kps, vps, kss, vss, dsteps, out, ws, step, i0, n
                                   wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws,
                                   wl.partition_tokens)
 
+    # Device page allocation on this batch's tables: every sequence whose newest
+    # token opens a page takes one from the free stack (alloc), and one sequence
+    # in 50 finishes and returns its pages (release).  Each call gets its own
+    # fresh copy of the table and the stack count, made before timing.
+    sl = s0["sl"]
+    B, MP = bt.shape
+    opens = (sl >= 1) & ((sl - 1) % wl.P == 0) & ((sl - 1) // wl.P < MP)
+    rows = torch.arange(B, device=bt.device)[opens]
+    cols = ((sl - 1) // wl.P).long()[opens]
+    bt_open = bt.clone()
+    bt_open[rows, cols] = -1
+    cap = B + 64
+    free_a = torch.arange(cap, dtype=torch.int32, device=bt.device)
+    rel = torch.zeros(B, dtype=torch.int32, device=bt.device)
+    rel[::50] = 1
+    free_r = torch.empty(wl.num_pages, dtype=torch.int32, device=bt.device)
+    ncopy = n + 3
+    bts_a = [bt_open.clone() for _ in range(ncopy)]
+    bts_r = [bt.clone() for _ in range(ncopy)]
+    cnt_a = [torch.full((1,), cap, dtype=torch.int32, device=bt.device) for _ in range(ncopy)]
+    cnt_r = [torch.zeros(1, dtype=torch.int32, device=bt.device) for _ in range(ncopy)]
+    calls = {"a": 0, "r": 0}
+
+    def alloc(i):
+        k = calls["a"]
+        calls["a"] += 1
+        pkv.alloc_pages(sl, bts_a[k], wl.P, free_a, cnt_a[k])
+
+    def release(i):
+        k = calls["r"]
+        calls["r"] += 1
+        pkv.release_pages(rel, sl, bts_r[k], wl.P, wl.num_pages, free_r, cnt_r[k])
+
     st = timed(lambda i: step(i0 + i))
     ap = timed(app)
     de = timed(dec)
     hot = timed(lambda i: step(i0 + i * layers))      # always the same cache copy
+    al = timed(alloc)
+    re = timed(release)
     q3 = lambda a: [round(float(np.percentile(a, p)), 2) for p in (50, 10, 90)]  # noqa: E731
     return {"note": "per-launch HIP events around each call (adds event packets); us as [median, p10, p90]",
             "decode_step_us": q3(st), "kv_append_us": q3(ap), "paged_decode_us": q3(de),
             "decode_step_same_cache_copy_us": q3(hot),
+            "alloc_pages_us": q3(al), "release_pages_us": q3(re),
+            "alloc_pages_requests": int(opens.sum().item()), "release_pages_sequences": int(rel.sum().item()),
             "seqs_per_s_append_plus_decode": round(wl.B / ((np.median(ap) + np.median(de)) * 1e-6), 1)}
 
 

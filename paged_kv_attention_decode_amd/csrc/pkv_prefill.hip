@@ -324,49 +324,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // ---- online softmax per row (log2 domain, lazy reference) -----------------
     // Unmasked scores are finite, so a column with any unmasked score has a
     // finite reference after its first tile; masked scores (-inf) get p = 0.
-    u32x4_t pb[NT];
+    // The reference of a column grows when the column's max passes it by more
+    // than TH.  Each lane first tests its own 8 scores; only when some lane
+    // passes does the wave form the column maxima across the four lanes of a
+    // column and rescale (the common case needs no cross-lane step).
+    float s[NT][2][4];
+    float lmax[NT];
+    bool pass = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float s[2][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[0][i] = acc[0][nt][i];
-        s[1][i] = acc[1][nt][i];
+        s[nt][0][i] = acc[0][nt][i];
+        s[nt][1][i] = acc[1][nt][i];
       }
       if (masked) {
+        // key t + 16 sub + 4 c4 + i lies past the row's position
+        const int lim = pos_n[nt] - t - 4 * c4;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (t + 16 * sub + 4 * c4 + i > pos_n[nt]) s[sub][i] = NEG_INF;
+            if (16 * sub + i > lim) s[nt][sub][i] = NEG_INF;
       }
-      float tmax = NEG_INF;
+      float x = NEG_INF;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[sub][i]);
-      tmax = colmax4(tmax);
-      const float tm = tmax == NEG_INF ? NEG_INF : tmax * scale_log2;
-      const bool grow = tm > m[nt] + TH;
-      const float mref = grow ? tm : m[nt];
-      if (__ballot(grow)) {
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, s[nt][sub][i]);
+      lmax[nt] = x;
+      // m = -inf gives +inf (passes) unless every score is masked (NaN: no)
+      pass |= __builtin_fmaf(x, scale_log2, -m[nt]) > TH;
+    }
+    if (__ballot(pass)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float cmax = colmax4(lmax[nt]);
+        const bool grow = __builtin_fmaf(cmax, scale_log2, -m[nt]) > TH;
+        const float mref = grow ? cmax * scale_log2 : m[nt];
         const float alpha = grow ? __builtin_amdgcn_exp2f(m[nt] - mref) : 1.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) scale_in_place(O[dt][nt], alpha);
         scale_in_place(Ls[nt], alpha);
+        m[nt] = mref;
       }
-      m[nt] = mref;
+    }
+    u32x4_t pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       float p[2][4];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][i], scale_log2, -mref));
+        for (int i = 0; i < 4; ++i)
+          p[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][sub][i], scale_log2, -m[nt]));
       if (masked) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (s[sub][i] == NEG_INF) p[sub][i] = 0.f;
+            if (s[nt][sub][i] == NEG_INF) p[sub][i] = 0.f;
       }
       pb[nt] = u32x4_t{pack_bf16_rne(p[0][0], p[0][1]), pack_bf16_rne(p[0][2], p[0][3]),
                        pack_bf16_rne(p[1][0], p[1][1]), pack_bf16_rne(p[1][2], p[1][3])};
