@@ -24,9 +24,11 @@
 //   contiguous runs per 16 lanes and no LDS round trip.
 // * The QK^T output layout (lane = head column, 4 token rows per lane) is
 //   exactly the PV B-operand layout, so probabilities never cross lanes.
-// * Online softmax in the log2 domain; the running max needs two cross-lane
-//   steps per tile; the running sum stays lane-local until the end.
-// * Probabilities enter the bf16 MFMA as a hi + lo bf16 pair (~16 bits).
+// * Online softmax in the log2 domain against a lazy reference: it grows only
+//   when a tile's max passes it by more than 8, so the common tile needs no
+//   cross-lane step; the running sum stays lane-local until the end.
+// * Probabilities enter the bf16 MFMA as a hi + lo bf16 pair (~16 bits; int4:
+//   one bf16).
 // * fp8 e4m3 is widened exactly to bf16 in registers; the K scale multiplies
 //   the logits, the V scale the probabilities.
 
@@ -47,7 +49,7 @@ namespace pkv {
 // Log-sum-exp merge of the n partial ranges of one (b, g) for 256 of its G*D
 // outputs, starting at x0, run by one wave.
 // Partial slot layout (floats): O[G][D] unnormalised, then m[G] (log2-domain
-// running max), then l[G] (sum of 2^(s - m)).  Contributor i is wave wf + i;
+// softmax reference), then l[G] (sum of 2^(s - m)).  Contributor i is wave wf + i;
 // its slot is slot0 for i = 0 and 2 * (wf + i) otherwise.
 //   out = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
 // Lanes own 4 consecutive (h, d) outputs; contributors are read 8 at a time so
@@ -133,6 +135,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   constexpr int NCH = I4 ? 4 : SCALED ? 2 : 1;   // bf16x8 operands per 16-byte group
   constexpr int NQ = NCH * NKK;
   static_assert(NKK >= 1, "head_dim too small for this element width");
+
+  constexpr float TH = 8.f;          // softmax reference lag allowed before a rescale (log2 units)
 
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, c4 = lane >> 4;
@@ -486,32 +490,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         }
       }
 
-      // ---- online softmax (log2 domain) -------------------------------------------
-      float tmax = NEG_INF;
+      // ---- online softmax (log2 domain, lazy reference) ---------------------------
+      // The reference m of a head column grows only when the column's max passes
+      // it by more than TH (so p <= 2^TH).  Each lane tests its own scores; the
+      // column max across the four lanes of a column is formed only when one
+      // passes, so the common tile has no cross-lane step.  m = -inf (no tile
+      // yet) is passed by any finite score.
+      float lmax = NEG_INF;
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[sub][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = mnew == NEG_INF ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+        for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, s[sub][i]);
+      if (__ballot(lmax > m + TH)) {
+        const float cmax = colmax4(lmax);
+        const bool grow = cmax > m + TH;
+        const float mref = grow ? cmax : m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mref) : 1.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+        if constexpr (I4) LP *= alpha;
+        l *= alpha;
+        m = mref;
+      }
       float p[NSUB][4];
       float lsum = 0.f;
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[sub][i] = __builtin_amdgcn_exp2f(s[sub][i] - mnew);
+          p[sub][i] = __builtin_amdgcn_exp2f(s[sub][i] - m);
           lsum += p[sub][i];
         }
-      l = l * alpha + lsum;
-      if (__ballot(mnew > m)) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
-        if constexpr (I4) LP *= alpha;
-      }
-      m = mnew;
+      l += lsum;
 
       // ---- O^T += V^T P^T: rows = 16 dims, columns = heads -------------------------
       if constexpr (KVT == KV_F32) {

@@ -60,27 +60,6 @@ namespace pkv {
 
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
-// v *= a element by element, each product written back into its own register
-// (a plain multiply inside a rarely taken branch makes the compiler give the
-// products new registers and copy every accumulator on the common path).
-__device__ __forceinline__ void scale_in_place(f32x4_t& v, float a) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float x = v[i];
-    asm("v_mul_f32 %0, %1, %0" : "+v"(x) : "v"(a));
-    v[i] = x;
-  }
-}
-
-// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one MFMA column):
-// the 16-lane row swap pairs rows 0-1 and 2-3, the 32-lane swap the halves.
-__device__ __forceinline__ float colmax4(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(ubits(x), ubits(x), false, false);
-  const float y = fmaxf(fbits(a[0]), fbits(a[1]));
-  const auto c = __builtin_amdgcn_permlane32_swap(ubits(y), ubits(y), false, false);
-  return fmaxf(fbits(c[0]), fbits(c[1]));
-}
-
 // ---------------------------------------------------------------------------
 // Chunk append.  Block (b, y) copies the chunk tokens of sequence b whose
 // position pair t / 2 is y (mod gridDim.y): the two tokens of a pair share
