@@ -166,14 +166,12 @@ __device__ __forceinline__ float colmax4(float x) {
   return fmaxf(fbits(c[0]), fbits(c[1]));
 }
 
-// Four fp8 e4m3 bytes -> four bf16 (exact: every e4m3 value is a bf16 value).
+// Four fp8 e4m3 bytes -> four bf16 (exact: every e4m3 value is a bf16 value),
+// two at a time by the hardware fp8 -> bf16 conversion with scale 1.
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  u32x2_t r;
-  r.x = pack_hi16(a.x, a.y);
-  r.y = pack_hi16(b.x, b.y);
-  return r;
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false);   // bytes 0, 1
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true);    // bytes 2, 3
+  return u32x2_t{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 // Four int8 bytes -> four bf16 (exact: |v| <= 128 has at most 8 significant
 // bits).  Each signed-byte conversion is one instruction (a sign-extending byte
