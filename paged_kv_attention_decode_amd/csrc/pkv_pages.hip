@@ -14,8 +14,11 @@
 // ceil(L_b / P) entries of its row and sets those entries to -1; pushes past
 // the stack's capacity are dropped.
 //
-// One wave does all of it: 64 sequences at a time, a prefix scan over the
-// requests gives each its rank, so the result does not depend on timing.
+// One wave does each of them, so the result does not depend on timing.
+// alloc takes 64 sequences at a time, and a prefix scan over the requests
+// gives each its rank.  release walks the marked sequences in order; for
+// each, the wave reads 64 table entries at a time, and a prefix scan over the
+// valid ones gives each its stack slot.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -61,27 +64,30 @@ __global__ __launch_bounds__(64) void release_pages_kernel(const int32_t* __rest
   int pushed = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int b = b0 + lane;
-    int n = 0, nvalid = 0;
-    if (b < B && release[b] != 0) {
-      const int L = seq_lens[b];
-      n = L > 0 ? min((L - 1) / P + 1, MP) : 0;
-      for (int i = 0; i < n; ++i) {
-        const int pg = bt[(size_t)b * MP + i];
-        nvalid += (unsigned)pg < (unsigned)NP;
+    const bool mark = b < B && release[b] != 0;
+    const int L = mark ? seq_lens[b] : 0;
+    uint64_t todo = __ballot(mark);
+    // marked sequences in order; the whole wave walks one sequence's table
+    // entries 64 at a time, and a prefix scan over the valid ones gives each
+    // its stack slot, so pages are pushed in sequence order, then entry order
+    while (todo) {
+      const int f = uniform(__builtin_ctzll(todo));
+      todo &= todo - 1;
+      const int be = b0 + f;
+      const int Lb = uniform(__builtin_amdgcn_readlane(L, f));
+      const int n = Lb > 0 ? min((Lb - 1) / P + 1, MP) : 0;
+      int32_t* row = bt + (size_t)be * MP;
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const int pg = i < n ? row[i] : -1;
+        const int valid = (unsigned)pg < (unsigned)NP;
+        const int incl = wave_incl_scan(valid, lane);
+        const int pos = count + pushed + incl - valid;
+        if (valid && pos < capacity) free_pages[pos] = pg;
+        if (i < n) row[i] = -1;
+        pushed = uniform(pushed + __builtin_amdgcn_readlane(incl, 63));
       }
     }
-    const int incl = wave_incl_scan(nvalid, lane);
-    int pos = count + pushed + incl - nvalid;       // this sequence's first slot
-    for (int i = 0; i < n; ++i) {
-      int32_t* e = bt + (size_t)b * MP + i;
-      const int pg = *e;
-      if ((unsigned)pg < (unsigned)NP) {
-        if (pos < capacity) free_pages[pos] = pg;
-        ++pos;
-      }
-      *e = -1;
-    }
-    pushed = uniform(pushed + __builtin_amdgcn_readlane(incl, 63));
   }
   if (lane == 0) free_count[0] = min(count + pushed, capacity);
 }

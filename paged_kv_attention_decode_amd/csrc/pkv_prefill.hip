@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     return badp;
   };
   auto slice = [&](int buf, int op) -> u32x4_t {
-    return *(volatile lds_u32x4_t*)(&s_kv[buf][op][lane]);
+    return *(lds_u32x4_t*)(&s_kv[buf][op][lane]);
   };
 
   // One tile from buffer buf.  masked (wave-uniform): the tile reaches past the
@@ -419,7 +419,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
         __builtin_amdgcn_s_waitcnt(WAIT_V0);
       }
+      asm volatile("" ::: "memory");           // LDS reads of earlier tiles stay above
       __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");           // and this tile's reads below the barrier
       const int nf = it + NBUF - 1;
       if (nf < ntiles && fetch_next(nf % NBUF)) bad_bits |= 1u << (nf & 31);
       const int t = it * TS;
