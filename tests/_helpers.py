@@ -79,6 +79,19 @@ class DeviceWorkload:
                       wl.Hkv, wl.D, wl.P)
 
 
+# Logit of token t (q = ones, K rows c_t / D, scale 1) for tests of the
+# softmax reference: it grows every tile, every few tiles, once, only in the
+# last tile, or at alternating tiles; and logits near 900.
+LOGIT_PROFILES = {
+    "fast_ramp_up": lambda t, L, r: 0.5 * t,                 # the reference grows every tile
+    "slow_ramp_up": lambda t, L, r: 0.02 * t,                # grows every few tiles, lags in between
+    "ramp_down": lambda t, L, r: 100.0 - 0.5 * t,            # the first tile sets it for good
+    "large_offset": lambda t, L, r: 900.0 + 2.0 * r.standard_normal(len(t)),
+    "last_token_spike": lambda t, L, r: np.where(t == L - 1, 60.0, 0.0),
+    "alternating": lambda t, L, r: np.where((t // 32) % 2 == 0, 0.0, 30.0),
+}
+
+
 def oracle_decode(wl, k_pool=None, v_pool=None, seq_lens=None, pairs=None):
     return c_oracle.decode(wl.q, wl.q_dtype, wl.k_pool if k_pool is None else k_pool,
                            wl.v_pool if v_pool is None else v_pool, wl.kv_dtype, wl.block_tables,

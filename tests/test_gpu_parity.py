@@ -12,7 +12,7 @@ import paged_kv_attention_decode_amd as pkv
 from oracle import c_oracle, paged
 from workloads import codec, configs, layout
 
-from _helpers import DeviceWorkload, check_close, dev_tensor, gpu_out, host_bytes, oracle_decode
+from _helpers import LOGIT_PROFILES, DeviceWorkload, check_close, dev_tensor, gpu_out, host_bytes, oracle_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -269,6 +269,31 @@ def test_workspace_reuse_across_calls():
         sl = np.array(lens, np.int32)
         out = gpu_out(dw.decode(seq_lens=dev_tensor(sl), partition_tokens=pt))
         check_close(out, oracle_decode(big, seq_lens=sl), "bf16", f"lens {lens} partition {pt}")
+
+
+@pytest.mark.parametrize("partition", [0, 512])
+def test_softmax_reference_paths(partition):
+    """Logit profiles that drive the softmax reference up every tile, now and then,
+    once, or only in the last (masked) tile, plus logits near 900: the lazy
+    reference must give the same output as the oracle's exact softmax."""
+    names = list(LOGIT_PROFILES)
+    lens = [700, 2100, 700, 1500, 333, 1024]
+    D, P, Hkv, G = 128, 64, 2, 4
+    wl = configs.custom(seed=67, lens=lens, Hq=Hkv * G, Hkv=Hkv, D=D, P=P, kv_dtype="bf16", scale=1.0,
+                        partition_tokens=partition)
+    wl.q = codec.f32_to_bf16_bits(np.ones(wl.q.shape, np.float32))
+    kidx = layout.k_chunk_index(P, D, "bf16")
+    r = np.random.default_rng(68)
+    for b, name in enumerate(names):
+        L = lens[b]
+        t = np.arange(L)
+        c = np.asarray(LOGIT_PROFILES[name](t, L, r), dtype=np.float64)
+        k = np.repeat((c / D)[:, None, None], Hkv, axis=1) * np.ones((1, 1, D))
+        pages = wl.block_tables[b, :(L + P - 1) // P]
+        layout.pack_sequence(wl.k_pool, pages, codec.f32_to_bf16_bits(k.astype(np.float32)), P, kidx, "bf16")
+    dw = DeviceWorkload(wl)
+    out = gpu_out(dw.decode())
+    check_close(out, oracle_decode(wl), "bf16", f"logit profiles, partition {partition}")
 
 
 def test_bad_page_id_gives_nan_row():

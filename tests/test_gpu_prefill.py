@@ -8,7 +8,7 @@ import torch
 import paged_kv_attention_decode_amd as pkv
 from oracle import paged
 from workloads import codec, configs, layout
-from tests._helpers import check_close, dev_tensor, gpu_out, host_bytes
+from tests._helpers import LOGIT_PROFILES, check_close, dev_tensor, gpu_out, host_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -147,6 +147,38 @@ def test_prefill_fp32_output_and_large_logits():
     ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
                         wl.scale)
     check_close(got, ref, "bf16", "prefill f32 out")
+
+
+def test_prefill_softmax_reference_paths():
+    """Each sequence's keys follow one logit profile (q = ones, scale 1) over its
+    cached tokens and its chunk, so the per-row softmax reference grows every
+    tile, now and then, once, only at the diagonal tile, or at alternating
+    tiles, or sits near 900: the lane test and the lazy reference must still
+    match the oracle's exact softmax."""
+    names = list(LOGIT_PROFILES)
+    ctx = [600, 1900, 600, 1300, 200, 900]
+    chunk = [100, 200, 100, 200, 133, 124]
+    Hkv, D, P = 2, 128, 64
+    wl = configs.prefill_case("p", 69, ctx, chunk, 4 * Hkv, Hkv, D, P)
+    wl.scale = np.float32(1.0)
+    wl.q = codec.f32_to_bf16_bits(np.ones(wl.q.shape, np.float32))
+    kidx = layout.k_chunk_index(P, D, "bf16")
+    r = np.random.default_rng(70)
+    for b, name in enumerate(names):
+        L = int(wl.seq_lens[b])
+        c = np.asarray(LOGIT_PROFILES[name](np.arange(L), L, r), dtype=np.float64)
+        k = codec.f32_to_bf16_bits((np.repeat((c / D)[:, None, None], Hkv, axis=1) * np.ones((1, 1, D)))
+                                   .astype(np.float32))
+        pages = wl.block_tables[b, :(ctx[b] + P - 1) // P]
+        layout.pack_sequence(wl.k_pool, pages, k[:ctx[b]], P, kidx, "bf16")
+        wl.k_new[wl.cu_q[b]:wl.cu_q[b + 1]] = k[ctx[b]:]
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    got = _gpu_prefill(wl, d)
+    kp, vp = _full_pools(wl)
+    ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                        wl.scale)
+    check_close(got, ref, "bf16", "prefill logit profiles", out_rounding=True)
 
 
 def test_prefill_rows_without_keys_zero_and_other_rows_untouched():
