@@ -50,6 +50,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -61,7 +62,8 @@ namespace pkv {
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
 // ---------------------------------------------------------------------------
-// Chunk append.  Block (b, y) copies the chunk tokens of sequence b whose
+// Chunk append (f32, fp8, int8 and int4 caches; bf16 below).  Block (b, y)
+// copies the chunk tokens of sequence b whose
 // position pair t / 2 is y (mod gridDim.y): the two tokens of a pair share
 // bytes of an int4 V group, so one block writes both.  Each thread copies a
 // pair of dims (one int4 K byte).  A sequence whose chunk does not fit (C > L,
@@ -98,6 +100,82 @@ __global__ __launch_bounds__(256) void append_chunk_kernel(
           put_code<KVT>(vpool, ch + v_elem<E>(j, d + i, D), get_code<KVT>(v_new, row0 + x + i));
         }
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk append, bf16 cache: block (b, y, g) writes kv head g of the 32-token V
+// blocks blk = first + y, first + y + gridDim.y, ... of sequence b's chunk (a
+// block lies in one page, P being a multiple of 32).  K: each token's 16-byte
+// groups of 8 dims are copied whole (tokens adjacent in the layout go to
+// adjacent lanes).  V: the block's rows are staged in LDS and each 16-byte
+// group of the layout (8 tokens of one dim) is assembled from them and stored
+// whole; a block the chunk covers only in part keeps the other tokens' values
+// of each group (read from the page first).  Same skip rules as above.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void append_chunk_bf16_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, const int32_t* __restrict__ cu,
+    int total, const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
+    uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, int MP, int NP, int Hkv, int P) {
+  constexpr int TB = 32;              // tokens per V block
+  constexpr int NG = D / 8;           // 16-byte K groups per token row
+  constexpr int NIT = TB * NG / 256;  // K groups (and V row pieces) per thread
+  static_assert(TB * NG % 256 == 0 && 4 * D % 256 == 0, "D must be 64 or 128");
+  __shared__ uint16_t s_v[TB][D + 8];           // V rows of the block (padded rows)
+  const int b = blockIdx.x, g = blockIdx.z;
+  const int r0 = cu[b], r1 = cu[b + 1];
+  const int L = seq_lens[b];
+  const int C = r1 - r0;
+  if (C <= 0 || r0 < 0 || r1 > total || C > L || (int64_t)L > (int64_t)MP * P) return;
+  const int t0 = L - C;
+  const int tid = threadIdx.x;
+  for (int blk = t0 / TB + (int)blockIdx.y; blk * TB < L; blk += gridDim.y) {
+    const int tb0 = blk * TB;
+    const int page = bt[(size_t)b * MP + tb0 / P];
+    if ((unsigned)page >= (unsigned)NP) continue;          // uniform: the whole block
+    const int j0 = tb0 % P;                                // slot of the block's first token
+    const size_t ch = chunk_elem(page, g, Hkv, P, D);
+    const bool full = tb0 >= t0 && tb0 + TB <= L;
+    __syncthreads();                                       // the previous block's LDS reads
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int x = it * 256 + tid;
+      const int r = x / NG, c = x % NG;                    // token r of the block, dims 8c ..
+      const int tk = tb0 + r;
+      if (tk >= t0 && tk < L) {
+        const size_t row = ((size_t)(r0 + tk - t0) * Hkv + g) * D + 8 * c;
+        const u32x4_t kv = ld16(reinterpret_cast<const uint8_t*>(k_new + row));
+        const u32x4_t vv = ld16(reinterpret_cast<const uint8_t*>(v_new + row));
+        *reinterpret_cast<u32x4_t*>(kpool + ch + k_elem<8>(j0 + r, 8 * c, P)) = kv;
+        *reinterpret_cast<u32x4_t*>(&s_v[r][8 * c]) = vv;
+      }
+    }
+    __syncthreads();
+    // V group (cc, d) of the block holds tokens 16 (e / 4) + 4 cc + e % 4, e = 0..7
+#pragma unroll
+    for (int it = 0; it < 4 * D / 256; ++it) {
+      const int x = it * 256 + tid;
+      const int cc = x / D, d = x % D;
+      uint16_t* dst = vpool + ch + v_elem<8>(j0 + 4 * cc, d, D);
+      u32x4_t old = {0, 0, 0, 0};
+      if (!full) old = *reinterpret_cast<const u32x4_t*>(dst);
+      u32x4_t w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t h[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int e = 2 * k + f;
+          const int r = 16 * (e >> 2) + 4 * cc + (e & 3);
+          const int tk = tb0 + r;
+          const uint32_t o = (old[k] >> (16 * f)) & 0xFFFFu;
+          h[f] = (full || (tk >= t0 && tk < L)) ? (uint32_t)s_v[r][d] : o;
+        }
+        w[k] = h[0] | (h[1] << 16);
+      }
+      *reinterpret_cast<u32x4_t*>(dst) = w;
     }
   }
 }
@@ -450,6 +528,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
 hipError_t launch_append_chunk(const AppendChunkArgs& a, hipStream_t s) {
   if (a.batch <= 0 || a.total <= 0) return hipSuccess;
+  if (a.kvt == KV_BF16 && (a.head_dim == 64 || a.head_dim == 128)) {
+    // 32-token blocks per sequence: about total / batch / 32 + 1 on average
+    const int ny = (int)std::min<int64_t>(64, (int64_t)a.total / a.batch / 32 + 2);
+    dim3 bgrid(a.batch, ny, a.num_kv_heads), bblock(256);
+#define PKV_APPEND_CHUNK_BF16(DD)                                                                   \
+    hipLaunchKernelGGL(append_chunk_bf16_kernel<DD>, bgrid, bblock, 0, s,                           \
+                       static_cast<const uint16_t*>(a.k_new), static_cast<const uint16_t*>(a.v_new), \
+                       a.cu_new, a.total, a.block_tables, a.seq_lens, static_cast<uint16_t*>(a.k_pool), \
+                       static_cast<uint16_t*>(a.v_pool), a.max_pages, a.num_pages, a.num_kv_heads,      \
+                       a.page_size)
+    if (a.head_dim == 128) PKV_APPEND_CHUNK_BF16(128); else PKV_APPEND_CHUNK_BF16(64);
+#undef PKV_APPEND_CHUNK_BF16
+    return hipGetLastError();
+  }
   dim3 grid(a.batch, 64), block(256);
 #define PKV_APPEND_CHUNK(K)                                                                          \
   hipLaunchKernelGGL(append_chunk_kernel<K>, grid, block, 0, s, a.k_new, a.v_new, a.cu_new, a.total,   \
