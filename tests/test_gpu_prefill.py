@@ -77,7 +77,7 @@ def _quantised_case(fmt, seed, ctx, chunk, Hq, Hkv, D, P):
 
 
 APPEND_CASES = [  # (fmt, D, P)
-    ("bf16", 128, 64), ("bf16", 64, 32), ("f32", 64, 16), ("fp8", 128, 64), ("i8", 64, 64), ("i4", 128, 128),
+    ("bf16", 128, 64), ("bf16", 64, 32), ("bf16", 128, 128), ("f32", 64, 16), ("fp8", 128, 64), ("i8", 64, 64), ("i4", 128, 128),
 ]
 
 
