@@ -304,6 +304,29 @@ def bench_prefill(args):
     print(json.dumps(rec), flush=True)
 
 
+def read_probe_gbs(pkv, gib=4, n=10):
+    """Streaming-read rate of this GPU: a 4 GiB buffer (16 times the MALL) read
+    once per call with 16-byte nontemporal loads and nothing else; median of n
+    timed calls (HIP events around each)."""
+    import numpy as np
+    import torch
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pkv.debug_read_probe(buf, sink)
+    ev = DeviceEvents(n)
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev.record(2 * i)
+        pkv.debug_read_probe(buf, sink)
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    ms = float(np.median([ev.elapsed_ms(i) for i in range(n)]))
+    ev.close()
+    del buf
+    return (gib << 30) / (ms * 1e-3) / 1e9
+
+
 def diagnostics(pkv, wl, q, bt, kps, vps, kss, vss, dsteps, out, ws, step, i0, n=30):
     """Per-launch spread and the parts of a step, measured after the timed region.
 
@@ -549,6 +572,9 @@ def main():
                                 "decode_step launch (decode_split_kernel + decode_merge_kernel)"),
                      "call_ms_mean": round(dec_mean, 5), "alg_bytes_per_call": int(step_bytes)},
     }
+    probe = read_probe_gbs(pkv)
+    diag["read_probe_GBs"] = round(probe, 1)
+    diag["frac_of_read_probe"] = round(achieved / probe, 4)
     rec["diagnostics"] = diag
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds)

@@ -384,6 +384,17 @@ int pkv_release_pages(const int32_t* release, const int32_t* seq_lens, int batch
                       int32_t* block_tables, int max_pages_per_seq, int page_size, int num_pages,
                       int32_t* free_pages, int32_t* free_count, int capacity, void* stream);
 
+/* debug_read_probe - read every byte of buf once with 16-byte nontemporal loads
+ * (the access of the decode's K/V stream) and nothing else: a measurement
+ * aid.  The first page ties decode throughput to memory bandwidth ("key
+ * performance parameters"); timing this call on a buffer much larger than
+ * the caches gives the streaming-read rate the decode is compared with.
+ * buf: device memory, 16-byte aligned, bytes a multiple of 16.  out: one
+ * device uint32, written only in the unlikely case that the folded words
+ * equal a fixed constant (so the loads cannot be dropped).
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (bytes % 16), PKV_E_ALIGN, PKV_E_HIP. */
+int pkv_debug_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
 /* debug_gather - copy each sequence's cached tokens out of the pages into
  * contiguous rows, through the same page-table lookup and chunk addressing
  * the decode kernels use (for bit-exact tests of that address path).

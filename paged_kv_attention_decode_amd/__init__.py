@@ -209,5 +209,12 @@ def debug_gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, num_kv_heads,
         num_kv_heads, head_dim, page_size, _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
+def debug_read_probe(buf, out, stream=None):
+    """Read every byte of ``buf`` once with 16-byte nontemporal loads (measures
+    the streaming-read rate; ``out`` is a one-element int32 device tensor)."""
+    _check("debug_read_probe", lib().pkv_debug_read_probe(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(out), _stream(stream)))
+
+
 def version() -> int:
     return int(lib().pkv_version())

@@ -30,6 +30,7 @@ SIGNATURES = {
     "pkv_alloc_pages": (_i, [_vp, _i, _vp, _i, _i, _vp, _vp, _i, _vp]),
     "pkv_release_pages": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _i, _vp]),
     "pkv_debug_gather": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "pkv_debug_read_probe": (_i, [_vp, _sz, _vp, _vp]),
     "pkv_strerror": (ctypes.c_char_p, [_i]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (_i, []),

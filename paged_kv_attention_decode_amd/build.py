@@ -24,6 +24,7 @@ SOURCES = {
     "pkv_kernels.hip": [],
     "pkv_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "pkv_pages.hip": [],
+    "pkv_probe.hip": [],
     "pkv_api.cpp": [],
 }
 

@@ -419,4 +419,16 @@ int pkv_debug_gather(const void* k_pool, const void* v_pool, pkv_dtype kv_dtype,
   return PKV_OK;
 }
 
+int pkv_debug_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  g_last_error.clear();
+  if (bytes == 0) return PKV_OK;
+  if (!buf || !out) return fail(PKV_E_NULL, "a required pointer is NULL");
+  if (bytes % 16) return fail(PKV_E_SHAPE, "bytes %zu not a multiple of 16", bytes);
+  int rc = check_align({buf});
+  if (rc) return rc;
+  hipError_t e = pkv::launch_read_probe(buf, bytes, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read probe launch");
+  return PKV_OK;
+}
+
 }  // extern "C"

@@ -126,6 +126,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 // Quantising append into a one-byte cache (fp8 or int8) with dynamic page scales.
 hipError_t launch_append_quant(const AppendQuantArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t s);
 // Launches the decode kernel and the log-sum-exp merge kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Compute units of the current device (cached per device); <= 0 on failure.

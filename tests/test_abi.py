@@ -24,7 +24,7 @@ def declared_symbols():
 def test_header_declares_the_expected_entry_points():
     syms = declared_symbols()
     for name in ("pkv_kv_append", "pkv_paged_attn_decode", "pkv_paged_attn_decode_fp8",
-                 "pkv_decode_workspace_bytes", "pkv_debug_gather"):
+                 "pkv_decode_workspace_bytes", "pkv_debug_gather", "pkv_debug_read_probe"):
         assert name in syms
 
 
@@ -216,3 +216,14 @@ def test_release_pages_rejects_bad_arguments():
     assert L.pkv_release_pages(None, F, 2, F, 4, 64, 8, F, F, 16, None) == -1
     assert L.pkv_release_pages(F, F, 2, F, 4, 64, 0, F, F, 16, None) == -2
     assert _alloc(b=0, sl=0, bt=0) == 0
+
+
+def test_read_probe_argument_errors():
+    """Rejected before any GPU call: NULL pointers, a size not a multiple of 16,
+    a misaligned buffer; zero bytes is a no-op."""
+    L = pkv.lib()
+    assert L.pkv_debug_read_probe(None, 16, F, None) == -1
+    assert L.pkv_debug_read_probe(F, 16, None, None) == -1
+    assert L.pkv_debug_read_probe(F, 17, F, None) == -2
+    assert L.pkv_debug_read_probe(F + 4, 16, F, None) == -6
+    assert L.pkv_debug_read_probe(None, 0, None, None) == 0
