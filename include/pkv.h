@@ -195,7 +195,9 @@ size_t pkv_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, 
  * Long sequences are split into ranges processed in parallel and combined by
  * their log-sum-exp; partition_tokens chooses the range granularity: 0 lets
  * the library choose, otherwise a positive multiple of TB (e.g. 512 tokens).
- * Accumulation is fp32; out is rounded to nearest-even when bf16.
+ * Accumulation is fp32; the bf16 products take each probability as a pair of
+ * bf16 values (about 16 significant bits); out is rounded to nearest-even
+ * when bf16.
  *
  * Supported dtypes (q / kv / out): F32/F32/F32, BF16/BF16/BF16, BF16/BF16/F32.
  * Sizes: D in {64, 128}; 1 <= G <= 16 with Hq % Hkv == 0; P a multiple of TB
@@ -222,9 +224,10 @@ int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype,
  * k_scales / v_scales [page][kv head].  Following the first page ("key
  * mechanisms": FP8 data is widened to 16 bits before the matrix product and
  * accumulated wide), bytes are widened exactly in registers; the K scale is
- * folded into the logits and the V scale into the probabilities; accumulation
- * is fp32.  q is BF16; out is BF16 or F32.  Same sizes and errors as above,
- * plus PKV_E_NULL when a scale pointer is NULL. */
+ * folded into the logits and the V scale into the probabilities, which enter
+ * the value product as one bf16 each (8 significant bits, more than an e4m3
+ * value carries); accumulation is fp32.  q is BF16; out is BF16 or F32.  Same
+ * sizes and errors as above, plus PKV_E_NULL when a scale pointer is NULL. */
 int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype,
                               const void* k_pool, const void* v_pool,
                               const float* k_scales, const float* v_scales,
