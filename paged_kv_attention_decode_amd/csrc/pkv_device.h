@@ -138,13 +138,6 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
   return __builtin_bit_cast(uint32_t, r);
 }
-// As split_probs_zip with one bf16 per probability (round to nearest even).
-__device__ __forceinline__ u32x4_t probs_zip_bf16(const float (&x)[4], const float (&y)[4], float mul) {
-  u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = pack_bf16_rne(x[i] * mul, y[i] * mul);
-  return r;
-}
 // v *= a element by element, each product written back into its own register
 // (a plain multiply inside a rarely taken branch makes the compiler give the
 // products new registers and copy every accumulator on the common path).

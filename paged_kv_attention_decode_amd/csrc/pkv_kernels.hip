@@ -27,8 +27,7 @@
 // * Online softmax in the log2 domain against a lazy reference: it grows only
 //   when a tile's max passes it by more than 8, so the common tile needs no
 //   cross-lane step; the running sum stays lane-local until the end.
-// * Probabilities enter the bf16 MFMA as a hi + lo bf16 pair (~16 bits) for
-//   bf16 and fp32 caches, as one bf16 for the fp8, int8 and int4 ones.
+// * Probabilities enter the bf16 MFMA as a hi + lo bf16 pair (~16 bits).
 // * fp8 e4m3 is widened exactly to bf16 in registers; the K scale multiplies
 //   the logits, the V scale the probabilities.
 
@@ -538,36 +537,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
           O[dt] = mfma_bf16(vr[dt], pl, O[dt]);
         }
       } else if constexpr (I4) {
-        // int4 values carry 4 bits: the probabilities enter as one bf16 each
-        // (round to nearest even, 8 significant bits), far finer than the data.
-        u32x4_t pb[4];
+        u32x4_t ph[4], pl[4];
         const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          pb[c] = probs_zip_bf16(p[2 * c], p[2 * c + 1], vmul);
-          LP = mfma_bf16(ones, pb[c], LP);
+          split_probs_zip(p[2 * c], p[2 * c + 1], vmul, ph[c], pl[c]);
+          LP = mfma_bf16(ones, ph[c], LP);
+          LP = mfma_bf16(ones, pl[c], LP);
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) O[dt] = mfma_bf16(nib8_to_bf16x8(vr[dt][c]), pb[c], O[dt]);
+          for (int c = 0; c < 4; ++c) {
+            const u32x4_t a = nib8_to_bf16x8(vr[dt][c]);
+            O[dt] = mfma_bf16(a, ph[c], O[dt]);
+            O[dt] = mfma_bf16(a, pl[c], O[dt]);
+          }
         }
       } else {
-        // one-byte values: the probabilities enter as one bf16 each (round to
-        // nearest even, 8 significant bits, as many as the values carry)
-        u32x4_t pb[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          pb[c] = u32x4_t{pack_bf16_rne(p[2 * c][0] * vmul, p[2 * c][1] * vmul),
-                          pack_bf16_rne(p[2 * c][2] * vmul, p[2 * c][3] * vmul),
-                          pack_bf16_rne(p[2 * c + 1][0] * vmul, p[2 * c + 1][1] * vmul),
-                          pack_bf16_rne(p[2 * c + 1][2] * vmul, p[2 * c + 1][3] * vmul)};
+        u32x4_t ph[2], pl[2];
+        split_probs(p[0], p[1], vmul, ph[0], pl[0]);
+        split_probs(p[2], p[3], vmul, ph[1], pl[1]);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const u32x4_t a0 = byte8_to_bf16x8<KVT>(vr[dt][0], vr[dt][1]);
           const u32x4_t a1 = byte8_to_bf16x8<KVT>(vr[dt][2], vr[dt][3]);
-          O[dt] = mfma_bf16(a0, pb[0], O[dt]);
-          O[dt] = mfma_bf16(a1, pb[1], O[dt]);
+          O[dt] = mfma_bf16(a0, ph[0], O[dt]);
+          O[dt] = mfma_bf16(a0, pl[0], O[dt]);
+          O[dt] = mfma_bf16(a1, ph[1], O[dt]);
+          O[dt] = mfma_bf16(a1, pl[1], O[dt]);
         }
       }
       if constexpr (!LAST) {

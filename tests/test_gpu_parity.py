@@ -185,6 +185,53 @@ EDGE = [
 ]
 
 
+def _random_cases(n=24, seed=90):
+    """Seeded draws over the decode's valid shapes: every cache type, G 1..16,
+    D 64/128, the page sizes each type allows, ragged and empty lengths (also
+    around page and V-block boundaries), range sizes, negative and large
+    scales, both output types."""
+    r = np.random.default_rng(seed)
+    tb = {"f32": 16, "bf16": 32, "fp8": 64, "i8": 64, "i4": 128}
+    pages = {"f32": [16, 32, 64], "bf16": [32, 64, 128, 256], "fp8": [64, 128], "i8": [64, 128], "i4": [128, 256]}
+    cases = []
+    for k in range(n):
+        kv = ["f32", "bf16", "bf16", "fp8", "i8", "i4"][k % 6]
+        D = 128 if kv == "i4" else int(r.choice([64, 128]))
+        P = int(r.choice(pages[kv]))
+        Hkv = int(r.choice([1, 2, 4, 8]))
+        G = int(r.choice([1, 2, 3, 4, 5, 8, 12, 16]))
+        B = int(r.integers(1, 25))
+        lens = []
+        for _ in range(B):
+            u = r.random()
+            if u < 0.08:
+                lens.append(0)
+            elif u < 0.25:
+                lens.append(int(r.integers(1, 4)))
+            elif u < 0.5:
+                lens.append(max(1, int(r.integers(1, 12)) * P + int(r.integers(-1, 2))))
+            else:
+                lens.append(int(r.integers(1, 3001)))
+        spec = dict(seed=1000 + k, lens=lens, Hq=Hkv * G, Hkv=Hkv, D=D, P=P, kv_dtype=kv,
+                    partition_tokens=int(r.choice([0, 0, 1, 2, 4, 16])) * tb[kv],
+                    scale=float(r.choice([-1.0, 1.0, 1.0, 1.0]) * r.uniform(0.02, 0.25)),
+                    q_mult=float(r.choice([1.0, 3.0])))
+        if kv != "f32" and r.random() < 0.4:
+            spec["out_dtype"] = "f32"
+        cases.append(spec)
+    return cases
+
+
+RANDOM_CASES = _random_cases()
+
+
+@pytest.mark.parametrize("spec", RANDOM_CASES,
+                         ids=lambda s: f"{s['kv_dtype']}-D{s['D']}-P{s['P']}-G{s['Hq'] // s['Hkv']}-B{len(s['lens'])}-s{s['seed']}")
+def test_decode_random_configs(spec):
+    wl = configs.custom(**spec)
+    _decode_vs_oracle(wl, f"random seed {spec['seed']}", out_rounding=True)
+
+
 @pytest.mark.parametrize("spec", EDGE, ids=lambda s: f"{s['kv_dtype']}-D{s['D']}-P{s['P']}-G{s['Hq'] // s['Hkv']}-s{s['seed']}")
 def test_decode_edge_cases(spec):
     wl = configs.custom(**spec)

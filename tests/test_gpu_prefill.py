@@ -181,6 +181,37 @@ def test_prefill_softmax_reference_paths():
     check_close(got, ref, "bf16", "prefill logit profiles", out_rounding=True)
 
 
+def _random_prefill_cases(n=12, seed=95):
+    """Seeded draws: G 1..16, D 64/128, P 32..128, 1-6 sequences with cached
+    contexts of 0..2000 tokens and chunks of 1..300, logits of std 1 or 3."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        B = int(r.integers(1, 7))
+        Hkv = int(r.choice([1, 2, 4]))
+        G = int(r.choice([1, 2, 3, 4, 8, 16]))
+        ctx = [int(r.choice([0, int(r.integers(1, 2001))])) for _ in range(B)]
+        chunk = [int(r.integers(1, 301)) for _ in range(B)]
+        cases.append(dict(seed=2000 + k, ctx=ctx, chunk=chunk, Hq=Hkv * G, Hkv=Hkv,
+                          D=int(r.choice([64, 128])), P=int(r.choice([32, 64, 128])),
+                          q_mult=float(r.choice([1.0, 3.0]))))
+    return cases
+
+
+@pytest.mark.parametrize("c", _random_prefill_cases(),
+                         ids=lambda c: f"G{c['Hq'] // c['Hkv']}-D{c['D']}-P{c['P']}-B{len(c['ctx'])}-s{c['seed']}")
+def test_prefill_random_configs(c):
+    wl = configs.prefill_case("p", c["seed"], c["ctx"], c["chunk"], c["Hq"], c["Hkv"], c["D"], c["P"],
+                              q_mult=c["q_mult"])
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    got = _gpu_prefill(wl, d)
+    kp, vp = _full_pools(wl)
+    ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                        wl.scale)
+    check_close(got, ref, "bf16", f"prefill random seed {c['seed']}", out_rounding=True)
+
+
 def test_prefill_rows_without_keys_zero_and_other_rows_untouched():
     wl = configs.prefill_case("p", 72, [0, 10, 0], [20, 0, 30], 8, 2, 64, 32)
     d = _up(wl)
