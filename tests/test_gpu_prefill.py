@@ -194,22 +194,22 @@ def _random_prefill_cases(n=12, seed=95):
         chunk = [int(r.integers(1, 301)) for _ in range(B)]
         cases.append(dict(seed=2000 + k, ctx=ctx, chunk=chunk, Hq=Hkv * G, Hkv=Hkv,
                           D=int(r.choice([64, 128])), P=int(r.choice([32, 64, 128])),
-                          q_mult=float(r.choice([1.0, 3.0]))))
+                          q_mult=float(r.choice([1.0, 3.0])), out="f32" if k % 2 else "bf16"))
     return cases
 
 
 @pytest.mark.parametrize("c", _random_prefill_cases(),
-                         ids=lambda c: f"G{c['Hq'] // c['Hkv']}-D{c['D']}-P{c['P']}-B{len(c['ctx'])}-s{c['seed']}")
+                         ids=lambda c: f"G{c['Hq'] // c['Hkv']}-D{c['D']}-P{c['P']}-B{len(c['ctx'])}-{c['out']}-s{c['seed']}")
 def test_prefill_random_configs(c):
     wl = configs.prefill_case("p", c["seed"], c["ctx"], c["chunk"], c["Hq"], c["Hkv"], c["D"], c["P"],
-                              q_mult=c["q_mult"])
+                              q_mult=c["q_mult"], out_dtype=c["out"])
     d = _up(wl)
     _gpu_append_chunk(wl, d)
     got = _gpu_prefill(wl, d)
     kp, vp = _full_pools(wl)
     ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
                         wl.scale)
-    check_close(got, ref, "bf16", f"prefill random seed {c['seed']}", out_rounding=True)
+    check_close(got, ref, "bf16", f"prefill random seed {c['seed']}", out_rounding=c["out"] == "bf16")
 
 
 def test_prefill_rows_without_keys_zero_and_other_rows_untouched():
