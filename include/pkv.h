@@ -225,9 +225,10 @@ int pkv_paged_attn_decode(const void* q, pkv_dtype q_dtype,
  * mechanisms": FP8 data is widened to 16 bits before the matrix product and
  * accumulated wide), bytes are widened exactly in registers; the K scale is
  * folded into the logits and the V scale into the probabilities, which enter
- * the value product as one bf16 each (8 significant bits, more than an e4m3
- * value carries); accumulation is fp32.  q is BF16; out is BF16 or F32.  Same
- * sizes and errors as above, plus PKV_E_NULL when a scale pointer is NULL. */
+ * the value product as a pair of bf16 each (a rounded high part and the
+ * remainder, 16 significant bits together); accumulation is fp32.  q is
+ * BF16; out is BF16 or F32.  Same sizes and errors as above, plus PKV_E_NULL
+ * when a scale pointer is NULL. */
 int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype,
                               const void* k_pool, const void* v_pool,
                               const float* k_scales, const float* v_scales,
