@@ -354,13 +354,15 @@ def diagnostics(pkv, wl, q, bt, kps, vps, kss, vss, dsteps, out, ws, step, i0, n
         return us
 
     def app(i):
+        # the timed loop's sequence of steps and cache copies, so that a
+        # quantising append meets the page-scale rises (and re-encodes) it meets there
+        k = i0 + i
+        s, c = dsteps[k % len(dsteps)], k % layers
         if quantises_on_write(wl):
-            append_quant_fn(pkv, wl.kv_dtype)(s0["kn"], s0["vn"], wl.new_dtype, bt, s0["sl"], kps[i % layers],
-                                              vps[i % layers], kss[i % layers], vss[i % layers], wl.Hkv, wl.D,
-                                              wl.P)
+            append_quant_fn(pkv, wl.kv_dtype)(s["kn"], s["vn"], wl.new_dtype, bt, s["sl"], kps[c], vps[c],
+                                              kss[c], vss[c], wl.Hkv, wl.D, wl.P)
         else:
-            pkv.kv_append(s0["kn"], s0["vn"], wl.kv_dtype, bt, s0["sl"], kps[i % layers], vps[i % layers],
-                          wl.Hkv, wl.D, wl.P)
+            pkv.kv_append(s["kn"], s["vn"], wl.kv_dtype, bt, s["sl"], kps[c], vps[c], wl.Hkv, wl.D, wl.P)
 
     def dec(i):
         if wl.kv_dtype in SCALED:

@@ -238,6 +238,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const float NEG_INF = -__builtin_inff();
   const bool hv = r16 < G;
 
+  // Length of sequence bb: those of the first NC * 64 sequences are in
+  // registers (lane bb mod 64 of Lc[bb / 64]); later ones are read.
+  static_assert(NC == 4, "len_of reads Lc[0..3]");
+  auto len_of = [&](int bb) -> int {
+    bb = uniform(bb);
+    const int c = bb >> 6, ln = bb & 63;
+    int v;
+    if (c == 0) v = __builtin_amdgcn_readlane(Lc[0], ln);
+    else if (c == 1) v = __builtin_amdgcn_readlane(Lc[1], ln);
+    else if (c == 2) v = __builtin_amdgcn_readlane(Lc[2], ln);
+    else if (c == 3) v = __builtin_amdgcn_readlane(Lc[3], ln);
+    else v = seq_lens[bb];
+    return uniform(v);
+  };
+  // first page id of the next segment, looked up one segment ahead
+  bool have_next = false;
+  int page_next = 0;
+
   for (int64_t u = u0; u < u1;) {
     const int64_t off = u - base;
     const int g = uniform((int)(off / npb));
@@ -346,7 +364,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) vr[dt] = ld16_stream(vb + 256 * dt);
     };
-    int page = page_of(pgi);
+    int page = (have_next && pgi == 0) ? page_next : page_of(pgi);
+    // The segment after this one, if the wave has one, starts at token 0 of kv
+    // head g + 1 of this sequence or of kv head 0 of the next sequence with
+    // tokens.  Its sequence and first page id are found now, so the switch
+    // waits only for its K / V loads.
+    int nb = b;
+    have_next = ue < u1;
+    if (have_next) {
+      if (g + 1 == Hkv) {
+        do ++nb;
+        while (ranges_of(len_of(nb), PT) == 0);
+      }
+      page_next = uniform(((const_i32_ptr)(bt + (size_t)nb * MP))[0]);
+    }
     // step entry: the wave that writes (b, g)'s descriptor also looks up the
     // page of slot Lb - 1, where the merge kernel stores the new token (-1:
     // beyond the table).  Scalar load; it is consumed only at the segment end.
@@ -620,11 +651,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     u = ue;
     if (u < u1 && u == base + (int64_t)npb * Hkv) {
       base = u;
-      do {
-        ++b;
-        Lb = uniform(seq_lens[b]);
-        npb = ranges_of(Lb, PT);
-      } while (npb == 0);
+      b = nb;
+      Lb = len_of(b);
+      npb = ranges_of(Lb, PT);
     }
   }
 }
@@ -828,31 +857,33 @@ __device__ __forceinline__ uint32_t lut4(const uint8_t* lut, uint32_t w) {
          ((uint32_t)lut[(w >> 16) & 0xFFu] << 16) | ((uint32_t)lut[w >> 24] << 24);
 }
 
-// Re-encode slots [0, j) of a K chunk: 16-byte groups (16 dims of one token).
-// Each lane issues the loads of up to 16 groups before converting any, so a
-// page costs about one memory round trip per 1024 groups.
+// Re-encode slots [0, j) of a K chunk.  Token t's dims E c .. E c + E - 1 are
+// the 16-byte group at chunk + 16 (c P + t); lane l takes tokens l, l + 64, ...
+// (TPL of them per round, all GPT groups of each), so no group index is
+// divided, and every load of a round is issued before any conversion.
 template <int KVT, int D>
 __device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uint8_t* lut, int lane) {
-  constexpr int GPL = 16;
   constexpr int GPT = D * Kv<KVT>::BITS / 128;       // 16-byte groups per token
-  const int ngrp = GPT * j;
-  for (int base = 0; base < ngrp; base += 64 * GPL) {
-    u32x4_t w[GPL];
-    int off[GPL];
+  constexpr int TPL = 16 / GPT;                      // tokens per lane per round
+  for (int t0 = 0; t0 < j; t0 += 64 * TPL) {
+    u32x4_t w[TPL][GPT];
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int gi = min(base + lane + 64 * i, ngrp - 1);     // clamped: in-bounds, stored only if owned
-      const int c = gi / j, jj = gi - c * j;
-      off[i] = (c * P + jj) * 16;
-      w[i] = *reinterpret_cast<const u32x4_t*>(pool + off[i]);
+    for (int a = 0; a < TPL; ++a) {
+      const int t = min(t0 + 64 * a + lane, j - 1);    // clamped: in-bounds, stored only if owned
+#pragma unroll
+      for (int c = 0; c < GPT; ++c) w[a][c] = *reinterpret_cast<const u32x4_t*>(pool + 16 * (c * P + t));
     }
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      if (base + lane + 64 * i < ngrp) {
-        u32x4_t r;
+    for (int a = 0; a < TPL; ++a) {
+      const int t = t0 + 64 * a + lane;
+      if (t < j) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[i][q]);
-        *reinterpret_cast<u32x4_t*>(pool + off[i]) = r;
+        for (int c = 0; c < GPT; ++c) {
+          u32x4_t r;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[a][c][q]);
+          *reinterpret_cast<u32x4_t*>(pool + 16 * (c * P + t)) = r;
+        }
       }
     }
   }
@@ -860,30 +891,40 @@ __device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uin
 
 // Re-encode a V chunk for a scale change at slot j: a 16-byte group holds E
 // tokens of one dim from one TB = 4E token block; blocks 0 .. j/TB are
-// rewritten group by group: tokens < j re-encoded, token j takes its new code
-// (nbj, from LDS), later slots keep theirs.
+// rewritten group by group.  Blocks before j's hold earlier slots only and are
+// re-encoded whole; in j's block, tokens < j are re-encoded, token j takes its
+// new code (nbj, from LDS) and later slots keep theirs.  A round's 64 * GPL
+// groups cover whole blocks (4 D groups each), so the block of a lane's i-th
+// group, and with it the choice between the two, is the same on every lane.
 template <int KVT, int D>
 __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* lut, const uint8_t* nbj,
                                           int lane) {
   constexpr int BITS = Kv<KVT>::BITS, E = 128 / BITS;
-  constexpr int GPL = 16, TB = 4 * E, BLK = TB * D * BITS / 8;   // bytes per V block
-  const int ngrp = (j / TB + 1) * 4 * D;
+  constexpr int GPL = 16, TB = 4 * E;
+  constexpr int GPB = 4 * D;    // 16-byte groups per V block (blocks are contiguous)
+  static_assert((64 * GPL) % GPB == 0 && GPB % 64 == 0, "a round covers whole blocks");
+  const int jb = j / TB;
+  const int ngrp = (jb + 1) * GPB;
   for (int base = 0; base < ngrp; base += 64 * GPL) {
     u32x4_t w[GPL];
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
       const int gi = min(base + lane + 64 * i, ngrp - 1);
-      const int blk = gi / (4 * D), rem = gi - blk * 4 * D;
-      w[i] = *reinterpret_cast<const u32x4_t*>(pool + (size_t)blk * BLK + (size_t)rem * 16);
+      w[i] = *reinterpret_cast<const u32x4_t*>(pool + (size_t)gi * 16);   // blocks are contiguous
     }
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
+      const int blk = uniform((base + 64 * i) / GPB);
+      if (blk > jb) continue;                          // past j's block (uniform)
       const int gi = base + lane + 64 * i;
-      if (gi < ngrp) {
-        const int blk = gi / (4 * D), rem = gi - blk * 4 * D;
+      u32x4_t r;
+      if (blk < jb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[i][q]);
+      } else {
+        const int rem = gi - blk * GPB;
         const int c = rem / D, d = rem - c * D;
         const uint32_t fresh = nbj[d];
-        u32x4_t r;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t re = lut4(lut, w[i][q]);
@@ -891,7 +932,7 @@ __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* l
           constexpr int PW = 32 / BITS;                  // elements per word
 #pragma unroll
           for (int x = 0; x < PW; ++x) {
-            // element e of the group holds token 16 * (e / 4) + 4c + e % 4 of block blk
+            // element e of the group holds token 16 * (e / 4) + 4c + e % 4 of the block
             const int e = PW * q + x;
             const int tok = blk * TB + 16 * (e >> 2) + 4 * c + (e & 3);
             constexpr uint32_t M = (1u << BITS) - 1u;
@@ -901,8 +942,8 @@ __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* l
           }
           r[q] = outw;
         }
-        *reinterpret_cast<u32x4_t*>(pool + (size_t)blk * BLK + (size_t)rem * 16) = r;
       }
+      *reinterpret_cast<u32x4_t*>(pool + (size_t)gi * 16) = r;
     }
   }
 }
@@ -1182,9 +1223,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   // tile is 128 * D bytes in every dtype), i.e. one wave per SIMD at D = 128.
   // More waves than that do not raise the streaming rate: two waves on one
   // SIMD issue in age order, so the second one starts late and finishes last,
-  // stretching the tail of the launch.  int4 is the exception: its tile is
-  // half the bytes and four times the widening work of a bf16 one, so the
-  // second wave on each SIMD hides ALU time rather than adding loads in flight.
+  // stretching the tail of the launch.  int4 is the exception: its tile holds
+  // the same bytes as a bf16 one but about ten times the vector ALU work
+  // (nibble widening, the bias sums), so the second wave on each SIMD hides
+  // ALU time rather than adding loads in flight.
   const int tile_waves = a.kvt == KV_INT4 ? 1024 : 512;
   const int Wmax = cus * std::min(waves_per_cu(fn, dev), tile_waves / a.head_dim);
   const int G = a.num_q_heads / a.num_kv_heads;

@@ -158,6 +158,22 @@ def test_gather_bit_exact(kv_dtype, P, D):
 
 # ------------------------------------------------------------ decode: edges ----
 
+def _gappy_lens(n, seed):
+    """n lengths of 1..199 tokens, about a third of them zero, with a run of
+    empty sequences across sequence 256 and an empty last one: a wave's range
+    then passes over empty sequences on its way to the next one with tokens,
+    both among the first 256 sequences and past them."""
+    r = np.random.default_rng(seed)
+    lens = [int(x) for x in r.integers(1, 200, n)]
+    for i in range(n):
+        if r.random() < 0.3:
+            lens[i] = 0
+    for i in range(250, 262):
+        lens[i] = 0
+    lens[-1] = 0
+    return lens
+
+
 EDGE = [
     dict(seed=41, lens=[1, 15, 16, 17, 100], Hq=4, Hkv=4, D=64, P=16, kv_dtype="f32"),
     dict(seed=42, lens=[3, 33, 250], Hq=8, Hkv=4, D=128, P=32, kv_dtype="f32"),
@@ -182,6 +198,8 @@ EDGE = [
     dict(seed=62, lens=[64, 300, 1300], Hq=16, Hkv=4, D=128, P=256, kv_dtype="i4", out_dtype="f32"),
     dict(seed=63, lens=[0, 100, 4097], Hq=64, Hkv=8, D=128, P=128, kv_dtype="i4", partition_tokens=512,
          q_mult=3.0),
+    dict(seed=64, lens=_gappy_lens(600, 64), Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16"),
+    dict(seed=65, lens=_gappy_lens(400, 65), Hq=32, Hkv=8, D=128, P=64, kv_dtype="fp8", out_dtype="f32"),
 ]
 
 
@@ -377,6 +395,7 @@ STEP_CASES = [
     dict(seed=75, lens=[1, 2, 3, 4, 5] * 100, Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16", out_dtype="f32"),
     dict(seed=77, lens=[1, 63, 64, 65, 129, 700], Hq=32, Hkv=8, D=128, P=64, kv_dtype="i8"),
     dict(seed=78, lens=[1, 127, 128, 129, 257, 700], Hq=32, Hkv=8, D=128, P=128, kv_dtype="i4"),
+    dict(seed=79, lens=_gappy_lens(300, 79), Hq=16, Hkv=4, D=128, P=64, kv_dtype="bf16"),
 ]
 
 

@@ -56,7 +56,10 @@ CASES = [  # (fmt, D, P, new_dtype, steps)
     (fmt, D, P, nd, st) for fmt in ("fp8", "i8")
     for (D, P, nd, st) in ((128, 128, "bf16", 140), (64, 64, "f32", 75), (128, 64, "bf16", 80),
                            (64, 128, "bf16", 135))
-] + [("i4", 128, 128, "bf16", 140), ("i4", 128, 256, "f32", 270)]
+] + [("i4", 128, 128, "bf16", 140), ("i4", 128, 256, "f32", 270),
+      # long pages: a re-encode takes more than one round of loads (K past 128
+      # or 256 slots, V past 1024 groups)
+      ("fp8", 128, 256, "bf16", 270), ("i8", 64, 512, "f32", 530)]
 
 
 @pytest.mark.parametrize("fmt,D,P,new_dtype,steps", CASES, ids=lambda v: str(v))
@@ -84,12 +87,12 @@ def test_append_bit_exact_every_step(fmt, D, P, new_dtype, steps):
         _compare(kp_d, vp_d, ks_d, vs_d, kp, vp, ks, vs, f"step {s}")
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_append_grows_at_every_slot(fmt):
+@pytest.mark.parametrize("fmt,P", [(f, 128) for f in FMTS] + [("fp8", 256)])
+def test_append_grows_at_every_slot(fmt, P):
     """One sequence, each new token larger than the last: the scale grows on every
     append, so every slot position re-encodes all earlier ones."""
     rng = np.random.default_rng(7)
-    B, Hkv, D, P = 1, 1, 128, 128
+    B, Hkv, D = 1, 1, 128
     bt = np.array([[2]], np.int32)
     kp, vp, ks, vs = empty_pools(fmt, 3, Hkv, P, D)
     kp_d, vp_d, ks_d, vs_d = (dev_tensor(a) for a in (kp, vp, ks, vs))
