@@ -255,10 +255,13 @@ int pkv_paged_attn_decode_int8(const void* q, pkv_dtype q_dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* paged_attn_decode_int4 - as pkv_paged_attn_decode_fp8 for a symmetric int4
- * cache (D = 128, P a multiple of 128).  Codes n widen to bf16 as 136 + n
- * exactly (an integer bit pattern, no conversion); 136 * (sum of q) is taken
- * back out of each logit and 136 * (sum of the probabilities, as the products
- * see them) out of each output.  Same sizes and errors as the fp8 entry. */
+ * cache (D = 128, P a multiple of 128).  K codes n widen to bf16 as 136 + n
+ * and V codes to fp16 as 1032 + n, exactly (integer bit patterns, no
+ * conversion); 136 * (sum of q) is taken back out of each logit and 1032 *
+ * (sum of the probabilities, as the products see them) out of each output.
+ * The value products take each probability as one fp16 (11 significant bits,
+ * p * 2^7 so that small weights stay in range) and apply the V scale to each
+ * tile's fp32 result.  Same sizes and errors as the fp8 entry. */
 int pkv_paged_attn_decode_int4(const void* q, pkv_dtype q_dtype,
                                const void* k_pool, const void* v_pool,
                                const float* k_scales, const float* v_scales,

@@ -12,6 +12,8 @@ namespace pkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -122,17 +124,6 @@ __device__ __forceinline__ void split_probs(const float (&x)[4], const float (&y
   hi = u32x4_t{a.x, b.x, c.x, d.x};
   lo = u32x4_t{a.y, b.y, c.y, d.y};
 }
-// As split_probs, with the two tiles interleaved: word i holds x[i] and y[i]
-// (the slot order of the int4 operands below).
-__device__ __forceinline__ void split_probs_zip(const float (&x)[4], const float (&y)[4], float mul,
-                                               u32x4_t& hi, u32x4_t& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x2_t a = split_pair(x[i] * mul, y[i] * mul);
-    hi[i] = a.x;
-    lo[i] = a.y;
-  }
-}
 // Two fp32 -> packed bf16 pair (round to nearest even), element a low.
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
@@ -194,6 +185,19 @@ __device__ __forceinline__ u32x4_t zip_halves(u32x4_t x) {
                  __builtin_amdgcn_perm(x[3], x[1], 0x05040100u), __builtin_amdgcn_perm(x[3], x[1], 0x07060302u)};
 }
 constexpr float INT4_BIAS = 136.f;
+// The same codes as fp16 operands: 0x6400 | u is 1024 + u, so a code n
+// (u = n + 8) becomes 1032 + n, in the slot order of nib8_to_bf16x8.
+__device__ __forceinline__ u32x4_t nib8_to_f16x8(uint32_t w) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = ((w >> (4 * i)) & 0x000F000Fu) ^ 0x64086408u;
+  return r;
+}
+constexpr float INT4_F16_BIAS = 1032.f;
+// Two fp32 -> packed fp16 pair (round to nearest even), element a low.
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
 
 // Eight one-byte cache elements (fp8 e4m3 or int8) -> a bf16x8 MFMA operand.
 template <int KVT>
@@ -206,6 +210,10 @@ __device__ __forceinline__ u32x4_t byte8_to_bf16x8(uint32_t w0, uint32_t w1) {
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

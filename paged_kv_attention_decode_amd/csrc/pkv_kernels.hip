@@ -27,9 +27,10 @@
 // * Online softmax in the log2 domain against a lazy reference: it grows only
 //   when a tile's max passes it by more than 8, so the common tile needs no
 //   cross-lane step; the running sum stays lane-local until the end.
-// * Probabilities enter the bf16 MFMA as a hi + lo bf16 pair (~16 bits).
+// * Probabilities enter the bf16 MFMA as a hi + lo bf16 pair (~16 bits);
+//   the int4 cache's value products run on fp16 operands, one fp16 each.
 // * fp8 e4m3 is widened exactly to bf16 in registers; the K scale multiplies
-//   the logits, the V scale the probabilities.
+//   the logits, the V scale the probabilities (int4: each tile's products).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -130,12 +131,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   constexpr int NKK = D / (4 * E);  // K groups per lane per 16-token tile
   constexpr int NDT = D / 16;       // 16-dim PV tiles
   constexpr bool I4 = KVT == KV_INT4;
-  constexpr bool SCALED = BITS <= 8;   // fp8, int8, int4: per-page scales, widened to bf16
+  constexpr bool SCALED = BITS <= 8;   // fp8, int8, int4: per-page scales, widened exactly
   constexpr int NCH = I4 ? 4 : SCALED ? 2 : 1;   // bf16x8 operands per 16-byte group
   constexpr int NQ = NCH * NKK;
   static_assert(NKK >= 1, "head_dim too small for this element width");
 
   constexpr float TH = 8.f;          // softmax reference lag allowed before a rescale (log2 units)
+  constexpr float P_SHIFT = 7.f;     // int4: probabilities enter fp16 products as p * 2^7
 
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, c4 = lane >> 4;
@@ -308,10 +310,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = NEG_INF, l = 0.f;
-    // int4: the widened operands are 136 + n; LP accumulates, like l, the sum
-    // of the probabilities exactly as the PV products see them (a product with
-    // an all-ones operand: every entry holds the column's sum), and qsum is the
-    // head's sum of query values, so that the bias comes back out exactly.
+    // int4: K codes widen to bf16 136 + n (QK^T), V codes to fp16 1032 + n
+    // (PV); LP accumulates the V-scaled sum of the probabilities exactly as the
+    // PV products see them (a product with an all-ones operand: every entry
+    // holds the column's sum), and qsum is the head's sum of query values, so
+    // that both biases come back out exactly.
     f32x4_t LP = {0.f, 0.f, 0.f, 0.f};
     float qsum = 0.f;
     if constexpr (I4) {
@@ -542,13 +545,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         l *= alpha;
         m = mref;
       }
+      // int4 takes the probabilities as p * 2^P_SHIFT (see the value product)
+      const float mp = I4 ? m - P_SHIFT : m;
       float p[NSUB][4];
       float lsum = 0.f;
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[sub][i] = __builtin_amdgcn_exp2f(s[sub][i] - m);
+          p[sub][i] = __builtin_amdgcn_exp2f(s[sub][i] - mp);
           lsum += p[sub][i];
         }
       l += lsum;
@@ -568,22 +573,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
           O[dt] = mfma_bf16(vr[dt], pl, O[dt]);
         }
       } else if constexpr (I4) {
-        u32x4_t ph[4], pl[4];
-        const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        // fp16 operands: the codes widen to 1032 + n, the probabilities are
+        // p * 2^P_SHIFT (at most 2^15 under the lazy reference, and values down
+        // to 2^-31 of the reference stay representable), one fp16 each.  The
+        // tile's products start from zero and enter O (and LP, the sum of the
+        // probabilities as the products see them) times the page's V scale, so
+        // no scale of any size meets the fp16 range.
+        u32x4_t pf[4];
+        const u32x4_t ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+        f32x4_t lp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          split_probs_zip(p[2 * c], p[2 * c + 1], vmul, ph[c], pl[c]);
-          LP = mfma_bf16(ones, ph[c], LP);
-          LP = mfma_bf16(ones, pl[c], LP);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pf[c][i] = pack_f16_rne(p[2 * c][i], p[2 * c + 1][i]);
+          lp = mfma_f16(ones, pf[c], lp);
         }
+        LP += lp * vmul;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const u32x4_t a = nib8_to_bf16x8(vr[dt][c]);
-            O[dt] = mfma_bf16(a, ph[c], O[dt]);
-            O[dt] = mfma_bf16(a, pl[c], O[dt]);
-          }
+          for (int c = 0; c < 4; ++c) acc = mfma_f16(nib8_to_f16x8(vr[dt][c]), pf[c], acc);
+          O[dt] += acc * vmul;
         }
       } else {
         u32x4_t ph[2], pl[2];
@@ -617,7 +628,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     lt += __shfl_xor(lt, 32);
     if constexpr (I4) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[dt] -= INT4_BIAS * LP[0];
+      for (int dt = 0; dt < NDT; ++dt) O[dt] -= INT4_F16_BIAS * LP[0];
     }
     const float qnan = __builtin_nanf("");
     if (complete) {
