@@ -336,6 +336,37 @@ def test_workspace_reuse_across_calls():
         check_close(out, oracle_decode(big, seq_lens=sl), "bf16", f"lens {lens} partition {pt}")
 
 
+def test_concurrent_streams_match_serial():
+    """Calls on two streams at once, each with its own workspace, output and
+    cache (a fused step on a bf16 cache on one, decodes of an fp8 cache on the
+    other), give bit for bit what the same calls give one at a time on one
+    stream."""
+    wa = configs.custom(seed=81, lens=[1, 700, 2100, 64, 3000, 129], Hq=32, Hkv=8, D=128, P=64, kv_dtype="bf16")
+    wb = configs.custom(seed=82, lens=[5000, 33, 1200], Hq=16, Hkv=4, D=128, P=64, kv_dtype="fp8")
+    rng = np.random.default_rng(83)
+    kn = codec.f32_to_bf16_bits(rng.standard_normal((wa.B, wa.Hkv, wa.D)).astype(np.float32))
+    vn = codec.f32_to_bf16_bits(rng.standard_normal((wa.B, wa.Hkv, wa.D)).astype(np.float32))
+
+    def run(sa, sb):
+        da, db = DeviceWorkload(wa), DeviceWorkload(wb)
+        kn_d, vn_d = dev_tensor(kn), dev_tensor(vn)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            with torch.cuda.stream(sa):
+                da.step(kn_d, vn_d, da.sl)
+            with torch.cuda.stream(sb):
+                db.decode()
+        torch.cuda.synchronize()
+        return gpu_out(da.out), gpu_out(db.out), host_bytes(da.k_pool), host_bytes(da.v_pool)
+
+    cur = torch.cuda.current_stream()
+    serial = run(cur, cur)
+    both = run(torch.cuda.Stream(), torch.cuda.Stream())
+    for name, x, y in zip(("out a", "out b", "k pool a", "v pool a"), serial, both):
+        assert np.array_equal(x, y), name
+    check_close(serial[1], oracle_decode(wb), "fp8", "fp8 cache on its own stream")
+
+
 @pytest.mark.parametrize("partition", [0, 512])
 def test_softmax_reference_paths(partition):
     """Logit profiles that drive the softmax reference up every tile, now and then,
