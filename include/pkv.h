@@ -241,9 +241,13 @@ int pkv_paged_attn_decode_fp8(const void* q, pkv_dtype q_dtype,
 
 /* paged_attn_decode_int8 - as pkv_paged_attn_decode_fp8 for a symmetric int8
  * cache: bytes are two's complement integers, real value = byte * scale.
- * Integers of at most 8 significant bits widen to bf16 exactly; scales are
- * folded in as for fp8; accumulation is fp32.  q is BF16; out is BF16 or F32.
- * Same sizes and errors as pkv_paged_attn_decode_fp8. */
+ * K bytes widen to bf16 exactly (at most 8 significant bits) and the K scale
+ * is folded into the logits; V bytes widen to fp16 as 1152 + b exactly, the
+ * value products take each probability as one fp16 (11 significant bits,
+ * p * 2^7), 1152 * (sum of the probabilities, as the products see them) is
+ * taken back out of each output, and the V scale multiplies each tile's fp32
+ * result; accumulation is fp32.  q is BF16; out is BF16 or F32.  Same sizes
+ * and errors as pkv_paged_attn_decode_fp8. */
 int pkv_paged_attn_decode_int8(const void* q, pkv_dtype q_dtype,
                                const void* k_pool, const void* v_pool,
                                const float* k_scales, const float* v_scales,

@@ -194,6 +194,16 @@ __device__ __forceinline__ u32x4_t nib8_to_f16x8(uint32_t w) {
   return r;
 }
 constexpr float INT4_F16_BIAS = 1032.f;
+// Four int8 bytes -> four fp16 values 1152 + b (bytes in order): with
+// u = b + 128 (the sign bit flipped), 0x6400 | u is 1024 + u, so one xor and
+// two byte permutes (each placing two bytes under the 0x64 exponent byte)
+// widen four values exactly.
+__device__ __forceinline__ u32x2_t i8x4_to_f16x4_biased(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  return u32x2_t{__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u),
+                 __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)};
+}
+constexpr float INT8_F16_BIAS = 1152.f;
 // Two fp32 -> packed fp16 pair (round to nearest even), element a low.
 __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));

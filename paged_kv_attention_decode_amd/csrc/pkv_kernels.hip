@@ -28,9 +28,11 @@
 //   when a tile's max passes it by more than 8, so the common tile needs no
 //   cross-lane step; the running sum stays lane-local until the end.
 // * Probabilities enter the bf16 MFMA as a hi + lo bf16 pair (~16 bits);
-//   the int4 cache's value products run on fp16 operands, one fp16 each.
+//   the int4 and int8 caches' value products run on fp16 operands, one
+//   fp16 each.
 // * fp8 e4m3 is widened exactly to bf16 in registers; the K scale multiplies
-//   the logits, the V scale the probabilities (int4: each tile's products).
+//   the logits, the V scale the probabilities (int4, int8: each tile's
+//   products).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -131,6 +133,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   constexpr int NKK = D / (4 * E);  // K groups per lane per 16-token tile
   constexpr int NDT = D / 16;       // 16-dim PV tiles
   constexpr bool I4 = KVT == KV_INT4;
+  // int4 and int8: the value products run on fp16 operands, the codes widened
+  // to V_BIAS + n and the bias taken back out through LP (see below)
+  constexpr bool F16PV = I4 || KVT == KV_INT8;
+  constexpr float V_BIAS = I4 ? INT4_F16_BIAS : INT8_F16_BIAS;
   constexpr bool SCALED = BITS <= 8;   // fp8, int8, int4: per-page scales, widened exactly
   constexpr int NCH = I4 ? 4 : SCALED ? 2 : 1;   // bf16x8 operands per 16-byte group
   constexpr int NQ = NCH * NKK;
@@ -311,10 +317,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = NEG_INF, l = 0.f;
     // int4: K codes widen to bf16 136 + n (QK^T), V codes to fp16 1032 + n
-    // (PV); LP accumulates the V-scaled sum of the probabilities exactly as the
-    // PV products see them (a product with an all-ones operand: every entry
-    // holds the column's sum), and qsum is the head's sum of query values, so
-    // that both biases come back out exactly.
+    // (PV; int8: V bytes to fp16 1152 + b); LP accumulates the V-scaled sum of
+    // the probabilities exactly as the PV products see them (a product with an
+    // all-ones operand: every entry holds the column's sum), and qsum is the
+    // head's sum of query values, so that the biases come back out exactly.
     f32x4_t LP = {0.f, 0.f, 0.f, 0.f};
     float qsum = 0.f;
     if constexpr (I4) {
@@ -541,12 +547,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         const float alpha = grow ? __builtin_amdgcn_exp2f(m - mref) : 1.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
-        if constexpr (I4) LP *= alpha;
+        if constexpr (F16PV) LP *= alpha;
         l *= alpha;
         m = mref;
       }
-      // int4 takes the probabilities as p * 2^P_SHIFT (see the value product)
-      const float mp = I4 ? m - P_SHIFT : m;
+      // int4 and int8 take the probabilities as p * 2^P_SHIFT (see the value product)
+      const float mp = F16PV ? m - P_SHIFT : m;
       float p[NSUB][4];
       float lsum = 0.f;
 #pragma unroll
@@ -596,6 +602,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
           for (int c = 0; c < 4; ++c) acc = mfma_f16(nib8_to_f16x8(vr[dt][c]), pf[c], acc);
           O[dt] += acc * vmul;
         }
+      } else if constexpr (KVT == KV_INT8) {
+        // as int4: fp16 operands, V bytes widened to 1152 + b, one fp16 per
+        // probability (p * 2^P_SHIFT), the tile's products times the V scale
+        u32x4_t pf[2];
+        const u32x4_t ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+        f32x4_t lp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          pf[c] = u32x4_t{pack_f16_rne(p[2 * c][0], p[2 * c][1]), pack_f16_rne(p[2 * c][2], p[2 * c][3]),
+                          pack_f16_rne(p[2 * c + 1][0], p[2 * c + 1][1]),
+                          pack_f16_rne(p[2 * c + 1][2], p[2 * c + 1][3])};
+          lp = mfma_f16(ones, pf[c], lp);
+        }
+        LP += lp * vmul;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const u32x2_t a = i8x4_to_f16x4_biased(vr[dt][0]), b = i8x4_to_f16x4_biased(vr[dt][1]);
+          const u32x2_t c = i8x4_to_f16x4_biased(vr[dt][2]), d = i8x4_to_f16x4_biased(vr[dt][3]);
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mfma_f16(u32x4_t{a.x, a.y, b.x, b.y}, pf[0], acc);
+          acc = mfma_f16(u32x4_t{c.x, c.y, d.x, d.y}, pf[1], acc);
+          O[dt] += acc * vmul;
+        }
       } else {
         u32x4_t ph[2], pl[2];
         split_probs(p[0], p[1], vmul, ph[0], pl[0]);
@@ -626,9 +655,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // ---- finish the segment ------------------------------------------------------
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
-    if constexpr (I4) {
+    if constexpr (F16PV) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[dt] -= INT4_F16_BIAS * LP[0];
+      for (int dt = 0; dt < NDT; ++dt) O[dt] -= V_BIAS * LP[0];
     }
     const float qnan = __builtin_nanf("");
     if (complete) {
