@@ -186,10 +186,19 @@ def cpu_baseline(wl, steps, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    # one decode of the first step's cache on a single thread: the oracle's own
+    # scaling with threads, for context
+    st = steps[0]
+    t1 = time.perf_counter()
+    c_oracle.decode(wl.q, wl.q_dtype, kp, vp, wl.kv_dtype, wl.block_tables, st["seq_lens"], wl.Hq, wl.P,
+                    wl.scale, ks, vs, nthreads=1)
+    el1 = time.perf_counter() - t1
+    d1, _, _ = alg_bytes(wl, st["seq_lens"])
     return {"value": kv_total / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seqs_per_s_per_layer": seqs / el,
             "sample": f"full batch of {wl.B} sequences, {reps} step(s) of append + fp64 decode "
-                      f"(C oracle, {threads} threads), {el:.1f} s"}
+                      f"(C oracle, {threads} threads), {el:.1f} s",
+            "one_thread_decode": {"value": d1 / el1 / 1e9, "unit": "GB/s", "seconds": round(el1, 2)}}
 
 
 def cpu_baseline_prefill(wl, seconds):
