@@ -464,6 +464,18 @@ def test_step_equals_append_then_decode(spec):
     check_close(out, ref, wl.kv_dtype, f"step seed {spec['seed']}", out_rounding=wl.out_dtype == "bf16")
 
 
+def _random_step_cases(n=12, seed=888):
+    """The random decode shapes (every cache type, G 1-16, ragged and empty
+    lengths, range sizes, both output types) as fused steps."""
+    return [dict(spec, seed=5000 + i) for i, spec in enumerate(_random_cases(n=n, seed=seed))]
+
+
+@pytest.mark.parametrize("spec", _random_step_cases(),
+                         ids=lambda s: f"{s['kv_dtype']}-D{s['D']}-P{s['P']}-G{s['Hq'] // s['Hkv']}-s{s['seed']}")
+def test_step_random_configs(spec):
+    test_step_equals_append_then_decode(spec)
+
+
 def test_step_bad_page_stores_nothing():
     wl = configs.custom(seed=76, lens=[70, 70], Hq=8, Hkv=2, D=128, P=64, kv_dtype="bf16")
     wl.block_tables[1, 1] = wl.num_pages + 3          # slot 69 of sequence 1 lies on a bad page
