@@ -47,6 +47,23 @@
 
 namespace pkv {
 
+// Cache stores of the append paths are nontemporal: the decode that reads the
+// cache next ran 5-14 us slower while the new tokens' lines sat dirty in L2
+// (whole-line stores made no difference; streaming stores did).
+template <typename T>
+__device__ __forceinline__ void store_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
+template <int KVT>
+__device__ __forceinline__ void put_code_nt(void* base, size_t x, uint32_t c) {
+  typedef typename Kv<KVT>::elem_t T;
+  if constexpr (Kv<KVT>::BITS == 4) {
+    uint8_t* p = static_cast<uint8_t*>(base) + (x >> 1);
+    const int sh = 4 * (int)(x & 1);
+    store_nt(p, (uint8_t)((*p & ~(0xF << sh)) | ((c & 0xFu) << sh)));
+  } else {
+    store_nt(static_cast<T*>(base) + x, (T)c);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the n partial ranges of one (b, g) for 256 of its G*D
 // outputs, starting at x0, run by one wave.
@@ -748,11 +765,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int j = (L - 1) % P;
     const size_t ch = chunk_elem(d.z, g, Hkv, P, D);
     if (lane < ngrp)
-      *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(kpool) + elem_byte<KVT>(ch + k_elem<E>(j, lane * E, P))) = kgrp;
+      store_nt(reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(kpool) + elem_byte<KVT>(ch + k_elem<E>(j, lane * E, P))), kgrp);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {                 // each dim's V element lies in its own byte
       const int dd = lane + 64 * i;
-      if (dd < D) put_code<KVT>(vpool, ch + v_elem<E>(j, dd, D), vv[i]);
+      if (dd < D) put_code_nt<KVT>(vpool, ch + v_elem<E>(j, dd, D), vv[i]);
     }
   }
 }
@@ -782,8 +799,8 @@ __global__ __launch_bounds__(256) void append_kernel(
     const size_t ch = chunk_elem(page, g, Hkv, P, D);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      put_code<KVT>(kpool, ch + k_elem<E>(j, d + i, P), get_code<KVT>(k_new, row0 + x + i));
-      put_code<KVT>(vpool, ch + v_elem<E>(j, d + i, D), get_code<KVT>(v_new, row0 + x + i));
+      put_code_nt<KVT>(kpool, ch + k_elem<E>(j, d + i, P), get_code<KVT>(k_new, row0 + x + i));
+      put_code_nt<KVT>(vpool, ch + v_elem<E>(j, d + i, D), get_code<KVT>(v_new, row0 + x + i));
     }
   }
 }
@@ -922,7 +939,7 @@ __device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uin
           u32x4_t r;
 #pragma unroll
           for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[a][c][q]);
-          *reinterpret_cast<u32x4_t*>(pool + 16 * (c * P + t)) = r;
+          store_nt(reinterpret_cast<u32x4_t*>(pool + 16 * (c * P + t)), r);
         }
       }
     }
@@ -983,7 +1000,7 @@ __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* l
           r[q] = outw;
         }
       }
-      *reinterpret_cast<u32x4_t*>(pool + (size_t)gi * 16) = r;
+      store_nt(reinterpret_cast<u32x4_t*>(pool + (size_t)gi * 16), r);
     }
   }
 }
@@ -1066,11 +1083,11 @@ __global__ __launch_bounds__(256) void append_quant_kernel(
   // (disjoint from the re-encoded slots): two bytes, or one int4 byte
   uint8_t* kt = kp + elem_byte<KVT>(k_elem<E>(j, d0, P));
   if constexpr (KVT == KV_INT4)
-    *kt = (uint8_t)(nbk[0] | (nbk[NPL - 1] << 4));
+    store_nt(kt, (uint8_t)(nbk[0] | (nbk[NPL - 1] << 4)));
   else if constexpr (NPL == 2)
-    *reinterpret_cast<uint16_t*>(kt) = (uint16_t)(nbk[0] | (nbk[NPL - 1] << 8));
+    store_nt(reinterpret_cast<uint16_t*>(kt), (uint16_t)(nbk[0] | (nbk[NPL - 1] << 8)));
   else
-    *kt = (uint8_t)nbk[0];
+    store_nt(kt, (uint8_t)nbk[0]);
   if (rv) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i) s_nb[wv][d0 + i] = (uint8_t)nbv[i];
@@ -1078,7 +1095,7 @@ __global__ __launch_bounds__(256) void append_quant_kernel(
     requant_v<KVT, D>(vp, j, lutv, s_nb[wv], lane);
   } else {
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) put_code<KVT>(vp, v_elem<E>(j, d0 + i, D), nbv[i]);   // own bytes
+    for (int i = 0; i < NPL; ++i) put_code_nt<KVT>(vp, v_elem<E>(j, d0 + i, D), nbv[i]);   // own bytes
   }
   if (lane == 0) {
     kscales[si] = sk;
