@@ -19,6 +19,10 @@ TOL = {"f32": (1e-2, 1e-3), "bf16": (1e-2, 1e-3), "fp8": (3e-2, None), "i8": (1e
 DECODE_SCALED = {"fp8": "paged_attn_decode_fp8", "i8": "paged_attn_decode_int8", "i4": "paged_attn_decode_int4"}
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
+# (what, kv dtype, elements, max-abs, mean-abs) of every full-workload comparison
+# made with ``report=True``; conftest prints them at the end of the run.
+PARITY_LOG: list = []
+
 
 def dev_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
     a = np.ascontiguousarray(a)
@@ -110,7 +114,7 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def check_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = "",
-                out_rounding: bool = False):
+                out_rounding: bool = False, report: bool = False):
     """Element-wise comparison at the parity bounds above; returns (max, mean).
 
     With ``out_rounding`` (bf16 outputs of large magnitude in edge-case tests),
@@ -122,6 +126,8 @@ def check_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = "",
     assert np.isfinite(got).all(), f"{what}: GPU produced non-finite values"
     err = np.abs(got - ref)
     mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    if report:
+        PARITY_LOG.append((what, kv_dtype, int(err.size), mx, mean))
     tmax, tmean = TOL[kv_dtype]
     allow = bf16_half_ulp(ref) if out_rounding else np.zeros_like(ref)
     worst = float((err - allow).max()) if err.size else 0.0

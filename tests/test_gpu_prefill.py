@@ -1,6 +1,8 @@
 """GPU parity of chunked prefill: pkv_kv_append_chunk (bit-exact against
 oracle.paged.append_chunk) and pkv_paged_prefill (against oracle.paged.prefill
 at the bf16 tolerance), through the C ABI."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -8,7 +10,7 @@ import torch
 import paged_kv_attention_decode_amd as pkv
 from oracle import paged
 from workloads import codec, configs, layout
-from tests._helpers import LOGIT_PROFILES, check_close, dev_tensor, gpu_out, host_bytes
+from tests._helpers import LOGIT_PROFILES, ORACLE_THREADS, check_close, dev_tensor, gpu_out, host_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -253,21 +255,38 @@ def test_prefill_padding_rows_not_written():
     assert np.isfinite(got[5:]).all() and not np.all(got[5:] == 7.0)
 
 
-def test_config_chunked_prefill_sampled_sequences():
-    """The full chunked-prefill workload in the launch the benchmark times; two
-    sequences (the shortest and the longest cached context) checked against the
-    oracle, every row finite."""
+@pytest.mark.timeout(900)
+def test_config_chunked_prefill_full_size():
+    """The full chunked-prefill workload (16 sequences, 8192 chunk tokens) in the
+    launch the benchmark times.  The GPU chunk append is compared byte for byte
+    with the oracle's append of the whole workload; the prefill output of six
+    sequences (the shortest and the longest cached context and four between,
+    3072 query rows) is compared with the oracle run on the oracle's own pools;
+    every output row is finite."""
     wl = configs.chunked_prefill_bf16()
     d = _up(wl)
     _gpu_append_chunk(wl, d)
     got = _gpu_prefill(wl, d)
     assert np.isfinite(got).all()
+    kp, vp = _full_pools(wl)
+    assert np.array_equal(host_bytes(d["k_pool"]), kp.view(np.uint8).reshape(-1)), "chunk append (K) differs"
+    assert np.array_equal(host_bytes(d["v_pool"]), vp.view(np.uint8).reshape(-1)), "chunk append (V) differs"
     ctx = wl.seq_lens - wl.chunk_lens
-    picks = [int(np.argmin(ctx)), int(np.argmax(ctx))]
-    kp = host_bytes(d["k_pool"]).view(np.uint16).reshape(wl.k_pool.shape)
-    vp = host_bytes(d["v_pool"]).view(np.uint16).reshape(wl.v_pool.shape)
-    ref = paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
-                        wl.scale, batches=picks)
-    for b in picks:
+    order = np.argsort(ctx, kind="stable")
+    picks = [int(order[i]) for i in (0, 3, 6, 9, 12, len(order) - 1)]
+    assert ctx[picks[0]] == ctx.min() and ctx[picks[-1]] == ctx.max()
+
+    def one(b):
+        return paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "bf16", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                             wl.scale, batches=[b])
+
+    with ThreadPoolExecutor(max_workers=min(len(picks), ORACLE_THREADS)) as ex:
+        refs = list(ex.map(one, picks))
+    rows_got, rows_ref = [], []
+    for b, ref in zip(picks, refs):
         r0, r1 = int(wl.cu_q[b]), int(wl.cu_q[b + 1])
-        check_close(got[r0:r1], ref[r0:r1], "bf16", f"sequence {b}", out_rounding=True)
+        check_close(got[r0:r1], ref[r0:r1], "bf16", f"sequence {b} (context {int(ctx[b])})", out_rounding=True)
+        rows_got.append(got[r0:r1])
+        rows_ref.append(ref[r0:r1])
+    check_close(np.concatenate(rows_got), np.concatenate(rows_ref), "bf16",
+                "chunked_prefill_bf16 (6 of 16 sequences)", out_rounding=True, report=True)

@@ -14,7 +14,7 @@ import torch
 import paged_kv_attention_decode_amd as pkv
 from oracle import paged
 from workloads import codec, configs, layout
-from tests._helpers import DeviceWorkload, check_close, dev_tensor, gpu_out, host_bytes, oracle_decode
+from tests._helpers import PARITY_LOG, DeviceWorkload, check_close, dev_tensor, gpu_out, host_bytes, oracle_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -159,12 +159,13 @@ def test_append_quant_errors():
     assert e.value.code == -3
 
 
-def _inflight_quant_run(fmt, B, n_steps, max_len, decode_every, pools_every=True):
+def _inflight_quant_run(fmt, B, n_steps, max_len, decode_every, pools_every=True, report=None):
     gen = {"fp8": configs.inflight_fp8, "i8": configs.inflight_int8, "i4": configs.inflight_int4}[fmt]
     wl = gen(B=B, n_steps=n_steps, max_len=max_len)
     dw = DeviceWorkload(wl)
     kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
     ks, vs = wl.k_scales.copy(), wl.v_scales.copy()
+    worst = (0.0, 0.0)
     for s, st in enumerate(wl.steps):
         sl = dev_tensor(st.seq_lens)
         gpu_append(fmt, dev_tensor(st.k_new), dev_tensor(st.v_new), "bf16", dw.bt, sl, dw.k_pool,
@@ -180,7 +181,10 @@ def _inflight_quant_run(fmt, B, n_steps, max_len, decode_every, pools_every=True
         if decode_every or s == n_steps - 1:
             out = gpu_out(dw.decode(seq_lens=sl))
             wl_now = configs.Workload(**{**wl.__dict__, "k_scales": ks, "v_scales": vs})
-            check_close(out, oracle_decode(wl_now, kp, vp, st.seq_lens), fmt, f"decode after step {s}")
+            mx, mean = check_close(out, oracle_decode(wl_now, kp, vp, st.seq_lens), fmt, f"decode after step {s}")
+            worst = (max(worst[0], mx), max(worst[1], mean))
+    if report:
+        PARITY_LOG.append((report, fmt, wl.B * wl.Hq * wl.D * n_steps) + worst)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -188,8 +192,11 @@ def test_config_inflight_quant_reduced_every_step(fmt):
     _inflight_quant_run(fmt, B=16, n_steps=16, max_len=4000, decode_every=True)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("fmt", FMTS)
 def test_config_inflight_quant_full(fmt):
-    """The in-flight batch with a one-byte cache: 16 quantise-on-write steps;
-    scales bit-exact after every step, pools after the last one, then decode."""
-    _inflight_quant_run(fmt, B=256, n_steps=16, max_len=32768, decode_every=False, pools_every=False)
+    """The in-flight batch with a quantised cache: 16 quantise-on-write steps;
+    scales bit-exact after every step, pools after the last one; every output
+    row decoded after every step against the oracle."""
+    _inflight_quant_run(fmt, B=256, n_steps=16, max_len=32768, decode_every=True, pools_every=False,
+                        report=f"inflight_{fmt} append+decode, 16 steps (worst)")
