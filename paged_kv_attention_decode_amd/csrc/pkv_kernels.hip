@@ -791,15 +791,21 @@ __global__ __launch_bounds__(256) void append_kernel(
   const int page = bt[(size_t)b * MP + pgi];
   if ((unsigned)page >= (unsigned)NP) return;
   // Each thread copies a pair of dims (d even): an int4 K pair is one byte of
-  // the pool, and its V elements lie in two different bytes, so no byte is
-  // written by two threads.
+  // the pool, stored whole from the row's byte; its V elements lie in two
+  // different bytes (each shared with another token's nibble, so read,
+  // patched and written back), so no byte is written by two threads.
   const size_t row0 = (size_t)b * Hkv * D;
   for (int x = 2 * threadIdx.x; x < Hkv * D; x += 2 * blockDim.x) {
     const int g = x / D, d = x - g * D;
     const size_t ch = chunk_elem(page, g, Hkv, P, D);
+    if constexpr (KVT == KV_INT4) {
+      store_nt(static_cast<uint8_t*>(kpool) + ((ch + k_elem<E>(j, d, P)) >> 1),
+               static_cast<const uint8_t*>(k_new)[(row0 + x) >> 1]);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      put_code_nt<KVT>(kpool, ch + k_elem<E>(j, d + i, P), get_code<KVT>(k_new, row0 + x + i));
+      if constexpr (KVT != KV_INT4)
+        put_code_nt<KVT>(kpool, ch + k_elem<E>(j, d + i, P), get_code<KVT>(k_new, row0 + x + i));
       put_code_nt<KVT>(vpool, ch + v_elem<E>(j, d + i, D), get_code<KVT>(v_new, row0 + x + i));
     }
   }
