@@ -304,6 +304,31 @@ int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const v
                     void* out, pkv_dtype out_dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* decode_step_noalloc - pkv_decode_step without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  It runs the same
+ * kernels as pkv_decode_step (same results, bit for bit) and makes no
+ * allocation of any kind: the workspace is a static device array inside the
+ * library, 40 MiB (41943040 bytes), one copy per device, created with the
+ * library's code on that device and held until the process ends.  Its address
+ * is looked up once per device, on the first call made with that device
+ * current.  Shapes whose pkv_decode_workspace_bytes exceed 40 MiB are rejected
+ * with PKV_E_WORKSPACE (on a 256-CU device every G <= 16 and D <= 128 fits
+ * for up to ~490 000 (sequence, kv head) pairs).  Nothing in the array needs
+ * to start at zero; each call overwrites what it reads.  Every call on one
+ * device shares that device's array: calls that may overlap on one device
+ * (different streams, or different host threads without ordering) race and
+ * give wrong results; serialise them.  Arguments, dtypes and errors are those
+ * of pkv_decode_step minus workspace / workspace_bytes. */
+int pkv_decode_step_noalloc(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_new,
+                            void* k_pool, void* v_pool, pkv_dtype kv_dtype,
+                            const float* k_scales, const float* v_scales,
+                            const int32_t* block_tables, int max_pages_per_seq,
+                            const int32_t* seq_lens, int batch, int num_pages,
+                            int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                            float scale, int partition_tokens,
+                            void* out, pkv_dtype out_dtype, void* stream);
+
 /* kv_append_chunk - write a chunk of new K/V tokens per sequence into its pages.
  *
  * The paged store of the first page ("key mechanisms", after the page-table

@@ -159,6 +159,20 @@ def decode_step(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, block_tables
         _stream(stream)))
 
 
+def decode_step_noalloc(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, block_tables, seq_lens,
+                        num_q_heads, num_kv_heads, head_dim, page_size, scale, out, out_dtype,
+                        k_scales=None, v_scales=None, partition_tokens=0, stream=None):
+    """decode_step with the library's static per-device scratch as its workspace
+    (no allocation; calls that overlap on one device race)."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("decode_step_noalloc", lib().pkv_decode_step_noalloc(
+        _ptr(q), _code(q_dtype), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _code(kv_dtype),
+        _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), MP, _ptr(seq_lens), B, NP, num_q_heads,
+        num_kv_heads, head_dim, page_size, float(scale), int(partition_tokens), _ptr(out),
+        _code(out_dtype), _stream(stream)))
+
+
 def kv_append_chunk(k_new, v_new, kv_dtype, cu_new, block_tables, seq_lens, k_pool, v_pool,
                     num_kv_heads, head_dim, page_size, stream=None):
     """Write each sequence's chunk of new tokens (rows cu_new[b] .. cu_new[b+1] of

@@ -68,12 +68,13 @@ int check_decode(const void* q, int q_dtype, const void* k_pool, const void* v_p
                  const int32_t* block_tables, int max_pages, const int32_t* seq_lens, int batch,
                  int num_pages, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
                  int partition_tokens, const void* out, int out_dtype, const void* workspace,
-                 size_t workspace_bytes) {
-  if (batch > 0 && (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out || !workspace))
+                 size_t workspace_bytes, bool static_ws) {
+  if (batch > 0 && (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out))
     return fail(PKV_E_NULL, "a required pointer is NULL");
+  if (batch > 0 && !static_ws && !workspace) return fail(PKV_E_NULL, "workspace is NULL");
   int rc = check_pool_shape(kv_dtype, max_pages, batch, num_pages, num_kv_heads, head_dim, page_size);
   if (rc) return rc;
-  if (batch > 0 && (rc = check_align({q, k_pool, v_pool, out, workspace}))) return rc;
+  if (batch > 0 && (rc = check_align({q, k_pool, v_pool, out, static_ws ? nullptr : workspace}))) return rc;
   const int want_q = kv_dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
   if (q_dtype != want_q)
     return fail(PKV_E_DTYPE, "q dtype %d unsupported with kv dtype %d (need %d)", q_dtype, kv_dtype, want_q);
@@ -90,7 +91,10 @@ int check_decode(const void* q, int q_dtype, const void* k_pool, const void* v_p
   if (batch > 0) {
     const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim);
     if (need == 0) return fail(PKV_E_HIP, "could not query the current HIP device");
-    if (workspace_bytes < need)
+    if (static_ws && need > pkv::kStaticScratchBytes)
+      return fail(PKV_E_WORKSPACE, "this shape needs %zu bytes of workspace; the static scratch holds %zu", need,
+                  pkv::kStaticScratchBytes);
+    if (!static_ws && workspace_bytes < need)
       return fail(PKV_E_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
   }
   return PKV_OK;
@@ -101,12 +105,16 @@ int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
                int max_pages, const int32_t* seq_lens, int batch, int num_pages, int num_q_heads,
                int num_kv_heads, int head_dim, int page_size, float scale, int partition_tokens,
                void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream,
-               const void* k_new = nullptr, const void* v_new = nullptr) {
+               const void* k_new = nullptr, const void* v_new = nullptr, bool static_ws = false) {
   int rc = check_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_pages, seq_lens, batch,
                         num_pages, num_q_heads, num_kv_heads, head_dim, page_size, partition_tokens,
-                        out, out_dtype, workspace, workspace_bytes);
+                        out, out_dtype, workspace, workspace_bytes, static_ws);
   if (rc) return rc;
   if (batch == 0) return PKV_OK;
+  if (static_ws) {      // every check has passed: only now look up this device's scratch array
+    hipError_t e = pkv::static_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "static scratch lookup");
+  }
   pkv::DecodeArgs a;
   a.q = q;
   a.k_new = k_new;
@@ -159,6 +167,27 @@ int append_quant(int kv_dtype, const void* k_new, const void* v_new, pkv_dtype n
   hipError_t e = pkv::launch_append_quant(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quantising append launch");
   return PKV_OK;
+}
+
+// Append + decode (the step entries): step-specific checks, then run_decode.
+int run_step(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+             pkv_dtype kv_dtype, const float* k_scales, const float* v_scales, const int32_t* block_tables,
+             int max_pages_per_seq, const int32_t* seq_lens, int batch, int num_pages, int num_q_heads,
+             int num_kv_heads, int head_dim, int page_size, float scale, int partition_tokens, void* out,
+             pkv_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream, bool static_ws) {
+  if (batch > 0 && (!k_new || !v_new)) return fail(PKV_E_NULL, "k_new / v_new are NULL");
+  if (batch > 0) {
+    const int rc = check_align({k_new, v_new});
+    if (rc) return rc;
+  }
+  if (scaled_dtype(kv_dtype)) {
+    if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 / int8 / int4 scales are NULL");
+  } else {
+    k_scales = v_scales = nullptr;
+  }
+  return run_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scales, v_scales, block_tables, max_pages_per_seq,
+                    seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
+                    partition_tokens, out, out_dtype, workspace, workspace_bytes, stream, k_new, v_new, static_ws);
 }
 
 }  // namespace
@@ -387,19 +416,20 @@ int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const v
                     int partition_tokens, void* out, pkv_dtype out_dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (batch > 0 && (!k_new || !v_new)) return fail(PKV_E_NULL, "k_new / v_new are NULL");
-  if (batch > 0) {
-    const int rc = check_align({k_new, v_new});
-    if (rc) return rc;
-  }
-  if (scaled_dtype(kv_dtype)) {
-    if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 / int8 / int4 scales are NULL");
-  } else {
-    k_scales = v_scales = nullptr;
-  }
-  return run_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scales, v_scales, block_tables, max_pages_per_seq,
-                    seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
-                    partition_tokens, out, out_dtype, workspace, workspace_bytes, stream, k_new, v_new);
+  return run_step(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, k_scales, v_scales, block_tables,
+                  max_pages_per_seq, seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size,
+                  scale, partition_tokens, out, out_dtype, workspace, workspace_bytes, stream, false);
+}
+
+int pkv_decode_step_noalloc(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_new, void* k_pool,
+                            void* v_pool, pkv_dtype kv_dtype, const float* k_scales, const float* v_scales,
+                            const int32_t* block_tables, int max_pages_per_seq, const int32_t* seq_lens, int batch,
+                            int num_pages, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                            float scale, int partition_tokens, void* out, pkv_dtype out_dtype, void* stream) {
+  g_last_error.clear();
+  return run_step(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, k_scales, v_scales, block_tables,
+                  max_pages_per_seq, seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size,
+                  scale, partition_tokens, out, out_dtype, nullptr, 0, stream, true);
 }
 
 int pkv_debug_gather(const void* k_pool, const void* v_pool, pkv_dtype kv_dtype, const int32_t* block_tables,

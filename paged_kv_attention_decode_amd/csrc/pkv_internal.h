@@ -15,8 +15,16 @@ inline int elem_bits(int kvt) { return kvt == KV_F32 ? 32 : kvt == KV_BF16 ? 16 
 inline int v_block_tokens(int kvt) { return 4 * (128 / elem_bits(kvt)); }
 
 // Upper bound on decode wavefronts per compute unit; sizes the partial-result
-// workspace together with the device's compute-unit count.
-constexpr int kMaxWavesPerCU = 16;
+// workspace together with the device's compute-unit count.  The launch never
+// exceeds it: at most 512 / D waves per CU (1024 / D for int4, D = 128 only).
+constexpr int kMaxWavesPerCU = 8;
+
+// Size of the library's static device scratch array, the workspace of the
+// allocation-free step entry point (one copy per device, held until the
+// process ends).  40 MiB covers the partial slots of every accepted group
+// size and head dimension on a 256-CU device (34 MB at G = 16, D = 128) plus
+// the 16-byte descriptors of up to ~490 000 (sequence, kv head) pairs.
+constexpr size_t kStaticScratchBytes = (size_t)40 << 20;
 
 // Workspace layout: partial slots (2 per wave) then B * Hkv 16-byte descriptors.
 inline size_t partials_bytes(int cus, int G, int D) {
@@ -131,5 +139,8 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipSt
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Compute units of the current device (cached per device); <= 0 on failure.
 int device_cu_count();
+// Device address of the current device's static scratch array
+// (kStaticScratchBytes), looked up once per device and cached.
+hipError_t static_scratch(void** ptr);
 
 }  // namespace pkv

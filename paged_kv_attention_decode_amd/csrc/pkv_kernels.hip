@@ -1144,6 +1144,12 @@ __global__ __launch_bounds__(256) void gather_kernel(
   }
 }
 
+// Workspace of the allocation-free step entry point: a file-scope device
+// array, one copy per device.  Host code never passes this name to a kernel
+// (on the host it is only a stand-in symbol); it passes the device address
+// that static_scratch() looks up.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
@@ -1151,6 +1157,7 @@ namespace {
 
 struct DevInfo {
   int cus = 0;
+  void* scratch = nullptr;   // device address of `scratch` on this device
 };
 std::mutex g_mu;
 DevInfo g_dev[64];
@@ -1215,6 +1222,24 @@ int device_cu_count() {
     g_dev[dev].cus = cus;
   }
   return g_dev[dev].cus;
+}
+
+hipError_t static_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_dev[dev].scratch) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // the current device's copy
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_dev[dev].scratch = p;
+  }
+  *ptr = g_dev[dev].scratch;
+  return hipSuccess;
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {

@@ -227,3 +227,28 @@ def test_read_probe_argument_errors():
     assert L.pkv_debug_read_probe(F, 17, F, None) == -2
     assert L.pkv_debug_read_probe(F + 4, 16, F, None) == -6
     assert L.pkv_debug_read_probe(None, 0, None, None) == 0
+
+
+def _step_noalloc(**over):
+    a = dict(q=F, qdt=1, kn=F, vn=F, kp=F, vp=F, kvdt=1, ks=0, vs=0, bt=F, mp=4, sl=F, b=2, np_=8, hq=8,
+             hkv=2, d=128, p=64, scale=0.1, pt=0, out=F, odt=1)
+    a.update(over)
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return pkv.lib().pkv_decode_step_noalloc(vp(a["q"]), a["qdt"], vp(a["kn"]), vp(a["vn"]), vp(a["kp"]),
+                                             vp(a["vp"]), a["kvdt"], vp(a["ks"]), vp(a["vs"]), vp(a["bt"]),
+                                             a["mp"], vp(a["sl"]), a["b"], a["np_"], a["hq"], a["hkv"], a["d"],
+                                             a["p"], a["scale"], a["pt"], vp(a["out"]), a["odt"], None)
+
+
+@pytest.mark.parametrize("over,code", [(dict(kn=0), -1), (dict(q=0), -1), (dict(kvdt=2, p=64), -1),
+                                       (dict(kvdt=2, p=32, ks=1, vs=1), -2), (dict(d=32), -2),
+                                       (dict(qdt=0), -3), (dict(hq=7), -2), (dict(kn=F + 8), -6),
+                                       (dict(out=F + 4), -6), (dict(odt=7), -3)])
+def test_step_noalloc_rejects_bad_arguments(over, code):
+    """The allocation-free step validates like decode_step, before it looks up
+    its static scratch (so no device is needed to reach these errors)."""
+    assert _step_noalloc(**over) == code
+
+
+def test_step_noalloc_batch_zero_is_a_noop_without_device():
+    assert _step_noalloc(b=0, q=0, kn=0, vn=0, kp=0, vp=0, bt=0, sl=0, out=0) == 0
