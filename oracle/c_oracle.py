@@ -20,22 +20,33 @@ DT = {"f32": 0, "bf16": 1, "fp8": 2, "i8": 3, "i4": 4}
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile pkv_oracle.c into liboracle.so with gcc (-O2, plain C, pthreads)."""
-    if force or not os.path.exists(LIB):
-        tmp = LIB + ".tmp"
-        subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", SRC,
+# Flags of the sanitizer build (address + undefined behaviour) that the CPU
+# tests load in a child process through PKV_ORACLE_LIB, with the sanitizer
+# runtime preloaded.
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"]
+
+
+def build(force: bool = True, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile pkv_oracle.c with gcc (-O2, plain C, pthreads) into liboracle.so,
+    or with ``sanitize`` under ASan + UBSan into ``out``."""
+    out = out or LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        flags = SAN_FLAGS if sanitize else ["-O2"]
+        subprocess.run(["gcc", *flags, "-std=c99", "-fPIC", "-shared", "-pthread", SRC,
                         "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, out)
+    return out
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        path = os.environ.get("PKV_ORACLE_LIB") or LIB
+        if path == LIB and not os.path.exists(LIB):
             build()
-        L = ctypes.CDLL(LIB)
+        L = ctypes.CDLL(path)
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.orc_decode.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                  i32, i32, f32, vp, i32, vp, i32]
