@@ -240,27 +240,72 @@ __device__ __forceinline__ u32x4_t ld16_stream(const uint8_t* p) {
 
 // ---------------------------------------------------------------------------
 // Work split.  Units are (b, g, range) in b-major, then g, then range order;
-// range r of (b, g) covers tokens [r*PT, min(L_b, (r+1)*PT)).  With T units and
-// at most Wmax waves, k = ceil(T / Wmax) and W = ceil(T / k) waves get work;
-// wave w owns units [floor(w*T/W), floor((w+1)*T/W)).
+// range r of (b, g) covers tokens [r*PT, min(L_b, (r+1)*PT)).  In front of the
+// ranges of each (b, g) sit SWITCH_UNITS cost-only units that stand for what a
+// wave pays to start a new (b, g) (its query, page id and first tile arrive
+// one round trip after another): a wave whose share begins on them starts at
+// the pair's first range, one whose share ends on them stops before the pair.
+// With T units (cost units included) and at most Wmax waves,
+// k = ceil(T / Wmax) and W = ceil(T / k) waves get work.  The waves of
+// workgroup i run on XCD i mod 8 (round-robin dispatch), and the waves of the
+// odd XCDs stream 8-10 % slower than those of the even ones (per-wave
+// timestamps of the decode, on every box measured), so when every share holds
+// at least 3 units (k >= 5) the shares are weighted (odd : even = 56 : 64,
+// the best of 64 down to 44 in same-box timings of four workloads, with two
+// switch units per (b, g), the best of 0, 1 and 2): wave w owns units
+// [T * C(w) / C(W), T * C(w + 1) / C(W)), C(w) = sum of the weights of waves
+// 0 .. w - 1 (even XCD: WEIGHT_EVEN, odd: WEIGHT_ODD); otherwise
+// [w * T / W, (w + 1) * T / W).
 // ---------------------------------------------------------------------------
+#ifndef PKV_WEIGHT_ODD
+#define PKV_WEIGHT_ODD 56
+#endif
+#ifndef PKV_SWITCH_UNITS
+#define PKV_SWITCH_UNITS 2
+#endif
+constexpr int WEIGHT_EVEN = 64, WEIGHT_ODD = PKV_WEIGHT_ODD;
+constexpr int SWITCH_UNITS = PKV_SWITCH_UNITS;
 struct Split {
   int64_t T;
   int64_t W;
+  int64_t CW;      // C(W) when weighted, else 0
 };
+// C(w): sum of the share weights of waves 0 .. w - 1 (32 waves = 8 workgroups
+// = one round of the 8 XCDs).
+__device__ __forceinline__ int64_t share_weight_sum(int64_t w) {
+  constexpr int64_t ROUND = 16 * WEIGHT_EVEN + 16 * WEIGHT_ODD;
+  const int r = (int)(w & 31), grp = r >> 2;
+  const int64_t c = (w >> 5) * ROUND + 4 * (((grp + 1) >> 1) * WEIGHT_EVEN + (grp >> 1) * WEIGHT_ODD);
+  return c + (r & 3) * ((grp & 1) ? WEIGHT_ODD : WEIGHT_EVEN);
+}
 __device__ __forceinline__ Split make_split(int64_t T, int Wmax) {
   Split s;
   s.T = T;
   const int64_t k = (T + Wmax - 1) / Wmax;
   s.W = T > 0 ? (T + k - 1) / k : 0;
+  s.CW = (k >= 5 && WEIGHT_ODD != WEIGHT_EVEN) ? share_weight_sum(s.W) : 0;
   return s;
 }
-__device__ __forceinline__ int64_t range_begin(const Split& s, int64_t w) { return w * s.T / s.W; }
-// The wave whose range contains unit idx.
+__device__ __forceinline__ int64_t range_begin(const Split& s, int64_t w) {
+  return s.CW ? s.T * share_weight_sum(w) / s.CW : w * s.T / s.W;
+}
+// The wave whose range contains unit idx: the last w with range_begin(w) <= idx.
 __device__ __forceinline__ int64_t wave_of(const Split& s, int64_t idx) {
-  return ((idx + 1) * s.W - 1) / s.T;
+  if (!s.CW) return ((idx + 1) * s.W - 1) / s.T;
+  // range_begin(w) <= idx  <=>  T * C(w) < (idx + 1) * C(W)
+  int64_t lo = 0, hi = s.W - 1;
+  const int64_t lim = (idx + 1) * s.CW;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (s.T * share_weight_sum(mid) < lim) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 __device__ __forceinline__ int ranges_of(int L, int PT) { return L > 0 ? (L + PT - 1) / PT : 0; }
+// Units of one (b, g) in the split: its ranges plus the switch-cost units
+// (which count only where a range is one tile, PT = tile size TS).
+__device__ __forceinline__ int units_of(int L, int PT, int A) { return L > 0 ? (L + PT - 1) / PT + A : 0; }
 
 // Store 4 consecutive outputs.
 template <bool OUT_BF16>

@@ -175,6 +175,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   // seq_lens of the first NC*64 sequences are read once, in one round trip, and
   // kept in registers (prefix counts of ranges); longer batches re-read the rest.
   constexpr int NC = 4;
+  const int A = PT == TS ? SWITCH_UNITS : 0;     // switch-cost units per (b, g)
   int Lc[NC], inclc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     inclc[c] = np_sum;
     if (c * 64 < B) {                     // uniform: skip chunks past the batch
       const int bb = c * 64 + lane;
-      const int np = ranges_of(Lc[c], PT);
+      const int np = units_of(Lc[c], PT, A);
       const int incl = wave_incl_scan(np, lane);
       inclc[c] = np_sum + incl;
       np_sum = uniform(np_sum + __builtin_amdgcn_readlane(incl, 63));
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   }
   for (int b0 = NC * 64; b0 < B; b0 += 64) {
     const int bb = b0 + lane;
-    const int np = ranges_of(bb < B ? seq_lens[bb] : 0, PT);
+    const int np = units_of(bb < B ? seq_lens[bb] : 0, PT, A);
     np_sum = uniform(np_sum + wave_sum(np));
     n_empty += __builtin_popcountll(__ballot(bb < B && np == 0));
   }
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (b < 0) {
-      const int np = ranges_of(Lc[c], PT);
+      const int np = units_of(Lc[c], PT, A);
       const uint64_t hit = __ballot((int64_t)inclc[c] * Hkv > u0);
       if (hit) {
         const int f = uniform(__builtin_ctzll(hit));
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int b0 = NC * 64;; b0 += 64) {
       const int bb = b0 + lane;
       const int L = bb < B ? seq_lens[bb] : 0;
-      const int np = ranges_of(L, PT);
+      const int np = units_of(L, PT, A);
       const int incl = run + wave_incl_scan(np, lane);
       const uint64_t hit = __ballot((int64_t)incl * Hkv > u0);
       if (hit) {
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   b = uniform(b);
   base = uniform64(base);
   Lb = uniform(Lb);
-  int npb = ranges_of(Lb, PT);
+  int cpb = units_of(Lb, PT, A);     // units of each (b, g) of sequence b
 
   const float NEG_INF = -__builtin_inff();
   const bool hv = r16 < G;
@@ -281,16 +282,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   bool have_next = false;
   int page_next = 0;
 
+  bool first = true;                 // no segment of this wave finished yet
   for (int64_t u = u0; u < u1;) {
     const int64_t off = u - base;
-    const int g = uniform((int)(off / npb));
-    const int rg = (int)(off - (int64_t)g * npb);
-    const int64_t S = base + (int64_t)g * npb, Eu = S + npb;
+    const int g = uniform((int)(off / cpb));
+    // ranges of (b, g) are units [S, Eu); the A units before S only carry cost
+    const int64_t S = base + (int64_t)g * cpb + A, Eu = base + (int64_t)(g + 1) * cpb;
+    if (u < S) {
+      u = S;
+      if (u >= u1) break;
+    }
+    const int rg = (int)(u - S);
     const int64_t ue = Eu < u1 ? Eu : u1;
     const int tok0 = uniform(rg * PT);
     const int tok1 = uniform(min(Lb, (int)(ue - S) * PT));
     const bool complete = (u == S) && (ue == Eu);
-    const bool first = (u == u0);
     const int h = g * G + r16;
 
     // ---- query operand: B matrix of QK^T (K dim = head dims, N = heads) --------
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // tokens.  Its sequence and first page id are found now, so the switch
     // waits only for its K / V loads.
     int nb = b;
-    have_next = ue < u1;
+    have_next = ue == Eu && Eu + A < u1;    // the next (b, g) starts inside this wave's share
     if (have_next) {
       if (g + 1 == Hkv) {
         do ++nb;
@@ -705,12 +711,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
 
     // ---- next segment ------------------------------------------------------------
+    first = false;
     u = ue;
-    if (u < u1 && u == base + (int64_t)npb * Hkv) {
+    if (u < u1 && u == base + (int64_t)cpb * Hkv) {
       base = u;
       b = nb;
       Lb = len_of(b);
-      npb = ranges_of(Lb, PT);
+      cpb = units_of(Lb, PT, A);
     }
   }
 }
