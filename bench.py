@@ -580,16 +580,15 @@ def bench_decode(args, name, nested=False):
     quant = quantises_on_write(wl)
 
     def step(i):
-        """One decode iteration of one layer: append + attention, in one decode_step
-        call; an fp8 cache fed bf16 rows quantises them on write first
-        (kv_append_fp8), then decodes."""
+        """One decode iteration of one layer: append + attention in one call
+        (decode_step; a quantised cache fed bf16 rows: decode_step_quant, which
+        quantises them on write inside the same two kernels)."""
         s = dsteps[i % len(dsteps)]
         kp, vp, ks, vs = kps[i % layers], vps[i % layers], kss[i % layers], vss[i % layers]
         if quant:
-            append_quant_fn(pkv, wl.kv_dtype)(s["kn"], s["vn"], wl.new_dtype, bt, s["sl"], kp, vp, ks, vs,
-                                              wl.Hkv, wl.D, wl.P)
-            decode_fn(pkv, wl.kv_dtype)(q, wl.q_dtype, kp, vp, ks, vs, bt, s["sl"], wl.Hq, wl.Hkv, wl.D, wl.P,
-                                        wl.scale, out, wl.out_dtype, ws, wl.partition_tokens)
+            pkv.decode_step_quant(q, wl.q_dtype, s["kn"], s["vn"], wl.new_dtype, kp, vp, wl.kv_dtype, ks, vs, bt,
+                                  s["sl"], wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws,
+                                  partition_tokens=wl.partition_tokens)
         else:
             pkv.decode_step(q, wl.q_dtype, s["kn"], s["vn"], kp, vp, wl.kv_dtype, bt, s["sl"], wl.Hq,
                             wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype, ws, k_scales=ks, v_scales=vs,
@@ -645,7 +644,8 @@ def bench_decode(args, name, nested=False):
                    "head_dim": wl.D, "page_size": wl.P,
                    "mean_seq_len": float(np.mean(steps[0]["seq_lens"])),
                    "partition_tokens": wl.partition_tokens, "layers_rotated": layers,
-                   "step": ("quantising append (dynamic page scales) then one-byte paged decode"
+                   "step": ("decode_step_quant: quantising append (dynamic page scales) fused into the "
+                            "paged decode (split kernel + LSE merge kernel)"
                             if quant else
                             "decode_step: kv_append fused into paged decode (split kernel + LSE merge kernel)")},
         "seqs_per_s_per_layer": round(wl.B / (ms_step * 1e-3), 1),
@@ -653,8 +653,8 @@ def bench_decode(args, name, nested=False):
         "kv_bytes_per_step": int(kv_bytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("quantising append + one-byte paged decode (append_quant_kernel + "
-                                "decode_split_kernel + decode_merge_kernel)" if quant else
+                     "kernel": ("decode_step_quant launch (decode_split_kernel + decode_merge_quant_kernel)"
+                                if quant else
                                 "decode_step launch (decode_split_kernel + decode_merge_kernel)"),
                      "call_ms_mean": round(dec_mean, 5), "alg_bytes_per_call": int(step_bytes)},
     }

@@ -304,6 +304,37 @@ int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const v
                     void* out, pkv_dtype out_dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* decode_step_quant - one decode iteration of a quantised cache (fp8-e4m3,
+ * int8 or int4) whose new rows arrive in bf16 or fp32: the quantising append
+ * of pkv_kv_append_fp8 / _int8 / _int4 followed by the attention of
+ * pkv_paged_attn_decode_fp8 / _int8 / _int4, with no launch of its own for
+ * the append.
+ *
+ * The first page's "compile-time graph optimization" section computes a
+ * dynamic scaling factor where data enters FP8, and its "runtime execution
+ * model" section has each iteration's attention update and read the cache
+ * pages.  Here the split kernel's waves that read the page holding slot
+ * L_b - 1 of (b, g) derive that page's new scales from the new rows and read
+ * the page as the append leaves it (earlier slots re-encoded in registers
+ * when a scale rises, the new token encoded); the merge kernel, after them
+ * on the stream, stores the codes, the re-encoded slots and the new scales.
+ * Results: pools and scales byte-identical to the quantising append of the
+ * same rows and seq_lens; out equal to the decode of that cache up to the
+ * rounding order.
+ * k_new, v_new: [B][Hkv][D] of new_dtype (PKV_BF16 or PKV_F32).
+ * k_scales, v_scales: read and written.  Other arguments, sizes, workspace and
+ * errors as pkv_decode_step; PKV_E_DTYPE unless kv_dtype is FP8_E4M3, INT8 or
+ * INT4 and new_dtype is BF16 or F32. */
+int pkv_decode_step_quant(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_new,
+                          pkv_dtype new_dtype, void* k_pool, void* v_pool, pkv_dtype kv_dtype,
+                          float* k_scales, float* v_scales,
+                          const int32_t* block_tables, int max_pages_per_seq,
+                          const int32_t* seq_lens, int batch, int num_pages,
+                          int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                          float scale, int partition_tokens,
+                          void* out, pkv_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* decode_step_noalloc - pkv_decode_step without a workspace argument, for
  * callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation.  It runs the same
@@ -314,7 +345,7 @@ int pkv_decode_step(const void* q, pkv_dtype q_dtype, const void* k_new, const v
  * is looked up once per device, on the first call made with that device
  * current.  Shapes whose pkv_decode_workspace_bytes exceed 40 MiB are rejected
  * with PKV_E_WORKSPACE (on a 256-CU device every G <= 16 and D <= 128 fits
- * for up to ~490 000 (sequence, kv head) pairs).  Nothing in the array needs
+ * for up to ~245 000 (sequence, kv head) pairs).  Nothing in the array needs
  * to start at zero; each call overwrites what it reads.  Every call on one
  * device shares that device's array: calls that may overlap on one device
  * (different streams, or different host threads without ordering) race and

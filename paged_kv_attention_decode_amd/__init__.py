@@ -159,6 +159,20 @@ def decode_step(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, block_tables
         _stream(stream)))
 
 
+def decode_step_quant(q, q_dtype, k_new, v_new, new_dtype, k_pool, v_pool, kv_dtype, k_scales, v_scales,
+                      block_tables, seq_lens, num_q_heads, num_kv_heads, head_dim, page_size, scale, out,
+                      out_dtype, workspace, partition_tokens=0, stream=None):
+    """Quantising append of bf16 / fp32 rows into an fp8 / int8 / int4 cache
+    (dynamic page scales) fused into the decode of that cache."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("decode_step_quant", lib().pkv_decode_step_quant(
+        _ptr(q), _code(q_dtype), _ptr(k_new), _ptr(v_new), _code(new_dtype), _ptr(k_pool), _ptr(v_pool),
+        _code(kv_dtype), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), MP, _ptr(seq_lens), B, NP,
+        num_q_heads, num_kv_heads, head_dim, page_size, float(scale), int(partition_tokens), _ptr(out),
+        _code(out_dtype), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def decode_step_noalloc(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, block_tables, seq_lens,
                         num_q_heads, num_kv_heads, head_dim, page_size, scale, out, out_dtype,
                         k_scales=None, v_scales=None, partition_tokens=0, stream=None):

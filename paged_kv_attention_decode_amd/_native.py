@@ -24,6 +24,8 @@ SIGNATURES = {
                                         _i, _i, _f, _i, _vp, _i, _vp, _sz, _vp]),
     "pkv_decode_step": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i,
                              _i, _f, _i, _vp, _i, _vp, _sz, _vp]),
+    "pkv_decode_step_quant": (_i, [_vp, _i, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i,
+                                   _i, _i, _f, _i, _vp, _i, _vp, _sz, _vp]),
     "pkv_decode_step_noalloc": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i,
                                      _i, _i, _f, _i, _vp, _i, _vp]),
     "pkv_kv_append_chunk": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp]),

@@ -105,7 +105,8 @@ int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
                int max_pages, const int32_t* seq_lens, int batch, int num_pages, int num_q_heads,
                int num_kv_heads, int head_dim, int page_size, float scale, int partition_tokens,
                void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream,
-               const void* k_new = nullptr, const void* v_new = nullptr, bool static_ws = false) {
+               const void* k_new = nullptr, const void* v_new = nullptr, bool static_ws = false,
+               int new_quant_dtype = -1) {
   int rc = check_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_pages, seq_lens, batch,
                         num_pages, num_q_heads, num_kv_heads, head_dim, page_size, partition_tokens,
                         out, out_dtype, workspace, workspace_bytes, static_ws);
@@ -130,6 +131,7 @@ int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
   a.descs = reinterpret_cast<int4*>(static_cast<char*>(workspace) +
                                       pkv::partials_bytes(pkv::device_cu_count(), num_q_heads / num_kv_heads,
                                                           head_dim));
+  a.qdescs = a.descs + (size_t)batch * num_kv_heads;
   a.kvt = kv_dtype;
   a.out_bf16 = out_dtype == PKV_BF16;
   a.batch = batch;
@@ -142,6 +144,8 @@ int run_decode(const void* q, int q_dtype, const void* k_pool, const void* v_poo
   // Default range granularity: one decode step (the V block), the finest split.
   a.partition_tokens = partition_tokens ? partition_tokens : pkv::v_block_tokens(kv_dtype);
   a.scale = scale;
+  a.new_quant = new_quant_dtype >= 0;
+  a.new_bf16 = new_quant_dtype == PKV_BF16;
   hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return PKV_OK;
@@ -216,9 +220,10 @@ size_t pkv_decode_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, 
     return 0;
   const int cus = pkv::device_cu_count();
   if (cus <= 0) return 0;
-  // two partial slots (first and last range) per resident wave, then the descriptors
+  // two partial slots (first and last range) per resident wave, then the
+  // merge descriptors and the quantising step's records (16 bytes each per (b, g))
   return pkv::partials_bytes(cus, num_q_heads / num_kv_heads, head_dim) +
-         (size_t)batch * (size_t)num_kv_heads * 16;
+         (size_t)batch * (size_t)num_kv_heads * 32;
 }
 
 int pkv_kv_append(const void* k_new, const void* v_new, pkv_dtype kv_dtype, const int32_t* block_tables,
@@ -430,6 +435,29 @@ int pkv_decode_step_noalloc(const void* q, pkv_dtype q_dtype, const void* k_new,
   return run_step(q, q_dtype, k_new, v_new, k_pool, v_pool, kv_dtype, k_scales, v_scales, block_tables,
                   max_pages_per_seq, seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size,
                   scale, partition_tokens, out, out_dtype, nullptr, 0, stream, true);
+}
+
+int pkv_decode_step_quant(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_new,
+                          pkv_dtype new_dtype, void* k_pool, void* v_pool, pkv_dtype kv_dtype, float* k_scales,
+                          float* v_scales, const int32_t* block_tables, int max_pages_per_seq,
+                          const int32_t* seq_lens, int batch, int num_pages, int num_q_heads, int num_kv_heads,
+                          int head_dim, int page_size, float scale, int partition_tokens, void* out,
+                          pkv_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!scaled_dtype(kv_dtype))
+    return fail(PKV_E_DTYPE, "quantising step: kv dtype %d is not fp8, int8 or int4", kv_dtype);
+  if (new_dtype != PKV_BF16 && new_dtype != PKV_F32)
+    return fail(PKV_E_DTYPE, "new-row dtype %d unsupported (bf16 or f32)", new_dtype);
+  if (batch > 0 && (!k_new || !v_new)) return fail(PKV_E_NULL, "k_new / v_new are NULL");
+  if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 / int8 / int4 scales are NULL");
+  if (batch > 0) {
+    const int rc = check_align({k_new, v_new});
+    if (rc) return rc;
+  }
+  return run_decode(q, q_dtype, k_pool, v_pool, kv_dtype, k_scales, v_scales, block_tables, max_pages_per_seq,
+                    seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale,
+                    partition_tokens, out, out_dtype, workspace, workspace_bytes, stream, k_new, v_new, false,
+                    (int)new_dtype);
 }
 
 int pkv_debug_gather(const void* k_pool, const void* v_pool, pkv_dtype kv_dtype, const int32_t* block_tables,

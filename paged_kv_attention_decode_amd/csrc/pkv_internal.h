@@ -23,10 +23,11 @@ constexpr int kMaxWavesPerCU = 8;
 // allocation-free step entry point (one copy per device, held until the
 // process ends).  40 MiB covers the partial slots of every accepted group
 // size and head dimension on a 256-CU device (34 MB at G = 16, D = 128) plus
-// the 16-byte descriptors of up to ~490 000 (sequence, kv head) pairs.
+// the 32 bytes of per-pair records of up to ~245 000 (sequence, kv head) pairs.
 constexpr size_t kStaticScratchBytes = (size_t)40 << 20;
 
-// Workspace layout: partial slots (2 per wave) then B * Hkv 16-byte descriptors.
+// Workspace layout: partial slots (2 per wave), then B * Hkv 16-byte merge
+// descriptors, then B * Hkv 16-byte records of the quantising step.
 inline size_t partials_bytes(int cus, int G, int D) {
   size_t b = 2 * (size_t)cus * kMaxWavesPerCU * (size_t)G * ((size_t)D + 2) * sizeof(float);
   return (b + 255) & ~(size_t)255;
@@ -79,11 +80,14 @@ struct DecodeArgs {
   void* out;
   float* partials;         // workspace: partial-result slots
   int4* descs;             // workspace: per-(b, g) merge descriptors
+  int4* qdescs;            // workspace: per-(b, g) old page scales (quantising step)
   int kvt;                 // KvType; q is f32 for KV_F32, bf16 otherwise
   bool out_bf16;
   int batch, max_pages, num_pages, num_q_heads, num_kv_heads, head_dim, page_size;
   int partition_tokens;    // > 0, multiple of v_block_tokens(kvt)
   float scale;
+  bool new_quant = false;  // quantising step: k_new / v_new are rows to quantise on write
+  bool new_bf16 = false;   // ... bf16 rows (else fp32)
 };
 
 // Chunk append: rows cu_new[b] .. cu_new[b+1] of k_new / v_new ([total][Hkv][D])

@@ -130,19 +130,358 @@ __device__ void merge_chunk(const float* __restrict__ partials, int64_t slot0, i
 }
 
 // ---------------------------------------------------------------------------
+// One-byte appends (fp8 e4m3 or int8) with dynamic page scales (quantise on
+// write).  QMAX = 448 (fp8) or 127 (int8); NOCLIP = 464 or 127.5, the largest
+// |x| / scale whose encoding is the largest code without clipping.
+//
+// One wave per (sequence, kv head); K and V each with their own scale:
+// a = max |x| of the new row (widened to fp32);
+//   slot j == 0 (first token of the page): s = a / QMAX (1 if a == 0);
+//   else, s0 = the page's scale: s = s0 if a / s0 <= NOCLIP,
+//   otherwise s = a / QMAX and every earlier slot is re-encoded,
+//   enc((dec(byte) * s0) / s);
+// the new row is stored as enc(x / s) and the page scale becomes s.
+// Every division and product is one correctly rounded fp32 operation.
+// ---------------------------------------------------------------------------
+
+// fp32 -> e4m3fn: nearest value, ties to the even significand, saturating at
+// +-448 (NaN -> 0x7F).  With e = max(exponent(|x|), -6), the e4m3 step at |x|
+// is 2^(e-3) (the subnormal step 2^-9 below 2^-6), k = rint(|x| / 2^(e-3)) is
+// exact in fp32, and the code is 8 * (e + 6) + k: a carry of k to 16 lands on
+// the next binade's first code, and below 2^-6 the code is k itself.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t sign = (ubits(x) >> 24) & 0x80u;
+  if (x != x) return 0x7Fu;
+  const float a = fminf(fabsf(x), 448.f);
+  const int e = max((int)((ubits(a) >> 23) & 0xFFu) - 127, -6);
+  const int k = (int)rintf(ldexpf(a, 3 - e));
+  return sign | (uint32_t)(8 * (e + 6) + k);
+}
+
+// fp32 -> symmetric int8 byte: nearest integer, ties to even, clamped to +-127.
+__device__ __forceinline__ uint32_t int8_encode(float x) {
+  const float r = fminf(fmaxf(rintf(x), -127.f), 127.f);
+  return (uint32_t)(int)r & 0xFFu;
+}
+
+template <int KVT> struct ByteFmt;
+template <> struct ByteFmt<KV_FP8> {
+  static constexpr float QMAX = 448.f, NOCLIP = 464.f;
+  __device__ static uint32_t enc(float y) { return e4m3_encode(y); }
+  __device__ static void dec4(uint32_t w, float (&v)[4]) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+  }
+};
+template <> struct ByteFmt<KV_INT8> {
+  static constexpr float QMAX = 127.f, NOCLIP = 127.5f;
+  __device__ static uint32_t enc(float y) { return int8_encode(y); }
+  __device__ static void dec4(uint32_t w, float (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(uint8_t)(w >> (8 * i));
+  }
+};
+// int4: codes are two's complement nibbles; symmetric, clamped to +-7.
+template <> struct ByteFmt<KV_INT4> {
+  static constexpr float QMAX = 7.f, NOCLIP = 7.5f;
+  __device__ static uint32_t enc(float y) {
+    const float r = fminf(fmaxf(rintf(y), -7.f), 7.f);
+    return (uint32_t)(int)r & 0xFu;
+  }
+  __device__ static float dec(uint32_t c) { return (float)(int)((c & 0xFu) ^ 8u) - 8.f; }
+};
+
+// One element re-encoded under a new scale: enc((dec(code) * s0) / s), the
+// product and the quotient each rounded once.
+template <int KVT>
+__device__ __forceinline__ uint32_t requant1(float v, float s0, float s) {
+  const float real = v * s0;
+  return ByteFmt<KVT>::enc(real / s);
+}
+// Four bytes of a word re-encoded (int4: both nibbles of each byte).
+template <int KVT>
+__device__ __forceinline__ uint32_t requant4(uint32_t w, float s0, float s) {
+  uint32_t r = 0;
+  if constexpr (KVT == KV_INT4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      r |= requant1<KVT>(ByteFmt<KVT>::dec(w >> (4 * i)), s0, s) << (4 * i);
+  } else {
+    float v[4];
+    ByteFmt<KVT>::dec4(w, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r |= requant1<KVT>(v[i], s0, s) << (8 * i);
+  }
+  return r;
+}
+
+// Scale decision for one row: returns the new scale; sets requant when the
+// page's earlier slots must be re-encoded.  A row fits the current scale while
+// its largest element encodes to the largest code without clipping:
+// |x| / s0 <= NOCLIP (fp8: 464, the midpoint above 448, rounds down to 448;
+// int8: 127.5 rounds to 128 and clamps to 127, still within half a step).
+template <int KVT>
+__device__ __forceinline__ float page_scale(float a, int j, float s0, bool& requant) {
+  requant = false;
+  if (j == 0) return a > 0.f ? a / ByteFmt<KVT>::QMAX : 1.f;
+  if (a / s0 <= ByteFmt<KVT>::NOCLIP) return s0;
+  requant = true;
+  return a / ByteFmt<KVT>::QMAX;
+}
+
+// A re-encode maps each old byte through enc((dec(byte) * s0) / s), a function
+// of the byte alone: the wave tabulates it once (4 codes per lane) in LDS and
+// then re-encodes by lookup.
+__device__ __forceinline__ uint32_t lut4(const uint8_t* lut, uint32_t w) {
+  return (uint32_t)lut[w & 0xFFu] | ((uint32_t)lut[(w >> 8) & 0xFFu] << 8) |
+         ((uint32_t)lut[(w >> 16) & 0xFFu] << 16) | ((uint32_t)lut[w >> 24] << 24);
+}
+
+// Re-encode slots [0, j) of a K chunk.  Token t's dims E c .. E c + E - 1 are
+// the 16-byte group at chunk + 16 (c P + t); lane l takes tokens l, l + 64, ...
+// (TPL of them per round, all GPT groups of each), so no group index is
+// divided, and every load of a round is issued before any conversion.
+template <int KVT, int D>
+__device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uint8_t* lut, int lane) {
+  constexpr int GPT = D * Kv<KVT>::BITS / 128;       // 16-byte groups per token
+  constexpr int TPL = 16 / GPT;                      // tokens per lane per round
+  for (int t0 = 0; t0 < j; t0 += 64 * TPL) {
+    u32x4_t w[TPL][GPT];
+#pragma unroll
+    for (int a = 0; a < TPL; ++a) {
+      const int t = min(t0 + 64 * a + lane, j - 1);    // clamped: in-bounds, stored only if owned
+#pragma unroll
+      for (int c = 0; c < GPT; ++c) w[a][c] = *reinterpret_cast<const u32x4_t*>(pool + 16 * (c * P + t));
+    }
+#pragma unroll
+    for (int a = 0; a < TPL; ++a) {
+      const int t = t0 + 64 * a + lane;
+      if (t < j) {
+#pragma unroll
+        for (int c = 0; c < GPT; ++c) {
+          u32x4_t r;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[a][c][q]);
+          store_nt(reinterpret_cast<u32x4_t*>(pool + 16 * (c * P + t)), r);
+        }
+      }
+    }
+  }
+}
+
+// Re-encode a V chunk for a scale change at slot j: a 16-byte group holds E
+// tokens of one dim from one TB = 4E token block; blocks 0 .. j/TB are
+// rewritten group by group.  Blocks before j's hold earlier slots only and are
+// re-encoded whole; in j's block, tokens < j are re-encoded, token j takes its
+// new code (nbj, from LDS) and later slots keep theirs.  A round's 64 * GPL
+// groups cover whole blocks (4 D groups each), so the block of a lane's i-th
+// group, and with it the choice between the two, is the same on every lane.
+template <int KVT, int D>
+__device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* lut, const uint8_t* nbj,
+                                          int lane) {
+  constexpr int BITS = Kv<KVT>::BITS, E = 128 / BITS;
+  constexpr int GPL = 16, TB = 4 * E;
+  constexpr int GPB = 4 * D;    // 16-byte groups per V block (blocks are contiguous)
+  static_assert((64 * GPL) % GPB == 0 && GPB % 64 == 0, "a round covers whole blocks");
+  const int jb = j / TB;
+  const int ngrp = (jb + 1) * GPB;
+  for (int base = 0; base < ngrp; base += 64 * GPL) {
+    u32x4_t w[GPL];
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int gi = min(base + lane + 64 * i, ngrp - 1);
+      w[i] = *reinterpret_cast<const u32x4_t*>(pool + (size_t)gi * 16);   // blocks are contiguous
+    }
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int blk = uniform((base + 64 * i) / GPB);
+      if (blk > jb) continue;                          // past j's block (uniform)
+      const int gi = base + lane + 64 * i;
+      u32x4_t r;
+      if (blk < jb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[i][q]);
+      } else {
+        const int rem = gi - blk * GPB;
+        const int c = rem / D, d = rem - c * D;
+        const uint32_t fresh = nbj[d];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t re = lut4(lut, w[i][q]);
+          uint32_t outw = 0;
+          constexpr int PW = 32 / BITS;                  // elements per word
+#pragma unroll
+          for (int x = 0; x < PW; ++x) {
+            // element e of the group holds token 16 * (e / 4) + 4c + e % 4 of the block
+            const int e = PW * q + x;
+            const int tok = blk * TB + 16 * (e >> 2) + 4 * c + (e & 3);
+            constexpr uint32_t M = (1u << BITS) - 1u;
+            const uint32_t code = tok < j ? (re >> (BITS * x)) & M
+                                : tok == j ? fresh : (w[i][q] >> (BITS * x)) & M;
+            outw |= code << (BITS * x);
+          }
+          r[q] = outw;
+        }
+      }
+      store_nt(reinterpret_cast<u32x4_t*>(pool + (size_t)gi * 16), r);
+    }
+  }
+}
+
+
+// New rows of (b, g) for the quantising append: lane l holds dims
+// l * D / 64 .. of the K and the V row, widened to fp32 (bf16 or fp32 input).
+template <int D>
+__device__ __forceinline__ void load_new_rows(const void* k_new, const void* v_new, bool in_bf16, size_t row,
+                                              float (&xk)[D / 64], float (&xv)[D / 64]) {
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    xk[i] = in_bf16 ? fbits((uint32_t)static_cast<const uint16_t*>(k_new)[row + i] << 16)
+                    : static_cast<const float*>(k_new)[row + i];
+    xv[i] = in_bf16 ? fbits((uint32_t)static_cast<const uint16_t*>(v_new)[row + i] << 16)
+                    : static_cast<const float*>(v_new)[row + i];
+  }
+}
+
+// Largest |x| of a row held D / 64 elements per lane (wave-uniform result):
+// rotations within each 16-lane row (DPP), then across the four rows.
+template <int NPL>
+__device__ __forceinline__ float row_amax(const float (&x)[NPL]) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) a = fmaxf(a, fabsf(x[i]));
+  a = fmaxf(a, fbits((uint32_t)__builtin_amdgcn_update_dpp(0, (int)ubits(a), 0x128, 0xF, 0xF, false)));  // row_ror:8
+  a = fmaxf(a, fbits((uint32_t)__builtin_amdgcn_update_dpp(0, (int)ubits(a), 0x124, 0xF, 0xF, false)));  // row_ror:4
+  a = fmaxf(a, fbits((uint32_t)__builtin_amdgcn_update_dpp(0, (int)ubits(a), 0x122, 0xF, 0xF, false)));  // row_ror:2
+  a = fmaxf(a, fbits((uint32_t)__builtin_amdgcn_update_dpp(0, (int)ubits(a), 0x121, 0xF, 0xF, false)));  // row_ror:1
+  return fbits(uniform((int)ubits(colmax4(a))));
+}
+
+// The quantising append of one (b, g) pair of rows into slot j of its page,
+// run by one wave (lane l holds dims d0 = l * D / 64 .. of each row): the new
+// page scales, the new codes, the re-encode of the page's earlier slots when a
+// scale rises, then the new scales.  kp / vp point at the page's K / V chunk,
+// si indexes its scales, sk0 / sv0 are their values before this append (read
+// by the caller; ignored for slot 0); lut (2 x 64 words) and nb (D bytes) are
+// this wave's LDS scratch.  Used by the standalone append and by the
+// quantising step.
+template <int KVT, int D>
+__device__ __forceinline__ void quant_store_row(const float (&xk)[D / 64], const float (&xv)[D / 64], int j,
+                                                uint8_t* kp, uint8_t* vp, int P, float* kscales, float* vscales,
+                                                size_t si, float sk0, float sv0, uint32_t (*lut)[64], uint8_t* nb,
+                                                int lane) {
+  constexpr int NPL = D / 64;
+  const int d0 = lane * NPL;
+  if (j == 0) sk0 = sv0 = 1.f;          // the page's first token: the old scales are not used
+  const float ak = row_amax(xk), av = row_amax(xv);
+  sk0 = fbits(uniform((int)ubits(sk0)));
+  sv0 = fbits(uniform((int)ubits(sv0)));
+  bool rk, rv;
+  const float sk = page_scale<KVT>(ak, j, sk0, rk);
+  const float sv = page_scale<KVT>(av, j, sv0, rv);
+  uint32_t nbk[NPL], nbv[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    nbk[i] = ByteFmt<KVT>::enc(xk[i] / sk);
+    nbv[i] = ByteFmt<KVT>::enc(xv[i] / sv);
+  }
+  const uint8_t* lutk = reinterpret_cast<const uint8_t*>(lut[0]);
+  const uint8_t* lutv = reinterpret_cast<const uint8_t*>(lut[1]);
+  if (rk || rv) {
+    const uint32_t codes = (uint32_t)(4 * lane) * 0x01010101u + 0x03020100u;   // 4 codes per lane
+    if (rk) lut[0][lane] = requant4<KVT>(codes, sk0, sk);
+    if (rv) lut[1][lane] = requant4<KVT>(codes, sv0, sv);
+    __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
+  }
+  constexpr int E = 128 / Kv<KVT>::BITS;
+  if (rk) requant_k<KVT, D>(kp, j, P, lutk, lane);
+  // the new K token's dims d0.. are consecutive elements of one group
+  // (disjoint from the re-encoded slots): two bytes, or one int4 byte
+  uint8_t* kt = kp + elem_byte<KVT>(k_elem<E>(j, d0, P));
+  if constexpr (KVT == KV_INT4)
+    store_nt(kt, (uint8_t)(nbk[0] | (nbk[NPL - 1] << 4)));
+  else if constexpr (NPL == 2)
+    store_nt(reinterpret_cast<uint16_t*>(kt), (uint16_t)(nbk[0] | (nbk[NPL - 1] << 8)));
+  else
+    store_nt(kt, (uint8_t)nbk[0]);
+  if (rv) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) nb[d0 + i] = (uint8_t)nbv[i];
+    __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
+    requant_v<KVT, D>(vp, j, lutv, nb, lane);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) put_code_nt<KVT>(vp, v_elem<E>(j, d0 + i, D), nbv[i]);   // own bytes
+  }
+  if (lane == 0) {
+    kscales[si] = sk;
+    vscales[si] = sv;
+  }
+}
+
+// One row (K if !IS_V, else V) of the quantising append into slot j of its
+// page: the row's page scale, its codes, the re-encode of slots [0, j) when
+// the scale rises, the new scale.  The K and V rows are independent (own
+// scales and tables), so the quantising step's merge kernel gives each its
+// own wave.  pc points at the page's K or V chunk, si indexes its scale, s0 is
+// the scale before this append (ignored for slot 0); lut (64 words) and nb (D
+// bytes) are the wave's LDS scratch.
+template <int KVT, int D, bool IS_V>
+__device__ __forceinline__ void quant_store_half(const float (&x)[D / 64], int j, uint8_t* pc, int P, float* scales,
+                                                 size_t si, float s0, uint32_t* lut, uint8_t* nb, int lane) {
+  constexpr int NPL = D / 64, E = 128 / Kv<KVT>::BITS;
+  const int d0 = lane * NPL;
+  if (j == 0) s0 = 1.f;
+  const float a = row_amax(x);
+  s0 = fbits(uniform((int)ubits(s0)));
+  bool r;
+  const float sc = page_scale<KVT>(a, j, s0, r);
+  uint32_t nbc[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) nbc[i] = ByteFmt<KVT>::enc(x[i] / sc);
+  const uint8_t* lutb = reinterpret_cast<const uint8_t*>(lut);
+  if (r) {
+    lut[lane] = requant4<KVT>((uint32_t)(4 * lane) * 0x01010101u + 0x03020100u, s0, sc);   // 4 codes per lane
+    __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
+  }
+  if constexpr (!IS_V) {
+    if (r) requant_k<KVT, D>(pc, j, P, lutb, lane);
+    uint8_t* kt = pc + elem_byte<KVT>(k_elem<E>(j, d0, P));
+    if constexpr (KVT == KV_INT4)
+      store_nt(kt, (uint8_t)(nbc[0] | (nbc[NPL - 1] << 4)));
+    else if constexpr (NPL == 2)
+      store_nt(reinterpret_cast<uint16_t*>(kt), (uint16_t)(nbc[0] | (nbc[NPL - 1] << 8)));
+    else
+      store_nt(kt, (uint8_t)nbc[0]);
+  } else {
+    if (r) {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) nb[d0 + i] = (uint8_t)nbc[i];
+      __builtin_amdgcn_wave_barrier();
+      requant_v<KVT, D>(pc, j, lutb, nb, lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) put_code_nt<KVT>(pc, v_elem<E>(j, d0 + i, D), nbc[i]);   // own bytes
+    }
+  }
+  if (lane == 0) scales[si] = sc;
+}
+
+// ---------------------------------------------------------------------------
 // Decode, part 1: each wave streams its unit range.  A (b, g) covered by one
 // wave is finished here; otherwise each covering wave leaves a partial and the
 // wave holding the first unit of (b, g) leaves a descriptor (first contributing
 // wave, number of contributors, slot of the first) for the merge kernel.
 // ---------------------------------------------------------------------------
-template <int KVT, int D, bool OUT_BF16>
+template <int KVT, int D, bool OUT_BF16, bool QNEW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
     const void* __restrict__ q_, const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
     const void* __restrict__ k_new, const void* __restrict__ v_new,
     const float* __restrict__ kscales, const float* __restrict__ vscales,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens, void* __restrict__ out_,
-    float* __restrict__ partials, int4* __restrict__ descs, int B, int MP, int NP, int Hq, int Hkv,
-    int G, int P, int PT, int Wmax, float scale_log2) {
+    float* __restrict__ partials, int4* __restrict__ descs, int4* __restrict__ qdescs, int B, int MP, int NP,
+    int Hq, int Hkv, int G, int P, int PT, int Wmax, float scale_log2, int new_bf16) {
   constexpr int BITS = Kv<KVT>::BITS;
   constexpr int E = 128 / BITS;     // elements per 16-byte group
   constexpr int TS = 4 * E;         // tokens per step (= V block)
@@ -170,6 +509,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   // per-wave LDS slots: the step entry's new K and V rows, the query operand
   __shared__ __attribute__((aligned(16))) uint8_t s_new[4][2 * D * BITS / 8];
   __shared__ u32x4_t s_q[4][NQ][64];
+  // quantising step: per-wave re-encode tables (K, V) of the last page, and
+  // the step's raw new K and V rows (bf16 or fp32)
+  __shared__ uint32_t s_lut[QNEW ? 4 : 1][2][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_row[QNEW ? 4 : 1][QNEW ? 2 * D * 4 : 16];
 
   // ---- this wave's unit range -------------------------------------------------
   // seq_lens of the first NC*64 sequences are read once, in one round trip, and
@@ -328,7 +671,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const bool has_new = k_new != nullptr && tok1 == Lb;
     constexpr int NEWCH = D * BITS / 128;           // 16-byte chunks per K (or V) row
     u32x4_t new_chunk = {0, 0, 0, 0};
-    if (has_new && lane < 2 * NEWCH) {
+    // Quantising step: k_new / v_new are bf16 or fp32 rows, quantised on write
+    // with the page scale rule of the quantising append.  A segment that reads
+    // any tile of (b, g)'s last page (the one holding slot Lb - 1) sees that
+    // page as the append leaves it: the new scales qsk / qsv, its earlier
+    // slots re-encoded when a scale rises (qrk / qrv, through LUTs built in
+    // LDS), token Lb - 1 encoded with the new scale.  The merge kernel makes
+    // the same decisions from the same values and stores them.
+    // The raw rows are loaded here, before the first tile's loads, in 16-byte
+    // pieces, and parked in LDS once those loads are out (as the step entry
+    // parks its pre-quantised row), so nothing waits on them in the tile loop.
+    constexpr int NPL = D / 64;
+    const int lp = (Lb - 1) / P;
+    const bool qfix = QNEW && k_new != nullptr && tok1 > lp * P;
+    const int rowb = D * (new_bf16 ? 2 : 4);        // bytes per raw row
+    const int nrch = rowb / 16;                      // 16-byte pieces per row
+    float qsk = 1.f, qsv = 1.f;
+    bool qrk = false, qrv = false;
+    u32x4_t qrow = {0, 0, 0, 0};
+    if constexpr (QNEW) {
+      if (qfix && lane < 2 * nrch) {
+        const size_t off = ((size_t)b * Hkv + g) * (size_t)rowb;
+        const uint8_t* src = lane < nrch ? static_cast<const uint8_t*>(k_new) + off + lane * 16
+                                         : static_cast<const uint8_t*>(v_new) + off + (lane - nrch) * 16;
+        qrow = ld16(src);
+      }
+    }
+    if (!QNEW && has_new && lane < 2 * NEWCH) {
       const size_t nrow = elem_byte<KVT>(((size_t)b * Hkv + g) * D);
       const uint8_t* src = lane < NEWCH ? static_cast<const uint8_t*>(k_new) + nrow
                                         : static_cast<const uint8_t*>(v_new) + nrow - NEWCH * 16;
@@ -426,15 +795,89 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     __builtin_amdgcn_wave_barrier();      // the previous segment's LDS reads are done
 #pragma unroll
     for (int i = 0; i < NQ; ++i) s_q[wv][i][lane] = qv_ld[i];
-    if (has_new && lane < 2 * NEWCH) *reinterpret_cast<u32x4_t*>(s_new[wv] + lane * 16) = new_chunk;
+    if (!QNEW && has_new && lane < 2 * NEWCH) *reinterpret_cast<u32x4_t*>(s_new[wv] + lane * 16) = new_chunk;
+    // Quantising step: the last page's old scales are loaded here, with the
+    // new rows; the decisions, LUTs and the new token's codes (qprep) wait for
+    // the first tile of that page, so these loads overlap the tiles before it.
+    float s0k = 1.f, s0v = 1.f;
+    int jl = 0, pgl = -1;
+    bool qready = false;
+    if constexpr (QNEW) {
+      if (qfix) {
+        if (lane < 2 * nrch) *reinterpret_cast<u32x4_t*>(s_row[wv] + lane * 16) = qrow;
+        pgl = page_of(lp);
+        jl = Lb - 1 - lp * P;
+        const size_t si = (size_t)((unsigned)pgl < (unsigned)NP ? pgl : 0) * Hkv + g;
+        if (jl > 0) {
+          s0k = kscales[si];
+          s0v = vscales[si];
+        }
+      }
+    }
+    auto qprep = [&]() {
+      if constexpr (QNEW) {
+        s0k = fbits(uniform((int)ubits(s0k)));
+        s0v = fbits(uniform((int)ubits(s0v)));
+        float qxk[NPL], qxv[NPL];
+        {
+          const int d0 = lane * NPL;
+#pragma unroll
+          for (int i = 0; i < NPL; ++i) {
+            if (new_bf16) {
+              const uint16_t* r = reinterpret_cast<const uint16_t*>(s_row[wv]);
+              qxk[i] = fbits((uint32_t)r[d0 + i] << 16);
+              qxv[i] = fbits((uint32_t)r[D + d0 + i] << 16);
+            } else {
+              const float* r = reinterpret_cast<const float*>(s_row[wv]);
+              qxk[i] = r[d0 + i];
+              qxv[i] = r[D + d0 + i];
+            }
+          }
+        }
+        qsk = page_scale<KVT>(row_amax(qxk), jl, s0k, qrk);
+        qsv = page_scale<KVT>(row_amax(qxv), jl, s0v, qrv);
+        // the merge kernel, which stores this append, takes the old scales from here
+        if (has_new && lane == 0) qdescs[(size_t)b * Hkv + g] = make_int4((int)ubits(s0k), (int)ubits(s0v), 0, 0);
+        if (qrk || qrv) {
+          const uint32_t codes = (uint32_t)(4 * lane) * 0x01010101u + 0x03020100u;   // 4 codes per lane
+          if (qrk) s_lut[wv][0][lane] = requant4<KVT>(codes, s0k, qsk);
+          if (qrv) s_lut[wv][1][lane] = requant4<KVT>(codes, s0v, qsv);
+        }
+        if (has_new) {        // token Lb - 1's codes, in the row layout the injection reads
+          constexpr int RB = D * BITS / 8;            // bytes per row
+          const int d0 = lane * NPL;
+          uint32_t ck[NPL], cv[NPL];
+#pragma unroll
+          for (int i = 0; i < NPL; ++i) {
+            ck[i] = ByteFmt<KVT>::enc(qxk[i] / qsk);
+            cv[i] = ByteFmt<KVT>::enc(qxv[i] / qsv);
+          }
+          if constexpr (I4) {
+            s_new[wv][d0 >> 1] = (uint8_t)(ck[0] | (ck[NPL - 1] << 4));
+            s_new[wv][RB + (d0 >> 1)] = (uint8_t)(cv[0] | (cv[NPL - 1] << 4));
+          } else {
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) {
+              s_new[wv][d0 + i] = (uint8_t)ck[i];
+              s_new[wv][RB + d0 + i] = (uint8_t)cv[i];
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();  // one wave's LDS operations complete in order
+        qready = true;
+      }
+    };
 
     // One tile of TS tokens.  Streaming tiles (LAST = false) always have a next
     // tile: its K loads go out as soon as QK^T has consumed kr and its V loads
     // as soon as PV has consumed vr (rolling pipeline, no stores, no masking).
     // The last tile of a segment (LAST = true) issues no loads; it masks tokens
     // at or past tok1 and, for the step entry, takes in the appended token.
-    auto tile = [&](const int t, auto last_tag) {
+    auto tile = [&](const int t, auto last_tag, auto fix_tag) {
       constexpr bool LAST = decltype(last_tag)::value;
+      // streaming tiles of the quantising step's last page (FIX) are their own
+      // instance, so the other streaming tiles carry none of its code
+      constexpr bool FIX = decltype(fix_tag)::value;
       int pgi_n = pgi, j_n = j0, page_n = page;
       if constexpr (!LAST) {
         j_n = j0 + TS;
@@ -446,7 +889,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       }
       const bool bad_n = (unsigned)page_n >= (unsigned)NP;
       const int pg_ld_n = bad_n ? 0 : page_n;
-      const float kmul = scale_log2 * ksc, vmul = vsc;
+      // quantising step: a tile of the last page takes the appended view of it
+      const bool fixp = QNEW && (LAST ? qfix && pgi == lp : FIX);
+      if constexpr (QNEW) {
+        if (fixp && !qready) qprep();
+        if (fixp && qrk) {
+          const uint8_t* lut = reinterpret_cast<const uint8_t*>(s_lut[wv][0]);
+#pragma unroll
+          for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+              for (int x = 0; x < 4; ++x) kr[sub][kk][x] = lut4(lut, kr[sub][kk][x]);
+        }
+        if (fixp && qrv) {
+          const uint8_t* lut = reinterpret_cast<const uint8_t*>(s_lut[wv][1]);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) vr[dt][x] = lut4(lut, vr[dt][x]);
+        }
+      }
+      const float kmul = scale_log2 * (fixp ? qsk : ksc), vmul = fixp ? qsv : vsc;
 
       if constexpr (LAST) {
         // ---- fused append (step entry): the tile holding token Lb-1 takes this
@@ -672,8 +1136,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     };
 
     int t = tok0;
-    for (; t + TS < tok1; t += TS) tile(t, std::false_type{});
-    tile(t, std::true_type{});
+    const int tfix = QNEW && qfix ? lp * P : tok1;      // first token of the tiles that need the appended view
+    for (; t + TS < tok1 && t < tfix; t += TS) tile(t, std::false_type{}, std::false_type{});
+    if constexpr (QNEW)
+      for (; t + TS < tok1; t += TS) tile(t, std::false_type{}, std::true_type{});
+    tile(t, std::true_type{}, std::false_type{});
 
     // ---- finish the segment ------------------------------------------------------
     float lt = l + __shfl_xor(l, 16);
@@ -781,6 +1248,59 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
 }
 
+// The quantising step's merge kernel: as decode_merge_kernel, with this
+// step's bf16 / fp32 rows quantised on write (quant_store_half) by two extra
+// waves per (b, g), one for K and one for V, which make the same scale
+// decisions the split kernel made for its view of the last page.
+template <int KVT, bool OUT_BF16, int D>
+__global__ __launch_bounds__(256) void decode_merge_quant_kernel(
+    const int4* __restrict__ descs, const float* __restrict__ partials, void* __restrict__ out_, int B,
+    int Hq, int Hkv, int G, int nchunk, const void* __restrict__ k_new, const void* __restrict__ v_new,
+    int new_bf16, uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool, float* __restrict__ kscales,
+    float* __restrict__ vscales, const int4* __restrict__ qdescs, int NP, int P) {
+  constexpr int NPL = D / 64;
+  __shared__ uint8_t s_nb[4][D];        // the new V row's codes (V pass of a re-encode)
+  __shared__ uint32_t s_lut[4][2][64];  // re-encode tables, K and V
+  const int wv = uniform(threadIdx.x >> 6);
+  const int wi = uniform(blockIdx.x * 4 + wv);
+  // nchunk merging waves and two appending waves (K, V) per (b, g), so the
+  // merge's and the append's dependent loads run side by side
+  const int bg = wi / (nchunk + 2), chunk = wi - bg * (nchunk + 2);
+  if (bg >= B * Hkv) return;
+  const int lane = threadIdx.x & 63;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const bool app = chunk >= nchunk, app_v = chunk == nchunk + 1;
+  float x[NPL];
+  if (app) {   // independent of the descriptor: issued first
+    const size_t row = ((size_t)b * Hkv + g) * D + (size_t)(lane * NPL);
+    const void* src = app_v ? v_new : k_new;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      x[i] = new_bf16 ? fbits((uint32_t)static_cast<const uint16_t*>(src)[row + i] << 16)
+                      : static_cast<const float*>(src)[row + i];
+  }
+  const int4 d = descs[bg];
+  // the page's scales before this append, as the split kernel read them (in
+  // the same round trip as the descriptor)
+  const int4 qd = app ? qdescs[bg] : make_int4(0, 0, 0, 0);
+  const int L = d.w;
+  if (L <= 0) return;
+  const int n = d.y >> 1;
+  if (!app && n > 1)
+    merge_chunk<OUT_BF16>(partials, 2 * (int64_t)d.x + (d.y & 1), d.x, n, out_,
+                          ((size_t)b * Hq + (size_t)g * G) * D, G, D, 256 * chunk, lane);
+  if (app && (unsigned)d.z < (unsigned)NP) {
+    const size_t ch = chunk_elem(d.z, g, Hkv, P, D);
+    const size_t si = (size_t)d.z * Hkv + g;
+    if (app_v)
+      quant_store_half<KVT, D, true>(x, (L - 1) % P, vpool + elem_byte<KVT>(ch), P, vscales, si,
+                                     fbits((uint32_t)qd.y), s_lut[wv][0], s_nb[wv], lane);
+    else
+      quant_store_half<KVT, D, false>(x, (L - 1) % P, kpool + elem_byte<KVT>(ch), P, kscales, si,
+                                      fbits((uint32_t)qd.x), s_lut[wv][0], s_nb[wv], lane);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Append: one workgroup per sequence; element-wise copy through the page table.
 // ---------------------------------------------------------------------------
@@ -818,206 +1338,6 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// One-byte appends (fp8 e4m3 or int8) with dynamic page scales (quantise on
-// write).  QMAX = 448 (fp8) or 127 (int8); NOCLIP = 464 or 127.5, the largest
-// |x| / scale whose encoding is the largest code without clipping.
-//
-// One wave per (sequence, kv head); K and V each with their own scale:
-// a = max |x| of the new row (widened to fp32);
-//   slot j == 0 (first token of the page): s = a / QMAX (1 if a == 0);
-//   else, s0 = the page's scale: s = s0 if a / s0 <= NOCLIP,
-//   otherwise s = a / QMAX and every earlier slot is re-encoded,
-//   enc((dec(byte) * s0) / s);
-// the new row is stored as enc(x / s) and the page scale becomes s.
-// Every division and product is one correctly rounded fp32 operation.
-// ---------------------------------------------------------------------------
-
-// fp32 -> e4m3fn: nearest value, ties to the even significand, saturating at
-// +-448 (NaN -> 0x7F).  With e = max(exponent(|x|), -6), the e4m3 step at |x|
-// is 2^(e-3) (the subnormal step 2^-9 below 2^-6), k = rint(|x| / 2^(e-3)) is
-// exact in fp32, and the code is 8 * (e + 6) + k: a carry of k to 16 lands on
-// the next binade's first code, and below 2^-6 the code is k itself.
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  const uint32_t sign = (ubits(x) >> 24) & 0x80u;
-  if (x != x) return 0x7Fu;
-  const float a = fminf(fabsf(x), 448.f);
-  const int e = max((int)((ubits(a) >> 23) & 0xFFu) - 127, -6);
-  const int k = (int)rintf(ldexpf(a, 3 - e));
-  return sign | (uint32_t)(8 * (e + 6) + k);
-}
-
-// fp32 -> symmetric int8 byte: nearest integer, ties to even, clamped to +-127.
-__device__ __forceinline__ uint32_t int8_encode(float x) {
-  const float r = fminf(fmaxf(rintf(x), -127.f), 127.f);
-  return (uint32_t)(int)r & 0xFFu;
-}
-
-template <int KVT> struct ByteFmt;
-template <> struct ByteFmt<KV_FP8> {
-  static constexpr float QMAX = 448.f, NOCLIP = 464.f;
-  __device__ static uint32_t enc(float y) { return e4m3_encode(y); }
-  __device__ static void dec4(uint32_t w, float (&v)[4]) {
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
-  }
-};
-template <> struct ByteFmt<KV_INT8> {
-  static constexpr float QMAX = 127.f, NOCLIP = 127.5f;
-  __device__ static uint32_t enc(float y) { return int8_encode(y); }
-  __device__ static void dec4(uint32_t w, float (&v)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(uint8_t)(w >> (8 * i));
-  }
-};
-// int4: codes are two's complement nibbles; symmetric, clamped to +-7.
-template <> struct ByteFmt<KV_INT4> {
-  static constexpr float QMAX = 7.f, NOCLIP = 7.5f;
-  __device__ static uint32_t enc(float y) {
-    const float r = fminf(fmaxf(rintf(y), -7.f), 7.f);
-    return (uint32_t)(int)r & 0xFu;
-  }
-  __device__ static float dec(uint32_t c) { return (float)(int)((c & 0xFu) ^ 8u) - 8.f; }
-};
-
-// One element re-encoded under a new scale: enc((dec(code) * s0) / s), the
-// product and the quotient each rounded once.
-template <int KVT>
-__device__ __forceinline__ uint32_t requant1(float v, float s0, float s) {
-  const float real = v * s0;
-  return ByteFmt<KVT>::enc(real / s);
-}
-// Four bytes of a word re-encoded (int4: both nibbles of each byte).
-template <int KVT>
-__device__ __forceinline__ uint32_t requant4(uint32_t w, float s0, float s) {
-  uint32_t r = 0;
-  if constexpr (KVT == KV_INT4) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      r |= requant1<KVT>(ByteFmt<KVT>::dec(w >> (4 * i)), s0, s) << (4 * i);
-  } else {
-    float v[4];
-    ByteFmt<KVT>::dec4(w, v);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r |= requant1<KVT>(v[i], s0, s) << (8 * i);
-  }
-  return r;
-}
-
-// Scale decision for one row: returns the new scale; sets requant when the
-// page's earlier slots must be re-encoded.  A row fits the current scale while
-// its largest element encodes to the largest code without clipping:
-// |x| / s0 <= NOCLIP (fp8: 464, the midpoint above 448, rounds down to 448;
-// int8: 127.5 rounds to 128 and clamps to 127, still within half a step).
-template <int KVT>
-__device__ __forceinline__ float page_scale(float a, int j, float s0, bool& requant) {
-  requant = false;
-  if (j == 0) return a > 0.f ? a / ByteFmt<KVT>::QMAX : 1.f;
-  if (a / s0 <= ByteFmt<KVT>::NOCLIP) return s0;
-  requant = true;
-  return a / ByteFmt<KVT>::QMAX;
-}
-
-// A re-encode maps each old byte through enc((dec(byte) * s0) / s), a function
-// of the byte alone: the wave tabulates it once (4 codes per lane) in LDS and
-// then re-encodes by lookup.
-__device__ __forceinline__ uint32_t lut4(const uint8_t* lut, uint32_t w) {
-  return (uint32_t)lut[w & 0xFFu] | ((uint32_t)lut[(w >> 8) & 0xFFu] << 8) |
-         ((uint32_t)lut[(w >> 16) & 0xFFu] << 16) | ((uint32_t)lut[w >> 24] << 24);
-}
-
-// Re-encode slots [0, j) of a K chunk.  Token t's dims E c .. E c + E - 1 are
-// the 16-byte group at chunk + 16 (c P + t); lane l takes tokens l, l + 64, ...
-// (TPL of them per round, all GPT groups of each), so no group index is
-// divided, and every load of a round is issued before any conversion.
-template <int KVT, int D>
-__device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uint8_t* lut, int lane) {
-  constexpr int GPT = D * Kv<KVT>::BITS / 128;       // 16-byte groups per token
-  constexpr int TPL = 16 / GPT;                      // tokens per lane per round
-  for (int t0 = 0; t0 < j; t0 += 64 * TPL) {
-    u32x4_t w[TPL][GPT];
-#pragma unroll
-    for (int a = 0; a < TPL; ++a) {
-      const int t = min(t0 + 64 * a + lane, j - 1);    // clamped: in-bounds, stored only if owned
-#pragma unroll
-      for (int c = 0; c < GPT; ++c) w[a][c] = *reinterpret_cast<const u32x4_t*>(pool + 16 * (c * P + t));
-    }
-#pragma unroll
-    for (int a = 0; a < TPL; ++a) {
-      const int t = t0 + 64 * a + lane;
-      if (t < j) {
-#pragma unroll
-        for (int c = 0; c < GPT; ++c) {
-          u32x4_t r;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[a][c][q]);
-          store_nt(reinterpret_cast<u32x4_t*>(pool + 16 * (c * P + t)), r);
-        }
-      }
-    }
-  }
-}
-
-// Re-encode a V chunk for a scale change at slot j: a 16-byte group holds E
-// tokens of one dim from one TB = 4E token block; blocks 0 .. j/TB are
-// rewritten group by group.  Blocks before j's hold earlier slots only and are
-// re-encoded whole; in j's block, tokens < j are re-encoded, token j takes its
-// new code (nbj, from LDS) and later slots keep theirs.  A round's 64 * GPL
-// groups cover whole blocks (4 D groups each), so the block of a lane's i-th
-// group, and with it the choice between the two, is the same on every lane.
-template <int KVT, int D>
-__device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* lut, const uint8_t* nbj,
-                                          int lane) {
-  constexpr int BITS = Kv<KVT>::BITS, E = 128 / BITS;
-  constexpr int GPL = 16, TB = 4 * E;
-  constexpr int GPB = 4 * D;    // 16-byte groups per V block (blocks are contiguous)
-  static_assert((64 * GPL) % GPB == 0 && GPB % 64 == 0, "a round covers whole blocks");
-  const int jb = j / TB;
-  const int ngrp = (jb + 1) * GPB;
-  for (int base = 0; base < ngrp; base += 64 * GPL) {
-    u32x4_t w[GPL];
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int gi = min(base + lane + 64 * i, ngrp - 1);
-      w[i] = *reinterpret_cast<const u32x4_t*>(pool + (size_t)gi * 16);   // blocks are contiguous
-    }
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int blk = uniform((base + 64 * i) / GPB);
-      if (blk > jb) continue;                          // past j's block (uniform)
-      const int gi = base + lane + 64 * i;
-      u32x4_t r;
-      if (blk < jb) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[i][q]);
-      } else {
-        const int rem = gi - blk * GPB;
-        const int c = rem / D, d = rem - c * D;
-        const uint32_t fresh = nbj[d];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t re = lut4(lut, w[i][q]);
-          uint32_t outw = 0;
-          constexpr int PW = 32 / BITS;                  // elements per word
-#pragma unroll
-          for (int x = 0; x < PW; ++x) {
-            // element e of the group holds token 16 * (e / 4) + 4c + e % 4 of the block
-            const int e = PW * q + x;
-            const int tok = blk * TB + 16 * (e >> 2) + 4 * c + (e & 3);
-            constexpr uint32_t M = (1u << BITS) - 1u;
-            const uint32_t code = tok < j ? (re >> (BITS * x)) & M
-                                : tok == j ? fresh : (w[i][q] >> (BITS * x)) & M;
-            outw |= code << (BITS * x);
-          }
-          r[q] = outw;
-        }
-      }
-      store_nt(reinterpret_cast<u32x4_t*>(pool + (size_t)gi * 16), r);
-    }
-  }
-}
-
 template <int KVT, bool IN_BF16, int D>
 __global__ __launch_bounds__(256) void append_quant_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new,
@@ -1032,17 +1352,9 @@ __global__ __launch_bounds__(256) void append_quant_kernel(
   if (bg >= B * Hkv) return;
   const int lane = threadIdx.x & 63;
   const int b = bg / Hkv, g = bg - b * Hkv;
-  const int d0 = lane * NPL;
   // the new rows do not depend on the table: their loads go first
-  const size_t row = ((size_t)b * Hkv + g) * D + (size_t)d0;
   float xk[NPL], xv[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    xk[i] = IN_BF16 ? fbits((uint32_t)static_cast<const uint16_t*>(k_new)[row + i] << 16)
-                    : static_cast<const float*>(k_new)[row + i];
-    xv[i] = IN_BF16 ? fbits((uint32_t)static_cast<const uint16_t*>(v_new)[row + i] << 16)
-                    : static_cast<const float*>(v_new)[row + i];
-  }
+  load_new_rows<D>(k_new, v_new, IN_BF16, ((size_t)b * Hkv + g) * D + (size_t)(lane * NPL), xk, xv);
   const int L = uniform(((const_i32_ptr)seq_lens)[b]);
   if (L <= 0) return;
   const int t = L - 1, pgi = t / P, j = t - pgi * P;
@@ -1056,64 +1368,8 @@ __global__ __launch_bounds__(256) void append_quant_kernel(
     sk0 = kscales[si];
     sv0 = vscales[si];
   }
-  float ak = 0.f, av = 0.f;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    ak = fmaxf(ak, fabsf(xk[i]));
-    av = fmaxf(av, fabsf(xv[i]));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    ak = fmaxf(ak, __shfl_xor(ak, o));
-    av = fmaxf(av, __shfl_xor(av, o));
-  }
-  ak = fbits(uniform((int)ubits(ak)));
-  av = fbits(uniform((int)ubits(av)));
-  sk0 = fbits(uniform((int)ubits(sk0)));
-  sv0 = fbits(uniform((int)ubits(sv0)));
-  bool rk, rv;
-  const float sk = page_scale<KVT>(ak, j, sk0, rk);
-  const float sv = page_scale<KVT>(av, j, sv0, rv);
-  uint32_t nbk[NPL], nbv[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    nbk[i] = ByteFmt<KVT>::enc(xk[i] / sk);
-    nbv[i] = ByteFmt<KVT>::enc(xv[i] / sv);
-  }
-  uint8_t* kp = kpool + elem_byte<KVT>(ch);
-  uint8_t* vp = vpool + elem_byte<KVT>(ch);
-  const uint8_t* lutk = reinterpret_cast<const uint8_t*>(s_lut[wv][0]);
-  const uint8_t* lutv = reinterpret_cast<const uint8_t*>(s_lut[wv][1]);
-  if (rk || rv) {
-    const uint32_t codes = (uint32_t)(4 * lane) * 0x01010101u + 0x03020100u;   // 4 codes per lane
-    if (rk) s_lut[wv][0][lane] = requant4<KVT>(codes, sk0, sk);
-    if (rv) s_lut[wv][1][lane] = requant4<KVT>(codes, sv0, sv);
-    __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
-  }
-  constexpr int E = 128 / Kv<KVT>::BITS;
-  if (rk) requant_k<KVT, D>(kp, j, P, lutk, lane);
-  // the new K token's dims d0.. are consecutive elements of one group
-  // (disjoint from the re-encoded slots): two bytes, or one int4 byte
-  uint8_t* kt = kp + elem_byte<KVT>(k_elem<E>(j, d0, P));
-  if constexpr (KVT == KV_INT4)
-    store_nt(kt, (uint8_t)(nbk[0] | (nbk[NPL - 1] << 4)));
-  else if constexpr (NPL == 2)
-    store_nt(reinterpret_cast<uint16_t*>(kt), (uint16_t)(nbk[0] | (nbk[NPL - 1] << 8)));
-  else
-    store_nt(kt, (uint8_t)nbk[0]);
-  if (rv) {
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) s_nb[wv][d0 + i] = (uint8_t)nbv[i];
-    __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
-    requant_v<KVT, D>(vp, j, lutv, s_nb[wv], lane);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) put_code_nt<KVT>(vp, v_elem<E>(j, d0 + i, D), nbv[i]);   // own bytes
-  }
-  if (lane == 0) {
-    kscales[si] = sk;
-    vscales[si] = sv;
-  }
+  quant_store_row<KVT, D>(xk, xv, j, kpool + elem_byte<KVT>(ch), vpool + elem_byte<KVT>(ch), P, kscales, vscales,
+                          si, sk0, sv0, s_lut[wv], s_nb[wv], lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1170,12 +1426,27 @@ std::mutex g_mu;
 DevInfo g_dev[64];
 
 typedef void (*decode_fn_t)(const void*, const uint8_t*, const uint8_t*, const void*, const void*, const float*,
-                            const float*, const int32_t*, const int32_t*, void*, float*, int4*, int, int, int,
-                            int, int, int, int, int, int, float);
+                            const float*, const int32_t*, const int32_t*, void*, float*, int4*, int4*, int, int,
+                            int, int, int, int, int, int, int, float, int);
 
-template <int KVT, int D, bool OB>
+template <int KVT, int D, bool OB, bool QNEW = false>
 decode_fn_t decode_fn() {
-  return decode_split_kernel<KVT, D, OB>;
+  return decode_split_kernel<KVT, D, OB, QNEW>;
+}
+
+// The quantising step's split kernels (fp8, int8: D 64 or 128; int4: D 128).
+decode_fn_t pick_decode_quant(int kvt, int D, bool ob) {
+  if (kvt == KV_FP8) {
+    if (D == 64) return ob ? decode_fn<KV_FP8, 64, true, true>() : decode_fn<KV_FP8, 64, false, true>();
+    return ob ? decode_fn<KV_FP8, 128, true, true>() : decode_fn<KV_FP8, 128, false, true>();
+  }
+  if (kvt == KV_INT8) {
+    if (D == 64) return ob ? decode_fn<KV_INT8, 64, true, true>() : decode_fn<KV_INT8, 64, false, true>();
+    return ob ? decode_fn<KV_INT8, 128, true, true>() : decode_fn<KV_INT8, 128, false, true>();
+  }
+  if (kvt == KV_INT4 && D == 128)
+    return ob ? decode_fn<KV_INT4, 128, true, true>() : decode_fn<KV_INT4, 128, false, true>();
+  return nullptr;
 }
 
 decode_fn_t pick_decode(int kvt, int D, bool ob) {
@@ -1312,7 +1583,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int cus = device_cu_count();
   if (cus <= 0) return hipErrorInvalidDevice;
-  decode_fn_t fn = pick_decode(a.kvt, a.head_dim, a.out_bf16);
+  decode_fn_t fn = a.new_quant ? pick_decode_quant(a.kvt, a.head_dim, a.out_bf16)
+                              : pick_decode(a.kvt, a.head_dim, a.out_bf16);
   if (!fn) return hipErrorInvalidValue;
   // Resident waves: enough for about 64 KB of K/V tiles in flight per CU (a
   // tile is 128 * D bytes in every dtype), i.e. one wave per SIMD at D = 128.
@@ -1330,8 +1602,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(fn, grid, block, 0, s, a.q, static_cast<const uint8_t*>(a.k_pool),
                      static_cast<const uint8_t*>(a.v_pool), a.k_new, a.v_new, a.k_scales,
                      a.v_scales, a.block_tables,
-                     a.seq_lens, a.out, a.partials, a.descs, a.batch, a.max_pages, a.num_pages,
-                     a.num_q_heads, a.num_kv_heads, G, a.page_size, a.partition_tokens, Wmax, scale_log2);
+                     a.seq_lens, a.out, a.partials, a.descs, a.qdescs, a.batch, a.max_pages, a.num_pages,
+                     a.num_q_heads, a.num_kv_heads, G, a.page_size, a.partition_tokens, Wmax, scale_log2,
+                     a.new_bf16 ? 1 : 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int pairs = a.batch * a.num_kv_heads;
@@ -1339,6 +1612,28 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   dim3 mgrid((unsigned)(((int64_t)pairs * nchunk + 3) / 4));
   void* kp = const_cast<void*>(a.k_pool);
   void* vp = const_cast<void*>(a.v_pool);
+  if (a.new_quant) {
+    float* ks = const_cast<float*>(a.k_scales);
+    float* vs = const_cast<float*>(a.v_scales);
+    mgrid = dim3((unsigned)(((int64_t)pairs * (nchunk + 2) + 3) / 4));   // plus two appending waves per pair
+#define PKV_MERGE_Q(K, OB, DD)                                                                      \
+  hipLaunchKernelGGL((decode_merge_quant_kernel<K, OB, DD>), mgrid, block, 0, s, a.descs, a.partials, a.out, \
+                     a.batch, a.num_q_heads, a.num_kv_heads, G, nchunk, a.k_new, a.v_new,                \
+                     a.new_bf16 ? 1 : 0, static_cast<uint8_t*>(kp), static_cast<uint8_t*>(vp), ks, vs,    \
+                     a.qdescs, a.num_pages, a.page_size)
+#define PKV_MERGE_QD(K, OB) \
+  if (a.head_dim == 64) PKV_MERGE_Q(K, OB, 64); else PKV_MERGE_Q(K, OB, 128);
+    if (a.kvt == KV_FP8) {
+      if (a.out_bf16) { PKV_MERGE_QD(KV_FP8, true) } else { PKV_MERGE_QD(KV_FP8, false) }
+    } else if (a.kvt == KV_INT8) {
+      if (a.out_bf16) { PKV_MERGE_QD(KV_INT8, true) } else { PKV_MERGE_QD(KV_INT8, false) }
+    } else {        // int4: D = 128 only
+      if (a.out_bf16) PKV_MERGE_Q(KV_INT4, true, 128); else PKV_MERGE_Q(KV_INT4, false, 128);
+    }
+#undef PKV_MERGE_QD
+#undef PKV_MERGE_Q
+    return hipGetLastError();
+  }
 #define PKV_MERGE(K, OB)                                                                           \
   hipLaunchKernelGGL((decode_merge_kernel<K, OB>), mgrid, block, 0, s, a.descs, a.partials, a.out,     \
                      a.batch, a.num_q_heads, a.num_kv_heads, G, a.head_dim, nchunk, a.k_new, a.v_new,  \

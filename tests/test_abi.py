@@ -252,3 +252,26 @@ def test_step_noalloc_rejects_bad_arguments(over, code):
 
 def test_step_noalloc_batch_zero_is_a_noop_without_device():
     assert _step_noalloc(b=0, q=0, kn=0, vn=0, kp=0, vp=0, bt=0, sl=0, out=0) == 0
+
+
+def _step_quant(**over):
+    a = dict(q=F, qdt=1, kn=F, vn=F, ndt=1, kp=F, vp=F, kvdt=2, ks=F, vs=F, bt=F, mp=4, sl=F, b=2, np_=8, hq=8,
+             hkv=2, d=128, p=64, scale=0.1, pt=0, out=F, odt=1, ws=F, wsb=1 << 30)
+    a.update(over)
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return pkv.lib().pkv_decode_step_quant(vp(a["q"]), a["qdt"], vp(a["kn"]), vp(a["vn"]), a["ndt"], vp(a["kp"]),
+                                           vp(a["vp"]), a["kvdt"], vp(a["ks"]), vp(a["vs"]), vp(a["bt"]), a["mp"],
+                                           vp(a["sl"]), a["b"], a["np_"], a["hq"], a["hkv"], a["d"], a["p"],
+                                           a["scale"], a["pt"], vp(a["out"]), a["odt"], vp(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [(dict(kvdt=1), -3), (dict(kvdt=0), -3), (dict(ndt=2), -3), (dict(ndt=7), -3),
+                                       (dict(kn=0), -1), (dict(ks=0), -1), (dict(vs=0), -1), (dict(p=32), -2),
+                                       (dict(kvdt=4, p=64), -2), (dict(kvdt=4, p=128, d=64), -2),
+                                       (dict(kn=F + 8), -6), (dict(hq=7), -2), (dict(qdt=0), -3)])
+def test_step_quant_rejects_bad_arguments(over, code):
+    assert _step_quant(**over) == code
+
+
+def test_step_quant_batch_zero_is_a_noop_without_device():
+    assert _step_quant(b=0, q=0, kn=0, vn=0, kp=0, vp=0, ks=0, vs=0, bt=0, sl=0, out=0, ws=0) == 0
