@@ -251,8 +251,8 @@ __device__ __forceinline__ u32x4_t ld16_stream(const uint8_t* p) {
 // odd XCDs stream 8-10 % slower than those of the even ones (per-wave
 // timestamps of the decode, on every box measured), so when every share holds
 // at least 3 units (k >= 5) the shares are weighted (odd : even = 56 : 64,
-// the best of 64 down to 44 in same-box timings of four workloads, with two
-// switch units per (b, g), the best of 0, 1 and 2): wave w owns units
+// the best of 64 down to 44 in same-box timings of four workloads, with three
+// switch units per (b, g), the best of 0 to 6): wave w owns units
 // [T * C(w) / C(W), T * C(w + 1) / C(W)), C(w) = sum of the weights of waves
 // 0 .. w - 1 (even XCD: WEIGHT_EVEN, odd: WEIGHT_ODD); otherwise
 // [w * T / W, (w + 1) * T / W).
@@ -261,7 +261,7 @@ __device__ __forceinline__ u32x4_t ld16_stream(const uint8_t* p) {
 #define PKV_WEIGHT_ODD 56
 #endif
 #ifndef PKV_SWITCH_UNITS
-#define PKV_SWITCH_UNITS 2
+#define PKV_SWITCH_UNITS 3
 #endif
 constexpr int WEIGHT_EVEN = 64, WEIGHT_ODD = PKV_WEIGHT_ODD;
 constexpr int SWITCH_UNITS = PKV_SWITCH_UNITS;
