@@ -378,8 +378,11 @@ def append_int8_dynamic(k_new, v_new, new_dtype, block_tables, seq_lens, k_pool,
 # decode.
 
 def prefill(q, q_dtype, cu_q, k_pool, v_pool, kv_dtype, block_tables, seq_lens, Hq, P, scale,
-            batches=None):
-    """fp64 [T, Hq, D] outputs of causal chunked prefill over the paged cache."""
+            batches=None, k_scales=None, v_scales=None):
+    """fp64 [T, Hq, D] outputs of causal chunked prefill over the paged cache.
+
+    For the scaled caches (fp8, int8, int4) a stored element's value is its
+    code times the (page, kv head) scale, as in decode."""
     cu = np.asarray(cu_q, dtype=np.int64)
     B = len(seq_lens)
     T = int(cu[-1])
@@ -396,8 +399,11 @@ def prefill(q, q_dtype, cu_q, k_pool, v_pool, kv_dtype, block_tables, seq_lens, 
         pos = L - C + np.arange(C)                          # position of each chunk token
         allowed = np.arange(L)[None, :] <= pos[:, None]      # [C, L] causal mask
         live = pos >= 0
-        k, v, _ = gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b)
+        k, v, pages = gather(k_pool, v_pool, kv_dtype, block_tables, seq_lens, P, b)
         kf, vf = widen(k, kv_dtype), widen(v, kv_dtype)
+        if kv_dtype in SCALED:
+            kf = kf * np.asarray(k_scales, np.float64)[pages].T[:, :, None]
+            vf = vf * np.asarray(v_scales, np.float64)[pages].T[:, :, None]
         for g in range(Hkv):
             qg = qf[r0:r1, g * G:(g + 1) * G]                # [C, G, D]
             s = float(scale) * np.einsum("cgd,ld->cgl", qg, kf[g])

@@ -184,3 +184,88 @@ def test_prefill_workload_shape_and_flops():
     assert wl.attended() == 19
     assert wl.flops() == 4 * 19 * 4 * 8
     assert wl.T == 6 and list(wl.cu_q) == [0, 4, 6]
+
+
+# ------------------------------------------------------- fp8 cache prefill ----
+# The cache holds e4m3 codes with per-(page, kv head) scales; a stored value is
+# code x scale.  Pins: torch SDPA on the rows the generator drew and quantised
+# (decoded here by torch's float8_e4m3fn, not through the oracle), chunks of
+# one token against the decode oracle, every row against the decode oracle over
+# its prefix, and the chunk append against the generator's packing of all L
+# tokens.
+
+FP8_CASE = dict(ctx_lens=[0, 23, 70, 130], chunk_lens=[19, 5, 66, 1], D=32, P=64)
+
+
+def _fp8_full_pools(wl):
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    paged.append_chunk(wl.k_new, wl.v_new, "fp8", wl.cu_q, wl.block_tables, wl.seq_lens, kp, vp, wl.P)
+    return kp, vp
+
+
+def _fp8_oracle(wl, kp, vp, **kw):
+    return paged.prefill(wl.q, wl.q_dtype, wl.cu_q, kp, vp, "fp8", wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
+                         wl.scale, k_scales=wl.k_scales, v_scales=wl.v_scales, **kw)
+
+
+def _torch_dequant(codes, scales, P):
+    """[L, Hkv, D] e4m3 codes times each token's logical-page scale, by torch."""
+    x = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+    s = torch.from_numpy(np.repeat(scales.astype(np.float64), P, axis=0)[:codes.shape[0]])   # [L, Hkv]
+    return x * s[:, :, None]
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (16, 2)])
+def test_fp8_prefill_matches_torch_sdpa_on_dequantised_rows(Hq, Hkv):
+    wl = configs.prefill_case("t", 21, Hq=Hq, Hkv=Hkv, kv_dtype="fp8", **FP8_CASE)
+    kp, vp = _fp8_full_pools(wl)
+    pre = _fp8_oracle(wl, kp, vp)
+    qf = _q64(wl)
+    G = Hq // Hkv
+    for b in range(wl.B):
+        L, C = int(wl.seq_lens[b]), int(wl.chunk_lens[b])
+        kc, vc, ks, vs = configs.seq_tokens(wl.seed, b, L, wl.Hkv, wl.D, "fp8", wl.P)
+        k = _torch_dequant(kc, ks, wl.P).permute(1, 0, 2).repeat_interleave(G, dim=0)     # [Hq, L, D]
+        v = _torch_dequant(vc, vs, wl.P).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        qt = torch.from_numpy(qf[wl.cu_q[b]:wl.cu_q[b + 1]]).permute(1, 0, 2)
+        mask = torch.arange(L)[None, :] <= (L - C + torch.arange(C))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, k, v, attn_mask=mask, scale=float(wl.scale))
+        np.testing.assert_allclose(pre[wl.cu_q[b]:wl.cu_q[b + 1]], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_fp8_chunks_of_one_equal_decode():
+    wl = configs.prefill_case("t", 22, ctx_lens=[0, 9, 63, 64, 100], chunk_lens=[1] * 5, Hq=8, Hkv=2, D=32, P=64,
+                              kv_dtype="fp8")
+    kp, vp = _fp8_full_pools(wl)
+    pre = _fp8_oracle(wl, kp, vp)
+    dec = paged.decode(wl.q, wl.q_dtype, kp, vp, "fp8", wl.block_tables, wl.seq_lens, wl.Hq, wl.P, wl.scale,
+                       wl.k_scales, wl.v_scales)
+    np.testing.assert_allclose(pre, dec, rtol=0, atol=1e-13)
+
+
+def test_fp8_each_row_equals_decode_over_its_prefix():
+    wl = configs.prefill_case("t", 23, Hq=4, Hkv=2, kv_dtype="fp8", **FP8_CASE)
+    kp, vp = _fp8_full_pools(wl)
+    pre = _fp8_oracle(wl, kp, vp)
+    for b in range(wl.B):
+        L, C = int(wl.seq_lens[b]), int(wl.chunk_lens[b])
+        for i in range(C):
+            r = int(wl.cu_q[b]) + i
+            dec = paged.decode(wl.q[r:r + 1], wl.q_dtype, kp, vp, "fp8", wl.block_tables[b:b + 1],
+                               np.array([L - C + i + 1], np.int32), wl.Hq, wl.P, wl.scale, wl.k_scales, wl.v_scales)
+            np.testing.assert_allclose(pre[r], dec[0], rtol=0, atol=1e-13)
+
+
+def test_fp8_chunk_append_gives_the_generators_full_packing():
+    wl = configs.prefill_case("t", 24, Hq=4, Hkv=2, kv_dtype="fp8", **FP8_CASE)
+    kp, vp = _fp8_full_pools(wl)
+    kidx, vidx = layout.k_chunk_index(wl.P, wl.D, "fp8"), layout.v_chunk_index(wl.P, wl.D, "fp8")
+    for b in range(wl.B):
+        L = int(wl.seq_lens[b])
+        k, v, ks, vs = configs.seq_tokens(wl.seed, b, L, wl.Hkv, wl.D, "fp8", wl.P)
+        pages = wl.block_tables[b, :-(-L // wl.P)]
+        kk, vv = kp.copy(), vp.copy()
+        layout.pack_sequence(kk, pages, k, wl.P, kidx, "fp8")
+        layout.pack_sequence(vv, pages, v, wl.P, vidx, "fp8")
+        assert np.array_equal(kk, kp) and np.array_equal(vv, vp), b
+        assert np.array_equal(wl.k_scales[pages], ks) and np.array_equal(wl.v_scales[pages], vs), b

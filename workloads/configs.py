@@ -260,11 +260,15 @@ def lognormal_lengths(rng: np.random.Generator, n: int, median: float, sigma: fl
 
 
 def _assemble(name, seed, B, Hq, Hkv, D, P, num_pages, kv_dtype, q_dtype, out_dtype,
-              scale, partition_tokens, L, bt, q_mult=1.0, pool_lens=None):
+              scale, partition_tokens, L, bt, q_mult=1.0, pool_lens=None, quant_lens=None):
     """Draw q/K/V and pack the pools.  ``pool_lens`` (default L) is how many tokens
-    of each sequence are resident in the pool."""
+    of each sequence are resident in the pool.  A scaled cache is quantised per
+    page over the first ``quant_lens`` (default pool_lens) tokens: with
+    quant_lens = L, the page scales come from every token a page will hold, so
+    tokens past pool_lens, packed later, fit the same scales."""
     max_pages = bt.shape[1]
     pool_lens = L if pool_lens is None else pool_lens
+    quant_lens = pool_lens if quant_lens is None else quant_lens
     q = draw_q(seed, B, Hq, D, q_dtype, q_mult)
     kpool = layout.empty_pool(num_pages, Hkv, P, D, kv_dtype)
     vpool = layout.empty_pool(num_pages, Hkv, P, D, kv_dtype)
@@ -277,12 +281,14 @@ def _assemble(name, seed, B, Hq, Hkv, D, P, num_pages, kv_dtype, q_dtype, out_dt
     def fill(b):
         n = int(pool_lens[b])
         pages = bt[b, :int(pages_needed(np.array([n]), P)[0])]
-        k, v, kls, vls = seq_tokens(seed, b, n, Hkv, D, kv_dtype, P)
-        layout.pack_sequence(kpool, pages, k, P, kidx, kv_dtype)
-        layout.pack_sequence(vpool, pages, v, P, vidx, kv_dtype)
-        if kv_dtype in SCALED and len(pages):
-            ks[pages] = kls
-            vs[pages] = vls
+        nq = int(quant_lens[b]) if kv_dtype in SCALED else n
+        k, v, kls, vls = seq_tokens(seed, b, nq, Hkv, D, kv_dtype, P)
+        layout.pack_sequence(kpool, pages, k[:n], P, kidx, kv_dtype)
+        layout.pack_sequence(vpool, pages, v[:n], P, vidx, kv_dtype)
+        if kv_dtype in SCALED and nq:
+            all_pages = bt[b, :int(pages_needed(np.array([nq]), P)[0])]
+            ks[all_pages] = kls
+            vs[all_pages] = vls
 
     # Sequences own disjoint pages, so they can be drawn and placed concurrently;
     # each draws from its own child stream, so the result does not depend on order.
@@ -495,7 +501,7 @@ class PrefillWorkload:
     P: int
     num_pages: int
     max_pages: int
-    kv_dtype: str                 # "f32" | "bf16"
+    kv_dtype: str                 # "f32" | "bf16" | "fp8"
     q_dtype: str
     out_dtype: str
     scale: np.float32
@@ -508,6 +514,8 @@ class PrefillWorkload:
     v_pool: np.ndarray
     k_new: np.ndarray             # [T, Hkv, D] stored format, the chunks' rows
     v_new: np.ndarray
+    k_scales: Optional[np.ndarray] = None   # fp8: [NP, Hkv] page scales (of the full pages)
+    v_scales: Optional[np.ndarray] = None
 
     @property
     def G(self) -> int:
@@ -537,9 +545,14 @@ class PrefillWorkload:
 def prefill_case(name: str, seed: int, ctx_lens, chunk_lens, Hq: int, Hkv: int, D: int, P: int,
                  kv_dtype: str = "bf16", out_dtype: Optional[str] = None, slack: float = 1.25,
                  q_mult: float = 1.0, extra_table_cols: int = 0) -> PrefillWorkload:
-    """Sequences with ``ctx_lens`` cached tokens and chunks of ``chunk_lens``."""
-    if kv_dtype not in ("f32", "bf16"):
-        raise ValueError("chunked prefill workloads are fp32 or bf16")
+    """Sequences with ``ctx_lens`` cached tokens and chunks of ``chunk_lens``.
+
+    fp8 cache: every sequence's L tokens are quantised per page (amax / 448 of
+    the tokens each page holds once the chunk is in), the pool holds the first
+    L - C tokens' bytes, the scales are those of the full pages, and k_new /
+    v_new are the chunk tokens' bytes (the chunk append copies them)."""
+    if kv_dtype not in ("f32", "bf16", "fp8"):
+        raise ValueError("chunked prefill workloads are fp32, bf16 or fp8")
     rng = np.random.default_rng(seed)
     ctx = np.asarray(ctx_lens, dtype=np.int32)
     C = np.asarray(chunk_lens, dtype=np.int32)
@@ -552,24 +565,34 @@ def prefill_case(name: str, seed: int, ctx_lens, chunk_lens, Hq: int, Hkv: int, 
     q_dtype = "f32" if kv_dtype == "f32" else "bf16"
     sc = np.float32(1.0 / math.sqrt(D))
     base = _assemble(name, seed, B, Hq, Hkv, D, P, NP, kv_dtype, q_dtype, out_dtype or q_dtype,
-                     sc, 0, L, bt, pool_lens=ctx)
+                     sc, 0, L, bt, pool_lens=ctx, quant_lens=L)
     cu = np.zeros(B + 1, dtype=np.int32)
     cu[1:] = np.cumsum(C)
     T = int(cu[-1])
     qf = _child(seed, 5).standard_normal((T, Hq, D), dtype=np.float32)
     if q_mult != 1.0:
         qf = qf * np.float32(q_mult)
-    kn = np.zeros((T, Hkv, D), dtype=np.float32)
-    vn = np.zeros((T, Hkv, D), dtype=np.float32)
-    for b in range(B):
-        n = int(L[b])
-        kn[cu[b]:cu[b + 1]] = draw_seq_f32(seed, 2, b, n, Hkv, D)[ctx[b]:]
-        vn[cu[b]:cu[b + 1]] = draw_seq_f32(seed, 3, b, n, Hkv, D)[ctx[b]:]
+    if kv_dtype in SCALED:
+        kn = np.zeros((T, Hkv, D), dtype=np.uint8)
+        vn = np.zeros((T, Hkv, D), dtype=np.uint8)
+        for b in range(B):
+            k, v, _, _ = seq_tokens(seed, b, int(L[b]), Hkv, D, kv_dtype, P)
+            kn[cu[b]:cu[b + 1]] = k[ctx[b]:]
+            vn[cu[b]:cu[b + 1]] = v[ctx[b]:]
+    else:
+        kn = np.zeros((T, Hkv, D), dtype=np.float32)
+        vn = np.zeros((T, Hkv, D), dtype=np.float32)
+        for b in range(B):
+            n = int(L[b])
+            kn[cu[b]:cu[b + 1]] = draw_seq_f32(seed, 2, b, n, Hkv, D)[ctx[b]:]
+            vn[cu[b]:cu[b + 1]] = draw_seq_f32(seed, 3, b, n, Hkv, D)[ctx[b]:]
+        kn, vn = _store(kn, kv_dtype), _store(vn, kv_dtype)
     return PrefillWorkload(name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, D=D, P=P, num_pages=NP,
                            max_pages=bt.shape[1], kv_dtype=kv_dtype, q_dtype=q_dtype,
                            out_dtype=base.out_dtype, scale=sc, seq_lens=L, chunk_lens=C, cu_q=cu,
                            block_tables=bt, q=_store(qf, q_dtype), k_pool=base.k_pool,
-                           v_pool=base.v_pool, k_new=_store(kn, kv_dtype), v_new=_store(vn, kv_dtype))
+                           v_pool=base.v_pool, k_new=kn, v_new=vn,
+                           k_scales=base.k_scales, v_scales=base.v_scales)
 
 
 def chunked_prefill_bf16(seed: int = 6, B: int = 16, chunk: int = 512) -> PrefillWorkload:
@@ -580,6 +603,16 @@ def chunked_prefill_bf16(seed: int = 6, B: int = 16, chunk: int = 512) -> Prefil
     return prefill_case("chunked_prefill_bf16", seed, ctx, np.full(B, chunk, np.int32), 32, 8, 128, 64)
 
 
+def chunked_prefill_fp8(seed: int = 6, B: int = 16, chunk: int = 512) -> PrefillWorkload:
+    """The chunked-prefill workload above (same draws and lengths) over an fp8
+    e4m3 cache with per-(page, kv head) scales amax / 448."""
+    rng = np.random.default_rng([seed, 0])
+    ctx = rng.integers(0, 7680, size=B, endpoint=True).astype(np.int32)
+    return prefill_case("chunked_prefill_fp8", seed, ctx, np.full(B, chunk, np.int32), 32, 8, 128, 64,
+                        kv_dtype="fp8", out_dtype="bf16")
+
+
 PREFILL_CONFIGS = {
     "chunked_prefill_bf16": chunked_prefill_bf16,
+    "chunked_prefill_fp8": chunked_prefill_fp8,
 }
