@@ -37,7 +37,8 @@ CSRC = os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc")
 DECODE_SRCS = ("pkv_kernels.hip", "pkv_device.h")
 PREFILL_SRCS = ("pkv_prefill.hip", "pkv_device.h")
 WORKLOADS = ["llama3_8b_bf16", "inflight_bf16", "long_splitkv_bf16", "fp8_kv", "inflight_fp8", "int8_kv",
-             "inflight_int8", "int4_kv", "inflight_int4", "tiny_fp32", "chunked_prefill_bf16"]
+             "inflight_int8", "int4_kv", "inflight_int4", "tiny_fp32", "chunked_prefill_bf16",
+             "chunked_prefill_fp8"]
 PREFILL_METRIC = "paged chunked prefill attention: TFLOP/s (causal pairs, algorithmic)"
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA peak
 SCALED = ("fp8", "i8", "i4")    # caches of one byte or less, with per-(page, kv head) scales
@@ -241,7 +242,7 @@ def cpu_baseline_prefill(wl, seconds):
 
     def one(b):
         paged.prefill(wl.q, wl.q_dtype, wl.cu_q, kp, vp, wl.kv_dtype, wl.block_tables, wl.seq_lens, wl.Hq, wl.P,
-                      wl.scale, batches=[b])
+                      wl.scale, batches=[b], k_scales=wl.k_scales, v_scales=wl.v_scales)
         L, C = int(wl.seq_lens[b]), int(wl.chunk_lens[b])
         return 4 * wl.Hq * wl.D * (C * (L - C + 1) + C * (C - 1) // 2)
 
@@ -289,6 +290,9 @@ def bench_prefill(args):
     kn, vn = T(wl.k_new), T(wl.v_new)
     kps = [T(wl.k_pool) for _ in range(layers)]
     vps = [T(wl.v_pool) for _ in range(layers)]
+    # an fp8 cache's page scales are set before the chunk lands (the append copies codes)
+    ks = None if wl.k_scales is None else T(wl.k_scales)
+    vs = None if wl.v_scales is None else T(wl.v_scales)
     out = torch.empty((wl.T, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
@@ -296,8 +300,12 @@ def bench_prefill(args):
         pkv.kv_append_chunk(kn, vn, wl.kv_dtype, cu, bt, sl, kps[i % layers], vps[i % layers], wl.Hkv, wl.D, wl.P)
 
     def attend(i):
-        pkv.paged_prefill(q, wl.q_dtype, cu, kps[i % layers], vps[i % layers], wl.kv_dtype, bt, sl, wl.Hq, wl.Hkv,
-                          wl.D, wl.P, wl.scale, out, wl.out_dtype)
+        if wl.kv_dtype == "fp8":
+            pkv.paged_prefill_fp8(q, wl.q_dtype, cu, kps[i % layers], vps[i % layers], ks, vs, bt, sl, wl.Hq,
+                                  wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype)
+        else:
+            pkv.paged_prefill(q, wl.q_dtype, cu, kps[i % layers], vps[i % layers], wl.kv_dtype, bt, sl, wl.Hq,
+                              wl.Hkv, wl.D, wl.P, wl.scale, out, wl.out_dtype)
 
     for i in range(args.warmup):
         append(i)
@@ -345,7 +353,8 @@ def bench_prefill(args):
     rec = {
         "metric": PREFILL_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 (kv) / bf16 (q, out, products)" if wl.kv_dtype == "fp8" else "bf16",
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled pages)",
         "config": {"workload": args.workload, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "page_size": wl.P, "chunk_tokens": int(wl.T),

@@ -401,7 +401,7 @@ int pkv_kv_append_chunk(const void* k_new, const void* v_new, pkv_dtype kv_dtype
  * q: bf16 [total_q][num_q_heads][head_dim]; out: bf16 or fp32, same shape;
  * cu_q: int32 [batch + 1] device array, non-decreasing, cu_q[batch] <= total_q
  * (rows of a sequence with a decreasing or out-of-range pair are not written);
- * kv_dtype must be BF16.  Pool layout and sizes as for decode.  Writes only the
+ * kv_dtype must be BF16 (fp8: pkv_paged_prefill_fp8).  Pool layout and sizes as for decode.  Writes only the
  * rows of out that belong to a sequence.  No workspace.  A key position whose
  * page id lies outside [0, num_pages) (or past the table row) makes every row
  * of that (sequence, kv head) block NaN.
@@ -415,6 +415,27 @@ int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int
                       const int32_t* seq_lens, int batch, int num_pages,
                       int num_q_heads, int num_kv_heads, int head_dim, int page_size,
                       float scale, void* out, pkv_dtype out_dtype, void* stream);
+
+/* paged_prefill_fp8 - pkv_paged_prefill over an fp8-e4m3 cache with
+ * per-(page, kv head) scales (a stored value is its code times the scale).
+ *
+ * The first page's "key mechanisms" section widens FP8 data back to 16 bits
+ * before the matrix product accumulates, and the yololab page ("NVIDIA
+ * TensorRT-LLM deep dive", FP8 section) gives FP8 as the way to halve the
+ * memory a cache needs.  Here every e4m3 code widens to bf16 exactly on its
+ * way into the products; the K scale joins the softmax scale of its tile and
+ * the V scale multiplies the probabilities that enter the value products (the
+ * row sums take the probabilities unscaled).
+ * k_scales, v_scales: fp32 [num_pages][num_kv_heads].  page_size a multiple of
+ * 64 (the fp8 V block).  Other arguments, results and errors as
+ * pkv_paged_prefill, with PKV_E_NULL for NULL scales. */
+int pkv_paged_prefill_fp8(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int total_q,
+                          const void* k_pool, const void* v_pool,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables, int max_pages_per_seq,
+                          const int32_t* seq_lens, int batch, int num_pages,
+                          int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                          float scale, void* out, pkv_dtype out_dtype, void* stream);
 
 /* alloc_pages - give every sequence the page its newest token opens, from a
  * free-page stack in device memory (no host round trip per step).

@@ -210,6 +210,17 @@ def paged_prefill(q, q_dtype, cu_q, k_pool, v_pool, kv_dtype, block_tables, seq_
         float(scale), _ptr(out), _code(out_dtype), _stream(stream)))
 
 
+def paged_prefill_fp8(q, q_dtype, cu_q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                      num_q_heads, num_kv_heads, head_dim, page_size, scale, out, out_dtype, stream=None):
+    """paged_prefill over an fp8-e4m3 cache with per-(page, kv head) scales."""
+    B, MP = block_tables.shape
+    NP = k_pool.shape[0]
+    _check("paged_prefill_fp8", lib().pkv_paged_prefill_fp8(
+        _ptr(q), _code(q_dtype), _ptr(cu_q), int(q.shape[0]), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales),
+        _ptr(v_scales), _ptr(block_tables), MP, _ptr(seq_lens), B, NP, num_q_heads, num_kv_heads, head_dim,
+        page_size, float(scale), _ptr(out), _code(out_dtype), _stream(stream)))
+
+
 def alloc_pages(seq_lens, block_tables, page_size, free_pages, free_count, stream=None):
     """Give each sequence the page its newest token opens, from the device free-page
     stack free_pages[0 .. free_count[0] - 1] (updated in place)."""

@@ -194,6 +194,40 @@ int run_step(const void* q, pkv_dtype q_dtype, const void* k_new, const void* v_
                     partition_tokens, out, out_dtype, workspace, workspace_bytes, stream, k_new, v_new, static_ws);
 }
 
+// Chunked prefill (bf16 or fp8 cache): checks, then the launch.
+int run_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int total_q, const void* k_pool,
+                const void* v_pool, pkv_dtype kv_dtype, const float* k_scales, const float* v_scales,
+                const int32_t* block_tables, int max_pages_per_seq, const int32_t* seq_lens, int batch, int num_pages,
+                int num_q_heads, int num_kv_heads, int head_dim, int page_size, float scale, void* out,
+                pkv_dtype out_dtype, void* stream) {
+  if (total_q < 0) return fail(PKV_E_SHAPE, "total_q %d < 0", total_q);
+  if (batch > 0 && (!cu_q || !block_tables || !seq_lens || !k_pool || !v_pool))
+    return fail(PKV_E_NULL, "a required pointer is NULL");
+  if (batch > 0 && total_q > 0 && (!q || !out)) return fail(PKV_E_NULL, "q / out is NULL");
+  int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
+  if (rc) return rc;
+  if (q_dtype != PKV_BF16) return fail(PKV_E_DTYPE, "chunked prefill takes bf16 queries (q dtype %d)", q_dtype);
+  if (out_dtype != PKV_BF16 && out_dtype != PKV_F32)
+    return fail(PKV_E_DTYPE, "out dtype %d not supported (bf16 or fp32)", out_dtype);
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(PKV_E_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  if (num_q_heads / num_kv_heads > 128)
+    return fail(PKV_E_SHAPE, "group size %d > 128", num_q_heads / num_kv_heads);
+  const int eb = kv_dtype == PKV_FP8_E4M3 ? 1 : 2;
+  if ((uint64_t)num_kv_heads * page_size * head_dim * eb >= (1ull << 32))
+    return fail(PKV_E_SHAPE, "a page of all kv heads (%d x %d x %d x %d bytes) must be below 4 GiB", num_kv_heads,
+                page_size, head_dim, eb);
+  if (batch == 0 || total_q == 0) return PKV_OK;
+  if ((rc = check_align({q, k_pool, v_pool, out}))) return rc;
+  pkv::PrefillArgs a{q,        cu_q,     total_q,      k_pool,   v_pool,    (int)kv_dtype, k_scales,
+                     v_scales, block_tables, seq_lens, out,      out_dtype == PKV_BF16, batch, max_pages_per_seq,
+                     num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale};
+  hipError_t e = pkv::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,31 +302,24 @@ int pkv_paged_prefill(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int
                       const int32_t* seq_lens, int batch, int num_pages, int num_q_heads, int num_kv_heads,
                       int head_dim, int page_size, float scale, void* out, pkv_dtype out_dtype, void* stream) {
   g_last_error.clear();
-  if (total_q < 0) return fail(PKV_E_SHAPE, "total_q %d < 0", total_q);
-  if (batch > 0 && (!cu_q || !block_tables || !seq_lens || !k_pool || !v_pool))
-    return fail(PKV_E_NULL, "a required pointer is NULL");
-  if (batch > 0 && total_q > 0 && (!q || !out)) return fail(PKV_E_NULL, "q / out is NULL");
-  int rc = check_pool_shape(kv_dtype, max_pages_per_seq, batch, num_pages, num_kv_heads, head_dim, page_size);
-  if (rc) return rc;
-  if (kv_dtype != PKV_BF16) return fail(PKV_E_DTYPE, "chunked prefill reads a bf16 cache (kv dtype %d)", kv_dtype);
-  if (q_dtype != PKV_BF16) return fail(PKV_E_DTYPE, "chunked prefill takes bf16 queries (q dtype %d)", q_dtype);
-  if (out_dtype != PKV_BF16 && out_dtype != PKV_F32)
-    return fail(PKV_E_DTYPE, "out dtype %d not supported (bf16 or fp32)", out_dtype);
-  if (num_q_heads <= 0 || num_q_heads % num_kv_heads)
-    return fail(PKV_E_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
-                num_kv_heads);
-  if (num_q_heads / num_kv_heads > 128)
-    return fail(PKV_E_SHAPE, "group size %d > 128", num_q_heads / num_kv_heads);
-  if ((uint64_t)num_kv_heads * page_size * head_dim * 2 >= (1ull << 32))
-    return fail(PKV_E_SHAPE, "a page of all kv heads (%d x %d x %d bf16) must be below 4 GiB", num_kv_heads,
-                page_size, head_dim);
-  if (batch == 0 || total_q == 0) return PKV_OK;
-  if ((rc = check_align({q, k_pool, v_pool, out}))) return rc;
-  pkv::PrefillArgs a{q, cu_q, total_q, k_pool, v_pool, block_tables, seq_lens, out, out_dtype == PKV_BF16,
-                     batch, max_pages_per_seq, num_pages, num_q_heads, num_kv_heads, head_dim, page_size, scale};
-  hipError_t e = pkv::launch_prefill(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  return PKV_OK;
+  if (kv_dtype != PKV_BF16)
+    return fail(PKV_E_DTYPE, "chunked prefill reads a bf16 cache here (kv dtype %d; fp8: pkv_paged_prefill_fp8)",
+                kv_dtype);
+  return run_prefill(q, q_dtype, cu_q, total_q, k_pool, v_pool, PKV_BF16, nullptr, nullptr, block_tables,
+                     max_pages_per_seq, seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size,
+                     scale, out, out_dtype, stream);
+}
+
+int pkv_paged_prefill_fp8(const void* q, pkv_dtype q_dtype, const int32_t* cu_q, int total_q, const void* k_pool,
+                          const void* v_pool, const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables, int max_pages_per_seq, const int32_t* seq_lens, int batch,
+                          int num_pages, int num_q_heads, int num_kv_heads, int head_dim, int page_size, float scale,
+                          void* out, pkv_dtype out_dtype, void* stream) {
+  g_last_error.clear();
+  if (batch > 0 && total_q > 0 && (!k_scales || !v_scales)) return fail(PKV_E_NULL, "fp8 scales are NULL");
+  return run_prefill(q, q_dtype, cu_q, total_q, k_pool, v_pool, PKV_FP8_E4M3, k_scales, v_scales, block_tables,
+                     max_pages_per_seq, seq_lens, batch, num_pages, num_q_heads, num_kv_heads, head_dim, page_size,
+                     scale, out, out_dtype, stream);
 }
 
 namespace {

@@ -104,14 +104,17 @@ struct AppendChunkArgs {
   int kvt, batch, max_pages, num_pages, num_kv_heads, head_dim, page_size;
 };
 
-// Causal chunked prefill over a bf16 cache: q and out are [total_q][Hq][D],
-// rows cu_q[b] .. cu_q[b+1] belong to sequence b.
+// Causal chunked prefill over a bf16 or fp8 cache: q and out are
+// [total_q][Hq][D], rows cu_q[b] .. cu_q[b+1] belong to sequence b.
 struct PrefillArgs {
   const void* q;            // bf16
   const int32_t* cu_q;
   int total_q;
   const void* k_pool;
   const void* v_pool;
+  int kvt;                  // KV_BF16 or KV_FP8
+  const float* k_scales;    // fp8 only
+  const float* v_scales;
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;

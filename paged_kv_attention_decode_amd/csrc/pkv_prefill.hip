@@ -60,6 +60,7 @@
 namespace pkv {
 
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
 
 // ---------------------------------------------------------------------------
 // Chunk append (f32, fp8, int8 and int4 caches; bf16 below).  Block (b, y)
@@ -199,18 +200,30 @@ __global__ __launch_bounds__(256) void append_chunk_bf16_kernel(
 // tile i + NBUF - 1 then fills.  Every wave runs every iteration (fetches and
 // barrier), computing only tiles below its own kv_end.
 // ---------------------------------------------------------------------------
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void prefill_kernel(
+template <int KVT, int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_FP8 ? 2 : 3, 3))) void prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ cu, int total_q,
-    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ seq_lens, void* __restrict__ out_, int B, int MP, int NP, int Hq, int Hkv,
-    int G, int TPW, int P, float scale_log2, uint32_t q_sign) {
-  constexpr int E = 8;              // bf16 elements per 16-byte group
-  constexpr int TS = 32;            // tokens per tile (one V block)
-  constexpr int NKK = D / 32;       // k steps of the QK^T MFMA
+    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const float* __restrict__ kscales,
+    const float* __restrict__ vscales, const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
+    void* __restrict__ out_, int B, int MP, int NP, int Hq, int Hkv, int G, int TPW, int P, float scale_log2,
+    uint32_t q_sign) {
+  // bf16 cache: a tile is one 32-token V block.  fp8 cache (e4m3 codes, a
+  // scale per (page, kv head)): a tile is one 64-token V block, the same 16 KB
+  // at D = 128, computed as two 32-key halves; codes widen to bf16 exactly on
+  // their way from LDS to the MFMA, the K scale joins the softmax scale and
+  // the V scale multiplies the probabilities that enter the PV products.
+  constexpr bool FP8 = KVT == KV_FP8;
+  constexpr int BITS = FP8 ? 8 : 16;
+  constexpr int E = 128 / BITS;     // elements per 16-byte group
+  constexpr int TS = 4 * E;         // tokens per tile (one V block)
+  constexpr int NSUB = TS / 16;     // 16-token QK^T sub-tiles per tile
+  constexpr int NHALF = NSUB / 2;   // 32-key halves per tile
+  constexpr int NCH = FP8 ? 2 : 1;  // bf16x8 operands per 16-byte group
+  constexpr int NKK = D / (4 * E);  // K groups per lane and sub-tile
+  constexpr int NQ = NKK * NCH;     // query operands per N tile (k steps of QK^T)
   constexpr int NDT = D / 16;       // 16-dim PV tiles
   constexpr int NT = 2;             // 16-row N tiles per wave
-  constexpr int NKOP = 2 * NKK;     // K slices per tile
+  constexpr int NKOP = NSUB * NKK;  // K slices per tile
   constexpr int NOP = NKOP + NDT;   // K and V slices per tile (16 at D = 128)
   constexpr int OPW = NOP / 4;      // slices each wave fetches
   constexpr float TH = 8.f;         // reference lag allowed before a rescale (log2 units)
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int kv_end = has_rows ? max(ctx + tok_last + 1, 0) : 0;  // keys this wave needs
 
   int pos_n[NT];                // position of this lane's row in each N tile (-1: none)
-  u32x4_t Q[NT][NKK];           // query operands (B of QK^T)
+  u32x4_t Q[NT][NQ];            // query operands (B of QK^T)
   auto out_row = [&](int nt) -> int64_t {
     const int rho = rho_w0 + 16 * nt + r16;
     const int tok = tok_base + rho / G, h = rho % G;
@@ -284,10 +297,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int64_t orow = out_row(nt);
     const int tok = tok_base + (rho_w0 + 16 * nt + r16) / G;
     pos_n[nt] = orow >= 0 ? max(ctx + tok, -1) : -1;
+    // operand i: dims E (c4 + 4 (i / NCH)) + 8 (i % NCH) .. + 7, the dims of
+    // the K operand it meets (a lane's K group, or half of it for fp8)
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      Q[nt][kk] = orow >= 0 ? ld16(reinterpret_cast<const uint8_t*>(q + orow + 8 * c4 + 32 * kk)) ^ q_sign
-                            : u32x4_t{0, 0, 0, 0};
+    for (int i = 0; i < NQ; ++i)
+      Q[nt][i] = orow >= 0 ? ld16(reinterpret_cast<const uint8_t*>(q + orow + E * (c4 + 4 * (i / NCH)) + 8 * (i % NCH))) ^ q_sign
+                           : u32x4_t{0, 0, 0, 0};
   }
 
   f32x4_t O[NDT][NT];
@@ -305,6 +320,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     Ls[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  // fp8: scales of the tiles in the buffers (this tile, the next, the one
+  // being fetched), loaded by every wave when it fetches a tile
+  float ksq[3] = {1.f, 1.f, 1.f}, vsq[3] = {1.f, 1.f, 1.f};
 
   const const_i32_ptr btrow = (const_i32_ptr)(bt + (size_t)b * MP);
   // Wave wv fetches slices wv, wv + 4, ...: the first OPW / 2 are K slices, the
@@ -319,9 +337,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int op = wv + 4 * o;
     if (o < OPW / 2) {
       const int sub = op / NKK, kk = op % NKK;
-      sl_off[o] = 2u * (uint32_t)k_elem<E>(16 * sub + r16, (c4 + 4 * kk) * E, P);
+      sl_off[o] = (uint32_t)(BITS / 8) * (uint32_t)k_elem<E>(16 * sub + r16, (c4 + 4 * kk) * E, P);
     } else {
-      sl_off[o] = 2u * (uint32_t)v_elem<E>(4 * c4, (op - NKOP) * 16 + r16, D);
+      sl_off[o] = (uint32_t)(BITS / 8) * (uint32_t)v_elem<E>(4 * c4, (op - NKOP) * 16 + r16, D);
     }
   }
   // Next tile to fetch: page index and token offset in it.  Returns whether its
@@ -329,15 +347,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   int f_pgi = 0, f_j = 0;
   // bytes per page (all kv heads; below 2^32, checked at the boundary) and from
   // a page to kv head g's chunk
-  const uint32_t page_bytes = uniform((uint32_t)(Hkv * P * D * 2));
-  const uint8_t* kg = kpool + (size_t)g * P * D * 2;
-  const uint8_t* vg = vpool + (size_t)g * P * D * 2;
+  const uint32_t page_bytes = uniform((uint32_t)(Hkv * P * D * (BITS / 8)));
+  const uint8_t* kg = kpool + (size_t)g * P * D * (BITS / 8);
+  const uint8_t* vg = vpool + (size_t)g * P * D * (BITS / 8);
   auto fetch_next = [&](int buf) -> bool {
     const int page = f_pgi < MP ? btrow[f_pgi] : -1;
     const bool badp = (unsigned)page >= (unsigned)NP;
+    if constexpr (FP8) {
+      ksq[2] = kscales[(size_t)(badp ? 0 : page) * Hkv + g];
+      vsq[2] = vscales[(size_t)(badp ? 0 : page) * Hkv + g];
+    }
     const uint64_t ch = (uint64_t)(uint32_t)(badp ? 0 : page) * page_bytes;
     const uint8_t* kc = kg + ch + 16 * f_j;
-    const uint8_t* vc = vg + ch + 2 * D * f_j;
+    const uint8_t* vc = vg + ch + (BITS / 8) * D * f_j;
 #pragma unroll
     for (int o = 0; o < OPW; ++o) {
       const uint8_t* src = (o < OPW / 2 ? kc : vc) + sl_off[o];
@@ -355,13 +377,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   auto slice = [&](int buf, int op) -> u32x4_t {
     return *(lds_u32x4_t*)(&s_kv[buf][op][lane]);
   };
+  // 8 bytes (one half) of a lane's slice: fp8 V groups hold the tokens of both
+  // halves of a tile, and each half reads only its own
+  auto slice_half = [&](int buf, int op, int h) -> u32x2_t {
+    return *((lds_u32x2_t*)(&s_kv[buf][op][lane]) + h);
+  };
 
-  // One tile from buffer buf.  masked (wave-uniform): the tile reaches past the
-  // wave's first row position (causal mask).  One body for every tile: the mask
-  // steps are small uniform branches, so the output accumulators never cross a
-  // branch of their own.  Keys past a row's position get p = 0; V of slots at or
-  // past L (which may hold anything) was zeroed in LDS when the tile arrived.
-  auto tile = [&](const int t, const int buf, const bool masked) {
+  // 32 keys (half h of the tile) from buffer buf.  masked (wave-uniform): the
+  // keys reach past the wave's first row position (causal mask).  One body for
+  // every tile: the mask steps are small uniform branches, so the output
+  // accumulators never cross a branch of their own.  Keys past a row's
+  // position get p = 0; V of slots at or past L (which may hold anything) was
+  // zeroed in LDS when the tile arrived.  ksl: the softmax scale times the
+  // tile's K scale (log2 domain); vs: the tile's V scale (fp8, else 1).
+  auto tile = [&](const int t, const int buf, const bool masked, const int h, const float ksl, const float vs) {
     // ---- S^T = K Q^T: rows = 16 tokens, columns = query rows (unscaled) ------
     f32x4_t acc[2][NT];
 #pragma unroll
@@ -371,11 +400,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4_t k0 = slice(buf, kk), k1 = slice(buf, NKK + kk);
+      const u32x4_t k0 = slice(buf, (2 * h) * NKK + kk), k1 = slice(buf, (2 * h + 1) * NKK + kk);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[0][nt] = mfma_bf16(k0, Q[nt][kk], acc[0][nt]);
-        acc[1][nt] = mfma_bf16(k1, Q[nt][kk], acc[1][nt]);
+      for (int c = 0; c < NCH; ++c) {
+        const u32x4_t a0 = FP8 ? byte8_to_bf16x8<KV_FP8>(k0[2 * c], k0[2 * c + 1]) : k0;
+        const u32x4_t a1 = FP8 ? byte8_to_bf16x8<KV_FP8>(k1[2 * c], k1[2 * c + 1]) : k1;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[0][nt] = mfma_bf16(a0, Q[nt][kk * NCH + c], acc[0][nt]);
+          acc[1][nt] = mfma_bf16(a1, Q[nt][kk * NCH + c], acc[1][nt]);
+        }
       }
     }
     // ---- online softmax per row (log2 domain, lazy reference) -----------------
@@ -385,6 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // than TH.  Each lane first tests its own 8 scores; only when some lane
     // passes does the wave form the column maxima across the four lanes of a
     // column and rescale (the common case needs no cross-lane step).
+    const int tk = t + 32 * h;                 // first key of these 32
     float s[NT][2][4];
     float lmax[NT];
     bool pass = false;
@@ -396,8 +431,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         s[nt][1][i] = acc[1][nt][i];
       }
       if (masked) {
-        // key t + 16 sub + 4 c4 + i lies past the row's position
-        const int lim = pos_n[nt] - t - 4 * c4;
+        // key tk + 16 sub + 4 c4 + i lies past the row's position
+        const int lim = pos_n[nt] - tk - 4 * c4;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -411,14 +446,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         for (int i = 0; i < 4; ++i) x = fmaxf(x, s[nt][sub][i]);
       lmax[nt] = x;
       // m = -inf gives +inf (passes) unless every score is masked (NaN: no)
-      pass |= __builtin_fmaf(x, scale_log2, -m[nt]) > TH;
+      pass |= __builtin_fmaf(x, ksl, -m[nt]) > TH;
     }
     if (__ballot(pass)) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float cmax = colmax4(lmax[nt]);
-        const bool grow = __builtin_fmaf(cmax, scale_log2, -m[nt]) > TH;
-        const float mref = grow ? cmax * scale_log2 : m[nt];
+        const bool grow = __builtin_fmaf(cmax, ksl, -m[nt]) > TH;
+        const float mref = grow ? cmax * ksl : m[nt];
         const float alpha = grow ? __builtin_amdgcn_exp2f(m[nt] - mref) : 1.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) scale_in_place(O[dt][nt], alpha);
@@ -426,7 +461,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         m[nt] = mref;
       }
     }
-    u32x4_t pb[NT];
+    u32x4_t pb[NT], pv[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float p[2][4];
@@ -434,7 +469,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          p[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][sub][i], scale_log2, -m[nt]));
+          p[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nt][sub][i], ksl, -m[nt]));
       if (masked) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
@@ -445,13 +480,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       pb[nt] = u32x4_t{pack_bf16_rne(p[0][0], p[0][1]), pack_bf16_rne(p[0][2], p[0][3]),
                        pack_bf16_rne(p[1][0], p[1][1]), pack_bf16_rne(p[1][2], p[1][3])};
       Ls[nt] = mfma_bf16(ones, pb[nt], Ls[nt]);
+      // the PV products take p times the tile's V scale (fp8); the row sums
+      // above take p itself
+      if constexpr (FP8)
+        pv[nt] = u32x4_t{pack_bf16_rne(p[0][0] * vs, p[0][1] * vs), pack_bf16_rne(p[0][2] * vs, p[0][3] * vs),
+                         pack_bf16_rne(p[1][0] * vs, p[1][1] * vs), pack_bf16_rne(p[1][2] * vs, p[1][3] * vs)};
+      else
+        pv[nt] = pb[nt];
     }
     // ---- O^T += V^T P^T: rows = 16 dims, columns = query rows -------------------
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const u32x4_t vv = slice(buf, NKOP + dt);
+      u32x4_t vv;
+      if constexpr (FP8) {
+        const u32x2_t w = slice_half(buf, NKOP + dt, h);
+        vv = byte8_to_bf16x8<KV_FP8>(w.x, w.y);
+      } else {
+        vv = slice(buf, NKOP + dt);
+      }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma_bf16(vv, pb[nt], O[dt][nt]);
+      for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma_bf16(vv, pv[nt], O[dt][nt]);
     }
   };
 
@@ -459,14 +507,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   // its maximum, lgkmcnt 11:8 = 0): all LDS reads done and at most n vector
   // memory operations (this wave's later fetches) outstanding
   constexpr int WAIT_V0 = 0x70, WAIT_V1 = 0x70 | OPW, WAIT_V2 = 0x70 | (2 * OPW);
-  static_assert(2 * OPW < 16 && NBUF >= 2 && NBUF <= 4, "waitcnt immediates assume < 16 loads, <= 3 tiles ahead");
+  static_assert(2 * OPW < 16 && NBUF == 3, "waitcnt immediates assume < 16 loads; the scale slots assume 3 buffers");
   bool bad = false;
   const int ntiles = (kv_end_wg + TS - 1) / TS;
   if (ntiles > 0) {
     uint32_t bad_bits = 0;                     // bit i % 32: tile i's page id is bad
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
+    for (int i = 0; i < NBUF - 1; ++i) {
       if (i < ntiles && fetch_next(i)) bad_bits |= 1u << i;
+      if constexpr (FP8) {       // tile i's scales into slot i
+        ksq[i] = ksq[2];
+        vsq[i] = vsq[2];
+      }
+    }
     for (int it = 0; it < ntiles; ++it) {
       const int buf = it % NBUF;
       // this wave's slices of tile `it` have landed (later tiles may be in flight)
@@ -479,14 +532,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         // zeroes the V elements of those slots in the slices it fetched (element
         // e of a lane's group is token 16 (e / 4) + 4 c4 + e % 4), so no 0 * NaN
         // reaches the products, and waits for its writes before the barrier.
+        constexpr int PW = 32 / BITS;          // elements per word
         u32x4_t keep;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t msk = 0;
 #pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            const int e = 2 * w + f;
-            if (it * TS + 16 * (e >> 2) + 4 * c4 + (e & 3) < L) msk |= 0xFFFFu << (16 * f);
+          for (int f = 0; f < PW; ++f) {
+            const int e = PW * w + f;
+            if (it * TS + 16 * (e >> 2) + 4 * c4 + (e & 3) < L) msk |= ((1u << BITS) - 1u) << (BITS * f);
           }
           keep[w] = msk;
         }
@@ -505,9 +559,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       const int t = it * TS;
       if (t < kv_end) {
         bad |= (bad_bits >> (it & 31)) & 1u;
-        tile(t, buf, t + TS - 1 > pos_first);
+        const float ksl = FP8 ? scale_log2 * ksq[0] : scale_log2;
+#pragma unroll
+        for (int h = 0; h < NHALF; ++h)
+          if (t + 32 * h < kv_end) tile(t, buf, t + 32 * h + 31 > pos_first, h, ksl, vsq[0]);
       }
       bad_bits &= ~(1u << (it & 31));
+      if constexpr (FP8) {       // the next tile's scales move up
+        ksq[0] = ksq[1];
+        ksq[1] = ksq[2];
+        vsq[0] = vsq[1];
+        vsq[1] = vsq[2];
+      }
     }
   }
 
@@ -568,19 +631,28 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const float scale_log2 = fabsf(a.scale) * 1.4426950408889634f;
   const uint32_t q_sign = std::signbit(a.scale) ? 0x80008000u : 0u;
   dim3 grid((unsigned)blocks), block(256);
-#define PKV_PREFILL(DD, OB)                                                                          \
-  hipLaunchKernelGGL((prefill_kernel<DD, OB>), grid, block, 0, s, static_cast<const uint16_t*>(a.q),  \
+#define PKV_PREFILL(K, DD, OB)                                                                       \
+  hipLaunchKernelGGL((prefill_kernel<K, DD, OB>), grid, block, 0, s, static_cast<const uint16_t*>(a.q), \
                      a.cu_q, a.total_q, static_cast<const uint8_t*>(a.k_pool),                         \
-                     static_cast<const uint8_t*>(a.v_pool), a.block_tables, a.seq_lens, a.out,        \
-                     a.batch, a.max_pages, a.num_pages, a.num_q_heads, a.num_kv_heads, G, TPW,        \
-                     a.page_size, scale_log2, q_sign)
-  if (a.head_dim == 128) {
-    if (a.out_bf16) PKV_PREFILL(128, true); else PKV_PREFILL(128, false);
-  } else if (a.head_dim == 64) {
-    if (a.out_bf16) PKV_PREFILL(64, true); else PKV_PREFILL(64, false);
+                     static_cast<const uint8_t*>(a.v_pool), a.k_scales, a.v_scales, a.block_tables,   \
+                     a.seq_lens, a.out, a.batch, a.max_pages, a.num_pages, a.num_q_heads,             \
+                     a.num_kv_heads, G, TPW, a.page_size, scale_log2, q_sign)
+#define PKV_PREFILL_K(K)                                                                             \
+  if (a.head_dim == 128) {                                                                           \
+    if (a.out_bf16) PKV_PREFILL(K, 128, true); else PKV_PREFILL(K, 128, false);                      \
+  } else if (a.head_dim == 64) {                                                                     \
+    if (a.out_bf16) PKV_PREFILL(K, 64, true); else PKV_PREFILL(K, 64, false);                        \
+  } else {                                                                                           \
+    return hipErrorInvalidValue;                                                                     \
+  }
+  if (a.kvt == KV_FP8) {
+    PKV_PREFILL_K(KV_FP8)
+  } else if (a.kvt == KV_BF16) {
+    PKV_PREFILL_K(KV_BF16)
   } else {
     return hipErrorInvalidValue;
   }
+#undef PKV_PREFILL_K
 #undef PKV_PREFILL
   return hipGetLastError();
 }

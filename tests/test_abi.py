@@ -275,3 +275,33 @@ def test_step_quant_rejects_bad_arguments(over, code):
 
 def test_step_quant_batch_zero_is_a_noop_without_device():
     assert _step_quant(b=0, q=0, kn=0, vn=0, kp=0, vp=0, ks=0, vs=0, bt=0, sl=0, out=0, ws=0) == 0
+
+
+def _prefill_fp8(**over):
+    a = dict(q=F, qdt=1, cu=F, tot=100, kp=F, vp=F, ks=F, vs=F, bt=F, mp=4, sl=F, b=2, np_=8, hq=8, hkv=2, d=128,
+             p=64, scale=0.1, out=F, odt=1)
+    a.update(over)
+    vp = lambda x: None if x in (0, None) else x  # noqa: E731
+    return pkv.lib().pkv_paged_prefill_fp8(vp(a["q"]), a["qdt"], vp(a["cu"]), a["tot"], vp(a["kp"]), vp(a["vp"]),
+                                           vp(a["ks"]), vp(a["vs"]), vp(a["bt"]), a["mp"], vp(a["sl"]), a["b"],
+                                           a["np_"], a["hq"], a["hkv"], a["d"], a["p"], a["scale"], vp(a["out"]),
+                                           a["odt"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ks=0), -1), (dict(vs=0), -1), (dict(q=0), -1), (dict(tot=-1), -2), (dict(p=32), -2), (dict(d=96), -2),
+    (dict(hq=7), -2), (dict(qdt=0), -3), (dict(odt=2), -3), (dict(kp=F + 4), -6),
+])
+def test_prefill_fp8_rejects_bad_arguments(over, code):
+    assert _prefill_fp8(**over) == code
+    assert pkv.lib().pkv_last_error()
+
+
+def test_prefill_fp8_empty_is_a_noop():
+    assert _prefill_fp8(b=0, q=0, cu=0, kp=0, vp=0, ks=0, vs=0, bt=0, sl=0, out=0) == 0
+    assert _prefill_fp8(tot=0, q=0, out=0) == 0
+
+
+def test_prefill_rejects_an_fp8_cache_and_names_the_fp8_entry():
+    assert _prefill(kvdt=2) == -3
+    assert b"pkv_paged_prefill_fp8" in pkv.lib().pkv_last_error()

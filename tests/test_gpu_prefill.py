@@ -16,8 +16,11 @@ pytestmark = pytest.mark.gpu
 
 
 def _up(wl):
-    return {k: dev_tensor(getattr(wl, k)) for k in ("q", "cu_q", "block_tables", "seq_lens", "k_pool", "v_pool",
-                                                    "k_new", "v_new")}
+    d = {k: dev_tensor(getattr(wl, k)) for k in ("q", "cu_q", "block_tables", "seq_lens", "k_pool", "v_pool",
+                                                 "k_new", "v_new")}
+    if wl.k_scales is not None:
+        d["k_scales"], d["v_scales"] = dev_tensor(wl.k_scales), dev_tensor(wl.v_scales)
+    return d
 
 
 def _gpu_append_chunk(wl, d, seq_lens=None, cu=None, bt=None):
@@ -30,9 +33,14 @@ def _gpu_prefill(wl, d, out_dtype=None, seq_lens=None, bt=None):
     odt = out_dtype or wl.out_dtype
     out = torch.full((wl.T, wl.Hq, wl.D), 7.0, dtype=torch.bfloat16 if odt == "bf16" else torch.float32,
                      device="cuda")
-    pkv.paged_prefill(d["q"], wl.q_dtype, d["cu_q"], d["k_pool"], d["v_pool"], wl.kv_dtype,
-                      d["block_tables"] if bt is None else bt, d["seq_lens"] if seq_lens is None else seq_lens,
-                      wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, odt)
+    btd = d["block_tables"] if bt is None else bt
+    sld = d["seq_lens"] if seq_lens is None else seq_lens
+    if wl.kv_dtype == "fp8":
+        pkv.paged_prefill_fp8(d["q"], wl.q_dtype, d["cu_q"], d["k_pool"], d["v_pool"], d["k_scales"], d["v_scales"],
+                              btd, sld, wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, odt)
+    else:
+        pkv.paged_prefill(d["q"], wl.q_dtype, d["cu_q"], d["k_pool"], d["v_pool"], wl.kv_dtype, btd, sld,
+                          wl.Hq, wl.Hkv, wl.D, wl.P, wl.scale, out, odt)
     torch.cuda.synchronize()
     return gpu_out(out)
 
@@ -290,3 +298,94 @@ def test_config_chunked_prefill_full_size():
         rows_ref.append(ref[r0:r1])
     check_close(np.concatenate(rows_got), np.concatenate(rows_ref), "bf16",
                 "chunked_prefill_bf16 (6 of 16 sequences)", out_rounding=True, report=True)
+
+
+# ------------------------------------------------------------ fp8 cache ----
+# K/V as e4m3 codes with per-(page, kv head) scales; the oracle multiplies each
+# code by its scale.  Bound: the fp8 one (max-abs <= 3e-2), with bf16 outputs
+# allowed their own half-ulp rounding.
+
+def _fp8_ref(wl, kp, vp, seq_lens=None, batches=None):
+    return paged.prefill(wl.q, "bf16", wl.cu_q, kp, vp, "fp8", wl.block_tables,
+                         wl.seq_lens if seq_lens is None else seq_lens, wl.Hq, wl.P, wl.scale, batches=batches,
+                         k_scales=wl.k_scales, v_scales=wl.v_scales)
+
+
+FP8_CASES = [  # (ctx, chunk, Hq, Hkv, D, P)
+    ([0, 5, 100, 300], [1, 70, 33, 130], 8, 2, 128, 64),
+    ([64, 0, 31], [64, 257, 97], 2, 2, 64, 64),
+    ([200, 9], [45, 300], 16, 2, 128, 128),
+    ([33, 0], [80, 19], 4, 2, 64, 128),
+    ([100], [40], 32, 2, 128, 64),
+    ([70, 1], [90, 130], 6, 2, 128, 64),
+    ([0, 0, 0], [1, 2, 300], 8, 2, 128, 64),
+]
+
+
+@pytest.mark.parametrize("ctx,chunk,Hq,Hkv,D,P", FP8_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+def test_fp8_prefill_matches_oracle(ctx, chunk, Hq, Hkv, D, P, odt):
+    wl = configs.prefill_case("p8", 160 + Hq + D + P, ctx, chunk, Hq, Hkv, D, P, kv_dtype="fp8", out_dtype=odt)
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    got = _gpu_prefill(wl, d)
+    kp, vp = _full_pools(wl)
+    assert np.array_equal(host_bytes(d["k_pool"]), kp.reshape(-1)) and np.array_equal(host_bytes(d["v_pool"]),
+                                                                                      vp.reshape(-1))
+    check_close(got, _fp8_ref(wl, kp, vp), "fp8", "fp8 prefill", out_rounding=odt == "bf16")
+
+
+def test_fp8_prefill_large_logits_and_reference_paths():
+    """Logits of std 3, and keys whose logits follow the softmax-reference profiles."""
+    wl = configs.prefill_case("p8", 171, [150, 20, 700], [70, 90, 200], 8, 2, 128, 64, kv_dtype="fp8",
+                              out_dtype="f32", q_mult=3.0)
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    kp, vp = _full_pools(wl)
+    check_close(_gpu_prefill(wl, d), _fp8_ref(wl, kp, vp), "fp8", "fp8 prefill std-3 logits")
+
+
+def test_fp8_prefill_rows_without_keys_and_bad_page():
+    wl = configs.prefill_case("p8", 172, [0, 10, 40], [20, 0, 30], 8, 2, 64, 64, kv_dtype="fp8", out_dtype="f32")
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    kp, vp = _full_pools(wl)
+    lens = wl.seq_lens.copy()
+    lens[0] = 12                                   # chunk of 20 over 12 keys: rows 0..7 at p < 0
+    got = _gpu_prefill(wl, d, seq_lens=dev_tensor(lens))
+    assert np.all(got[:8] == 0)
+    check_close(got, _fp8_ref(wl, kp, vp, seq_lens=lens), "fp8", "fp8 prefill p < 0")
+    bt = wl.block_tables.copy()
+    bt[2, 0] = wl.num_pages + 3                    # sequence 2's first page id out of range
+    got = _gpu_prefill(wl, d, bt=dev_tensor(bt))
+    r0, r1 = int(wl.cu_q[2]), int(wl.cu_q[3])
+    assert np.all(np.isnan(got[r0:r1])) and np.isfinite(got[:r0]).all()
+
+
+@pytest.mark.timeout(900)
+def test_config_chunked_prefill_fp8_full_size():
+    """The fp8 chunked-prefill workload (16 sequences x 512 chunk tokens): the
+    chunk append byte-exact against the oracle's; the prefill of six sequences
+    (shortest and longest context and four between) against the oracle on the
+    oracle's pools; every row finite."""
+    wl = configs.chunked_prefill_fp8()
+    d = _up(wl)
+    _gpu_append_chunk(wl, d)
+    got = _gpu_prefill(wl, d)
+    assert np.isfinite(got).all()
+    kp, vp = _full_pools(wl)
+    assert np.array_equal(host_bytes(d["k_pool"]), kp.reshape(-1)), "chunk append (K) differs"
+    assert np.array_equal(host_bytes(d["v_pool"]), vp.reshape(-1)), "chunk append (V) differs"
+    ctx = wl.seq_lens - wl.chunk_lens
+    order = np.argsort(ctx, kind="stable")
+    picks = [int(order[i]) for i in (0, 3, 6, 9, 12, len(order) - 1)]
+    with ThreadPoolExecutor(max_workers=min(len(picks), ORACLE_THREADS)) as ex:
+        refs = list(ex.map(lambda b: _fp8_ref(wl, kp, vp, batches=[b]), picks))
+    rows_got, rows_ref = [], []
+    for b, ref in zip(picks, refs):
+        r0, r1 = int(wl.cu_q[b]), int(wl.cu_q[b + 1])
+        check_close(got[r0:r1], ref[r0:r1], "fp8", f"sequence {b} (context {int(ctx[b])})", out_rounding=True)
+        rows_got.append(got[r0:r1])
+        rows_ref.append(ref[r0:r1])
+    check_close(np.concatenate(rows_got), np.concatenate(rows_ref), "fp8",
+                "chunked_prefill_fp8 (6 of 16 sequences)", out_rounding=True, report=True)
