@@ -28,8 +28,8 @@
 //   operand feeds two MFMAs (one per N tile).  The workgroups of a kv head g are
 //   blockIdx = g (mod Hkv), so with eight kv heads all readers of one head's
 //   pages run on one XCD and share its L2.
-// * Workgroups holding the later (longer-range) blocks of a sequence are
-//   dispatched first.
+// * Workgroups are dispatched longest first (by the keys their rows reach,
+//   over all sequences), so the long ones do not start late and leave a tail.
 // * S^T = K Q^T leaves four tokens of one query row per lane, which is the
 //   B-operand layout of O^T += V^T P^T: probabilities never cross lanes.  They
 //   enter the MFMA as one bf16 value (round to nearest even); the row sums come
@@ -239,30 +239,86 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
   const int unit = uniform((int)(blockIdx.x / (unsigned)Hkv));
 
   // ---- (sequence, token block) of this workgroup (same in every wave) ---------
-  // blocks of sequence b: ceil(C_b / TPW); units are numbered in sequence order,
-  // and within a sequence from the last block to the first.
+  // Units (b, qb) are taken longest first: unit number u (from blockIdx) is the
+  // u-th in descending order of the keys the block reads, kv_end(b, qb) =
+  // max(ctx_b + min(C_b, TPW (qb + 1)), 0), ties by sequence then block.  The
+  // blocks of sequence b: ceil(C_b / TPW), kv_end rising with qb, so those with
+  // kv_end >= w are its last n_b(w) blocks, n_b(w) in closed form; a binary
+  // search over w finds the u-th key, then a scan over the sequences the unit.
+  // Lengths are clamped to the table's reach for the ordering only.
+  const int cap = (int)min((int64_t)MP * P, (int64_t)1 << 30);
+  auto seq_at = [&](int bb, int& C, int& Lc, int& nb) {
+    C = 0;
+    Lc = 0;
+    if (bb < B) {
+      const int ra = cu[bb], rb = cu[bb + 1];
+      C = (ra >= 0 && rb <= total_q && rb > ra) ? rb - ra : 0;
+      Lc = min(max(seq_lens[bb], 0), cap);
+    }
+    nb = (C + TPW - 1) / TPW;
+  };
+  // blocks of one sequence with kv_end >= w
+  auto n_ge = [&](int C, int Lc, int nb, int w) -> int {
+    if (w <= 0) return nb;
+    if (nb == 0 || Lc < w) return 0;
+    const int y = w - (Lc - C);                // rows the block must reach: TPW (qb + 1) >= y
+    return y <= TPW ? nb : nb - ((y + TPW - 1) / TPW - 1);
+  };
+  auto wave_total = [&](int v) -> int { return uniform(__builtin_amdgcn_readlane(wave_incl_scan(v, lane), 63)); };
+  // all units with kv_end >= w (wave-uniform)
+  auto count_ge = [&](int w) -> int {
+    int tot = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      int C, Lc, nb;
+      seq_at(b0 + lane, C, Lc, nb);
+      tot += wave_total(n_ge(C, Lc, nb, w));
+    }
+    return tot;
+  };
   int b = -1, qb = 0;
   {
-    int run = 0;
+    int n_units = 0, lmax = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
-      const int bb = b0 + lane;
-      int C = 0;
-      if (bb < B) {
-        const int r0 = cu[bb], r1 = cu[bb + 1];
-        C = (r0 >= 0 && r1 <= total_q && r1 > r0) ? r1 - r0 : 0;
+      int C, Lc, nb;
+      seq_at(b0 + lane, C, Lc, nb);
+      n_units += wave_total(nb);
+      int x = nb > 0 ? Lc : 0;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+      lmax = max(lmax, uniform(x));
+    }
+    if (unit < n_units) {
+      // largest w with count_ge(w) > unit: the unit's kv_end
+      int lo = 0, hi = lmax + 1, c_hi = 0;     // count_ge(lo) > unit >= count_ge(hi)
+      while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        const int c = count_ge(mid);
+        if (c > unit) {
+          lo = mid;
+        } else {
+          hi = mid;
+          c_hi = c;
+        }
       }
-      const int nb = (C + TPW - 1) / TPW;
-      const int incl = run + wave_incl_scan(nb, lane);
-      const uint64_t hit = __ballot(bb < B && incl > unit);
-      if (hit) {
-        const int f = uniform(__builtin_ctzll(hit));
-        b = b0 + f;
-        const int nbf = __builtin_amdgcn_readlane(nb, f);
-        const int excl = __builtin_amdgcn_readlane(incl - nb, f);
-        qb = nbf - 1 - (unit - excl);
-        break;
+      // the unit is number j among those with kv_end == lo, by sequence
+      const int j = unit - c_hi;
+      int run = 0;
+      for (int b0 = 0; b0 < B; b0 += 64) {
+        int C, Lc, nb;
+        seq_at(b0 + lane, C, Lc, nb);
+        const int top = n_ge(C, Lc, nb, lo);
+        const int eq = top - n_ge(C, Lc, nb, lo + 1);
+        const int incl = run + wave_incl_scan(eq, lane);
+        const uint64_t hit = __ballot(b0 + lane < B && incl > j);
+        if (hit) {
+          const int f = uniform(__builtin_ctzll(hit));
+          b = b0 + f;
+          const int excl = __builtin_amdgcn_readlane(incl - eq, f);
+          qb = __builtin_amdgcn_readlane(nb - top, f) + (j - excl);
+          break;
+        }
+        run = uniform(__builtin_amdgcn_readlane(incl, 63));
       }
-      run = uniform(__builtin_amdgcn_readlane(incl, 63));
     }
   }
   if (b < 0) return;                           // the whole workgroup: no unit
