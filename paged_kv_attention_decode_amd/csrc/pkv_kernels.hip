@@ -52,6 +52,29 @@ namespace pkv {
 // (whole-line stores made no difference; streaming stores did).
 template <typename T>
 __device__ __forceinline__ void store_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
+// The new token's V codes of a lane (NPL dims, element indexes x[i]; each
+// in its own 16-byte group).  int4 codes share their byte with a neighbouring
+// token, so the old bytes are loaded first, all of them before any store (a
+// load after a store would wait for the store as well).
+template <int KVT, int NPL>
+__device__ __forceinline__ void put_row_codes_nt(void* base, const size_t (&x)[NPL], const uint32_t (&c)[NPL]) {
+  if constexpr (Kv<KVT>::BITS == 4) {
+    uint8_t* b = static_cast<uint8_t*>(base);
+    uint8_t old[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) old[i] = b[x[i] >> 1];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int sh = 4 * (int)(x[i] & 1);
+      store_nt(b + (x[i] >> 1), (uint8_t)((old[i] & ~(0xF << sh)) | ((c[i] & 0xFu) << sh)));
+    }
+  } else {
+    typedef typename Kv<KVT>::elem_t T;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) store_nt(static_cast<T*>(base) + x[i], (T)c[i]);
+  }
+}
+
 template <int KVT>
 __device__ __forceinline__ void put_code_nt(void* base, size_t x, uint32_t c) {
   typedef typename Kv<KVT>::elem_t T;
@@ -270,6 +293,17 @@ __device__ __forceinline__ void requant_k(uint8_t* pool, int j, int P, const uin
   }
 }
 
+// Masks of a run of four consecutive elements of BITS bits starting at bit o
+// of a word, whose tokens are k0 .. k0 + 3 places after slot j (k = j - first
+// token of the run): elements before j go into lt, the one at j into eq.
+template <int BITS>
+__device__ __forceinline__ void run_masks(int k, int o, uint32_t& lt, uint32_t& eq) {
+  constexpr uint32_t RUN = BITS == 8 ? 0xFFFFFFFFu : 0xFFFFu, EL = (1u << BITS) - 1u;
+  const int n = min(max(k, 0), 4);
+  lt |= (n == 4 ? RUN : ((1u << (BITS * n)) - 1u)) << o;
+  if (k >= 0 && k < 4) eq |= EL << (BITS * k + o);
+}
+
 // Re-encode a V chunk for a scale change at slot j: a 16-byte group holds E
 // tokens of one dim from one TB = 4E token block; blocks 0 .. j/TB are
 // rewritten group by group.  Blocks before j's hold earlier slots only and are
@@ -303,25 +337,23 @@ __device__ __forceinline__ void requant_v(uint8_t* pool, int j, const uint8_t* l
 #pragma unroll
         for (int q = 0; q < 4; ++q) r[q] = lut4(lut, w[i][q]);
       } else {
+        // element e of the group holds token 16 (e / 4) + 4c + e % 4 of the
+        // block: each word holds runs of four consecutive tokens (one run of
+        // bytes, or two runs of nibbles 16 tokens apart), so per word the
+        // elements before j, at j and after j are three bit masks
         const int rem = gi - blk * GPB;
         const int c = rem / D, d = rem - c * D;
-        const uint32_t fresh = nbj[d];
+        const uint32_t fresh = nbj[d] * (BITS == 4 ? 0x11111111u : 0x01010101u);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t re = lut4(lut, w[i][q]);
-          uint32_t outw = 0;
-          constexpr int PW = 32 / BITS;                  // elements per word
-#pragma unroll
-          for (int x = 0; x < PW; ++x) {
-            // element e of the group holds token 16 * (e / 4) + 4c + e % 4 of the block
-            const int e = PW * q + x;
-            const int tok = blk * TB + 16 * (e >> 2) + 4 * c + (e & 3);
-            constexpr uint32_t M = (1u << BITS) - 1u;
-            const uint32_t code = tok < j ? (re >> (BITS * x)) & M
-                                : tok == j ? fresh : (w[i][q] >> (BITS * x)) & M;
-            outw |= code << (BITS * x);
+          uint32_t lt = 0, eq = 0;
+          if constexpr (BITS == 4) {
+            run_masks<4>(j - (blk * TB + 32 * q + 4 * c), 0, lt, eq);
+            run_masks<4>(j - (blk * TB + 32 * q + 16 + 4 * c), 16, lt, eq);
+          } else {
+            run_masks<8>(j - (blk * TB + 16 * q + 4 * c), 0, lt, eq);
           }
-          r[q] = outw;
+          r[q] = (lut4(lut, w[i][q]) & lt) | (fresh & eq) | (w[i][q] & ~(lt | eq));
         }
       }
       store_nt(reinterpret_cast<u32x4_t*>(pool + (size_t)gi * 16), r);
@@ -411,8 +443,10 @@ __device__ __forceinline__ void quant_store_row(const float (&xk)[D / 64], const
     __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
     requant_v<KVT, D>(vp, j, lutv, nb, lane);
   } else {
+    size_t xv[NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) put_code_nt<KVT>(vp, v_elem<E>(j, d0 + i, D), nbv[i]);   // own bytes
+    for (int i = 0; i < NPL; ++i) xv[i] = v_elem<E>(j, d0 + i, D);
+    put_row_codes_nt<KVT, NPL>(vp, xv, nbv);   // own codes
   }
   if (lane == 0) {
     kscales[si] = sk;
@@ -461,8 +495,10 @@ __device__ __forceinline__ void quant_store_half(const float (&x)[D / 64], int j
       __builtin_amdgcn_wave_barrier();
       requant_v<KVT, D>(pc, j, lutb, nb, lane);
     } else {
+      size_t xv[NPL];
 #pragma unroll
-      for (int i = 0; i < NPL; ++i) put_code_nt<KVT>(pc, v_elem<E>(j, d0 + i, D), nbc[i]);   // own bytes
+      for (int i = 0; i < NPL; ++i) xv[i] = v_elem<E>(j, d0 + i, D);
+      put_row_codes_nt<KVT, NPL>(pc, xv, nbc);   // own codes
     }
   }
   if (lane == 0) scales[si] = sc;
@@ -1240,10 +1276,29 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const size_t ch = chunk_elem(d.z, g, Hkv, P, D);
     if (lane < ngrp)
       store_nt(reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(kpool) + elem_byte<KVT>(ch + k_elem<E>(j, lane * E, P))), kgrp);
+    if constexpr (Kv<KVT>::BITS == 4) {
+      // int4: each code shares its byte with a neighbouring token; both old
+      // bytes are loaded before either store (clamped index: in bounds)
+      uint8_t* vb = static_cast<uint8_t*>(vpool);
+      size_t xv[2];
+      uint8_t old[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {                 // each dim's V element lies in its own byte
-      const int dd = lane + 64 * i;
-      if (dd < D) put_code_nt<KVT>(vpool, ch + v_elem<E>(j, dd, D), vv[i]);
+      for (int i = 0; i < 2; ++i) {
+        xv[i] = ch + v_elem<E>(j, min(lane + 64 * i, D - 1), D);
+        old[i] = vb[xv[i] >> 1];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int sh = 4 * (int)(xv[i] & 1);
+        if (lane + 64 * i < D)
+          store_nt(vb + (xv[i] >> 1), (uint8_t)((old[i] & ~(0xF << sh)) | ((vv[i] & 0xFu) << sh)));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {               // each dim's V element lies in its own byte
+        const int dd = lane + 64 * i;
+        if (dd < D) put_code_nt<KVT>(vpool, ch + v_elem<E>(j, dd, D), vv[i]);
+      }
     }
   }
 }
