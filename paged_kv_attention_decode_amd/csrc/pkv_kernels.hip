@@ -454,16 +454,17 @@ __device__ __forceinline__ void quant_store_row(const float (&xk)[D / 64], const
   }
 }
 
-// One row (K if !IS_V, else V) of the quantising append into slot j of its
-// page: the row's page scale, its codes, the re-encode of slots [0, j) when
-// the scale rises, the new scale.  The K and V rows are independent (own
-// scales and tables), so the quantising step's merge kernel gives each its
-// own wave.  pc points at the page's K or V chunk, si indexes its scale, s0 is
-// the scale before this append (ignored for slot 0); lut (64 words) and nb (D
-// bytes) are the wave's LDS scratch.
+// One row (K if !IS_V, else V) of the quantising step's append into slot j
+// of its page: the row's page scale, its codes, the new scale.  When the
+// scale rises, the split kernel has already stored the page as the append
+// leaves it (slots [0, j) re-encoded, slot j's new codes), so only the scale
+// is written here.  The K and V rows are independent (own scales), so the
+// merge kernel gives each its own wave.  pc points at the page's K or V
+// chunk, si indexes its scale, s0 is the scale before this append (ignored
+// for slot 0).
 template <int KVT, int D, bool IS_V>
 __device__ __forceinline__ void quant_store_half(const float (&x)[D / 64], int j, uint8_t* pc, int P, float* scales,
-                                                 size_t si, float s0, uint32_t* lut, uint8_t* nb, int lane) {
+                                                 size_t si, float s0, int lane) {
   constexpr int NPL = D / 64, E = 128 / Kv<KVT>::BITS;
   const int d0 = lane * NPL;
   if (j == 0) s0 = 1.f;
@@ -471,29 +472,18 @@ __device__ __forceinline__ void quant_store_half(const float (&x)[D / 64], int j
   s0 = fbits(uniform((int)ubits(s0)));
   bool r;
   const float sc = page_scale<KVT>(a, j, s0, r);
-  uint32_t nbc[NPL];
+  if (!r) {
+    uint32_t nbc[NPL];
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) nbc[i] = ByteFmt<KVT>::enc(x[i] / sc);
-  const uint8_t* lutb = reinterpret_cast<const uint8_t*>(lut);
-  if (r) {
-    lut[lane] = requant4<KVT>((uint32_t)(4 * lane) * 0x01010101u + 0x03020100u, s0, sc);   // 4 codes per lane
-    __builtin_amdgcn_wave_barrier();     // one wave's LDS operations complete in order
-  }
-  if constexpr (!IS_V) {
-    if (r) requant_k<KVT, D>(pc, j, P, lutb, lane);
-    uint8_t* kt = pc + elem_byte<KVT>(k_elem<E>(j, d0, P));
-    if constexpr (KVT == KV_INT4)
-      store_nt(kt, (uint8_t)(nbc[0] | (nbc[NPL - 1] << 4)));
-    else if constexpr (NPL == 2)
-      store_nt(reinterpret_cast<uint16_t*>(kt), (uint16_t)(nbc[0] | (nbc[NPL - 1] << 8)));
-    else
-      store_nt(kt, (uint8_t)nbc[0]);
-  } else {
-    if (r) {
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) nb[d0 + i] = (uint8_t)nbc[i];
-      __builtin_amdgcn_wave_barrier();
-      requant_v<KVT, D>(pc, j, lutb, nb, lane);
+    for (int i = 0; i < NPL; ++i) nbc[i] = ByteFmt<KVT>::enc(x[i] / sc);
+    if constexpr (!IS_V) {
+      uint8_t* kt = pc + elem_byte<KVT>(k_elem<E>(j, d0, P));
+      if constexpr (KVT == KV_INT4)
+        store_nt(kt, (uint8_t)(nbc[0] | (nbc[NPL - 1] << 4)));
+      else if constexpr (NPL == 2)
+        store_nt(reinterpret_cast<uint16_t*>(kt), (uint16_t)(nbc[0] | (nbc[NPL - 1] << 8)));
+      else
+        store_nt(kt, (uint8_t)nbc[0]);
     } else {
       size_t xv[NPL];
 #pragma unroll
@@ -801,6 +791,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) vr[dt] = ld16_stream(vb + 256 * dt);
     };
+    // the quantising step's stores of a re-encoded tile (same addresses)
+    auto store_k = [&](int pg, int j) {
+      uint8_t* kc = const_cast<uint8_t*>(kpool) + elem_byte<KVT>(chunk_elem(pg, g, Hkv, P, D)) + 16 * (size_t)j;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        uint8_t* kb = kc + (size_t)(64 * P * kk) + k_lane;
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) store_nt(reinterpret_cast<u32x4_t*>(kb + 256 * sub), kr[sub][kk]);
+      }
+    };
+    auto store_v = [&](int pg, int j) {
+      uint8_t* vb = const_cast<uint8_t*>(vpool) + elem_byte<KVT>(chunk_elem(pg, g, Hkv, P, D)) +
+                    (size_t)j * (D * BITS / 8) + v_lane;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) store_nt(reinterpret_cast<u32x4_t*>(vb + 256 * dt), vr[dt]);
+    };
     int page = (have_next && pgi == 0) ? page_next : page_of(pgi);
     // The segment after this one, if the wave has one, starts at token 0 of kv
     // head g + 1 of this sequence or of kv head 0 of the next sequence with
@@ -927,23 +933,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       const int pg_ld_n = bad_n ? 0 : page_n;
       // quantising step: a tile of the last page takes the appended view of it
       const bool fixp = QNEW && (LAST ? qfix && pgi == lp : FIX);
+      // slot jl of the last page, relative to this tile's first token: codes of
+      // earlier slots are re-encoded, later ones (masked out of the attention)
+      // keep their bytes, since a rising scale's tiles are stored back below
+      const int jrel = jl - j0;
       if constexpr (QNEW) {
         if (fixp && !qready) qprep();
         if (fixp && qrk) {
           const uint8_t* lut = reinterpret_cast<const uint8_t*>(s_lut[wv][0]);
 #pragma unroll
-          for (int sub = 0; sub < NSUB; ++sub)
+          for (int sub = 0; sub < NSUB; ++sub) {
+            const bool before = 16 * sub + r16 < jrel;     // token of the lane's K groups
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-              for (int x = 0; x < 4; ++x) kr[sub][kk][x] = lut4(lut, kr[sub][kk][x]);
+              for (int x = 0; x < 4; ++x) {
+                const uint32_t m = lut4(lut, kr[sub][kk][x]);
+                kr[sub][kk][x] = before ? m : kr[sub][kk][x];
+              }
+          }
         }
         if (fixp && qrv) {
           const uint8_t* lut = reinterpret_cast<const uint8_t*>(s_lut[wv][1]);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) vr[dt][x] = lut4(lut, vr[dt][x]);
+            for (int x = 0; x < 4; ++x) {
+              // element e of the lane's group holds token 16 (e / 4) + 4 c4 + e % 4
+              uint32_t lt = 0, eq = 0;
+              if constexpr (I4) {
+                run_masks<4>(jrel - (32 * x + 4 * c4), 0, lt, eq);
+                run_masks<4>(jrel - (32 * x + 16 + 4 * c4), 16, lt, eq);
+              } else {
+                run_masks<8>(jrel - (16 * x + 4 * c4), 0, lt, eq);
+              }
+              vr[dt][x] = (lut4(lut, vr[dt][x]) & lt) | (vr[dt][x] & ~lt);
+            }
         }
       }
       const float kmul = scale_log2 * (fixp ? qsk : ksc), vmul = fixp ? qsv : vsc;
@@ -985,6 +1010,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
               }
             }
           }
+        }
+      }
+
+      // quantising step, a scale that rises: this tile of the last page is stored
+      // back as the append leaves it (re-encoded slots, the new token, later
+      // slots unchanged), so the merge kernel writes only the scale
+      if constexpr (QNEW) {
+        if (fixp && (qrk || qrv) && (unsigned)pgl < (unsigned)NP) {
+          if (qrk) store_k(pgl, j0);
+          if (qrv) store_v(pgl, j0);
         }
       }
 
@@ -1314,8 +1349,6 @@ __global__ __launch_bounds__(256) void decode_merge_quant_kernel(
     int new_bf16, uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool, float* __restrict__ kscales,
     float* __restrict__ vscales, const int4* __restrict__ qdescs, int NP, int P) {
   constexpr int NPL = D / 64;
-  __shared__ uint8_t s_nb[4][D];        // the new V row's codes (V pass of a re-encode)
-  __shared__ uint32_t s_lut[4][2][64];  // re-encode tables, K and V
   const int wv = uniform(threadIdx.x >> 6);
   const int wi = uniform(blockIdx.x * 4 + wv);
   // nchunk merging waves and two appending waves (K, V) per (b, g), so the
@@ -1349,10 +1382,10 @@ __global__ __launch_bounds__(256) void decode_merge_quant_kernel(
     const size_t si = (size_t)d.z * Hkv + g;
     if (app_v)
       quant_store_half<KVT, D, true>(x, (L - 1) % P, vpool + elem_byte<KVT>(ch), P, vscales, si,
-                                     fbits((uint32_t)qd.y), s_lut[wv][0], s_nb[wv], lane);
+                                     fbits((uint32_t)qd.y), lane);
     else
       quant_store_half<KVT, D, false>(x, (L - 1) % P, kpool + elem_byte<KVT>(ch), P, kscales, si,
-                                      fbits((uint32_t)qd.x), s_lut[wv][0], s_nb[wv], lane);
+                                      fbits((uint32_t)qd.x), lane);
   }
 }
 
