@@ -28,8 +28,10 @@
 //   operand feeds two MFMAs (one per N tile).  The workgroups of a kv head g are
 //   blockIdx = g (mod Hkv), so with eight kv heads all readers of one head's
 //   pages run on one XCD and share its L2.
-// * Workgroups are dispatched longest first (by the keys their rows reach,
-//   over all sequences), so the long ones do not start late and leave a tail.
+// * Workgroups are dispatched longest sequence first, and within a sequence
+//   from its last (longest-range) block to its first: the long ones do not
+//   start late and leave a tail, and the blocks of one sequence, which read
+//   the same pages, run close together and share them in L2.
 // * S^T = K Q^T leaves four tokens of one query row per lane, which is the
 //   B-operand layout of O^T += V^T P^T: probabilities never cross lanes.  They
 //   enter the MFMA as one bf16 value (round to nearest even); the row sums come
@@ -239,12 +241,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
   const int unit = uniform((int)(blockIdx.x / (unsigned)Hkv));
 
   // ---- (sequence, token block) of this workgroup (same in every wave) ---------
-  // Units (b, qb) are taken longest first: unit number u (from blockIdx) is the
-  // u-th in descending order of the keys the block reads, kv_end(b, qb) =
-  // max(ctx_b + min(C_b, TPW (qb + 1)), 0), ties by sequence then block.  The
-  // blocks of sequence b: ceil(C_b / TPW), kv_end rising with qb, so those with
-  // kv_end >= w are its last n_b(w) blocks, n_b(w) in closed form; a binary
-  // search over w finds the u-th key, then a scan over the sequences the unit.
+  // Unit number u (from blockIdx) is the u-th block in this order: sequences
+  // by length L_b descending (ties by index), each sequence's ceil(C_b / TPW)
+  // blocks from the last to the first.  With n(w) = the blocks of sequences
+  // with L_b >= w, a binary search over w finds the length of unit u's
+  // sequence, then a scan over the sequences of that length finds it.
   // Lengths are clamped to the table's reach for the ordering only.
   const int cap = (int)min((int64_t)MP * P, (int64_t)1 << 30);
   auto seq_at = [&](int bb, int& C, int& Lc, int& nb) {
@@ -257,15 +258,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
     }
     nb = (C + TPW - 1) / TPW;
   };
-  // blocks of one sequence with kv_end >= w
-  auto n_ge = [&](int C, int Lc, int nb, int w) -> int {
-    if (w <= 0) return nb;
-    if (nb == 0 || Lc < w) return 0;
-    const int y = w - (Lc - C);                // rows the block must reach: TPW (qb + 1) >= y
-    return y <= TPW ? nb : nb - ((y + TPW - 1) / TPW - 1);
-  };
+  // blocks of one sequence counted by n(w)
+  auto n_ge = [&](int C, int Lc, int nb, int w) -> int { return (w <= 0 || Lc >= w) ? nb : 0; };
   auto wave_total = [&](int v) -> int { return uniform(__builtin_amdgcn_readlane(wave_incl_scan(v, lane), 63)); };
-  // all units with kv_end >= w (wave-uniform)
+  // n(w), over all sequences (wave-uniform)
   auto count_ge = [&](int w) -> int {
     int tot = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
@@ -288,7 +284,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
       lmax = max(lmax, uniform(x));
     }
     if (unit < n_units) {
-      // largest w with count_ge(w) > unit: the unit's kv_end
+      // largest w with n(w) > unit: the length of the unit's sequence
       int lo = 0, hi = lmax + 1, c_hi = 0;     // count_ge(lo) > unit >= count_ge(hi)
       while (hi - lo > 1) {
         const int mid = lo + (hi - lo) / 2;
@@ -300,7 +296,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
           c_hi = c;
         }
       }
-      // the unit is number j among those with kv_end == lo, by sequence
+      // the unit is number j among the blocks of sequences of length lo, by sequence
       const int j = unit - c_hi;
       int run = 0;
       for (int b0 = 0; b0 < B; b0 += 64) {
@@ -314,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
           const int f = uniform(__builtin_ctzll(hit));
           b = b0 + f;
           const int excl = __builtin_amdgcn_readlane(incl - eq, f);
-          qb = __builtin_amdgcn_readlane(nb - top, f) + (j - excl);
+          qb = __builtin_amdgcn_readlane(nb, f) - 1 - (j - excl);   // last block first
           break;
         }
         run = uniform(__builtin_amdgcn_readlane(incl, 63));
