@@ -429,11 +429,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
   auto slice = [&](int buf, int op) -> u32x4_t {
     return *(lds_u32x4_t*)(&s_kv[buf][op][lane]);
   };
-  // 8 bytes (one half) of a lane's slice: fp8 V groups hold the tokens of both
-  // halves of a tile, and each half reads only its own
-  auto slice_half = [&](int buf, int op, int h) -> u32x2_t {
-    return *((lds_u32x2_t*)(&s_kv[buf][op][lane]) + h);
-  };
 
   // 32 keys (half h of the tile) from buffer buf.  masked (wave-uniform): the
   // keys reach past the wave's first row position (causal mask).  One body for
@@ -442,6 +437,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
   // position get p = 0; V of slots at or past L (which may hold anything) was
   // zeroed in LDS when the tile arrived.  ksl: the softmax scale times the
   // tile's K scale (log2 domain); vs: the tile's V scale (fp8, else 1).
+  u32x2_t vhi[NDT];            // fp8: the second half's bytes of each V group
   auto tile = [&](const int t, const int buf, const bool masked, const int h, const float ksl, const float vs) {
     // ---- S^T = K Q^T: rows = 16 tokens, columns = query rows (unscaled) ------
     f32x4_t acc[2][NT];
@@ -545,7 +541,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVT == KV_F
     for (int dt = 0; dt < NDT; ++dt) {
       u32x4_t vv;
       if constexpr (FP8) {
-        const u32x2_t w = slice_half(buf, NKOP + dt, h);
+        // the first half reads the whole 16-byte group (conflict-free) and
+        // keeps the second half's 8 bytes for it
+        u32x2_t w;
+        if (h == 0) {
+          const u32x4_t f = slice(buf, NKOP + dt);
+          w = u32x2_t{f.x, f.y};
+          vhi[dt] = u32x2_t{f.z, f.w};
+        } else {
+          w = vhi[dt];
+        }
         vv = byte8_to_bf16x8<KV_FP8>(w.x, w.y);
       } else {
         vv = slice(buf, NKOP + dt);
