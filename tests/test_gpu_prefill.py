@@ -133,6 +133,9 @@ PREFILL_CASES = [  # (ctx, chunk, Hq, Hkv, D, P)
     ([100], [40], 32, 2, 128, 64),                                # G 16
     ([70, 1], [90, 130], 6, 2, 128, 32),                          # G 3: padding rows in every block
     ([0, 0, 0], [1, 2, 300], 8, 2, 128, 64),                      # pure prefill (no cached tokens)
+    ([5, 60], [33, 2], 32, 1, 128, 64),                           # G 32: 4 chunk tokens per block
+    ([40, 3], [9, 5], 64, 1, 128, 64),                            # G 64: 2 chunk tokens per block
+    ([17], [7], 128, 1, 64, 32),                                  # G 128, the largest: 1 token per block
 ]
 
 
@@ -319,6 +322,8 @@ FP8_CASES = [  # (ctx, chunk, Hq, Hkv, D, P)
     ([100], [40], 32, 2, 128, 64),
     ([70, 1], [90, 130], 6, 2, 128, 64),
     ([0, 0, 0], [1, 2, 300], 8, 2, 128, 64),
+    ([40, 3], [9, 5], 64, 1, 128, 64),
+    ([17], [7], 128, 1, 128, 64),
 ]
 
 
