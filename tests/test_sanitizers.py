@@ -3,7 +3,7 @@
 Two builds, each in a child process with the ASan runtime preloaded (leak
 checking off: the Python interpreter itself is not instrumented), so that an
 out-of-bounds access, use-after-free or undefined operation aborts the run
-instead of silently corrupting a verdict:
+instead of silently corrupting a parity result:
 
 * the C oracle (pkv_oracle.c), rebuilt with -fsanitize=address,undefined and
   selected through PKV_ORACLE_LIB, runs the oracle pins that call it
