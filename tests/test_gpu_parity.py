@@ -200,6 +200,11 @@ EDGE = [
          q_mult=3.0),
     dict(seed=64, lens=_gappy_lens(600, 64), Hq=8, Hkv=2, D=64, P=32, kv_dtype="bf16"),
     dict(seed=65, lens=_gappy_lens(400, 65), Hq=32, Hkv=8, D=128, P=64, kv_dtype="fp8", out_dtype="f32"),
+    # the largest pages the boundary accepts (1024 tokens) and 512
+    dict(seed=90, lens=[1, 1023, 1024, 1025, 3000], Hq=32, Hkv=8, D=128, P=1024, kv_dtype="bf16"),
+    dict(seed=91, lens=[100, 512, 513, 2049], Hq=16, Hkv=4, D=64, P=512, kv_dtype="bf16", out_dtype="f32"),
+    dict(seed=92, lens=[64, 1024, 1500], Hq=32, Hkv=8, D=128, P=1024, kv_dtype="fp8"),
+    dict(seed=93, lens=[128, 1025, 2048], Hq=16, Hkv=4, D=128, P=1024, kv_dtype="i4", out_dtype="f32"),
 ]
 
 
@@ -427,6 +432,8 @@ STEP_CASES = [
     dict(seed=77, lens=[1, 63, 64, 65, 129, 700], Hq=32, Hkv=8, D=128, P=64, kv_dtype="i8"),
     dict(seed=78, lens=[1, 127, 128, 129, 257, 700], Hq=32, Hkv=8, D=128, P=128, kv_dtype="i4"),
     dict(seed=79, lens=_gappy_lens(300, 79), Hq=16, Hkv=4, D=128, P=64, kv_dtype="bf16"),
+    dict(seed=80, lens=[1, 1023, 1024, 1025, 2500], Hq=32, Hkv=8, D=128, P=1024, kv_dtype="bf16"),
+    dict(seed=83, lens=[1, 1023, 1024, 1025], Hq=32, Hkv=8, D=128, P=1024, kv_dtype="i8"),
 ]
 
 
