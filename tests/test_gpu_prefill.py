@@ -136,6 +136,7 @@ PREFILL_CASES = [  # (ctx, chunk, Hq, Hkv, D, P)
     ([5, 60], [33, 2], 32, 1, 128, 64),                           # G 32: 4 chunk tokens per block
     ([40, 3], [9, 5], 64, 1, 128, 64),                            # G 64: 2 chunk tokens per block
     ([17], [7], 128, 1, 64, 32),                                  # G 128, the largest: 1 token per block
+    ([20000, 0], [64, 1100], 8, 1, 128, 1024),                    # 1024-token pages, a long cached context
 ]
 
 
@@ -324,6 +325,7 @@ FP8_CASES = [  # (ctx, chunk, Hq, Hkv, D, P)
     ([0, 0, 0], [1, 2, 300], 8, 2, 128, 64),
     ([40, 3], [9, 5], 64, 1, 128, 64),
     ([17], [7], 128, 1, 128, 64),
+    ([3000, 10], [50, 700], 8, 2, 128, 1024),
 ]
 
 
